@@ -1,0 +1,69 @@
+"""Pins of the token-budget policy oracle (CPU only).
+
+The paged simulation is checked against a second formulation that keeps one
+flat list of token ids (no pages, no compaction), and against the size bound.
+"""
+
+import numpy as np
+
+from oracle import budget, clces
+
+
+def _scores(n_tokens, n_layers, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.lognormal(0, 0.5, n_tokens)
+    return np.sqrt(u[:, None] * rng.chisquare(64, (n_tokens, n_layers))).astype(np.float32)
+
+
+def test_paged_policy_matches_flat_list():
+    T, B, frames, L, W = 8, 20, 12, 6, 5
+    table = _scores(T * frames, L, seed=1)
+    for layer in range(L):
+        c = budget.BudgetCache(layer, T, B, num_pages=frames, window=W, lam=0.5)
+        flat = np.zeros(0, np.int64)
+        for t in range(frames):
+            c.append(t)
+            flat = np.concatenate([flat, t * T + np.arange(T)])
+            ran = c.score_and_compact(table)
+            if len(flat) > B:
+                assert ran
+                lw = clces.window_layers(layer, W)
+                res = clces.clces(np.stack([table[flat, l] for l in lw]), 0.5)
+                flat = flat[clces.topk_keep(res["s_hat"], B)]
+            else:
+                assert not ran
+            np.testing.assert_array_equal(c.all_ids(), flat)
+            assert len(c.all_ids()) <= max(B, T)
+            # bookkeeping: unique ids, no empty page, free + used = pool
+            pids = [p for p, _, _ in c.page_table()]
+            assert len(set(pids)) == len(pids)
+            assert all(n > 0 for _, _, n in c.page_table())
+            assert set(pids) | c.free == set(range(frames))
+            # page order follows frame order and ids inside a page stay sorted
+            fr = [f for _, f, _ in c.page_table()]
+            assert fr == sorted(fr)
+            for _, f, ids in c.table:
+                assert (np.diff(ids) > 0).all() and (ids // T == f).all()
+
+
+def test_scale_frames_are_never_scored():
+    T, B, frames = 4, 6, 9
+    table = _scores(T * frames, 1, seed=2)
+    c = budget.BudgetCache(0, T, B, num_pages=frames, window=5, lam=0.5, scale_frames=2)
+    for t in range(frames):
+        c.append(t)
+        c.score_and_compact(table)
+        ids = c.all_ids()
+        if t >= 1:
+            assert list(ids[:2 * T]) == list(range(2 * T))
+        assert len(c.candidate_ids()) <= max(B, T)
+
+
+def test_budget_step_keeps_exactly_budget():
+    T, B = 10, 25
+    table = _scores(T * 5, 3, seed=3)
+    c = budget.BudgetCache(2, T, B, num_pages=5)
+    for t in range(5):
+        c.append(t)
+        c.score_and_compact(table)
+        assert len(c.all_ids()) == min((t + 1) * T, B) if (t + 1) * T > B else (t + 1) * T
