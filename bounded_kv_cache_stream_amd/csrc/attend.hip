@@ -1,0 +1,326 @@
+// Frame-to-cache attention over a paged KV cache, gfx950.
+//
+// Computes, per query row i and head h, softmax(sm_scale * q_i . k_j) v_j over
+// every token j of a layer's attended page list (GCTStream explainer,
+// "Frame-by-Frame Causal Processing": each new frame attends to the cached
+// keys/values of earlier frames; "Scale-Frame Phase": the first frames attend
+// to each other).  No token mask: a frame sees all of its own tokens.
+//
+// bf16 path (the hot one): flash-style online softmax with both contractions
+// on MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+//   * workgroup = 4 waves = 128 query rows of one head; each wave owns 32 rows;
+//   * KV streamed in 64-token tiles, staged through LDS (K as [key][d], V as
+//     [d][key] -- the page already stores V transposed, so both LDS reads that
+//     feed the MFMAs are single 16-byte reads);
+//   * scores are computed transposed, S^T = K Q^T, so each lane's accumulator
+//     column is one query: the row max / row sum need one cross-lane exchange
+//     (lane l with l^32), the O rescale is lane-local, and the accumulator
+//     registers are directly the B operand of O^T += V^T P^T.  For that, the
+//     A-operand row m of the K read is taken from key pi(m) with
+//     pi(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3), which makes the
+//     8 probabilities a lane holds for one 16-key MFMA step 8 consecutive keys;
+//   * the KV axis is split across workgroups (split-KV); partial (O, m, l) are
+//     merged by attend_combine.  Workgroup ids are remapped so that all query
+//     tiles of one (head, split) land on the same XCD and share its L2.
+// fp32 path: one wave per (query, head), lanes over d -- a plain reference-
+// grade kernel for fp32 caches.
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace kvs {
+namespace {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = kHeadDim;
+constexpr int BM = 128;      // query rows per workgroup
+constexpr int BN = kTile;    // keys per tile
+constexpr int LDS_LD = 72;   // bf16 per LDS row (64 + 8 pad)
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ inline int perm_key(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+
+// Bijective XCD-aware remap: consecutive logical ids land on one XCD.
+__device__ inline int xcd_remap(int bid, int nwg) {
+  const int nx = 8;
+  int xcd = bid % nx, round = bid / nx;
+  int base = nwg / nx, extra = nwg % nx;
+  int start = xcd * base + (xcd < extra ? xcd : extra);
+  return start + round;
+}
+
+__device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__global__ __launch_bounds__(256) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * LDS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[D * LDS_LD];
+
+  const int H = g.heads;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = logical % qtiles;
+  const int rest = logical / qtiles;
+  const int sp = rest % p.splits;
+  const int h = rest / p.splits;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int ql = lane & 31;
+  const int grp = lane >> 5;
+  const int qrow = qt * BM + wave * 32 + ql;
+  const bool qvalid = qrow < p.n_q;
+
+  const bf16* q = static_cast<const bf16*>(p.q);
+  bf16x8 qf[4];
+  if (qvalid) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((int64_t)qrow * H + h) * D);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = src[2 * ks + grp];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8{};
+  }
+
+  const int t_begin = (int)((int64_t)sp * p.total_tiles / p.splits);
+  const int t_end = (int)((int64_t)(sp + 1) * p.total_tiles / p.splits);
+
+  // entry holding tile t_begin (binary search on tile_start)
+  int e = 0;
+  {
+    int lo = 0, hi = p.n_entries - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (p.table[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+  }
+
+  f32x16 oacc[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; }
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int lrow = tid >> 3;  // 0..31
+  const int lchunk = tid & 7; // 8-element chunk
+  const int64_t head_k = (int64_t)h * g.ts * D;       // elements
+  const int64_t head_v = (int64_t)h * D * g.ts;       // elements
+
+  bf16x8 kreg[2], vreg[2];
+  int cur_nvalid = 0;
+  auto load_tile = [&](int t, bf16x8* kr, bf16x8* vr) -> int {
+    while (t >= p.table[e].tile_start + ((p.table[e].len + BN - 1) / BN)) ++e;
+    const DevEntry en = p.table[e];
+    const int row0 = (t - en.tile_start) * BN;
+    const int nvalid = min(BN, en.len - row0);
+    const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
+    const bf16* kt = reinterpret_cast<const bf16*>(page + g.k_off) + head_k + (int64_t)row0 * D;
+    const bf16* vt = reinterpret_cast<const bf16*>(page + g.v_off) + head_v + row0;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int r = lrow + 32 * pp;
+      kr[pp] = *reinterpret_cast<const bf16x8*>(kt + r * D + lchunk * 8);
+      bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + (int64_t)r * g.ts + lchunk * 8);
+      if (nvalid < BN) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (lchunk * 8 + i >= nvalid) vv[i] = (bf16)0.f;
+      }
+      vr[pp] = vv;
+    }
+    return nvalid;
+  };
+
+  if (t_begin < t_end) cur_nvalid = load_tile(t_begin, kreg, vreg);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int nvalid = cur_nvalid;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int r = lrow + 32 * pp;
+      *reinterpret_cast<bf16x8*>(&Ks[r * LDS_LD + lchunk * 8]) = kreg[pp];
+      *reinterpret_cast<bf16x8*>(&Vs[r * LDS_LD + lchunk * 8]) = vreg[pp];
+    }
+    __syncthreads();
+    if (t + 1 < t_end) cur_nvalid = load_tile(t + 1, kreg, vreg);
+
+    // S^T = K_pi Q^T : two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      const int krow = 32 * kb + perm_key(ql);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[krow * LDS_LD + ks * 16 + grp * 8]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // key of accumulator register r of block kb: 32*kb + 16*(r>>3) + 8*grp + (r&7)
+    if (nvalid < BN) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 16 * (r >> 3) + 8 * grp + (r & 7) >= nvalid) sacc[kb][r] = -INFINITY;
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m_run, mx * p.scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+
+    float lsum = 0.f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -m_new));
+        lsum += pv;
+        pb[kb][r >> 3][r & 7] = (bf16)pv;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[(32 * db + ql) * LDS_LD + 32 * kb + 16 * s + 8 * grp]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][s], oacc[db], 0, 0, 0);
+        }
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + wave_xor32(l_run);
+  if (!qvalid) return;
+  if (p.splits == 1) {
+    const float inv = 1.f / l_tot;
+    bf16* out = static_cast<bf16*>(p.out) + ((int64_t)qrow * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        bf16x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = (bf16)(oacc[db][rb * 4 + j] * inv);
+        *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * rb + 4 * grp) = o;
+      }
+    if (p.lse && grp == 0) p.lse[(int64_t)qrow * H + h] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+  } else {
+    const int64_t row = ((int64_t)sp * p.n_q + qrow) * H + h;
+    float* po = p.part_o + row * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = oacc[db][rb * 4 + j];
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rb + 4 * grp) = o;
+      }
+    if (grp == 0) {
+      p.part_ml[row * 2 + 0] = m_run;
+      p.part_ml[row * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// Merge split-KV partials: O = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s.
+template <typename OutT>
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p, int H) {
+  const int64_t rows = (int64_t)p.n_q * H;
+  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;  // 4 d values each
+  if (idx >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_ml[(s * rows + idx) * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.splits; ++s) {
+    const float ms = p.part_ml[(s * rows + idx) * 2];
+    const float w = __builtin_amdgcn_exp2f(ms - m);
+    L += w * p.part_ml[(s * rows + idx) * 2 + 1];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + (s * rows + idx) * D + sub * 4);
+    acc += w * o;
+  }
+  const float inv = 1.f / L;
+  OutT* out = static_cast<OutT*>(p.out) + idx * D + sub * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = (OutT)(acc[j] * inv);
+  if (p.lse && sub == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
+}
+
+// fp32 caches: one wave per (query, head); lane = d.
+__global__ __launch_bounds__(256) void attend_f32_kernel(PageGeom g, AttendParams p) {
+  const int H = g.heads;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)p.n_q * H;
+  if (wid >= rows) return;
+  const int qrow = (int)(wid / H), h = (int)(wid % H);
+  const float* q = static_cast<const float*>(p.q);
+  const float qv = q[((int64_t)qrow * H + h) * D + lane];
+  float m_run = -INFINITY, l_run = 0.f, o = 0.f;
+  for (int e = 0; e < p.n_entries; ++e) {
+    const DevEntry en = p.table[e];
+    const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
+    const float* kt = reinterpret_cast<const float*>(page + g.k_off) + (int64_t)h * g.ts * D;
+    const float* vt = reinterpret_cast<const float*>(page + g.v_off) + ((int64_t)h * D + lane) * g.ts;
+    for (int j = 0; j < en.len; ++j) {
+      float s = qv * kt[(int64_t)j * D + lane];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+      const float x = s * p.scale_log2;
+      const float m_new = fmaxf(m_run, x);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float pv = __builtin_amdgcn_exp2f(x - m_new);
+      l_run = l_run * alpha + pv;
+      o = o * alpha + pv * vt[j];
+      m_run = m_new;
+    }
+  }
+  float* out = static_cast<float*>(p.out);
+  out[((int64_t)qrow * H + h) * D + lane] = o / l_run;
+  if (p.lse && lane == 0) p.lse[(int64_t)qrow * H + h] = (m_run + __builtin_log2f(l_run)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s) {
+  if (!bf16) {
+    const int64_t rows = (int64_t)p.n_q * g.heads;
+    attend_f32_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(g, p);
+    return hipGetLastError();
+  }
+  const int qtiles = (p.n_q + BM - 1) / BM;
+  const int64_t nwg = (int64_t)qtiles * g.heads * p.splits;
+  attend_bf16_kernel<<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.splits == 1) return err;
+  const int64_t rows = (int64_t)p.n_q * g.heads;
+  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(p, g.heads);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

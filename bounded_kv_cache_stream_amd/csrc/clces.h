@@ -1,0 +1,50 @@
+// Internal interface of the CLCES scoring + top-k + compaction pipeline.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace kvs {
+
+constexpr int32_t kClcesErrNan = 1;    // a raw score is NaN or negative
+constexpr int32_t kClcesErrRow = 2;    // a token id is outside the score table
+constexpr int32_t kRankTile = 2048;    // keys per radix-sort workgroup
+constexpr int32_t kMaxPageTokensScored = 8192;
+
+// Byte offsets of the CLCES buffers inside its workspace region.
+struct ClcesSizes {
+  int64_t n_max;
+  int32_t p_max, w_max, nblk_max;
+  size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts, plan,
+      flag, total;
+};
+
+ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max);
+
+struct ClcesArgs {
+  char* ws;  // start of the CLCES workspace region
+  ClcesSizes sizes;
+  char* pool;
+  PageGeom geom;
+  const DevEntry* entries_host;  // candidate pages (phys, len, tok_start)
+  int32_t n_entries;
+  int32_t n_tokens;
+  const float* score_table;
+  int64_t score_rows;
+  int32_t score_cols;
+  int32_t first_layer;  // oldest window layer
+  int32_t n_window;
+  double lambda;
+  int64_t keep;
+  int32_t* keep_ids_out;
+  int32_t* ranks_out;
+};
+
+// Enqueues the whole step, then waits for it and returns the new page
+// lengths (one per candidate entry) and the error flags.
+hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s);
+
+}  // namespace kvs

@@ -1,0 +1,588 @@
+// CLCES scoring, top-k keep and page-local compaction, gfx950.
+//
+// StreamCacheVGGT article, section 2.1: per window layer the N candidate
+// tokens are ranked by raw score (2.1.1), the ranks are normalised to [0,1]
+// and their mean / variance over the window give Cons = max(0, 1 -
+// sigma*sqrt(12)) (2.1.2), fused as s_hat = s * (1 + lambda*Cons) (2.1.3).
+// Top-k keep by s_hat and in-place compaction of the kept rows follow the
+// article's "pure eviction" description (section 1) and the InfiniteVGGT
+// explainer ("Rolling Memory", "Prune and roll the memory").
+//
+// Pipeline (one launch each, all on the caller's stream, one final sync):
+//   gather   raw scores of every candidate at every window layer (by global
+//            token id), validate them, write 32-bit order keys;
+//   rank     stable LSD radix sort, 4 passes of 8 bits, all window layers at
+//            once (histogram / scan / scatter; the scatter is made stable
+//            with wave ballots); the last pass writes rank[token] directly;
+//   fuse     float64 mean, population variance, Cons and s_hat with a fixed
+//            operation order and no contraction (bit-exact reproducible);
+//   select   radix select of the keep_count-th largest s_hat (8 passes of 8
+//            bits over the 64-bit pattern, which orders non-negative doubles);
+//   mark     per page: count of s_hat above / equal to the threshold;
+//   plan     per page: rank base among ties (index order), kept count, offset;
+//   compact  one workgroup per (page, K head | V head | token ids): gather the
+//            kept slots to the page's front, in chunks whose reads all finish
+//            before their writes (every source slot is at or after its
+//            destination, so no chunk overwrites data a later chunk reads).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <utility>
+
+#include "clces.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = kRankTile / kThreads;  // 8
+
+struct SelState {
+  unsigned long long prefix;
+  long long k_rem;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+__device__ inline uint32_t order_key(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return b == 0x80000000u ? 0u : b;  // -0.0 ranks as +0.0
+}
+
+__global__ void zero_kernel(uint32_t* sel_hist, int32_t* counts, int n_counts, int32_t* flag) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 8 * 256) sel_hist[i] = 0;
+  if (i < n_counts) counts[i] = 0;
+  if (i == 0) *flag = 0;
+}
+
+struct GatherArgs {
+  const DevEntry* entries;
+  const char* pool;
+  int64_t page_bytes, id_off;
+  const float* table;
+  int64_t rows;
+  int32_t cols, first_layer, n_win, N;
+  uint32_t* keys;  // [n_win][N]
+  float* scur;     // [N]
+  int32_t* flag;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
+  const DevEntry en = g.entries[blockIdx.x];
+  const int j = blockIdx.y * kThreads + threadIdx.x;
+  if (j >= en.len) return;
+  const int32_t* ids = reinterpret_cast<const int32_t*>(g.pool + (int64_t)en.phys * g.page_bytes + g.id_off);
+  const int32_t tok = ids[j];
+  const int idx = en.tok_start + j;
+  if (tok < 0 || (int64_t)tok >= g.rows) {
+    atomicOr(g.flag, kClcesErrRow);
+    return;
+  }
+  const float* row = g.table + (int64_t)tok * g.cols + g.first_layer;
+  float s = 0.f;
+  for (int w = 0; w < g.n_win; ++w) {
+    s = row[w];
+    if (!(s >= 0.f)) atomicOr(g.flag, kClcesErrNan);
+    g.keys[(int64_t)w * g.N + idx] = order_key(s);
+  }
+  g.scur[idx] = __uint_as_float(order_key(s));
+}
+
+__global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* hist, int N, int nblk,
+                                                             int shift, const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t cnt[256];
+  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const uint32_t* k = keys + (int64_t)w * N;
+  for (int j = 0; j < kItems; ++j) {
+    const int i = blk * kRankTile + j * kThreads + tid;
+    if (i < N) atomicAdd(&cnt[(k[i] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  hist[((int64_t)w * 256 + tid) * nblk + blk] = cnt[tid];
+}
+
+// Exclusive scan of one segment's [256][nblk] histogram, in place.
+__global__ __launch_bounds__(1024) void rank_scan_kernel(uint32_t* hist, int nblk, const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t sums[1024];
+  const int tid = threadIdx.x;
+  const int64_t M = 256 * (int64_t)nblk;
+  uint32_t* h = hist + blockIdx.x * M;
+  const int64_t per = (M + 1023) / 1024;
+  const int64_t b = tid * per, e = b + per < M ? b + per : M;
+  uint32_t local = 0;
+  for (int64_t i = b; i < e; ++i) local += h[i];
+  sums[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    uint32_t v = tid >= off ? sums[tid - off] : 0u;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = sums[tid] - local;
+  for (int64_t i = b; i < e; ++i) {
+    uint32_t v = h[i];
+    h[i] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
+                                                                uint32_t* keys_out, uint32_t* vals_out,
+                                                                int32_t* ranks, const uint32_t* hist, int N,
+                                                                int nblk, int shift, int last, const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t base[256], run[256], wcnt[4][256];
+  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  base[tid] = hist[((int64_t)w * 256 + tid) * nblk + blk];
+  run[tid] = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+  __syncthreads();
+  const int64_t seg = (int64_t)w * N;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int j = 0; j < kItems; ++j) {
+    const int i = blk * kRankTile + j * kThreads + tid;
+    const bool valid = i < N;
+    const uint32_t key = valid ? keys_in[seg + i] : 0u;
+    const uint32_t d = (key >> shift) & 255u;
+    const uint32_t val = valid ? (vals_in ? vals_in[seg + i] : (uint32_t)i) : 0u;
+    unsigned long long m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (d >> bit) & 1u;
+      const unsigned long long bb = __ballot(on);
+      m &= on ? bb : ~bb;
+    }
+    const uint32_t rnk = (uint32_t)__popcll(m & lt);
+    if (valid && rnk == 0) wcnt[wave][d] = (uint32_t)__popcll(m);
+    __syncthreads();
+    if (valid) {
+      uint32_t off = base[d] + run[d] + rnk;
+      for (int q = 0; q < wave; ++q) off += wcnt[q][d];
+      if (last) {
+        ranks[seg + val] = (int32_t)off;
+      } else {
+        keys_out[seg + off] = key;
+        vals_out[seg + off] = val;
+      }
+    }
+    __syncthreads();
+    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fuse_kernel(const int32_t* ranks, const float* scur,
+                                                        unsigned long long* shat, int N, int n_win, double lambda,
+                                                        double sqrt12, const int32_t* flag) {
+#pragma clang fp contract(off)
+  if (*flag) return;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= N) return;
+  const double denom = (double)(N - 1);
+  double r[8];
+  double acc = 0.0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    if (w < n_win) {
+      r[w] = N > 1 ? (double)ranks[(int64_t)w * N + i] / denom : 0.0;
+      acc = acc + r[w];
+    }
+  }
+  const double mu = acc / (double)n_win;
+  double acc2 = 0.0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    if (w < n_win) {
+      const double d = r[w] - mu;
+      acc2 = acc2 + d * d;
+    }
+  }
+  const double var = acc2 / (double)n_win;
+  const double sigma = sqrt(var);
+  const double c = 1.0 - sigma * sqrt12;
+  const double cons = c > 0.0 ? c : 0.0;
+  const double sh = (double)scur[i] * (1.0 + lambda * cons) + 0.0;
+  shat[i] = (unsigned long long)__double_as_longlong(sh);
+}
+
+// State after `passes` select passes: digits fixed so far and how many of the
+// elements matching them are still to be taken (from the largest down).
+__device__ SelState select_state(const uint32_t* sel_hist, long long keep, int passes, uint32_t* lds) {
+  __shared__ SelState st;
+  if (threadIdx.x == 0) st = SelState{0ull, keep};
+  __syncthreads();
+  for (int p = 0; p < passes; ++p) {
+    lds[threadIdx.x] = sel_hist[p * 256 + threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == 0 && st.k_rem > 0) {
+      long long cum = 0;
+      for (int d = 255; d >= 0; --d) {
+        const long long c = lds[d];
+        if (cum + c >= st.k_rem) {
+          st.prefix |= (unsigned long long)d << (56 - 8 * p);
+          st.k_rem -= cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
+  }
+  SelState out = st;
+  __syncthreads();
+  return out;
+}
+
+__global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned long long* keys, int N,
+                                                               uint32_t* sel_hist, long long keep, int p,
+                                                               const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t lds[256];
+  __shared__ uint32_t cnt[256];
+  const SelState st = select_state(sel_hist, keep, p, lds);
+  cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int shift = 56 - 8 * p;
+  const unsigned long long hi = p == 0 ? 0ull : (~0ull << (shift + 8));
+  for (int j = 0; j < kItems; ++j) {
+    const int i = blockIdx.x * kRankTile + j * kThreads + threadIdx.x;
+    if (i < N) {
+      const unsigned long long k = keys[i];
+      if ((k & hi) == st.prefix) atomicAdd(&cnt[(k >> shift) & 255ull], 1u);
+    }
+  }
+  __syncthreads();
+  if (cnt[threadIdx.x]) atomicAdd(&sel_hist[p * 256 + threadIdx.x], cnt[threadIdx.x]);
+}
+
+struct MarkArgs {
+  const DevEntry* entries;
+  const unsigned long long* shat;
+  const uint32_t* sel_hist;
+  long long keep;
+  int32_t* n_gt;
+  int32_t* n_eq;
+  SelState* final_state;
+  const int32_t* flag;
+};
+
+__global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
+  if (*a.flag) return;
+  __shared__ uint32_t lds[256];
+  __shared__ int32_t sg, se;
+  SelState st = select_state(a.sel_hist, a.keep, 8, lds);
+  if (a.keep == 0) st = SelState{~0ull, 0};
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.final_state = st;
+  if (threadIdx.x == 0) { sg = 0; se = 0; }
+  __syncthreads();
+  const DevEntry en = a.entries[blockIdx.x];
+  const int j = blockIdx.y * kThreads + threadIdx.x;
+  int gt = 0, eq = 0;
+  if (j < en.len) {
+    const unsigned long long k = a.shat[en.tok_start + j];
+    gt = k > st.prefix;
+    eq = k == st.prefix;
+  }
+  const unsigned long long bg = __ballot(gt), be = __ballot(eq);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&sg, (int32_t)__popcll(bg));
+    atomicAdd(&se, (int32_t)__popcll(be));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (sg) atomicAdd(&a.n_gt[blockIdx.x], sg);
+    if (se) atomicAdd(&a.n_eq[blockIdx.x], se);
+  }
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads max).
+template <int NT>
+__device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    int32_t t = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += t;
+    __syncthreads();
+  }
+  const int32_t incl = lds[tid];
+  if (total) *total = lds[NT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+struct PlanArgs {
+  const int32_t* n_gt;
+  const int32_t* n_eq;
+  const SelState* final_state;
+  int32_t* eq_base;
+  int32_t* keep_base;
+  int32_t* new_len;
+  int n_entries;
+  const int32_t* flag;
+};
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
+  if (*a.flag) return;
+  __shared__ int32_t lds[1024];
+  const int tid = threadIdx.x;
+  const long long k_rem = a.final_state->k_rem;
+  const int per = (a.n_entries + 1023) / 1024;
+  const int b = tid * per, e = min(b + per, a.n_entries);
+  int32_t s_eq = 0;
+  for (int i = b; i < e; ++i) s_eq += a.n_eq[i];
+  int32_t eq_run = block_excl_scan<1024>(s_eq, lds, nullptr);
+  int32_t s_keep = 0;
+  for (int i = b; i < e; ++i) {
+    long long take = k_rem - eq_run;
+    take = take < 0 ? 0 : (take > a.n_eq[i] ? a.n_eq[i] : take);
+    a.eq_base[i] = eq_run;
+    const int32_t kc = a.n_gt[i] + (int32_t)take;
+    a.new_len[i] = kc;
+    s_keep += kc;
+    eq_run += a.n_eq[i];
+  }
+  int32_t keep_run = block_excl_scan<1024>(s_keep, lds, nullptr);
+  for (int i = b; i < e; ++i) {
+    a.keep_base[i] = keep_run;
+    keep_run += a.new_len[i];
+  }
+}
+
+struct CompactArgs {
+  const DevEntry* entries;
+  const unsigned long long* shat;
+  const SelState* final_state;
+  const int32_t* eq_base;
+  const int32_t* keep_base;
+  const int32_t* new_len;
+  char* pool;
+  PageGeom g;
+  int32_t* keep_ids_out;
+  const int32_t* flag;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+  if (*a.flag) return;
+  __shared__ uint16_t kidx[kMaxPageTokensScored];
+  __shared__ int32_t scan[kThreads];
+  const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int H = a.g.heads;
+  const DevEntry en = a.entries[e];
+  const int len = en.len, nl = a.new_len[e];
+  const bool ids_part = part == 2 * H;
+  if (!ids_part && nl == len) return;  // nothing dropped: K and V stay
+
+  // kept slots of this page in order: kidx[0..nl)
+  const SelState st = *a.final_state;
+  const int per = (len + kThreads - 1) / kThreads;
+  const int b = tid * per, end = min(b + per, len);
+  const unsigned long long* sh = a.shat + en.tok_start;
+  int32_t n_eq = 0;
+  for (int j = b; j < end; ++j) n_eq += sh[j] == st.prefix;
+  const int32_t eq_start = a.eq_base[e] + block_excl_scan<kThreads>(n_eq, scan, nullptr);
+  int32_t eq_rank = eq_start;
+  int32_t n_keep = 0;
+  for (int j = b; j < end; ++j) {
+    const unsigned long long k = sh[j];
+    bool keep = k > st.prefix;
+    if (k == st.prefix) keep = eq_rank++ < st.k_rem;
+    n_keep += keep;
+  }
+  int32_t pos = block_excl_scan<kThreads>(n_keep, scan, nullptr);
+  eq_rank = eq_start;
+  for (int j = b; j < end; ++j) {
+    const unsigned long long k = sh[j];
+    bool keep = k > st.prefix;
+    if (k == st.prefix) keep = eq_rank++ < st.k_rem;
+    if (keep) kidx[pos++] = (uint16_t)j;
+  }
+  __syncthreads();
+
+  char* page = a.pool + (int64_t)en.phys * a.g.page_bytes;
+  if (part < H) {
+    // K rows of head `part`: 64 elements each, moved as 16-byte vectors
+    constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
+    typedef int4 V16;
+    V16* rows = reinterpret_cast<V16*>(page + a.g.k_off) + (int64_t)part * a.g.ts * VPR;
+    constexpr int RPS = kThreads / 8;  // rows per step, 8 threads per row
+    const int r = tid >> 3, c = tid & 7;
+    for (int i0 = 0; i0 < nl; i0 += RPS) {
+      const int i = i0 + r;
+      const int src = i < nl ? kidx[i] : i;
+      const bool move = i < nl && src != i;
+      V16 v[VPR / 8];
+      if (move)
+#pragma unroll
+        for (int u = 0; u < VPR / 8; ++u) v[u] = rows[(int64_t)src * VPR + c + 8 * u];
+      __syncthreads();
+      if (move)
+#pragma unroll
+        for (int u = 0; u < VPR / 8; ++u) rows[(int64_t)i * VPR + c + 8 * u] = v[u];
+      __syncthreads();
+    }
+  } else if (part < 2 * H) {
+    // V^T rows (one per d) of head part-H: out[i] = row[kidx[i]], 8 outputs per thread
+    const int h = part - H;
+    T* vt = reinterpret_cast<T*>(page + a.g.v_off) + (int64_t)h * kHeadDim * a.g.ts;
+    const int d = tid >> 3, c = tid & 7;  // 32 rows x 64 outputs per step
+    for (int dh = 0; dh < kHeadDim; dh += 32) {
+      T* row = vt + (int64_t)(dh + d) * a.g.ts;
+      for (int i0 = 0; i0 < nl; i0 += 64) {
+        T v[8];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + c * 8 + u;
+          const int src = i < nl ? kidx[i] : i;
+          any |= i < nl && src != i;
+          v[u] = i < nl && src != i ? row[src] : T(0.f);
+        }
+        __syncthreads();
+        if (any) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + c * 8 + u;
+            if (i < nl && kidx[i] != i) row[i] = v[u];
+          }
+        }
+        __syncthreads();
+      }
+    }
+  } else {
+    // token ids, and the list of kept ids in table order
+    int32_t* ids = reinterpret_cast<int32_t*>(page + a.g.id_off);
+    const int32_t kb = a.keep_base[e];
+    for (int i0 = 0; i0 < nl; i0 += kThreads) {
+      const int i = i0 + tid;
+      int32_t id = 0;
+      if (i < nl) id = ids[kidx[i]];
+      __syncthreads();
+      if (i < nl) {
+        if (kidx[i] != i) ids[i] = id;
+        if (a.keep_ids_out) a.keep_ids_out[kb + i] = id;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace
+
+ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max) {
+  ClcesSizes z{};
+  z.n_max = n_max;
+  z.p_max = p_max;
+  z.w_max = w_max;
+  z.nblk_max = (int32_t)((n_max + kRankTile - 1) / kRankTile);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t wn = (size_t)w_max * (size_t)n_max;
+  z.keys_a = take(wn * 4);
+  z.keys_b = take(wn * 4);
+  z.vals_a = take(wn * 4);
+  z.vals_b = take(wn * 4);
+  z.ranks = take(wn * 4);
+  z.scur = take((size_t)n_max * 4);
+  z.shat = take((size_t)n_max * 8);
+  z.hist = take((size_t)w_max * 256 * z.nblk_max * 4);
+  z.sel_hist = take(8 * 256 * 4);
+  z.sel_state = take(sizeof(SelState));
+  z.entries = take((size_t)p_max * sizeof(DevEntry));
+  z.counts = take((size_t)p_max * 2 * 4);
+  z.plan = take((size_t)p_max * 3 * 4);
+  z.flag = take(4);
+  z.total = off;
+  return z;
+}
+
+hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s) {
+  const ClcesSizes& z = a.sizes;
+  char* ws = a.ws;
+  auto* entries = reinterpret_cast<DevEntry*>(ws + z.entries);
+  auto* keys_a = reinterpret_cast<uint32_t*>(ws + z.keys_a);
+  auto* keys_b = reinterpret_cast<uint32_t*>(ws + z.keys_b);
+  auto* vals_a = reinterpret_cast<uint32_t*>(ws + z.vals_a);
+  auto* vals_b = reinterpret_cast<uint32_t*>(ws + z.vals_b);
+  auto* ranks = a.ranks_out ? a.ranks_out : reinterpret_cast<int32_t*>(ws + z.ranks);
+  auto* scur = reinterpret_cast<float*>(ws + z.scur);
+  auto* shat = reinterpret_cast<unsigned long long*>(ws + z.shat);
+  auto* hist = reinterpret_cast<uint32_t*>(ws + z.hist);
+  auto* sel_hist = reinterpret_cast<uint32_t*>(ws + z.sel_hist);
+  auto* sel_state = reinterpret_cast<SelState*>(ws + z.sel_state);
+  auto* counts = reinterpret_cast<int32_t*>(ws + z.counts);
+  auto* plan = reinterpret_cast<int32_t*>(ws + z.plan);
+  auto* flag = reinterpret_cast<int32_t*>(ws + z.flag);
+  const int P = a.n_entries, N = a.n_tokens, W = a.n_window;
+  if (P > z.p_max || (int64_t)N > z.n_max || W > z.w_max || a.geom.ts > kMaxPageTokensScored)
+    return hipErrorInvalidValue;
+
+  hipError_t e = launch_table_upload(entries, a.entries_host, P, s);
+  if (e != hipSuccess) return e;
+  const int nz = std::max(8 * 256, 2 * P);
+  zero_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(sel_hist, counts, 2 * P, flag);
+
+  GatherArgs g{entries, a.pool, a.geom.page_bytes, a.geom.id_off, a.score_table, a.score_rows, a.score_cols,
+               a.first_layer, W, N, keys_a, scur, flag};
+  gather_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(g);
+
+  const int nblk = (N + kRankTile - 1) / kRankTile;
+  uint32_t* kin = keys_a;
+  uint32_t* kout = keys_b;
+  uint32_t* vin = nullptr;
+  uint32_t* vout = vals_b;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift, flag);
+    rank_scan_kernel<<<dim3((unsigned)W), dim3(1024), 0, s>>>(hist, nblk, flag);
+    rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(
+        kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
+    std::swap(kin, kout);
+    vin = vout;
+    vout = vout == vals_b ? vals_a : vals_b;
+  }
+  fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
+      ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), flag);
+  if (a.keep > 0) {
+    for (int p = 0; p < 8; ++p)
+      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, a.keep, p, flag);
+  }
+  MarkArgs m{entries, shat, sel_hist, a.keep, counts, counts + P, sel_state, flag};
+  mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
+  PlanArgs pa{counts, counts + P, sel_state, plan, plan + P, plan + 2 * P, P, flag};
+  plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(pa);
+  CompactArgs ca{entries, shat, sel_state, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag};
+  dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
+  if (a.geom.esize == 2)
+    compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
+  else
+    compact_kernel<float><<<cg, dim3(kThreads), 0, s>>>(ca);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(new_lens_host, plan + 2 * P, sizeof(int32_t) * (size_t)P, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(err_flag_host, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(s);
+}
+
+}  // namespace kvs

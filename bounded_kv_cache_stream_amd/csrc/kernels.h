@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI runtime (kvstream.cpp) and the HIP
+// kernels (*.hip).  Not installed; callers use include/kvstream.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kvs {
+
+constexpr int kHeadDim = 64;
+constexpr int kTile = 64;  // KV tile (tokens) of the attention kernel, and page-stride unit
+
+// One entry of the device copy of a layer's attended table.
+struct DevEntry {
+  int32_t phys;        // physical page index in the pool
+  int32_t len;         // valid tokens
+  int32_t tile_start;  // number of kTile tiles in the entries before this one
+  int32_t tok_start;   // number of tokens in the entries before this one
+};
+
+// Geometry of one page (bytes), see kv_pool_layout in include/kvstream.h.
+struct PageGeom {
+  int64_t page_bytes;
+  int64_t k_off, v_off, id_off;
+  int32_t ts;    // token stride
+  int32_t heads;
+  int32_t esize; // 2 (bf16) or 4 (fp32)
+};
+
+constexpr int kUploadChunk = 192;
+struct TableChunk {
+  int32_t first;
+  int32_t count;
+  DevEntry e[kUploadChunk];
+};
+
+hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStream_t s);
+
+hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
+                         int64_t first_token_id, hipStream_t s);
+
+struct AttendParams {
+  const void* q;
+  void* out;
+  float* lse;
+  float* part_o;   // [splits][n_q][H][D] fp32 (splits > 1)
+  float* part_ml;  // [splits][n_q][H][2] fp32 (splits > 1)
+  const char* pool;
+  const DevEntry* table;
+  int32_t n_entries;
+  int32_t total_tiles;
+  int32_t splits;
+  int32_t n_q;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s);
+
+}  // namespace kvs

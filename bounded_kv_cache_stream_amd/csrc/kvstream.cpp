@@ -1,0 +1,424 @@
+// C-ABI runtime of the bounded streaming KV cache (see include/kvstream.h).
+//
+// Owns host metadata only: per-layer page tables and page-id pools
+// (policy.h), the carve-up of the caller's workspace, and the launch of the
+// HIP kernels on the caller's stream.  Never allocates device memory.
+
+#include "kvstream.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "clces.h"
+#include "kernels.h"
+#include "policy.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kv_status fail(kv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kv_status fail(kv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+kv_status ok() {
+  g_err.clear();
+  return KV_OK;
+}
+
+kv_status hip_fail(hipError_t e, const char* what) {
+  return fail(KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  kvs::PageGeom geom;
+  int64_t layer_pages;  // pages per layer including the transient page
+  size_t pool_bytes;
+  // workspace regions (byte offsets)
+  size_t tables, part_o, part_ml, clces, ws_bytes;
+  int64_t part_rows;  // capacity in (split x query) rows
+  kvs::ClcesSizes cl;
+};
+
+kv_status validate(const kv_pool_config* c) {
+  if (!c) return fail(KV_ERR_ARG, "config is NULL");
+  if (c->num_layers < 1 || c->num_layers > 4096) return fail(KV_ERR_ARG, "num_layers %d out of range", c->num_layers);
+  if (c->num_heads < 1 || c->num_heads > 1024) return fail(KV_ERR_ARG, "num_heads %d out of range", c->num_heads);
+  if (c->head_dim != kvs::kHeadDim) return fail(KV_ERR_ARG, "head_dim must be 64 (got %d)", c->head_dim);
+  if (c->page_tokens < 1 || c->page_tokens > 8192)
+    return fail(KV_ERR_ARG, "page_tokens %d out of range 1..8192", c->page_tokens);
+  if (c->dtype != KV_BF16 && c->dtype != KV_FP32) return fail(KV_ERR_ARG, "unknown dtype %d", c->dtype);
+  if (c->scale_frames < 0 || c->sliding_window < 0) return fail(KV_ERR_ARG, "negative scale_frames/window");
+  if (c->keyframe_interval < 1) return fail(KV_ERR_ARG, "keyframe_interval must be >= 1");
+  if (c->pages_per_layer < 1) return fail(KV_ERR_ARG, "pages_per_layer must be >= 1");
+  if ((int64_t)c->pages_per_layer * c->page_tokens > (int64_t)1 << 30)
+    return fail(KV_ERR_ARG, "pages_per_layer * page_tokens too large");
+  if (c->max_queries < 1) return fail(KV_ERR_ARG, "max_queries must be >= 1");
+  if (c->max_splits < 1 || c->max_splits > 64) return fail(KV_ERR_ARG, "max_splits must be 1..64");
+  if (c->max_window < 1 || c->max_window > 8) return fail(KV_ERR_ARG, "max_window must be 1..8");
+  return KV_OK;
+}
+
+Layout make_layout(const kv_pool_config* c) {
+  Layout L{};
+  const int64_t E = c->dtype == KV_BF16 ? 2 : 4;
+  const int64_t ts = (c->page_tokens + kvs::kTile - 1) / kvs::kTile * kvs::kTile;
+  const int64_t H = c->num_heads, D = kvs::kHeadDim;
+  L.geom.esize = (int32_t)E;
+  L.geom.ts = (int32_t)ts;
+  L.geom.heads = (int32_t)H;
+  L.geom.k_off = 0;
+  L.geom.v_off = H * ts * D * E;
+  L.geom.id_off = 2 * H * ts * D * E;
+  L.geom.page_bytes = (int64_t)align_up((size_t)(L.geom.id_off + ts * 4));
+  L.layer_pages = (int64_t)c->pages_per_layer + 1;
+  L.pool_bytes = (size_t)(L.layer_pages * c->num_layers * L.geom.page_bytes);
+
+  size_t off = 0;
+  L.tables = off;
+  off = align_up(off + sizeof(kvs::DevEntry) * (size_t)(L.layer_pages * c->num_layers));
+  L.part_rows = (int64_t)c->max_splits * std::min(c->max_queries, c->page_tokens);
+  L.part_o = off;
+  off = align_up(off + (size_t)L.part_rows * H * D * 4);
+  L.part_ml = off;
+  off = align_up(off + (size_t)L.part_rows * H * 2 * 4);
+  L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window);
+  L.clces = off;
+  off = align_up(off + L.cl.total);
+  L.ws_bytes = off;
+  return L;
+}
+
+}  // namespace
+
+struct kv_pool {
+  kv_pool_config cfg;
+  Layout lay;
+  char* pool = nullptr;
+  char* ws = nullptr;
+  bool meta_only = false;
+  int32_t splits_override = 0;
+  std::vector<kvs::LayerPolicy> layers;
+  std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
+};
+
+namespace {
+
+kv_status check_layer(const kv_pool_t* p, int32_t layer) {
+  if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+  if (layer < 0 || layer >= p->cfg.num_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
+  return KV_OK;
+}
+
+int64_t phys_page(const kv_pool_t* p, int32_t layer, int32_t page) {
+  const int32_t id = page < 0 ? p->cfg.pages_per_layer : page;  // -1 = transient page
+  return (int64_t)layer * p->lay.layer_pages + id;
+}
+
+kvs::DevEntry* dev_table(const kv_pool_t* p, int32_t layer) {
+  return reinterpret_cast<kvs::DevEntry*>(p->ws + p->lay.tables) + (int64_t)layer * p->lay.layer_pages;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_pool_required_bytes(const kv_pool_config* cfg, size_t* pool_bytes, size_t* workspace_bytes) {
+  kv_status s = validate(cfg);
+  if (s != KV_OK) return s;
+  Layout L = make_layout(cfg);
+  if (pool_bytes) *pool_bytes = L.pool_bytes;
+  if (workspace_bytes) *workspace_bytes = L.ws_bytes;
+  return ok();
+}
+
+kv_status kv_pool_get_layout(const kv_pool_config* cfg, kv_pool_layout* out) {
+  kv_status s = validate(cfg);
+  if (s != KV_OK) return s;
+  if (!out) return fail(KV_ERR_ARG, "out is NULL");
+  Layout L = make_layout(cfg);
+  out->page_bytes = L.geom.page_bytes;
+  out->k_offset = L.geom.k_off;
+  out->v_offset = L.geom.v_off;
+  out->id_offset = L.geom.id_off;
+  out->token_stride = L.geom.ts;
+  out->elem_bytes = L.geom.esize;
+  return ok();
+}
+
+kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_bytes, void* workspace_dev,
+                         size_t workspace_bytes, kv_pool_t** out) {
+  kv_status s = validate(cfg);
+  if (s != KV_OK) return s;
+  if (!out) return fail(KV_ERR_ARG, "out is NULL");
+  Layout L = make_layout(cfg);
+  const bool meta = pool_dev == nullptr && workspace_dev == nullptr;
+  if (!meta) {
+    if (!pool_dev || !workspace_dev) return fail(KV_ERR_ARG, "pool and workspace must both be given or both NULL");
+    if (pool_bytes < L.pool_bytes)
+      return fail(KV_ERR_SHAPE, "pool buffer too small: %zu < %zu bytes", pool_bytes, L.pool_bytes);
+    if (workspace_bytes < L.ws_bytes)
+      return fail(KV_ERR_SHAPE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(pool_dev) | reinterpret_cast<uintptr_t>(workspace_dev)) % kAlign)
+      return fail(KV_ERR_ARG, "pool and workspace must be 256-byte aligned");
+  }
+  kv_pool_t* p = new (std::nothrow) kv_pool_t();
+  if (!p) return fail(KV_ERR_ARG, "out of host memory");
+  p->cfg = *cfg;
+  p->lay = L;
+  p->pool = static_cast<char*>(pool_dev);
+  p->ws = static_cast<char*>(workspace_dev);
+  p->meta_only = meta;
+  p->layers.resize((size_t)cfg->num_layers);
+  for (auto& l : p->layers)
+    l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens);
+  *out = p;
+  return ok();
+}
+
+kv_status kv_pool_destroy(kv_pool_t* pool) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  delete pool;
+  return ok();
+}
+
+kv_status kv_reset(kv_pool_t* pool) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  for (auto& l : pool->layers) l.reset();
+  return ok();
+}
+
+kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev, const void* v_dev,
+                          int32_t n_tokens, uint32_t flags, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (n_tokens != pool->cfg.page_tokens)
+    return fail(KV_ERR_SHAPE, "n_tokens %d != page_tokens %d", n_tokens, pool->cfg.page_tokens);
+  if (frame_idx < 0) return fail(KV_ERR_ARG, "negative frame index");
+  if (frame_idx > (int64_t)(INT32_MAX / pool->cfg.page_tokens) - 1)
+    return fail(KV_ERR_ARG, "frame index %lld too large for 32-bit token ids", (long long)frame_idx);
+  if (flags & ~KV_TRANSIENT) return fail(KV_ERR_ARG, "unknown flags 0x%x", flags);
+  auto& L = pool->layers[(size_t)layer];
+  int32_t page = 0;
+  int rc = L.plan_append(frame_idx, (flags & KV_TRANSIENT) != 0, &page);
+  if (rc == 1)
+    return fail(KV_ERR_STATE, "layer %d: frame %lld after frame %lld%s", layer, (long long)frame_idx,
+                (long long)L.last_frame, L.transient_pending ? " (a transient frame is still pending)" : "");
+  if (rc == 2) return fail(KV_ERR_NO_PAGES, "layer %d: all %d page ids in use", layer, pool->cfg.pages_per_layer);
+  if (!pool->meta_only) {
+    if (!k_dev || !v_dev) return fail(KV_ERR_ARG, "k or v is NULL");
+    char* dst = pool->pool + phys_page(pool, layer, page) * pool->lay.geom.page_bytes;
+    hipError_t e = kvs::launch_append(pool->lay.geom, dst, k_dev, v_dev, n_tokens,
+                                      frame_idx * pool->cfg.page_tokens, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "page write launch");
+  }
+  L.commit_append(frame_idx, page);
+  return ok();
+}
+
+kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  int32_t n = pool->layers[(size_t)layer].evict();
+  if (n_evicted) *n_evicted = n;
+  return ok();
+}
+
+kv_status kv_set_attend_splits(kv_pool_t* pool, int32_t splits) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  if (splits < 0 || splits > pool->cfg.max_splits) return fail(KV_ERR_ARG, "splits %d out of 0..max_splits", splits);
+  pool->splits_override = splits;
+  return ok();
+}
+
+kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q, float sm_scale,
+                        void* out_dev, float* lse_dev, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (n_q < 1 || n_q > pool->cfg.max_queries)
+    return fail(KV_ERR_SHAPE, "n_q %d out of 1..max_queries (%d)", n_q, pool->cfg.max_queries);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_ERR_ARG, "sm_scale must be finite and > 0");
+  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+  if (!q_dev || !out_dev) return fail(KV_ERR_ARG, "q or out is NULL");
+  auto& L = pool->layers[(size_t)layer];
+  auto& ent = pool->scratch;
+  ent.clear();
+  int32_t tiles = 0, toks = 0;
+  auto add = [&](int32_t page, int32_t len) {
+    if (len <= 0) return;
+    kvs::DevEntry d;
+    d.phys = (int32_t)phys_page(pool, layer, page);
+    d.len = len;
+    d.tile_start = tiles;
+    d.tok_start = toks;
+    tiles += (len + kvs::kTile - 1) / kvs::kTile;
+    toks += len;
+    ent.push_back(d);
+  };
+  for (const auto& e : L.table) add(e.page, e.len);
+  if (L.transient_pending) add(-1, pool->cfg.page_tokens);
+  if (ent.empty()) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kvs::DevEntry* dt = dev_table(pool, layer);
+  hipError_t e = kvs::launch_table_upload(dt, ent.data(), (int)ent.size(), st);
+  if (e != hipSuccess) return hip_fail(e, "table upload launch");
+
+  const bool bf16 = pool->cfg.dtype == KV_BF16;
+  int32_t splits = 1;
+  if (bf16) {
+    const int64_t qtiles = (n_q + 127) / 128;
+    const int64_t base = qtiles * pool->cfg.num_heads;
+    if (pool->splits_override > 0) {
+      splits = pool->splits_override;
+    } else {
+      const int64_t target = 1024;  // workgroups to fill 256 CUs x 4 slots
+      splits = (int32_t)std::max<int64_t>(1, (target + base / 2) / base);
+    }
+    splits = std::min<int32_t>(splits, pool->cfg.max_splits);
+    splits = std::min<int32_t>(splits, tiles);
+    splits = (int32_t)std::min<int64_t>(splits, std::max<int64_t>(1, pool->lay.part_rows / n_q));
+    splits = std::max(splits, 1);
+  }
+  kvs::AttendParams ap{};
+  ap.q = q_dev;
+  ap.out = out_dev;
+  ap.lse = lse_dev;
+  ap.part_o = reinterpret_cast<float*>(pool->ws + pool->lay.part_o);
+  ap.part_ml = reinterpret_cast<float*>(pool->ws + pool->lay.part_ml);
+  ap.pool = pool->pool;
+  ap.table = dt;
+  ap.n_entries = (int32_t)ent.size();
+  ap.total_tiles = tiles;
+  ap.splits = splits;
+  ap.n_q = n_q;
+  ap.scale_log2 = sm_scale * 1.4426950408889634f;
+  e = kvs::launch_attend(pool->lay.geom, ap, bf16, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  L.transient_pending = false;
+  return ok();
+}
+
+kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_table_dev, int64_t score_rows,
+                            const kv_clces_params* params, int32_t* keep_ids_out_dev, int32_t* ranks_out_dev,
+                            int64_t* n_kept, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (!params) return fail(KV_ERR_ARG, "params is NULL");
+  if (params->window < 1 || params->window > pool->cfg.max_window)
+    return fail(KV_ERR_ARG, "window %d out of 1..max_window (%d)", params->window, pool->cfg.max_window);
+  if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
+  if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
+  auto& L = pool->layers[(size_t)layer];
+  const size_t first = L.first_candidate();
+  int64_t N = 0;
+  for (size_t i = first; i < L.table.size(); ++i) N += L.table[i].len;
+  if (N <= params->keep_count) {
+    if (n_kept) *n_kept = N;
+    return ok();
+  }
+  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+  if (!score_table_dev) return fail(KV_ERR_ARG, "score table is NULL");
+  if (score_rows < 1) return fail(KV_ERR_ARG, "score_rows must be >= 1");
+
+  auto& ent = pool->scratch;
+  ent.clear();
+  int32_t toks = 0;
+  for (size_t i = first; i < L.table.size(); ++i) {
+    kvs::DevEntry d;
+    d.phys = (int32_t)phys_page(pool, layer, L.table[i].page);
+    d.len = L.table[i].len;
+    d.tile_start = 0;
+    d.tok_start = toks;
+    toks += d.len;
+    ent.push_back(d);
+  }
+  const int32_t n_win = std::min<int32_t>(params->window, layer + 1);
+  kvs::ClcesArgs a{};
+  a.ws = pool->ws + pool->lay.clces;
+  a.sizes = pool->lay.cl;
+  a.pool = pool->pool;
+  a.geom = pool->lay.geom;
+  a.entries_host = ent.data();
+  a.n_entries = (int32_t)ent.size();
+  a.n_tokens = (int32_t)N;
+  a.score_table = score_table_dev;
+  a.score_rows = score_rows;
+  a.score_cols = pool->cfg.num_layers;
+  a.first_layer = layer - n_win + 1;
+  a.n_window = n_win;
+  a.lambda = params->lambda;
+  a.keep = params->keep_count;
+  a.keep_ids_out = keep_ids_out_dev;
+  a.ranks_out = ranks_out_dev;
+  std::vector<int32_t> new_lens((size_t)a.n_entries);
+  int32_t err_flag = 0;
+  hipError_t e = kvs::run_clces(a, new_lens.data(), &err_flag, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "CLCES step");
+  if (err_flag & kvs::kClcesErrNan) return fail(KV_ERR_NAN, "layer %d: a raw score is NaN or negative", layer);
+  if (err_flag & kvs::kClcesErrRow) return fail(KV_ERR_ARG, "layer %d: a token id is >= score_rows", layer);
+  if (err_flag) return fail(KV_ERR_HIP, "layer %d: CLCES consistency check failed (flag %d)", layer, err_flag);
+  int64_t kept = 0;
+  for (int32_t v : new_lens) kept += v;
+  if (kept != params->keep_count)
+    return fail(KV_ERR_HIP, "layer %d: kept %lld tokens, expected %lld", layer, (long long)kept,
+                (long long)params->keep_count);
+  L.apply_compaction(new_lens, kept);
+  if (n_kept) *n_kept = kept;
+  return ok();
+}
+
+kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (!out) return fail(KV_ERR_ARG, "out is NULL");
+  const auto& L = pool->layers[(size_t)layer];
+  out->persisted_frames = (int32_t)L.table.size();
+  out->pages_used = (int32_t)L.table.size();
+  out->pages_free = (int32_t)L.free_ids.size();
+  out->transient_pending = L.transient_pending ? 1 : 0;
+  out->tokens = L.tokens();
+  out->bytes = (int64_t)L.table.size() * pool->lay.geom.page_bytes;
+  out->evictions = L.evictions;
+  out->compactions = L.compactions;
+  out->last_keep_count = L.last_keep;
+  return ok();
+}
+
+kv_status kv_get_page_table(const kv_pool_t* pool, int32_t layer, int32_t* page_ids, int32_t* page_lens,
+                            int64_t* frame_ids, int32_t cap, int32_t* n_out) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (cap < 0) return fail(KV_ERR_ARG, "negative cap");
+  const auto& L = pool->layers[(size_t)layer];
+  const int32_t n = (int32_t)L.table.size();
+  for (int32_t i = 0; i < n && i < cap; ++i) {
+    if (page_ids) page_ids[i] = L.table[(size_t)i].page;
+    if (page_lens) page_lens[i] = L.table[(size_t)i].len;
+    if (frame_ids) frame_ids[i] = L.table[(size_t)i].frame;
+  }
+  if (n_out) *n_out = n;
+  return ok();
+}
+
+const char* kv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Page write and page-table upload, gfx950.
+//
+// Page write (LingBot-Map 20 FPS explainer, "Page-Aligned Tensor Layout":
+// a frame's tokens go straight into a page-aligned layout, no padding between
+// frames, no extra copies).  A frame's K and V arrive as [T][H][D]; the page
+// stores K as [H][Ts][D] and V transposed as [H][D][Ts] (Ts = T rounded up to
+// 64), plus the global token id of every slot.  One workgroup moves a
+// 64-token x 64-dim block of one head: K rows are copied with 16-byte
+// accesses, V goes through LDS to be transposed so that both the HBM reads
+// and the HBM writes are whole 128-byte rows.  Slots T..Ts-1 are zero-filled.
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace kvs {
+namespace {
+
+constexpr int D = kHeadDim;
+
+template <typename T>
+struct Vec8 {
+  T v[8];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(PageGeom g, char* page, const T* __restrict__ k,
+                                                     const T* __restrict__ v, int n_tokens,
+                                                     int64_t first_id) {
+  __shared__ T vt[64][D + 1];
+  const int H = g.heads;
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int r = tid >> 3;      // 0..31
+  const int c = tid & 7;       // chunk of 8 elements
+  T* kdst = reinterpret_cast<T*>(page + g.k_off) + (int64_t)h * g.ts * D;
+  T* vdst = reinterpret_cast<T*>(page + g.v_off) + (int64_t)h * D * g.ts;
+
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int t = t0 + r + 32 * pp;
+    Vec8<T> kk, vv;
+    if (t < n_tokens) {
+      kk = *reinterpret_cast<const Vec8<T>*>(k + ((int64_t)t * H + h) * D + c * 8);
+      vv = *reinterpret_cast<const Vec8<T>*>(v + ((int64_t)t * H + h) * D + c * 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { kk.v[i] = (T)0.f; vv.v[i] = (T)0.f; }
+    }
+    *reinterpret_cast<Vec8<T>*>(kdst + (int64_t)t * D + c * 8) = kk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vt[r + 32 * pp][c * 8 + i] = vv.v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int d = r + 32 * pp;
+    Vec8<T> o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.v[i] = vt[c * 8 + i][d];
+    *reinterpret_cast<Vec8<T>*>(vdst + (int64_t)d * g.ts + t0 + c * 8) = o;
+  }
+  if (h == 0 && tid < 64) {
+    const int t = t0 + tid;
+    int32_t* ids = reinterpret_cast<int32_t*>(page + g.id_off);
+    ids[t] = t < n_tokens ? (int32_t)(first_id + t) : -1;
+  }
+}
+
+__global__ void table_upload_kernel(DevEntry* dst, TableChunk chunk) {
+  const int i = threadIdx.x;
+  if (i < chunk.count) dst[chunk.first + i] = chunk.e[i];
+}
+
+}  // namespace
+
+hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStream_t s) {
+  for (int first = 0; first < n; first += kUploadChunk) {
+    TableChunk c;
+    c.first = first;
+    c.count = n - first < kUploadChunk ? n - first : kUploadChunk;
+    for (int i = 0; i < c.count; ++i) c.e[i] = src[first + i];
+    table_upload_kernel<<<dim3(1), dim3(kUploadChunk), 0, s>>>(dst, c);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
+                         int64_t first_token_id, hipStream_t s) {
+  dim3 grid((unsigned)(g.ts / 64), (unsigned)g.heads);
+  if (g.esize == 2)
+    append_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, page, static_cast<const __bf16*>(k),
+                                                      static_cast<const __bf16*>(v), n_tokens, first_token_id);
+  else
+    append_kernel<float><<<grid, dim3(256), 0, s>>>(g, page, static_cast<const float*>(k),
+                                                     static_cast<const float*>(v), n_tokens, first_token_id);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,145 @@
+// Host-side cache policy of one layer: keyframe rule, page allocation,
+// sliding-window eviction, and application of compaction results.
+//
+// Pages: GCTStream explainer ("KV Cache Lifecycle Management": skip-append of
+// non-keyframes; "Sliding Window Eviction": the oldest blocks go once the
+// cache is over the window); LingBot-Map 20 FPS explainer ("Sliding-Window
+// Eviction Strategy": the window counts frames, the first scale frames are
+// kept).  Readings: the window counts persisted non-scale frames; frame t is
+// a keyframe iff t < S or (t - S) % k == 0; page ids come from a per-layer
+// pool, lowest free id first; a frame's page is allocated before the
+// eviction of the same frame; freed ids are free at once.
+#pragma once
+
+#include <stdint.h>
+
+#include <set>
+#include <vector>
+
+namespace kvs {
+
+struct PageEntry {
+  int32_t page;   // layer-local page id
+  int32_t len;    // valid tokens in the page
+  int64_t frame;  // frame index
+};
+
+class LayerPolicy {
+ public:
+  void init(int32_t pages, int32_t scale_frames, int32_t window, int32_t keyframe_interval,
+            int32_t page_tokens) {
+    pages_ = pages;
+    S_ = scale_frames;
+    W_ = window;
+    k_ = keyframe_interval;
+    T_ = page_tokens;
+    reset();
+  }
+
+  void reset() {
+    table.clear();
+    free_ids.clear();
+    for (int32_t i = 0; i < pages_; ++i) free_ids.insert(i);
+    transient_pending = false;
+    transient_frame = -1;
+    last_frame = -1;
+    evictions = 0;
+    compactions = 0;
+    last_keep = 0;
+  }
+
+  bool is_keyframe(int64_t t) const { return t < S_ || (t - S_) % k_ == 0; }
+
+  // Page that frame t would go to: a fresh page id, or -1 for the transient
+  // page.  Returns 0 on success, else an error code (1 order, 2 no page).
+  int plan_append(int64_t t, bool force_transient, int32_t* page) const {
+    if (t <= last_frame || transient_pending) return 1;
+    if (force_transient || !is_keyframe(t)) {
+      *page = -1;
+      return 0;
+    }
+    if (free_ids.empty()) return 2;
+    *page = *free_ids.begin();
+    return 0;
+  }
+
+  void commit_append(int64_t t, int32_t page) {
+    last_frame = t;
+    if (page < 0) {
+      transient_pending = true;
+      transient_frame = t;
+      return;
+    }
+    free_ids.erase(page);
+    table.push_back(PageEntry{page, T_, t});
+  }
+
+  int32_t evict() {
+    if (W_ <= 0) return 0;
+    int32_t n = 0;
+    for (;;) {
+      int32_t nonscale = 0;
+      for (const auto& e : table)
+        if (e.frame >= S_) ++nonscale;
+      if (nonscale <= W_) break;
+      for (size_t i = 0; i < table.size(); ++i) {
+        if (table[i].frame >= S_) {
+          free_ids.insert(table[i].page);
+          table.erase(table.begin() + (long)i);
+          break;
+        }
+      }
+      ++n;
+    }
+    evictions += n;
+    return n;
+  }
+
+  // Index of the first table entry that is not a scale frame.
+  size_t first_candidate() const {
+    size_t i = 0;
+    while (i < table.size() && table[i].frame < S_) ++i;
+    return i;
+  }
+
+  // New lengths for entries first_candidate().. (same count); empty pages
+  // leave the table and their ids are freed.
+  void apply_compaction(const std::vector<int32_t>& new_lens, int64_t kept) {
+    size_t f = first_candidate();
+    std::vector<PageEntry> out(table.begin(), table.begin() + (long)f);
+    for (size_t i = f; i < table.size(); ++i) {
+      PageEntry e = table[i];
+      e.len = new_lens[i - f];
+      if (e.len == 0)
+        free_ids.insert(e.page);
+      else
+        out.push_back(e);
+    }
+    table.swap(out);
+    ++compactions;
+    last_keep = kept;
+  }
+
+  int64_t tokens() const {
+    int64_t n = 0;
+    for (const auto& e : table) n += e.len;
+    return n;
+  }
+
+  int32_t pages() const { return pages_; }
+  int32_t page_tokens() const { return T_; }
+
+  std::vector<PageEntry> table;
+  std::set<int32_t> free_ids;
+  bool transient_pending = false;
+  int64_t transient_frame = -1;
+  int64_t last_frame = -1;
+  int64_t evictions = 0;
+  int64_t compactions = 0;
+  int64_t last_keep = 0;
+
+ private:
+  int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0;
+};
+
+}  // namespace kvs

@@ -1,0 +1,292 @@
+"""ctypes binding of ``libkvstream.so`` (C ABI declared in include/kvstream.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  The functions below carry the C names; ``KVCache`` adds PyTorch
+plumbing (device buffers, the current stream, tensor checks).  Loading fails
+loudly when the library has not been built -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvstream.so")
+
+KV_OK, KV_ERR_ARG, KV_ERR_SHAPE, KV_ERR_NO_PAGES, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_NAN = 0, -1, -2, -3, -4, -5, -6
+KV_BF16, KV_FP32 = 0, 1
+KV_TRANSIENT = 1
+
+EXPORTED = (
+    "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
+    "kv_append_frame", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
+    "kv_get_page_table", "kv_set_attend_splits", "kv_last_error",
+)
+
+
+class kv_pool_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "num_heads", "head_dim", "page_tokens", "dtype", "scale_frames", "sliding_window",
+        "keyframe_interval", "pages_per_layer", "max_queries", "max_splits", "max_window")]
+
+
+class kv_clces_params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lambda_", ctypes.c_double),
+                ("keep_count", ctypes.c_int64)]
+
+
+class kv_cache_info(ctypes.Structure):
+    _fields_ = [("persisted_frames", ctypes.c_int32), ("pages_used", ctypes.c_int32),
+                ("pages_free", ctypes.c_int32), ("transient_pending", ctypes.c_int32),
+                ("tokens", ctypes.c_int64), ("bytes", ctypes.c_int64), ("evictions", ctypes.c_int64),
+                ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64)]
+
+
+class kv_pool_layout(ctypes.Structure):
+    _fields_ = [("page_bytes", ctypes.c_int64), ("k_offset", ctypes.c_int64), ("v_offset", ctypes.c_int64),
+                ("id_offset", ctypes.c_int64), ("token_stride", ctypes.c_int32), ("elem_bytes", ctypes.c_int32)]
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kvstream status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bounded_kv_cache_stream_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ, U32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_float
+        cfgp = ctypes.POINTER(kv_pool_config)
+        sig = {
+            "kv_pool_required_bytes": [cfgp, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+            "kv_pool_get_layout": [cfgp, ctypes.POINTER(kv_pool_layout)],
+            "kv_pool_create": [cfgp, P, SZ, P, SZ, ctypes.POINTER(P)],
+            "kv_pool_destroy": [P],
+            "kv_reset": [P],
+            "kv_append_frame": [P, I32, I64, P, P, I32, U32, P],
+            "kv_evict": [P, I32, ctypes.POINTER(I32)],
+            "stream_attend": [P, I32, P, I32, F32, P, P, P],
+            "score_and_compact": [P, I32, P, I64, ctypes.POINTER(kv_clces_params), P, P, ctypes.POINTER(I64), P],
+            "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
+            "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
+            "kv_set_attend_splits": [P, I32],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.kv_last_error.argtypes = []
+        L.kv_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def kv_last_error() -> str:
+    return lib().kv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != KV_OK:
+        raise KVError(status, kv_last_error())
+
+
+def make_config(num_layers=1, num_heads=16, head_dim=64, page_tokens=1004, dtype=KV_BF16, scale_frames=8,
+                sliding_window=64, keyframe_interval=1, pages_per_layer=73, max_queries=8032, max_splits=16,
+                max_window=5) -> kv_pool_config:
+    return kv_pool_config(num_layers, num_heads, head_dim, page_tokens, dtype, scale_frames, sliding_window,
+                          keyframe_interval, pages_per_layer, max_queries, max_splits, max_window)
+
+
+def kv_pool_required_bytes(cfg: kv_pool_config) -> tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kv_pool_required_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def kv_pool_get_layout(cfg: kv_pool_config) -> dict:
+    out = kv_pool_layout()
+    _check(lib().kv_pool_get_layout(ctypes.byref(cfg), ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in out._fields_}
+
+
+def kv_pool_create(cfg, pool_ptr, pool_bytes, ws_ptr, ws_bytes) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib().kv_pool_create(ctypes.byref(cfg), pool_ptr, pool_bytes, ws_ptr, ws_bytes, ctypes.byref(h)))
+    return h
+
+
+def kv_pool_destroy(pool) -> None:
+    _check(lib().kv_pool_destroy(pool))
+
+
+def kv_reset(pool) -> None:
+    _check(lib().kv_reset(pool))
+
+
+def kv_append_frame(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags=0, stream=None) -> None:
+    _check(lib().kv_append_frame(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, stream))
+
+
+def kv_evict(pool, layer) -> int:
+    n = ctypes.c_int32()
+    _check(lib().kv_evict(pool, layer, ctypes.byref(n)))
+    return n.value
+
+
+def stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr=None, stream=None) -> None:
+    _check(lib().stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr, stream))
+
+
+def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_count, keep_ids_ptr=None,
+                      ranks_ptr=None, stream=None) -> int:
+    prm = kv_clces_params(window, 0, lam, keep_count)
+    n = ctypes.c_int64()
+    _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
+                                   ctypes.byref(n), stream))
+    return n.value
+
+
+def kv_get_info(pool, layer) -> dict:
+    out = kv_cache_info()
+    _check(lib().kv_get_info(pool, layer, ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in out._fields_}
+
+
+def kv_get_page_table(pool, layer) -> tuple[list, list, list]:
+    n = ctypes.c_int32()
+    _check(lib().kv_get_page_table(pool, layer, None, None, None, 0, ctypes.byref(n)))
+    cap = n.value
+    ids = (ctypes.c_int32 * max(cap, 1))()
+    lens = (ctypes.c_int32 * max(cap, 1))()
+    frames = (ctypes.c_int64 * max(cap, 1))()
+    _check(lib().kv_get_page_table(pool, layer, ids, lens, frames, cap, ctypes.byref(n)))
+    return list(ids[:cap]), list(lens[:cap]), list(frames[:cap])
+
+
+def kv_set_attend_splits(pool, splits: int) -> None:
+    _check(lib().kv_set_attend_splits(pool, splits))
+
+
+class KVCache:
+    """A pool with its device buffers allocated by PyTorch (``device=None``: metadata only)."""
+
+    def __init__(self, cfg: kv_pool_config, device=None):
+        self.cfg = cfg
+        self.layout = kv_pool_get_layout(cfg)
+        self.pool_bytes, self.ws_bytes = kv_pool_required_bytes(cfg)
+        self.device = device
+        self.pool_buf = self.ws_buf = None
+        if device is None:
+            self.handle = kv_pool_create(cfg, None, 0, None, 0)
+        else:
+            import torch
+            self.torch = torch
+            self.pool_buf = torch.empty(self.pool_bytes + 256, dtype=torch.uint8, device=device)
+            self.ws_buf = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+            self.pool_ptr = (self.pool_buf.data_ptr() + 255) // 256 * 256
+            self.ws_ptr = (self.ws_buf.data_ptr() + 255) // 256 * 256
+            self.handle = kv_pool_create(cfg, self.pool_ptr, self.pool_bytes, self.ws_ptr, self.ws_bytes)
+        self.dtype_name = "bf16" if cfg.dtype == KV_BF16 else "fp32"
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- marshalling helpers -------------------------------------------------
+    def _stream(self):
+        if self.device is None:
+            return None
+        return ctypes.c_void_p(self.torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _tensor(self, t, rows=None):
+        torch = self.torch
+        want = torch.bfloat16 if self.cfg.dtype == KV_BF16 else torch.float32
+        if t.dtype != want or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"expected a contiguous {want} CUDA tensor, got {t.dtype} on {t.device}")
+        if t.dim() != 3 or t.shape[1] != self.cfg.num_heads or t.shape[2] != self.cfg.head_dim:
+            raise ValueError(f"expected [n, {self.cfg.num_heads}, {self.cfg.head_dim}], got {tuple(t.shape)}")
+        if rows is not None and t.shape[0] != rows:
+            raise ValueError(f"expected {rows} rows, got {t.shape[0]}")
+        return ctypes.c_void_p(t.data_ptr())
+
+    # -- the C calls -----------------------------------------------------------
+    def append(self, layer, frame_idx, k=None, v=None, transient=False):
+        flags = KV_TRANSIENT if transient else 0
+        if self.device is None:
+            kv_append_frame(self.handle, layer, frame_idx, None, None, self.cfg.page_tokens, flags, None)
+            return
+        kv_append_frame(self.handle, layer, frame_idx, self._tensor(k), self._tensor(v), k.shape[0], flags,
+                        self._stream())
+
+    def evict(self, layer) -> int:
+        return kv_evict(self.handle, layer)
+
+    def attend(self, layer, q, sm_scale, out=None, lse=None):
+        torch = self.torch
+        if out is None:
+            out = torch.empty_like(q)
+        qp = self._tensor(q)
+        op = self._tensor(out, q.shape[0])
+        lp = None
+        if lse is not None:
+            if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != q.shape[0] * q.shape[1]:
+                raise ValueError("lse must be a contiguous fp32 tensor of n_q * H elements")
+            lp = ctypes.c_void_p(lse.data_ptr())
+        stream_attend(self.handle, layer, qp, q.shape[0], float(sm_scale), op, lp, self._stream())
+        return out
+
+    def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None) -> int:
+        torch = self.torch
+        if score_table.dtype != torch.float32 or not score_table.is_contiguous() or score_table.dim() != 2 \
+                or score_table.shape[1] != self.cfg.num_layers:
+            raise ValueError("score table must be a contiguous fp32 [rows, num_layers] tensor")
+        for t in (keep_ids, ranks):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError("keep_ids / ranks must be contiguous int32 tensors")
+        return score_and_compact(self.handle, layer, ctypes.c_void_p(score_table.data_ptr()), score_table.shape[0],
+                                 window, lam, keep_count,
+                                 None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),
+                                 None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream())
+
+    def page_table(self, layer):
+        return kv_get_page_table(self.handle, layer)
+
+    def info(self, layer) -> dict:
+        return kv_get_info(self.handle, layer)
+
+    def reset(self):
+        kv_reset(self.handle)
+
+    def set_splits(self, splits):
+        kv_set_attend_splits(self.handle, splits)
+
+    # -- reading pages back (tests) -------------------------------------------
+    def page_view(self, layer, page_id):
+        """(K [H, Ts, D], V^T [H, D, Ts], ids [Ts]) views of one page in the pool."""
+        torch = self.torch
+        L = self.layout
+        base = self.pool_ptr - self.pool_buf.data_ptr() + \
+            (layer * (self.cfg.pages_per_layer + 1) + page_id) * L["page_bytes"]
+        raw = self.pool_buf[base: base + L["page_bytes"]]
+        dt = torch.bfloat16 if self.cfg.dtype == KV_BF16 else torch.float32
+        H, D, Ts, E = self.cfg.num_heads, self.cfg.head_dim, L["token_stride"], L["elem_bytes"]
+        k = raw[L["k_offset"]: L["k_offset"] + H * Ts * D * E].view(dt).view(H, Ts, D)
+        v = raw[L["v_offset"]: L["v_offset"] + H * D * Ts * E].view(dt).view(H, D, Ts)
+        ids = raw[L["id_offset"]: L["id_offset"] + Ts * 4].view(torch.int32)
+        return k, v, ids

@@ -1,0 +1,209 @@
+/*
+ * kvstream.h -- C ABI of the bounded streaming KV cache for one AMD Instinct
+ * MI355X (gfx950): paged frame-to-cache attention plus the cache-management
+ * step (page write, sliding-window eviction, CLCES scoring, top-k compaction).
+ *
+ * The operations follow these pages:
+ *   [GCT]  "How GCTStream Implements Streaming 3D Reconstruction with KV Cache"
+ *          (instagit explainer of Robbyant/lingbot-map)
+ *   [FPS]  "Can LingBot-Map Achieve 20 FPS Streaming 3D Reconstruction?"
+ *          (instagit explainer of Robbyant/lingbot-map)
+ *   [SCV]  "StreamCacheVGGT: ..." (CSDN article), section 2.1 (CLCES)
+ *   [INF]  "InfiniteVGGT: Visual Geometry Grounded Transformer for Endless
+ *          Streams" (howistudyai explainer)
+ *
+ * Conventions for every entry point:
+ *   - Every function returns a kv_status; nothing throws across the ABI.
+ *     On any error the pool's state is unchanged and kv_last_error() returns
+ *     a message for the calling thread.
+ *   - All buffers named *_dev are device memory owned by the caller (the
+ *     library never allocates device memory).  Host pointers are named
+ *     plainly.  "stream" is a hipStream_t passed as void* (NULL = the null
+ *     stream); device work is enqueued on it and the call returns without
+ *     waiting, except where a function says it synchronises.
+ *   - Layouts are row-major.  A frame's K, V and Q are [n_tokens][H][D].
+ *   - Calls on one pool must not overlap from several host threads.
+ */
+#ifndef KVSTREAM_H
+#define KVSTREAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kv_pool kv_pool_t;
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_ARG = -1,      /* null pointer, bad layer, out-of-range parameter        */
+  KV_ERR_SHAPE = -2,    /* n_tokens != page_tokens, n_q out of range, bad sizes   */
+  KV_ERR_NO_PAGES = -3, /* the layer's page pool is exhausted                     */
+  KV_ERR_STATE = -4,    /* call out of order (frame index, empty cache, no device) */
+  KV_ERR_HIP = -5,      /* a HIP runtime call failed                              */
+  KV_ERR_NAN = -6       /* a raw score is NaN or negative                         */
+} kv_status;
+
+typedef enum { KV_BF16 = 0, KV_FP32 = 1 } kv_dtype;
+
+/* kv_append_frame flag: attend this frame once, never persist it ([GCT]
+ * "Selective Frame Caching with Skip Append", _set_skip_append(True)). */
+#define KV_TRANSIENT 1u
+
+/* Pool configuration.  The defaults of the pages are sliding_window = 64
+ * frames and scale_frames = 8 ([FPS] "Sliding-Window Eviction Strategy"). */
+typedef struct {
+  int32_t num_layers;        /* >= 1                                               */
+  int32_t num_heads;         /* >= 1                                               */
+  int32_t head_dim;          /* must be 64                                         */
+  int32_t page_tokens;       /* tokens per frame = tokens per page, 1..65536       */
+  int32_t dtype;             /* kv_dtype of K, V, Q and the output                 */
+  int32_t scale_frames;      /* first frames never evicted nor scored (0 = none)   */
+  int32_t sliding_window;    /* persisted non-scale frames kept (0 = no window)    */
+  int32_t keyframe_interval; /* >= 1: frame t persists iff t < S or (t-S) % k == 0 */
+  int32_t pages_per_layer;   /* page ids per layer, >= 1                           */
+  int32_t max_queries;       /* largest n_q of stream_attend, >= 1                 */
+  int32_t max_splits;        /* split-KV partitions of one attention call, 1..64   */
+  int32_t max_window;        /* largest CLCES layer window, 1..8                   */
+} kv_pool_config;
+
+/* Parameters of one CLCES step ([SCV] 2.1.1-2.1.3): window W = 5 layers,
+ * lambda = 0.5 on the pages; keep_count = tokens kept (the budget). */
+typedef struct {
+  int32_t window;
+  int32_t reserved;
+  double lambda;
+  int64_t keep_count;
+} kv_clces_params;
+
+/* Cache statistics ([GCT] "Cache Monitoring", get_kv_cache_info()). */
+typedef struct {
+  int32_t persisted_frames; /* pages in the layer's table                         */
+  int32_t pages_used;       /* = persisted_frames                                 */
+  int32_t pages_free;
+  int32_t transient_pending;/* 1 if a transient frame waits for stream_attend     */
+  int64_t tokens;           /* tokens in the table (sum of page lengths)          */
+  int64_t bytes;            /* device bytes of the used pages                     */
+  int64_t evictions;        /* pages evicted by the window since the last reset   */
+  int64_t compactions;      /* score_and_compact steps that dropped tokens        */
+  int64_t last_keep_count;  /* tokens kept by the last such step                  */
+} kv_cache_info;
+
+/* Device memory layout of the pool, for callers that read pages directly.
+ * The pool holds num_layers * (pages_per_layer + 1) pages; page id p of layer
+ * l starts at byte (l * (pages_per_layer + 1) + p) * page_bytes; page id
+ * pages_per_layer of each layer is that layer's transient page.  Inside a
+ * page, with E = element size, Ts = token_stride (page_tokens rounded up to
+ * 64), H heads and D = 64:
+ *   K   at k_offset: [H][Ts][D]  -- token rows of each head, in slot order
+ *   V   at v_offset: [H][D][Ts]  -- each head's V stored transposed
+ *   ids at id_offset: int32 [Ts] -- global token id frame*page_tokens + slot
+ * Slots >= the page's length hold no data of the cache. */
+typedef struct {
+  int64_t page_bytes;
+  int64_t k_offset, v_offset, id_offset;
+  int32_t token_stride;
+  int32_t elem_bytes;
+} kv_pool_layout;
+
+/* Sizes of the pool and workspace buffers that kv_pool_create needs. */
+kv_status kv_pool_required_bytes(const kv_pool_config* cfg, size_t* pool_bytes,
+                                 size_t* workspace_bytes);
+
+kv_status kv_pool_get_layout(const kv_pool_config* cfg, kv_pool_layout* out);
+
+/* Create a pool over caller-owned device buffers of at least the required
+ * sizes (256-byte aligned).  With pool_dev == NULL and workspace_dev == NULL
+ * the pool is metadata-only: append/evict/score bookkeeping runs on the host
+ * but every call that would touch the device returns KV_ERR_STATE.
+ * The caller keeps ownership of both buffers; they must outlive the pool. */
+kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_bytes,
+                         void* workspace_dev, size_t workspace_bytes, kv_pool_t** out);
+
+kv_status kv_pool_destroy(kv_pool_t* pool);
+
+/* Drop every cached frame of every layer and reset statistics and frame
+ * order ([GCT] "Cache Initialization and Cleanup", clean_kv_cache()).
+ * Host-only; device contents are left as they are. */
+kv_status kv_reset(kv_pool_t* pool);
+
+/* Write frame frame_idx of one layer into the cache ([FPS] "Page-Aligned
+ * Tensor Layout", _write_patch_page; [GCT] "Frame-by-Frame Causal
+ * Processing").  k_dev, v_dev: [n_tokens][H][D] of the pool's dtype,
+ * n_tokens must equal page_tokens.  A keyframe (see kv_pool_config) gets the
+ * lowest free page id of the layer, appended at the end of its table; any
+ * other frame, or any frame with KV_TRANSIENT, goes to the layer's transient
+ * page and is attended by the next stream_attend only.  frame_idx must
+ * increase from call to call on a layer (KV_ERR_STATE otherwise, and also
+ * when a transient frame is still pending).  KV_ERR_NO_PAGES if no page id
+ * is free.  Asynchronous on stream. */
+kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev,
+                          const void* v_dev, int32_t n_tokens, uint32_t flags, void* stream);
+
+/* Sliding-window eviction ([GCT] "Sliding Window Eviction"; [FPS]
+ * "Sliding-Window Eviction Strategy", _apply_kv_cache_eviction_causal):
+ * while the layer holds more than sliding_window persisted non-scale frames,
+ * release the oldest one (whole page).  Scale frames are never evicted.
+ * Host metadata only, no device work.  n_evicted may be NULL. */
+kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted);
+
+/* Frame-to-cache attention ([GCT] "Frame-by-Frame Causal Processing" and
+ * "Scale-Frame Phase"): for each query row i and head h,
+ *   out[i,h,:] = sum_j softmax_j(sm_scale * q[i,h,:] . k[j,h,:]) v[j,h,:]
+ * over every token j of the layer's table in table order, plus the pending
+ * transient frame (which is consumed).  No token mask: a frame sees all of
+ * its own tokens and, in the scale phase, the other scale frames.
+ * q_dev, out_dev: [n_q][H][D] in the pool's dtype, 1 <= n_q <= max_queries.
+ * lse_dev: optional fp32 [n_q][H] = natural log of the softmax denominator
+ * (with the max included).  KV_ERR_STATE if the layer holds no token.
+ * Asynchronous on stream; bf16 inputs use MFMA with fp32 accumulation. */
+kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q,
+                        float sm_scale, void* out_dev, float* lse_dev, void* stream);
+
+/* One CLCES step on a layer ([SCV] 2.1.1-2.1.4; top-k keep and compaction as
+ * in [SCV] section 1 and [INF] "Rolling Memory").  Candidates: the tokens of
+ * the layer's table, scale-frame pages excluded, in table order (N of them).
+ * If N <= keep_count nothing happens and *n_kept = N.  Otherwise, for the
+ * window layers w = max(0, layer-W+1) .. layer:
+ *   R_w   = stable ascending rank of the raw score of each candidate at layer w
+ *   r_w   = R_w / (N-1);  mu, sigma = mean and population std. deviation of r
+ *   Cons  = max(0, 1 - sigma*sqrt(12));  s_hat = s_layer * (1 + lambda*Cons)
+ * (float64, fixed order, no fused multiply-add), keep the keep_count
+ * candidates first in (s_hat descending, index ascending) order, and pack
+ * each page's kept rows of K, V and token ids to the front of that page in
+ * their order; emptied pages are released.
+ * score_table_dev: fp32 [score_rows][num_layers], row = global token id.
+ * keep_ids_out_dev: optional int32 [keep_count], kept global token ids in
+ * table order.  ranks_out_dev: optional int32 [n_window][N], oldest window
+ * layer first.  n_kept: optional host int64.
+ * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
+ * for a token id >= score_rows or a bad parameter.  Synchronises the stream
+ * once to read the new page lengths. */
+kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_table_dev,
+                            int64_t score_rows, const kv_clces_params* params,
+                            int32_t* keep_ids_out_dev, int32_t* ranks_out_dev, int64_t* n_kept,
+                            void* stream);
+
+/* Statistics of a layer ([GCT] "Cache Monitoring"). */
+kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out);
+
+/* The layer's persisted table in logical order: page ids (layer-local),
+ * lengths and frame indices, cap entries at most; *n_out = table size (may
+ * exceed cap).  Any output pointer may be NULL. */
+kv_status kv_get_page_table(const kv_pool_t* pool, int32_t layer, int32_t* page_ids,
+                            int32_t* page_lens, int64_t* frame_ids, int32_t cap, int32_t* n_out);
+
+/* Split-KV partitions of stream_attend: 0 = automatic (default), else the
+ * number to use, capped by max_splits, the token tiles and the workspace. */
+kv_status kv_set_attend_splits(kv_pool_t* pool, int32_t splits);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSTREAM_H */
