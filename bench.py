@@ -1,0 +1,214 @@
+"""Benchmark of the streaming frame-to-cache step on one MI355X.
+
+Workload: one attention layer at the LingBot-Map frame shape -- 1004 tokens per
+frame, 16 heads x 64 dims, bf16, scale_frames 8, sliding window 64 frames,
+keyframe interval 1 -- streamed frame by frame with frame-correlated Q/K/V.
+The first 72 frames fill the cache (8 scale frames attended jointly, then
+frame by frame); every later frame is a steady-state step:
+
+    append(frame) -> evict(oldest) -> attend(1004 queries over 72,288 cached tokens)
+
+Untimed: the fill and ``--warmup`` steps.  Timed: exactly ``--steps`` steps,
+bracketed by device synchronisation; the inputs of every timed frame are
+generated into HBM before the clock starts.  With the defaults the stream is
+200 frames long (72 + 8 + 120).
+
+Printed: one JSON line (metric frames/s per layer) with the attention kernel's
+roofline position (MFMA-bound; algorithmic FLOP = 4*H*D*n_q*N per call) and
+the CPU oracle timed on this host as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk/CU)
+PEAK_HBM_GBS = 8000.0
+ATTEND_SOURCE = os.path.join(ROOT, "bounded_kv_cache_stream_amd", "csrc", "attend.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=120)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per attention call from the committed counter summary, if it matches this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(ATTEND_SOURCE):
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(frames_kv, q_frame, attended):
+    """The fp64 oracle on this host: one steady-state frame (all 1004 queries over 72 frames)."""
+    import numpy as np
+    from oracle import attention, window
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    sim = window.WindowCache(8, 64, 1, 73)
+    for t in range(attended[-1] + 1):  # policy bookkeeping of the whole stream so far
+        sim.append(t)
+        sim.evict()
+        sim.attended()
+    K = np.concatenate([frames_kv[f][0] for f in attended]).astype(np.float64)
+    V = np.concatenate([frames_kv[f][1] for f in attended]).astype(np.float64)
+    attention.attend(q_frame.astype(np.float64), K, V, 1.0)
+    sec = time.perf_counter() - t0
+    return {"value": 1.0 / sec, "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"one steady-state frame: 1004 queries x {K.shape[0]} cached tokens x 16 heads, fp64 numpy, "
+                      f"plus the window-policy simulation of {attended[-1] + 1} frames ({sec:.1f} s)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "
+                                   "without any exchange, and no multi-GPU run is part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+    from bounded_kv_cache_stream_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[1]
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    S, Wf = w["scale_frames"], w["window"]
+    cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
+                         keyframe_interval=1, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=16)
+    cache = kv.KVCache(cfg, device=dev)
+    if args.splits:
+        cache.set_splits(args.splits)
+    ar = synth.AR1Stream(1, 0, (T, H, D), device=dev)
+    fill = S + Wf  # frames 0..71 fill the cache; from frame 71 on the cache holds 72 frames
+    total = fill + args.warmup + args.steps
+
+    # generate every frame's inputs into HBM first
+    frames = [ar.next() for _ in range(total)]
+    torch.cuda.synchronize()
+
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    out_scale = torch.empty((S * T, H, D), dtype=torch.bfloat16, device=dev)
+    scale_q = []
+    for t in range(fill):
+        q, k, v = frames[t]
+        cache.append(0, t, k, v)
+        cache.evict(0)
+        if t < S:
+            scale_q.append(q)
+            if t == S - 1:
+                cache.attend(0, torch.cat(scale_q), 1.0, out=out_scale)
+        else:
+            cache.attend(0, q, 1.0, out=out)
+    assert cache.info(0)["persisted_frames"] == S + Wf
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(t, evp=None):
+        q, k, v = frames[t]
+        cache.append(0, t, k, v)
+        cache.evict(0)
+        if evp is not None:
+            evp[0].record(stream)
+        cache.attend(0, q, 1.0, out=out)
+        if evp is not None:
+            evp[1].record(stream)
+
+    for i in range(args.warmup):
+        step(fill + i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(fill + args.warmup + i, ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    info = cache.info(0)
+    assert info["persisted_frames"] == S + Wf and info["tokens"] == (S + Wf) * T
+
+    attend_ms = [a.elapsed_time(b) for a, b in ev]
+    attend_avg_s = sum(attend_ms) / len(attend_ms) / 1e3
+    n_keys = (S + Wf) * T
+    flops = 4.0 * H * D * T * n_keys
+    achieved = flops / attend_avg_s / 1e12
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": "frames/sec per layer at 1004 tok/frame, 72-frame cache; % bf16 MFMA peak",
+        "value": args.steps / (ms_total / 1e3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_total / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded AR(1) frame-correlated Q/K/V, bf16)",
+        "config": {"workload": w["name"], "tokens_per_frame": T, "heads": H, "head_dim": D,
+                   "cache_frames": S + Wf, "cached_tokens": n_keys, "scale_frames": S, "sliding_window": Wf,
+                   "keyframe_interval": 1, "step": "append+evict+attend", "layers": 1,
+                   "stream_frames": total},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(),
+                     "kernel": "stream_attend (attend_bf16_kernel + split-KV combine)",
+                     "avg_call_us": attend_avg_s * 1e6, "flop_per_call": flops},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        last = fill + args.warmup + args.steps - 1
+        attended = list(range(S)) + list(range(last - Wf + 1, last + 1))
+        frames_kv = {f: (frames[f][1].float().cpu().numpy(), frames[f][2].float().cpu().numpy()) for f in attended}
+        result["cpu_baseline"] = cpu_baseline(frames_kv, frames[last][0].float().cpu().numpy(), attended)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+"""GPU parity of score_and_compact (CLCES ranks, fused score, top-k, compaction).
+
+Bit-exact against the oracle: ranks of every window layer, the kept global
+token ids (index tie-break), page tables and the bytes of the compacted pages.
+Attention over the ragged pages left by compaction is checked within the
+bf16 tolerance.
+"""
+
+import numpy as np
+import pytest
+
+from bounded_kv_cache_stream_amd import kvstream as kv
+from bounded_kv_cache_stream_amd import synth
+from oracle import attention, budget
+from tests.gpu_common import assert_close, say, to64, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(layers, T, pages, H=16, window=5, scale_frames=0, max_queries=None, dtype=kv.KV_BF16):
+    return kv.make_config(num_layers=layers, num_heads=H, page_tokens=T, dtype=dtype, scale_frames=scale_frames,
+                          sliding_window=0, keyframe_interval=1, pages_per_layer=pages,
+                          max_queries=max_queries or T, max_splits=8, max_window=window)
+
+
+def _page_bytes_equal(cache, layer, page_id, n, k_rows, v_rows, ids):
+    """Compare the first n slots of a page with expected [n,H,D] K/V rows (CPU tensors) and ids, bit-exact."""
+    torch = cache.torch
+    k, vt, pid = cache.page_view(layer, page_id)
+    ek = k_rows.permute(1, 0, 2).contiguous()          # [H, n, D]
+    ev = v_rows.permute(1, 2, 0).contiguous()          # [H, D, n]
+    gk = k[:, :n, :].cpu()
+    gv = vt[:, :, :n].cpu()
+    assert torch.equal(gk.view(torch.int16), ek.view(torch.int16)), f"K bytes of page {page_id}"
+    assert torch.equal(gv.view(torch.int16), ev.view(torch.int16)), f"V bytes of page {page_id}"
+    assert pid[:n].cpu().numpy().tolist() == list(ids), f"token ids of page {page_id}"
+
+
+def _fill(cache, layer, frames, T, H, wid, host=None):
+    torch = cache.torch
+    for t in range(frames):
+        _, k, v = synth.iid_frame(wid, layer, t, (T, H, 64), device="cuda", dtype=torch.bfloat16)
+        cache.append(layer, t, k, v)
+        if host is not None:
+            host[t] = (k.cpu(), v.cpu())
+
+
+def test_clces_small_edge_cases():
+    torch = torch_cuda()
+    T, H, L = 64, 2, 3
+    cache = kv.KVCache(_cfg(L, T, 6, H=H), device="cuda")
+    for layer in range(L):
+        _fill(cache, layer, 4, T, H, 90)
+    scores = synth.raw_scores(90, 4 * T, L)
+    table = torch.from_numpy(scores).cuda()
+    # N <= keep: nothing happens
+    assert cache.score_and_compact(0, table, 5, 0.5, 4 * T) == 4 * T
+    assert cache.page_table(0)[1] == [T] * 4
+    # NaN score: error, state unchanged
+    bad = table.clone()
+    bad[5, 2] = float("nan")
+    with pytest.raises(kv.KVError) as e:
+        cache.score_and_compact(2, bad, 5, 0.5, 10)
+    assert e.value.status == kv.KV_ERR_NAN
+    assert cache.page_table(2)[1] == [T] * 4
+    # negative score likewise
+    bad = table.clone()
+    bad[7, 1] = -1.0
+    with pytest.raises(kv.KVError) as e:
+        cache.score_and_compact(1, bad, 5, 0.5, 10)
+    assert e.value.status == kv.KV_ERR_NAN
+    # score table too short for the token ids
+    with pytest.raises(kv.KVError) as e:
+        cache.score_and_compact(1, table[: 2 * T].contiguous(), 5, 0.5, 10)
+    assert e.value.status == kv.KV_ERR_ARG
+    assert cache.page_table(1)[1] == [T] * 4
+    # keep 0: every candidate page is released
+    assert cache.score_and_compact(1, table, 5, 0.5, 0) == 0
+    assert cache.page_table(1) == ([], [], [])
+    # ties everywhere (integer scores): index tie-break, window of one layer at layer 0
+    tie = torch.from_numpy(np.floor(scores / 8.0).astype(np.float32)).cuda()
+    ranks = torch.empty((1, 4 * T), dtype=torch.int32, device="cuda")
+    keep = torch.empty(77, dtype=torch.int32, device="cuda")
+    cache.score_and_compact(0, tie, 5, 0.5, 77, keep_ids=keep, ranks=ranks)
+    b = budget.BudgetCache(0, T, 77, 6)
+    for t in range(4):
+        b.append(t)
+    b.score_and_compact(np.floor(scores / 8.0).astype(np.float32))
+    assert ranks.cpu().numpy().tolist() == b.last["ranks"].tolist()
+    assert keep.cpu().numpy().tolist() == b.last["keep_ids"].tolist()
+    ids, lens, fr = cache.page_table(0)
+    assert list(zip(ids, fr, lens)) == b.page_table()
+
+
+def test_clces_scale_frames_protected():
+    torch = torch_cuda()
+    T, H = 64, 2
+    cache = kv.KVCache(_cfg(2, T, 6, H=H, scale_frames=2), device="cuda")
+    host = {}
+    _fill(cache, 1, 5, T, H, 91, host)
+    scores = synth.raw_scores(91, 5 * T, 2)
+    keep = torch.empty(100, dtype=torch.int32, device="cuda")
+    cache.score_and_compact(1, torch.from_numpy(scores).cuda(), 5, 0.5, 100, keep_ids=keep)
+    b = budget.BudgetCache(1, T, 100, 6, scale_frames=2)
+    for t in range(5):
+        b.append(t)
+    b.score_and_compact(scores)
+    assert keep.cpu().numpy().tolist() == b.last["keep_ids"].tolist()
+    ids, lens, fr = cache.page_table(1)
+    assert list(zip(ids, fr, lens)) == b.page_table()
+    for (pid, f, idv) in b.table:
+        sl = torch.from_numpy(idv - f * T)
+        _page_bytes_equal(cache, 1, pid, len(idv), host[f][0][sl], host[f][1][sl], idv)
+
+
+def test_budget_stream_small_ragged_pages():
+    # per frame: append -> attend over ragged pages -> score_and_compact, every frame checked
+    torch = torch_cuda()
+    T, H, L, B, F = 100, 4, 6, 230, 14
+    cache = kv.KVCache(_cfg(L, T, F, H=H, max_queries=T), device="cuda")
+    scores = synth.raw_scores(92, F * T, L)
+    table = torch.from_numpy(scores).cuda()
+    sims = [budget.BudgetCache(l, T, B, F) for l in range(L)]
+    streams = [synth.AR1Stream(92, l, (T, H, 64), device="cuda") for l in range(L)]
+    host = {l: {} for l in range(L)}
+    for t in range(F):
+        for l in range(L):
+            q, k, v = streams[l].next()
+            host[l][t] = (k.cpu(), v.cpu())
+            cache.append(l, t, k, v)
+            sims[l].append(t)
+            out = cache.attend(l, q, 1.0)
+            ids = sims[l].all_ids()
+            K = attention.gather_tokens(lambda f: host[l][f][0].float().numpy(), ids, T).astype(np.float64)
+            V = attention.gather_tokens(lambda f: host[l][f][1].float().numpy(), ids, T).astype(np.float64)
+            ref, _ = attention.attend(to64(q), K, V, 1.0)
+            assert_close(to64(out), ref, bf16=True, what=f"frame {t} layer {l}")
+            keep = torch.empty(B, dtype=torch.int32, device="cuda")
+            n_win = min(5, l + 1)
+            ranks = torch.empty((n_win, len(ids)), dtype=torch.int32, device="cuda")
+            n = cache.score_and_compact(l, table, 5, 0.5, B, keep_ids=keep, ranks=ranks)
+            ran = sims[l].score_and_compact(scores)
+            assert n == min(len(ids), B)
+            if ran:
+                assert ranks.cpu().numpy().tolist() == sims[l].last["ranks"].tolist(), (t, l)
+                assert keep.cpu().numpy().tolist() == sims[l].last["keep_ids"].tolist(), (t, l)
+            pids, lens, fr = cache.page_table(l)
+            assert list(zip(pids, fr, lens)) == sims[l].page_table(), (t, l)
+    # bytes of every page of the last layer
+    l = L - 1
+    for pid, f, idv in sims[l].table:
+        sl = torch.from_numpy(idv - f * T)
+        _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
+
+
+def test_clces_24_layers_72288_tokens_keep_half():
+    torch = torch_cuda()
+    w = synth.WORKLOADS[3]
+    T, H, L, F, K = w["tokens"], w["heads"], w["layers"], w["cache_frames"], w["keep"]
+    N = F * T
+    cache = kv.KVCache(_cfg(L, T, F, H=H), device="cuda")
+    check_bytes = {0, 4, 23}
+    host = {l: {} for l in check_bytes}
+    for l in range(L):
+        _fill(cache, l, F, T, H, 3, host.get(l))
+    scores = synth.raw_scores(3, N, L)
+    table = torch.from_numpy(scores).cuda()
+    for l in range(L):
+        n_win = min(w["clces_window"], l + 1)
+        ranks = torch.empty((n_win, N), dtype=torch.int32, device="cuda")
+        keep = torch.empty(K, dtype=torch.int32, device="cuda")
+        assert cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep, ranks=ranks) == K
+        b = budget.BudgetCache(l, T, K, F, window=w["clces_window"], lam=w["lam"])
+        for t in range(F):
+            b.append(t)
+        assert b.score_and_compact(scores)
+        assert np.array_equal(ranks.cpu().numpy(), b.last["ranks"]), f"ranks layer {l}"
+        assert np.array_equal(keep.cpu().numpy(), b.last["keep_ids"]), f"keep set layer {l}"
+        ids, lens, fr = cache.page_table(l)
+        assert list(zip(ids, fr, lens)) == b.page_table(), f"page table layer {l}"
+        if l in check_bytes:
+            for pid, f, idv in b.table:
+                sl = torch.from_numpy(idv - f * T)
+                _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
+        say(f"CLCES layer {l}: ranks, {K} kept ids and {len(ids)} page lengths bit-exact")
