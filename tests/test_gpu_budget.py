@@ -1,0 +1,86 @@
+"""GPU parity of the full 24-layer token-budget stack (500 frames).
+
+Per frame and layer: append -> attend over the (ragged) pages -> score and
+compact down to 128,512 tokens.  Page tables of every layer after every frame
+and the kept ids of every compaction step are compared with digests written
+from the oracle by tests/golden/make_budget_golden.py; attention is compared
+with the oracle on 128 sampled query rows at frames {130, 250, 499} of layers
+{0, 11, 23} (the oracle's retained ids come from its own simulation).
+"""
+
+import json
+import multiprocessing
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+import pytest
+
+from bounded_kv_cache_stream_amd import kvstream as kv
+from bounded_kv_cache_stream_amd import synth
+from oracle import attention
+from tests.golden.make_budget_golden import ids_digest, simulate_layer, table_digest
+from tests.gpu_common import assert_close, say, to64, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "budget_l24_f500.json")
+CHECK_FRAMES = (130, 250, 499)
+CHECK_LAYERS = (0, 11, 23)
+
+
+def test_budget_stack_24_layers_500_frames():
+    torch = torch_cuda()
+    w = synth.WORKLOADS[4]
+    T, H, L, B, F = w["tokens"], w["heads"], w["layers"], w["budget"], w["frames"]
+    gold = json.load(open(GOLDEN))
+    # the oracle's own simulation of the sampled layers runs on the host meanwhile
+    pool = ProcessPoolExecutor(len(CHECK_LAYERS), mp_context=multiprocessing.get_context("spawn"))
+    sims = {l: pool.submit(simulate_layer, l, None, CHECK_FRAMES) for l in CHECK_LAYERS}
+
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=0,
+                         keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16,
+                         max_window=w["clces_window"])
+    cache = kv.KVCache(cfg, device="cuda")
+    scores = synth.raw_scores(4, F * T, L)
+    table = torch.from_numpy(scores).cuda()
+    streams = [synth.AR1Stream(4, l, (T, H, 64), device="cuda") for l in range(L)]
+    host = {l: {} for l in CHECK_LAYERS}
+    rng = np.random.default_rng(4)
+    rows = {key: np.sort(rng.choice(T, 128, replace=False)) for key in
+            [(t, l) for t in CHECK_FRAMES for l in CHECK_LAYERS]}
+    saved = {}
+    keep = torch.empty(B, dtype=torch.int32, device="cuda")
+    for t in range(F):
+        for l in range(L):
+            q, k, v = streams[l].next()
+            if l in host:
+                host[l][t] = (k.cpu(), v.cpu())
+            cache.append(l, t, k, v)
+            out = cache.attend(l, q, w["sm_scale"])
+            if (t, l) in rows:
+                r = rows[(t, l)]
+                saved[(t, l)] = (to64(q)[r], to64(out)[r])
+            n = cache.score_and_compact(l, table, w["clces_window"], w["lam"], B, keep_ids=keep)
+            ids, lens, fr = cache.page_table(l)
+            assert table_digest(zip(ids, fr, lens)) == gold["tables"][str(l)][t], f"page table, frame {t} layer {l}"
+            g = gold["keeps"][str(l)][t]
+            if g is not None:
+                assert n == B
+                assert ids_digest(keep.cpu().numpy()) == g, f"kept ids, frame {t} layer {l}"
+        if t % 50 == 0 or t == F - 1:
+            say(f"budget stack: frame {t}, layer 23 holds {cache.info(23)['tokens']} tokens "
+                f"in {cache.info(23)['persisted_frames']} pages")
+    torch.cuda.synchronize()
+    for l in CHECK_LAYERS:
+        _, tables, _, attended = sims[l].result()
+        assert tables == gold["tables"][str(l)]
+        for t in CHECK_FRAMES:
+            ids = attended[t]
+            K = attention.gather_tokens(lambda f: host[l][f][0].float().numpy(), ids, T).astype(np.float64)
+            V = attention.gather_tokens(lambda f: host[l][f][1].float().numpy(), ids, T).astype(np.float64)
+            q64, o64 = saved[(t, l)]
+            ref, _ = attention.attend(q64, K, V, w["sm_scale"])
+            ma, rl = assert_close(o64, ref, bf16=True, what=f"frame {t} layer {l}")
+            say(f"attention frame {t} layer {l}: {len(ids)} tokens, max_abs {ma:.2e} rel_l2 {rl:.2e}")
+    pool.shutdown()
