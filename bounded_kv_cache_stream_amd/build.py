@@ -23,6 +23,9 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["attend.hip", "pages.hip", "clces.hip"]
+# per-file extra flags: keep MFMA accumulators in architectural VGPRs (the
+# softmax reads every score accumulator; AGPR copies would cost VALU slots)
+EXTRA_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HOST_SOURCES = ["kvstream.cpp"]
 
 HIPCC_FLAGS = [
@@ -51,7 +54,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

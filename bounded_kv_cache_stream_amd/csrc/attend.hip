@@ -8,17 +8,25 @@
 //
 // bf16 path (the hot one): flash-style online softmax with both contractions
 // on MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation.
-//   * workgroup = 4 waves = 128 query rows of one head; each wave owns 32 rows;
-//   * KV streamed in 64-token tiles, staged through LDS (K as [key][d], V as
-//     [d][key] -- the page already stores V transposed, so both LDS reads that
-//     feed the MFMAs are single 16-byte reads);
+//   * workgroup = 4 waves = 256 query rows of one head; each wave owns two
+//     32-row query blocks, so every K or V operand read from LDS feeds two
+//     MFMAs (LDS reads, LDS staging and HBM->LDS traffic per flop are halved
+//     against one block per wave);
+//   * KV streamed in 64-token tiles, double-buffered in LDS with the next
+//     tile's global loads in flight during the current tile (K as [key][d], V
+//     as [d][key] -- the page already stores V transposed, so both LDS reads
+//     that feed the MFMAs are single 16-byte reads);
 //   * scores are computed transposed, S^T = K Q^T, so each lane's accumulator
-//     column is one query: the row max / row sum need one cross-lane exchange
-//     (lane l with l^32), the O rescale is lane-local, and the accumulator
-//     registers are directly the B operand of O^T += V^T P^T.  For that, the
-//     A-operand row m of the K read is taken from key pi(m) with
+//     column is one query: the row max needs one cross-lane exchange (lane l
+//     with l^32), the O rescale is lane-local, and the accumulator registers
+//     are directly the B operand of O^T += V^T P^T.  For that, the A-operand
+//     row m of the K read is taken from key pi(m) with
 //     pi(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3), which makes the
 //     8 probabilities a lane holds for one 16-key MFMA step 8 consecutive keys;
+//   * online softmax in the log2 domain (exp2 on v_exp_f32); the running max
+//     is only raised when a tile exceeds it by more than 8 (probabilities stay
+//     below 2^8, O and l are rescaled rarely); the row sum is accumulated with
+//     v_dot2_f32_bf16 over the same bf16 probabilities that enter the PV MFMA;
 //   * the KV axis is split across workgroups (split-KV); partial (O, m, l) are
 //     merged by attend_combine.  Workgroup ids are remapped so that all query
 //     tiles of one (head, split) land on the same XCD and share its L2.
@@ -35,11 +43,12 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
-constexpr int BM = 128;      // query rows per workgroup
+constexpr int BM = kAttendRows;  // query rows per workgroup (4 waves x 64)
 constexpr int BN = kTile;    // keys per tile
 constexpr int LDS_LD = 72;   // bf16 per LDS row (64 + 8 pad)
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -59,9 +68,10 @@ __device__ inline int xcd_remap(int bid, int nwg) {
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-__global__ __launch_bounds__(256) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * LDS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[D * LDS_LD];
+// two waves per SIMD: 256 VGPRs per lane for the two query blocks' accumulators
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * LDS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * LDS_LD];
 
   const int H = g.heads;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -75,24 +85,28 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(PageGeom g, AttendPara
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int grp = lane >> 5;
-  const int qrow = qt * BM + wave * 32 + ql;
-  const bool qvalid = qrow < p.n_q;
-
+  // each wave owns two 32-row query blocks
+  int qrow[2];
+  bool qvalid[2];
   const bf16* q = static_cast<const bf16*>(p.q);
-  bf16x8 qf[4];
-  if (qvalid) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((int64_t)qrow * H + h) * D);
+  bf16x8 qf[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = src[2 * ks + grp];
-  } else {
+  for (int qb = 0; qb < 2; ++qb) {
+    qrow[qb] = qt * BM + wave * 64 + qb * 32 + ql;
+    qvalid[qb] = qrow[qb] < p.n_q;
+    if (qvalid[qb]) {
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((int64_t)qrow[qb] * H + h) * D);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8{};
+      for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = src[2 * ks + grp];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = bf16x8{};
+    }
   }
 
   const int t_begin = (int)((int64_t)sp * p.total_tiles / p.splits);
   const int t_end = (int)((int64_t)(sp + 1) * p.total_tiles / p.splits);
 
-  // entry holding tile t_begin (binary search on tile_start)
   int e = 0;
   {
     int lo = 0, hi = p.n_entries - 1;
@@ -103,20 +117,21 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(PageGeom g, AttendPara
     e = lo;
   }
 
-  f32x16 oacc[2];
+  f32x16 oacc[2][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; }
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { oacc[qb][0][i] = 0.f; oacc[qb][1][i] = 0.f; }
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
 
-  const int lrow = tid >> 3;  // 0..31
-  const int lchunk = tid & 7; // 8-element chunk
-  const int64_t head_k = (int64_t)h * g.ts * D;       // elements
-  const int64_t head_v = (int64_t)h * D * g.ts;       // elements
+  const int lrow = tid >> 3;
+  const int lchunk = tid & 7;
+  const int64_t head_k = (int64_t)h * g.ts * D;
+  const int64_t head_v = (int64_t)h * D * g.ts;
 
   bf16x8 kreg[2], vreg[2];
-  int cur_nvalid = 0;
-  auto load_tile = [&](int t, bf16x8* kr, bf16x8* vr) -> int {
+  auto load_tile = [&](int t) -> int {
     while (t >= p.table[e].tile_start + ((p.table[e].len + BN - 1) / BN)) ++e;
     const DevEntry en = p.table[e];
     const int row0 = (t - en.tile_start) * BN;
@@ -127,121 +142,149 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(PageGeom g, AttendPara
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int r = lrow + 32 * pp;
-      kr[pp] = *reinterpret_cast<const bf16x8*>(kt + r * D + lchunk * 8);
-      bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + (int64_t)r * g.ts + lchunk * 8);
-      if (nvalid < BN) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (lchunk * 8 + i >= nvalid) vv[i] = (bf16)0.f;
-      }
-      vr[pp] = vv;
+      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + r * D + lchunk * 8);
+      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + (int64_t)r * g.ts + lchunk * 8);
     }
     return nvalid;
   };
-
-  if (t_begin < t_end) cur_nvalid = load_tile(t_begin, kreg, vreg);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int nvalid = cur_nvalid;
+  auto stage = [&](int b, int nvalid) {
+    if (nvalid < BN) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (lchunk * 8 + i >= nvalid) vreg[pp][i] = (bf16)0.f;
+    }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int r = lrow + 32 * pp;
-      *reinterpret_cast<bf16x8*>(&Ks[r * LDS_LD + lchunk * 8]) = kreg[pp];
-      *reinterpret_cast<bf16x8*>(&Vs[r * LDS_LD + lchunk * 8]) = vreg[pp];
+      *reinterpret_cast<bf16x8*>(&Ks[b][r * LDS_LD + lchunk * 8]) = kreg[pp];
+      *reinterpret_cast<bf16x8*>(&Vs[b][r * LDS_LD + lchunk * 8]) = vreg[pp];
     }
-    __syncthreads();
-    if (t + 1 < t_end) cur_nvalid = load_tile(t + 1, kreg, vreg);
+  };
 
-    // S^T = K_pi Q^T : two 32-key blocks
-    f32x16 sacc[2];
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  const f32x16 zero = {};
+  const int krow0 = perm_key(ql);
+  int nv_cur = BN, nv_nxt = BN;
+  if (t_begin < t_end) {
+    nv_cur = load_tile(t_begin);
+    stage(0, nv_cur);
+    if (t_begin + 1 < t_end) nv_nxt = load_tile(t_begin + 1);
+  }
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int b = (t - t_begin) & 1;
+    __syncthreads();  // tile t is in buffer b; buffer b^1 (tile t-1) is free
+    const int nvalid = nv_cur;
+    if (t + 1 < t_end) stage(b ^ 1, nv_nxt);
+    int nv_after = BN;
+    if (t + 2 < t_end) nv_after = load_tile(t + 2);
+
+    // S^T = K_pi Q^T for both query blocks; each K operand feeds two MFMAs
+    f32x16 sc[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int krow = 32 * kb + perm_key(ql);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[b][(32 * kb + krow0) * LDS_LD + ks * 16 + grp * 8]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[krow * LDS_LD + ks * 16 + grp * 8]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
+        for (int qb = 0; qb < 2; ++qb)
+          sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks == 0 ? zero : sc[qb][kb], 0, 0, 0);
       }
-    }
 
-    // key of accumulator register r of block kb: 32*kb + 16*(r>>3) + 8*grp + (r&7)
-    if (nvalid < BN) {
+    bf16x8 pb[2][2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // key of accumulator register r of block kb: 32*kb + 16*(r>>3) + 8*grp + (r&7)
+      if (nvalid < BN) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 16 * (r >> 3) + 8 * grp + (r & 7) >= nvalid) sc[qb][kb][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float mt = mx * p.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + 8.f) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { oacc[qb][0][i] *= alpha; oacc[qb][1][i] *= alpha; }
+      }
+      const float nm = -m_run[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + 16 * (r >> 3) + 8 * grp + (r & 7) >= nvalid) sacc[kb][r] = -INFINITY;
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    float lsum = 0.f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -m_new));
-        lsum += pv;
-        pb[kb][r >> 3][r & 7] = (bf16)pv;
-      }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
+          pb[qb][kb][r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[qb][kb][r], p.scale_log2, nm));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[(32 * db + ql) * LDS_LD + 32 * kb + 16 * s + 8 * grp]);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][s], oacc[db], 0, 0, 0);
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x2 pr = {pb[qb][kb][s][2 * j], pb[qb][kb][s][2 * j + 1]};
+            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
+          }
+    }
+
+    // O^T += V^T P^T for both query blocks; each V operand feeds two MFMAs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[b][(32 * db + ql) * LDS_LD + 32 * kb + 16 * s + 8 * grp]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][kb][s], oacc[qb][db], 0, 0, 0);
         }
-    __syncthreads();
+    nv_cur = nv_nxt;
+    nv_nxt = nv_after;
   }
 
-  const float l_tot = l_run + wave_xor32(l_run);
-  if (!qvalid) return;
-  if (p.splits == 1) {
-    const float inv = 1.f / l_tot;
-    bf16* out = static_cast<bf16*>(p.out) + ((int64_t)qrow * H + h) * D;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = l_run[qb] + wave_xor32(l_run[qb]);
+    if (!qvalid[qb]) continue;
+    if (p.splits == 1) {
+      const float inv = 1.f / l_tot;
+      bf16* out = static_cast<bf16*>(p.out) + ((int64_t)qrow[qb] * H + h) * D;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        bf16x4 o;
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = (bf16)(oacc[db][rb * 4 + j] * inv);
-        *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * rb + 4 * grp) = o;
+        for (int rb = 0; rb < 4; ++rb) {
+          bf16x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = (bf16)(oacc[qb][db][rb * 4 + j] * inv);
+          *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * rb + 4 * grp) = o;
+        }
+      if (p.lse && grp == 0) p.lse[(int64_t)qrow[qb] * H + h] = (m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
+    } else {
+      const int64_t row = ((int64_t)sp * p.n_q + qrow[qb]) * H + h;
+      float* po = p.part_o + row * D;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          f32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = oacc[qb][db][rb * 4 + j];
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rb + 4 * grp) = o;
+        }
+      if (grp == 0) {
+        p.part_ml[row * 2 + 0] = m_run[qb];
+        p.part_ml[row * 2 + 1] = l_tot;
       }
-    if (p.lse && grp == 0) p.lse[(int64_t)qrow * H + h] = (m_run + __builtin_log2f(l_tot)) * kLn2;
-  } else {
-    const int64_t row = ((int64_t)sp * p.n_q + qrow) * H + h;
-    float* po = p.part_o + row * D;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        f32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = oacc[db][rb * 4 + j];
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rb + 4 * grp) = o;
-      }
-    if (grp == 0) {
-      p.part_ml[row * 2 + 0] = m_run;
-      p.part_ml[row * 2 + 1] = l_tot;
     }
   }
 }

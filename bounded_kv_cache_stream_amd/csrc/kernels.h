@@ -9,6 +9,7 @@ namespace kvs {
 
 constexpr int kHeadDim = 64;
 constexpr int kTile = 64;  // KV tile (tokens) of the attention kernel, and page-stride unit
+constexpr int kAttendRows = 256;  // query rows per attention workgroup
 
 // One entry of the device copy of a layer's attended table.
 struct DevEntry {

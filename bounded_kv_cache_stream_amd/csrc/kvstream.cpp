@@ -285,12 +285,12 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   const bool bf16 = pool->cfg.dtype == KV_BF16;
   int32_t splits = 1;
   if (bf16) {
-    const int64_t qtiles = (n_q + 127) / 128;
+    const int64_t qtiles = (n_q + kvs::kAttendRows - 1) / kvs::kAttendRows;
     const int64_t base = qtiles * pool->cfg.num_heads;
     if (pool->splits_override > 0) {
       splits = pool->splits_override;
     } else {
-      const int64_t target = 1024;  // workgroups to fill 256 CUs x 4 slots
+      const int64_t target = 1024;  // workgroups: two rounds of 256 CUs x 2 resident workgroups
       splits = (int32_t)std::max<int64_t>(1, (target + base / 2) / base);
     }
     splits = std::min<int32_t>(splits, pool->cfg.max_splits);
