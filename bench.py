@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["stream", "clces"], default="stream",
+                    help="stream: the attention step (default); clces: score_and_compact on the 24-layer cache")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -89,8 +91,64 @@ def cpu_baseline(frames_kv, q_frame, attended):
                       f"plus the window-policy simulation of {attended[-1] + 1} frames ({sec:.1f} s)"}
 
 
+def moved_tokens(keep_mask_pages):
+    """Tokens a page-local left-pack moves: kept slots after the page's first dropped slot."""
+    n = 0
+    for m in keep_mask_pages:
+        drop = [i for i, k in enumerate(m) if not k]
+        if drop:
+            n += sum(1 for i in range(drop[0], len(m)) if m[i])
+    return n
+
+
+def run_clces(args):
+    """score_and_compact on 24 layers x 72 frames x 1004 tokens, W=5, lambda=0.5, keep 50%."""
+    import numpy as np
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+    from bounded_kv_cache_stream_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[3]
+    T, H, L, F, K = w["tokens"], w["heads"], w["layers"], w["cache_frames"], w["keep"]
+    N = F * T
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=0,
+                         keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=8, max_window=5)
+    cache = kv.KVCache(cfg, device=dev)
+    for l in range(L):
+        for t in range(F):
+            _, k, v = synth.iid_frame(3, l, t, (T, H, 64), device=dev, dtype=torch.bfloat16)
+            cache.append(l, t, k, v)
+    table = torch.from_numpy(synth.raw_scores(3, N, L)).to(dev)
+    keep = torch.empty(K, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    times = []
+    moved = 0
+    for l in range(L):
+        t0 = time.perf_counter()
+        cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep)
+        times.append(time.perf_counter() - t0)  # the call synchronises once (new page lengths)
+        kept = set(keep.cpu().numpy().tolist())
+        moved += moved_tokens([[(t * T + j) in kept for j in range(T)] for t in range(F)])
+    times.sort()
+    med = times[len(times) // 2]
+    bytes_per_layer = moved / L * 2 * H * 64 * 2 * 2  # read + write of K and V rows, bf16
+    print(json.dumps({
+        "metric": "score_and_compact us per layer (CLCES W=5, lambda=0.5, keep 50%)", "value": med * 1e6,
+        "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": L, "dtype": "fp64 score / bf16 pages",
+        "data": "synthetic (seeded chi-square raw scores, iid N(0,1) K/V)",
+        "config": {"workload": w["name"], "layers": L, "tokens": N, "keep": K, "window": w["clces_window"]},
+        "p90_us": times[int(0.9 * (L - 1))] * 1e6, "moved_tokens_per_layer": moved / L,
+        "compaction_bytes_per_layer": bytes_per_layer,
+    }), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "clces":
+        return run_clces(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "

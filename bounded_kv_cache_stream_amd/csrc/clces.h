@@ -19,10 +19,10 @@ struct ClcesSizes {
   int64_t n_max;
   int32_t p_max, w_max, nblk_max;
   size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts, plan,
-      flag, total;
+      kidx, first_drop, flag, total;
 };
 
-ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max);
+ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_max);
 
 struct ClcesArgs {
   char* ws;  // start of the CLCES workspace region

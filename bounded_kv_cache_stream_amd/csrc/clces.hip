@@ -91,6 +91,24 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   g.scur[idx] = __uint_as_float(order_key(s));
 }
 
+// Block-wide exclusive scan of one value per thread (1024 threads max).
+template <int NT>
+__device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    int32_t t = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += t;
+    __syncthreads();
+  }
+  const int32_t incl = lds[tid];
+  if (total) *total = lds[NT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
 __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* hist, int N, int nblk,
                                                              int shift, const int32_t* flag) {
   if (*flag) return;
@@ -107,42 +125,28 @@ __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* key
   hist[((int64_t)w * 256 + tid) * nblk + blk] = cnt[tid];
 }
 
-// Exclusive scan of one segment's [256][nblk] histogram, in place.
-__global__ __launch_bounds__(1024) void rank_scan_kernel(uint32_t* hist, int nblk, const int32_t* flag) {
-  if (*flag) return;
-  __shared__ uint32_t sums[1024];
-  const int tid = threadIdx.x;
-  const int64_t M = 256 * (int64_t)nblk;
-  uint32_t* h = hist + blockIdx.x * M;
-  const int64_t per = (M + 1023) / 1024;
-  const int64_t b = tid * per, e = b + per < M ? b + per : M;
-  uint32_t local = 0;
-  for (int64_t i = b; i < e; ++i) local += h[i];
-  sums[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    uint32_t v = tid >= off ? sums[tid - off] : 0u;
-    __syncthreads();
-    sums[tid] += v;
-    __syncthreads();
-  }
-  uint32_t run = sums[tid] - local;
-  for (int64_t i = b; i < e; ++i) {
-    uint32_t v = h[i];
-    h[i] = run;
-    run += v;
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
                                                                 uint32_t* keys_out, uint32_t* vals_out,
                                                                 int32_t* ranks, const uint32_t* hist, int N,
                                                                 int nblk, int shift, int last, const int32_t* flag) {
   if (*flag) return;
   __shared__ uint32_t base[256], run[256], wcnt[4][256];
+  __shared__ int32_t scan[kThreads];
   const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  base[tid] = hist[((int64_t)w * 256 + tid) * nblk + blk];
+  // offset of this block's digit-tid keys: keys of smaller digits in the whole
+  // segment, plus keys of digit tid in the blocks before this one
+  {
+    const uint32_t* hrow = hist + ((int64_t)w * 256 + tid) * nblk;
+    uint32_t tot = 0, before = 0;
+    for (int bb = 0; bb < nblk; ++bb) {
+      const uint32_t v = hrow[bb];
+      tot += v;
+      before += bb < blk ? v : 0u;
+    }
+    const int32_t digit_base = block_excl_scan<kThreads>((int32_t)tot, scan, nullptr);
+    base[tid] = (uint32_t)digit_base + before;
+  }
   run[tid] = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
@@ -217,41 +221,58 @@ __global__ __launch_bounds__(kThreads) void fuse_kernel(const int32_t* ranks, co
   shat[i] = (unsigned long long)__double_as_longlong(sh);
 }
 
-// State after `passes` select passes: digits fixed so far and how many of the
-// elements matching them are still to be taken (from the largest down).
-__device__ SelState select_state(const uint32_t* sel_hist, long long keep, int passes, uint32_t* lds) {
-  __shared__ SelState st;
-  if (threadIdx.x == 0) st = SelState{0ull, keep};
+// One select step: from the state before pass p and that pass's digit
+// histogram, fix digit p (the largest digit whose suffix count reaches k_rem)
+// and reduce k_rem by the count of larger digits.  Wave 0 runs a suffix scan
+// over its 64 lanes (4 digits each); the result is broadcast through LDS.
+__device__ SelState select_advance(SelState st, const uint32_t* hist, int p) {
+  __shared__ uint32_t cnt[256];
+  __shared__ SelState out;
+  cnt[threadIdx.x] = hist[threadIdx.x];
+  if (threadIdx.x == 0) out = st;
   __syncthreads();
-  for (int p = 0; p < passes; ++p) {
-    lds[threadIdx.x] = sel_hist[p * 256 + threadIdx.x];
-    __syncthreads();
-    if (threadIdx.x == 0 && st.k_rem > 0) {
-      long long cum = 0;
-      for (int d = 255; d >= 0; --d) {
-        const long long c = lds[d];
+  if (threadIdx.x < 64 && st.k_rem > 0) {
+    const int lane = threadIdx.x;
+    long long own = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) own += cnt[4 * lane + j];
+    long long suf = own;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += t;
+    }
+    long long above = __shfl_down(suf, 1, 64);  // lanes > lane
+    if (lane == 63) above = 0;
+    if (above < st.k_rem && suf >= st.k_rem) {
+      long long cum = above;
+      for (int j = 3; j >= 0; --j) {
+        const long long c = cnt[4 * lane + j];
         if (cum + c >= st.k_rem) {
-          st.prefix |= (unsigned long long)d << (56 - 8 * p);
-          st.k_rem -= cum;
+          out.prefix = st.prefix | ((unsigned long long)(4 * lane + j) << (56 - 8 * p));
+          out.k_rem = st.k_rem - cum;
           break;
         }
         cum += c;
       }
     }
-    __syncthreads();
   }
-  SelState out = st;
   __syncthreads();
-  return out;
+  const SelState r = out;
+  __syncthreads();
+  return r;
 }
 
+// Pass p histograms digit p of the keys that match the digits fixed so far.
+// The state before pass p is advanced once from the previous pass's state
+// (stored by its workgroup 0) and histogram; workgroup 0 stores it in turn.
 __global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned long long* keys, int N,
-                                                               uint32_t* sel_hist, long long keep, int p,
-                                                               const int32_t* flag) {
+                                                               uint32_t* sel_hist, SelState* states, long long keep,
+                                                               int p, const int32_t* flag) {
   if (*flag) return;
-  __shared__ uint32_t lds[256];
   __shared__ uint32_t cnt[256];
-  const SelState st = select_state(sel_hist, keep, p, lds);
+  const SelState st = p == 0 ? SelState{0ull, keep} : select_advance(states[p - 1], sel_hist + (p - 1) * 256, p - 1);
+  if (blockIdx.x == 0 && threadIdx.x == 0) states[p] = st;
   cnt[threadIdx.x] = 0;
   __syncthreads();
   const int shift = 56 - 8 * p;
@@ -274,17 +295,16 @@ struct MarkArgs {
   long long keep;
   int32_t* n_gt;
   int32_t* n_eq;
-  SelState* final_state;
+  SelState* states;  // [0..7] states before each pass, [8] the final threshold
   const int32_t* flag;
 };
 
 __global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
   if (*a.flag) return;
-  __shared__ uint32_t lds[256];
   __shared__ int32_t sg, se;
-  SelState st = select_state(a.sel_hist, a.keep, 8, lds);
-  if (a.keep == 0) st = SelState{~0ull, 0};
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.final_state = st;
+  // threshold = the keep_count-th largest key; keep 0 keeps nothing
+  SelState st = a.keep == 0 ? SelState{~0ull, 0} : select_advance(a.states[7], a.sel_hist + 7 * 256, 7);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.states[8] = st;
   if (threadIdx.x == 0) { sg = 0; se = 0; }
   __syncthreads();
   const DevEntry en = a.entries[blockIdx.x];
@@ -307,28 +327,10 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
   }
 }
 
-// Block-wide exclusive scan of one value per thread (1024 threads max).
-template <int NT>
-__device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int32_t t = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += t;
-    __syncthreads();
-  }
-  const int32_t incl = lds[tid];
-  if (total) *total = lds[NT - 1];
-  __syncthreads();
-  return incl - v;
-}
-
 struct PlanArgs {
   const int32_t* n_gt;
   const int32_t* n_eq;
-  const SelState* final_state;
+  const SelState* final_state;  // states[8]
   int32_t* eq_base;
   int32_t* keep_base;
   int32_t* new_len;
@@ -365,6 +367,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 
 struct CompactArgs {
   const DevEntry* entries;
+  uint16_t* kidx;        // [P][ts] kept slots per page
+  int32_t* first_drop;   // [P]
   const unsigned long long* shat;
   const SelState* final_state;
   const int32_t* eq_base;
@@ -376,35 +380,37 @@ struct CompactArgs {
   const int32_t* flag;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+// Per page: the kept slots in order (kidx[0..new_len)) and the first dropped
+// slot.  Ties at the threshold are kept in index order: the page's tie rank
+// base comes from the plan step.
+__global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   if (*a.flag) return;
-  __shared__ uint16_t kidx[kMaxPageTokensScored];
   __shared__ int32_t scan[kThreads];
-  const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
-  const int H = a.g.heads;
+  __shared__ int32_t first_drop;
+  const int e = blockIdx.x, tid = threadIdx.x;
   const DevEntry en = a.entries[e];
-  const int len = en.len, nl = a.new_len[e];
-  const bool ids_part = part == 2 * H;
-  if (!ids_part && nl == len) return;  // nothing dropped: K and V stay
-
-  // kept slots of this page in order: kidx[0..nl)
+  const int len = en.len;
   const SelState st = *a.final_state;
   const int per = (len + kThreads - 1) / kThreads;
   const int b = tid * per, end = min(b + per, len);
   const unsigned long long* sh = a.shat + en.tok_start;
+  if (tid == 0) first_drop = len;
   int32_t n_eq = 0;
   for (int j = b; j < end; ++j) n_eq += sh[j] == st.prefix;
   const int32_t eq_start = a.eq_base[e] + block_excl_scan<kThreads>(n_eq, scan, nullptr);
   int32_t eq_rank = eq_start;
   int32_t n_keep = 0;
+  int my_drop = len;
   for (int j = b; j < end; ++j) {
     const unsigned long long k = sh[j];
     bool keep = k > st.prefix;
     if (k == st.prefix) keep = eq_rank++ < st.k_rem;
     n_keep += keep;
+    if (!keep && j < my_drop) my_drop = j;
   }
+  if (my_drop < len) atomicMin(&first_drop, my_drop);
   int32_t pos = block_excl_scan<kThreads>(n_keep, scan, nullptr);
+  uint16_t* kidx = a.kidx + (int64_t)e * a.g.ts;
   eq_rank = eq_start;
   for (int j = b; j < end; ++j) {
     const unsigned long long k = sh[j];
@@ -413,55 +419,111 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     if (keep) kidx[pos++] = (uint16_t)j;
   }
   __syncthreads();
+  if (tid == 0) a.first_drop[e] = first_drop;
+}
+
+constexpr int kStageBytes = 16384;  // LDS staging of V^T rows in the compaction kernel
+constexpr int kVSplit = 2;          // workgroups per V head (each takes 64 / kVSplit rows)
+
+// One workgroup per (page, K head | V head part | token ids): move the kept slots
+// of the page to its front.  Slots before the first dropped one stay.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+  if (*a.flag) return;
+  __shared__ uint16_t kidx[kMaxPageTokensScored];
+  __shared__ __attribute__((aligned(16))) char stage_buf[kStageBytes];
+  const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int H = a.g.heads;
+  const DevEntry en = a.entries[e];
+  const int len = en.len, nl = a.new_len[e];
+  const bool ids_part = part == (1 + kVSplit) * H;
+  if (!ids_part && nl == len) return;  // nothing dropped: K and V stay
+  const int fd = a.first_drop[e];     // slots [0, fd) are kept in place
+  const uint16_t* gk = a.kidx + (int64_t)e * a.g.ts;
+  for (int i = fd + tid; i < nl; i += kThreads) kidx[i] = gk[i];
+  __syncthreads();
 
   char* page = a.pool + (int64_t)en.phys * a.g.page_bytes;
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte vector
+  typedef int4 V16;
   if (part < H) {
-    // K rows of head `part`: 64 elements each, moved as 16-byte vectors
+    // K rows of head `part`: out row i <- row kidx[i]; 8 threads per row,
+    // 8 row groups in flight per thread (256 rows per step)
     constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
-    typedef int4 V16;
+    constexpr int TPR = 8;                    // threads per row
+    constexpr int UPR = VPR / TPR;            // vectors per thread per row
+    constexpr int G = 8;
+    constexpr int RPS = kThreads / TPR * G;
     V16* rows = reinterpret_cast<V16*>(page + a.g.k_off) + (int64_t)part * a.g.ts * VPR;
-    constexpr int RPS = kThreads / 8;  // rows per step, 8 threads per row
-    const int r = tid >> 3, c = tid & 7;
-    for (int i0 = 0; i0 < nl; i0 += RPS) {
-      const int i = i0 + r;
-      const int src = i < nl ? kidx[i] : i;
-      const bool move = i < nl && src != i;
-      V16 v[VPR / 8];
-      if (move)
+    const int r = tid / TPR, c = tid % TPR;
+    for (int i0 = fd; i0 < nl; i0 += RPS) {
+      V16 v[G][UPR];
 #pragma unroll
-        for (int u = 0; u < VPR / 8; ++u) v[u] = rows[(int64_t)src * VPR + c + 8 * u];
+      for (int gq = 0; gq < G; ++gq) {
+        const int i = i0 + gq * (kThreads / TPR) + r;
+        if (i < nl)
+#pragma unroll
+          for (int u = 0; u < UPR; ++u) v[gq][u] = rows[(int64_t)kidx[i] * VPR + c + TPR * u];
+      }
       __syncthreads();
-      if (move)
 #pragma unroll
-        for (int u = 0; u < VPR / 8; ++u) rows[(int64_t)i * VPR + c + 8 * u] = v[u];
+      for (int gq = 0; gq < G; ++gq) {
+        const int i = i0 + gq * (kThreads / TPR) + r;
+        if (i < nl)
+#pragma unroll
+          for (int u = 0; u < UPR; ++u) rows[(int64_t)i * VPR + c + TPR * u] = v[gq][u];
+      }
       __syncthreads();
     }
-  } else if (part < 2 * H) {
-    // V^T rows (one per d) of head part-H: out[i] = row[kidx[i]], 8 outputs per thread
-    const int h = part - H;
-    T* vt = reinterpret_cast<T*>(page + a.g.v_off) + (int64_t)h * kHeadDim * a.g.ts;
-    const int d = tid >> 3, c = tid & 7;  // 32 rows x 64 outputs per step
-    for (int dh = 0; dh < kHeadDim; dh += 32) {
-      T* row = vt + (int64_t)(dh + d) * a.g.ts;
-      for (int i0 = 0; i0 < nl; i0 += 64) {
-        T v[8];
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + c * 8 + u;
-          const int src = i < nl ? kidx[i] : i;
-          any |= i < nl && src != i;
-          v[u] = i < nl && src != i ? row[src] : T(0.f);
+  } else if (part < (1 + kVSplit) * H) {
+    // V^T rows (one per d) of one head, 64 / kVSplit of them per workgroup:
+    // stage whole rows in LDS (the in-place hazard is per row), then write
+    // out[i] = row[kidx[i]] for i >= fd as 16-byte vectors.  A row of up to
+    // 8192 bf16 (4096 fp32) fits the staging buffer; a longer fp32 row takes
+    // the chunked gather path below.
+    const int h = (part - H) / kVSplit, dpart = (part - H) % kVSplit;
+    constexpr int DR = kHeadDim / kVSplit;
+    T* vt = reinterpret_cast<T*>(page + a.g.v_off) + ((int64_t)h * kHeadDim + dpart * DR) * a.g.ts;
+    const int rowv = (len + VEC - 1) / VEC;             // vectors to stage per row
+    const int rows_per = max(1, kStageBytes / (rowv * 16));
+    const int v0 = fd / VEC;                            // first output vector that changes
+    const int v1 = (nl + VEC - 1) / VEC;
+    T* stage = reinterpret_cast<T*>(stage_buf);
+    if (rowv * 16 <= kStageBytes) {
+      for (int d0 = 0; d0 < DR; d0 += rows_per) {
+        const int nr = min(rows_per, DR - d0);
+        for (int x = tid; x < nr * rowv; x += kThreads) {
+          const int rr = x / rowv, cv = x % rowv;
+          reinterpret_cast<V16*>(stage)[rr * rowv + cv] =
+              reinterpret_cast<const V16*>(vt + (int64_t)(d0 + rr) * a.g.ts)[cv];
         }
         __syncthreads();
-        if (any) {
+        const int nvo = v1 - v0;
+        for (int x = tid; x < nr * nvo; x += kThreads) {
+          const int rr = x / nvo, cv = v0 + x % nvo;
+          T o[VEC];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = i0 + c * 8 + u;
-            if (i < nl && kidx[i] != i) row[i] = v[u];
+          for (int u = 0; u < VEC; ++u) {
+            const int i = cv * VEC + u;
+            o[u] = stage[rr * rowv * VEC + (i < fd ? i : (i < nl ? kidx[i] : min(i, len - 1)))];
           }
+          *reinterpret_cast<V16*>(vt + (int64_t)(d0 + rr) * a.g.ts + cv * VEC) = *reinterpret_cast<V16*>(o);
         }
         __syncthreads();
+      }
+    } else {
+      // a row longer than the staging buffer: gather in output chunks; every
+      // source of a chunk lies at or after its outputs, so reading the whole
+      // chunk's sources before writing it is safe
+      for (int d = 0; d < DR; ++d) {
+        T* row = vt + (int64_t)d * a.g.ts;
+        for (int i0 = fd; i0 < nl; i0 += kThreads) {
+          const int i = i0 + tid;
+          T x = i < nl ? row[kidx[i]] : T(0.f);
+          __syncthreads();
+          if (i < nl) row[i] = x;
+          __syncthreads();
+        }
       }
     }
   } else {
@@ -471,10 +533,10 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     for (int i0 = 0; i0 < nl; i0 += kThreads) {
       const int i = i0 + tid;
       int32_t id = 0;
-      if (i < nl) id = ids[kidx[i]];
+      if (i < nl) id = ids[i < fd ? i : kidx[i]];
       __syncthreads();
       if (i < nl) {
-        if (kidx[i] != i) ids[i] = id;
+        if (i >= fd) ids[i] = id;
         if (a.keep_ids_out) a.keep_ids_out[kb + i] = id;
       }
       __syncthreads();
@@ -484,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
 
 }  // namespace
 
-ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max) {
+ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_max) {
   ClcesSizes z{};
   z.n_max = n_max;
   z.p_max = p_max;
@@ -506,10 +568,12 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max) {
   z.shat = take((size_t)n_max * 8);
   z.hist = take((size_t)w_max * 256 * z.nblk_max * 4);
   z.sel_hist = take(8 * 256 * 4);
-  z.sel_state = take(sizeof(SelState));
+  z.sel_state = take(9 * sizeof(SelState));
   z.entries = take((size_t)p_max * sizeof(DevEntry));
   z.counts = take((size_t)p_max * 2 * 4);
   z.plan = take((size_t)p_max * 3 * 4);
+  z.kidx = take((size_t)p_max * ts_max * 2);
+  z.first_drop = take((size_t)p_max * 4);
   z.flag = take(4);
   z.total = off;
   return z;
@@ -553,7 +617,6 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
     rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift, flag);
-    rank_scan_kernel<<<dim3((unsigned)W), dim3(1024), 0, s>>>(hist, nblk, flag);
     rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(
         kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
     std::swap(kin, kout);
@@ -564,14 +627,17 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
       ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), flag);
   if (a.keep > 0) {
     for (int p = 0; p < 8; ++p)
-      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, a.keep, p, flag);
+      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, a.keep, p,
+                                                                         flag);
   }
   MarkArgs m{entries, shat, sel_hist, a.keep, counts, counts + P, sel_state, flag};
   mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
-  PlanArgs pa{counts, counts + P, sel_state, plan, plan + P, plan + 2 * P, P, flag};
+  PlanArgs pa{counts, counts + P, sel_state + 8, plan, plan + P, plan + 2 * P, P, flag};
   plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(pa);
-  CompactArgs ca{entries, shat, sel_state, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag};
-  dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
+  CompactArgs ca{entries, reinterpret_cast<uint16_t*>(ws + z.kidx), reinterpret_cast<int32_t*>(ws + z.first_drop),
+                 shat, sel_state + 8, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag};
+  index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
+  dim3 cg((unsigned)P, (unsigned)((1 + kVSplit) * a.geom.heads + 1));
   if (a.geom.esize == 2)
     compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
   else

@@ -100,7 +100,8 @@ Layout make_layout(const kv_pool_config* c) {
   off = align_up(off + (size_t)L.part_rows * H * D * 4);
   L.part_ml = off;
   off = align_up(off + (size_t)L.part_rows * H * 2 * 4);
-  L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window);
+  L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window,
+                          (int32_t)ts);
   L.clces = off;
   off = align_up(off + L.cl.total);
   L.ws_bytes = off;
