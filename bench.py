@@ -43,8 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["stream", "clces"], default="stream",
-                    help="stream: the attention step (default); clces: score_and_compact on the 24-layer cache")
+    ap.add_argument("--workload", choices=["stream", "clces", "append"], default="stream",
+                    help="stream: the attention step (default); clces: score_and_compact on the 24-layer "
+                         "cache; append: one frame's page write for 24 layers in one launch")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -145,10 +146,63 @@ def run_clces(args):
     }), flush=True)
 
 
+def run_append(args):
+    """kv_append_frame_layers: one 1004-token frame of 24 layers (197.4 MB read + written) per step."""
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, T, H, D = 24, 1004, 16, 64
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=4,
+                         keyframe_interval=1, pages_per_layer=5, max_queries=T, max_splits=4)
+    cache = kv.KVCache(cfg, device=dev)
+    frames = [(torch.randn(L, T, H, D, device=dev).bfloat16(), torch.randn(L, T, H, D, device=dev).bfloat16())
+              for _ in range(4)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t, evp=None):
+        k, v = frames[t % 4]
+        if evp is not None:
+            evp[0].record(stream)
+        cache.append_layers(0, t, k, v)
+        if evp is not None:
+            evp[1].record(stream)
+        for l in range(L):
+            cache.evict(l)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    nbytes = 2 * 2 * L * T * H * D * 2  # K and V, read and written, bf16
+    t0 = time.perf_counter()
+    for l in range(L):
+        cache.evict(l)
+    evict_us = (time.perf_counter() - t0) / L * 1e6
+    print(json.dumps({
+        "metric": "page write GB/s (one 1004-token frame x 24 layers per launch)", "value": nbytes / (med * 1e-3) / 1e9,
+        "unit": "GB/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic N(0,1)", "config": {"workload": "append_l24_t1004_h16_d64", "layers": L},
+        "ms_per_launch_median": med, "bytes_per_launch": nbytes,
+        "roofline": {"bound": "hbm", "achieved": nbytes / (med * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "evict_host_us_per_layer": evict_us,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "clces":
         return run_clces(args)
+    if args.workload == "append":
+        return run_append(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "

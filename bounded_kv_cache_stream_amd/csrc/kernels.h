@@ -40,6 +40,16 @@ hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStr
 hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
                          int64_t first_token_id, hipStream_t s);
 
+// Destination pages of one multi-layer append launch (byte offsets into the pool).
+constexpr int kAppendLayersChunk = 128;
+struct AppendLayers {
+  int64_t page_offset[kAppendLayersChunk];
+};
+// k, v: [n_layers][n_tokens][H][D]; n_layers <= kAppendLayersChunk.
+hipError_t launch_append_layers(const PageGeom& g, char* pool, const AppendLayers& al, int n_layers,
+                                const void* k, const void* v, int n_tokens, int64_t first_token_id,
+                                hipStream_t s);
+
 struct AttendParams {
   const void* q;
   void* out;

@@ -235,6 +235,47 @@ kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, con
   return ok();
 }
 
+kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, int64_t frame_idx,
+                                 const void* k_dev, const void* v_dev, int32_t n_tokens, uint32_t flags,
+                                 void* stream) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  if (n_layers < 1 || first_layer < 0 || first_layer + n_layers > pool->cfg.num_layers)
+    return fail(KV_ERR_ARG, "layers %d..%d out of range", first_layer, first_layer + n_layers - 1);
+  if (n_tokens != pool->cfg.page_tokens)
+    return fail(KV_ERR_SHAPE, "n_tokens %d != page_tokens %d", n_tokens, pool->cfg.page_tokens);
+  if (frame_idx < 0) return fail(KV_ERR_ARG, "negative frame index");
+  if (frame_idx > (int64_t)(INT32_MAX / pool->cfg.page_tokens) - 1)
+    return fail(KV_ERR_ARG, "frame index %lld too large for 32-bit token ids", (long long)frame_idx);
+  if (flags & ~KV_TRANSIENT) return fail(KV_ERR_ARG, "unknown flags 0x%x", flags);
+  std::vector<int32_t> pages((size_t)n_layers);
+  for (int32_t i = 0; i < n_layers; ++i) {  // check every layer before changing any
+    auto& L = pool->layers[(size_t)(first_layer + i)];
+    int rc = L.plan_append(frame_idx, (flags & KV_TRANSIENT) != 0, &pages[(size_t)i]);
+    if (rc == 1)
+      return fail(KV_ERR_STATE, "layer %d: frame %lld after frame %lld%s", first_layer + i, (long long)frame_idx,
+                  (long long)L.last_frame, L.transient_pending ? " (a transient frame is still pending)" : "");
+    if (rc == 2)
+      return fail(KV_ERR_NO_PAGES, "layer %d: all %d page ids in use", first_layer + i, pool->cfg.pages_per_layer);
+  }
+  if (!pool->meta_only) {
+    if (!k_dev || !v_dev) return fail(KV_ERR_ARG, "k or v is NULL");
+    const int64_t frame_bytes = (int64_t)n_tokens * pool->cfg.num_heads * kvs::kHeadDim * pool->lay.geom.esize;
+    for (int32_t c0 = 0; c0 < n_layers; c0 += kvs::kAppendLayersChunk) {
+      const int32_t nc = std::min<int32_t>(kvs::kAppendLayersChunk, n_layers - c0);
+      kvs::AppendLayers al;
+      for (int32_t i = 0; i < nc; ++i)
+        al.page_offset[i] = phys_page(pool, first_layer + c0 + i, pages[(size_t)(c0 + i)]) * pool->lay.geom.page_bytes;
+      hipError_t e = kvs::launch_append_layers(pool->lay.geom, pool->pool, al, nc,
+                                               static_cast<const char*>(k_dev) + c0 * frame_bytes,
+                                               static_cast<const char*>(v_dev) + c0 * frame_bytes, n_tokens,
+                                               frame_idx * pool->cfg.page_tokens, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "multi-layer page write launch");
+    }
+  }
+  for (int32_t i = 0; i < n_layers; ++i) pool->layers[(size_t)(first_layer + i)].commit_append(frame_idx, pages[(size_t)i]);
+  return ok();
+}
+
 kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;

@@ -23,14 +23,12 @@ struct Vec8 {
   T v[8];
 };
 
+// One workgroup: tokens t0..t0+63 of head h of one frame into one page.
 template <typename T>
-__global__ __launch_bounds__(256) void append_kernel(PageGeom g, char* page, const T* __restrict__ k,
-                                                     const T* __restrict__ v, int n_tokens,
-                                                     int64_t first_id) {
+__device__ void append_block(const PageGeom& g, char* page, const T* __restrict__ k, const T* __restrict__ v,
+                             int n_tokens, int64_t first_id, int h, int t0) {
   __shared__ T vt[64][D + 1];
   const int H = g.heads;
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
   const int tid = threadIdx.x;
   const int r = tid >> 3;      // 0..31
   const int c = tid & 7;       // chunk of 8 elements
@@ -68,12 +66,42 @@ __global__ __launch_bounds__(256) void append_kernel(PageGeom g, char* page, con
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(PageGeom g, char* page, const T* __restrict__ k,
+                                                     const T* __restrict__ v, int n_tokens, int64_t first_id) {
+  append_block<T>(g, page, k, v, n_tokens, first_id, blockIdx.y, blockIdx.x * 64);
+}
+
+// Several layers' frames in one launch: blockIdx.z = layer within the chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void append_layers_kernel(PageGeom g, char* pool, AppendLayers al,
+                                                            const T* __restrict__ k, const T* __restrict__ v,
+                                                            int n_tokens, int64_t first_id) {
+  const int64_t frame_elems = (int64_t)n_tokens * g.heads * D;
+  const int z = blockIdx.z;
+  append_block<T>(g, pool + al.page_offset[z], k + z * frame_elems, v + z * frame_elems, n_tokens, first_id,
+                  blockIdx.y, blockIdx.x * 64);
+}
+
 __global__ void table_upload_kernel(DevEntry* dst, TableChunk chunk) {
   const int i = threadIdx.x;
   if (i < chunk.count) dst[chunk.first + i] = chunk.e[i];
 }
 
 }  // namespace
+
+hipError_t launch_append_layers(const PageGeom& g, char* pool, const AppendLayers& al, int n_layers,
+                                const void* k, const void* v, int n_tokens, int64_t first_token_id,
+                                hipStream_t s) {
+  dim3 grid((unsigned)(g.ts / 64), (unsigned)g.heads, (unsigned)n_layers);
+  if (g.esize == 2)
+    append_layers_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, pool, al, static_cast<const __bf16*>(k),
+                                                             static_cast<const __bf16*>(v), n_tokens, first_token_id);
+  else
+    append_layers_kernel<float><<<grid, dim3(256), 0, s>>>(g, pool, al, static_cast<const float*>(k),
+                                                            static_cast<const float*>(v), n_tokens, first_token_id);
+  return hipGetLastError();
+}
 
 hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStream_t s) {
   for (int first = 0; first < n; first += kUploadChunk) {

@@ -20,7 +20,7 @@ KV_TRANSIENT = 1
 
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
-    "kv_append_frame", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
+    "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
     "kv_get_page_table", "kv_set_attend_splits", "kv_last_error",
 )
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "kv_pool_destroy": [P],
             "kv_reset": [P],
             "kv_append_frame": [P, I32, I64, P, P, I32, U32, P],
+            "kv_append_frame_layers": [P, I32, I32, I64, P, P, I32, U32, P],
             "kv_evict": [P, I32, ctypes.POINTER(I32)],
             "stream_attend": [P, I32, P, I32, F32, P, P, P],
             "score_and_compact": [P, I32, P, I64, ctypes.POINTER(kv_clces_params), P, P, ctypes.POINTER(I64), P],
@@ -134,6 +135,12 @@ def kv_reset(pool) -> None:
 
 def kv_append_frame(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags=0, stream=None) -> None:
     _check(lib().kv_append_frame(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, stream))
+
+
+def kv_append_frame_layers(pool, first_layer, n_layers, frame_idx, k_ptr, v_ptr, n_tokens, flags=0,
+                           stream=None) -> None:
+    _check(lib().kv_append_frame_layers(pool, first_layer, n_layers, frame_idx, k_ptr, v_ptr, n_tokens, flags,
+                                        stream))
 
 
 def kv_evict(pool, layer) -> int:
@@ -233,6 +240,21 @@ class KVCache:
             return
         kv_append_frame(self.handle, layer, frame_idx, self._tensor(k), self._tensor(v), k.shape[0], flags,
                         self._stream())
+
+    def append_layers(self, first_layer, frame_idx, k=None, v=None, n_layers=None, transient=False):
+        """k, v: [n_layers, T, H, D] contiguous (one frame of several layers)."""
+        flags = KV_TRANSIENT if transient else 0
+        if self.device is None:
+            kv_append_frame_layers(self.handle, first_layer, n_layers, frame_idx, None, None, self.cfg.page_tokens,
+                                   flags, None)
+            return
+        if k.dim() != 4 or k.shape != v.shape:
+            raise ValueError("k and v must be [n_layers, T, H, D] tensors of the same shape")
+        self._tensor(k[0])
+        if not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("k and v must be contiguous")
+        kv_append_frame_layers(self.handle, first_layer, k.shape[0], frame_idx, ctypes.c_void_p(k.data_ptr()),
+                               ctypes.c_void_p(v.data_ptr()), k.shape[1], flags, self._stream())
 
     def evict(self, layer) -> int:
         return kv_evict(self.handle, layer)

@@ -58,7 +58,7 @@ typedef struct {
   int32_t num_layers;        /* >= 1                                               */
   int32_t num_heads;         /* >= 1                                               */
   int32_t head_dim;          /* must be 64                                         */
-  int32_t page_tokens;       /* tokens per frame = tokens per page, 1..65536       */
+  int32_t page_tokens;       /* tokens per frame = tokens per page, 1..8192        */
   int32_t dtype;             /* kv_dtype of K, V, Q and the output                 */
   int32_t scale_frames;      /* first frames never evicted nor scored (0 = none)   */
   int32_t sliding_window;    /* persisted non-scale frames kept (0 = no window)    */
@@ -141,6 +141,14 @@ kv_status kv_reset(kv_pool_t* pool);
  * is free.  Asynchronous on stream. */
 kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev,
                           const void* v_dev, int32_t n_tokens, uint32_t flags, void* stream);
+
+/* The same page write for layers first_layer .. first_layer+n_layers-1 in one
+ * launch: k_dev, v_dev are [n_layers][n_tokens][H][D] (layer-major, each layer's
+ * frame as for kv_append_frame).  Every layer is checked first; on any error no
+ * layer changes.  Asynchronous on stream. */
+kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, int64_t frame_idx,
+                                 const void* k_dev, const void* v_dev, int32_t n_tokens, uint32_t flags,
+                                 void* stream);
 
 /* Sliding-window eviction ([GCT] "Sliding Window Eviction"; [FPS]
  * "Sliding-Window Eviction Strategy", _apply_kv_cache_eviction_causal):

@@ -192,3 +192,28 @@ def test_long_stream_keyframe4_10000_frames():
         ma, rl = assert_close(on.astype(np.float64), ref, bf16=True, what=f"long stream frame {t}")
         assert max_abs(ln.astype(np.float64).reshape(ref_lse.shape), ref_lse) <= LSE_ABS
         say(f"long stream frame {t}: {len(att)} frames attended, max_abs {ma:.2e} rel_l2 {rl:.2e}")
+
+
+def test_multi_layer_append_matches_single_layer_append():
+    torch = torch_cuda()
+    T, H, L = 100, 4, 3
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=2,
+                         keyframe_interval=1, pages_per_layer=3, max_queries=T, max_splits=4)
+    a = kv.KVCache(cfg, device="cuda")
+    b = kv.KVCache(cfg, device="cuda")
+    for t in range(5):
+        k = torch.randn(L, T, H, 64, device="cuda").bfloat16()
+        v = torch.randn(L, T, H, 64, device="cuda").bfloat16()
+        a.append_layers(0, t, k, v)
+        for l in range(L):
+            b.append(l, t, k[l].contiguous(), v[l].contiguous())
+            a.evict(l)
+            b.evict(l)
+    torch.cuda.synchronize()
+    for l in range(L):
+        ids, lens, fr = a.page_table(l)
+        assert (ids, lens, fr) == b.page_table(l)
+        for pid, n in zip(ids, lens):
+            for x, y in zip(a.page_view(l, pid), b.page_view(l, pid)):
+                assert torch.equal(x.cpu().view(torch.uint8) if x.dtype != torch.int32 else x.cpu(),
+                                   y.cpu().view(torch.uint8) if y.dtype != torch.int32 else y.cpu())

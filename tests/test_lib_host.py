@@ -164,3 +164,20 @@ def test_reset_replay_identical_and_sizes():
     assert lay["page_bytes"] == 2 * 16 * 1024 * 64 * 2 + 1024 * 4
     pool, ws = kv.kv_pool_required_bytes(cfg)
     assert pool == 74 * lay["page_bytes"]
+
+
+def test_multi_layer_append_is_all_or_nothing():
+    c = _meta_pool(1, 4, 1, 6, layers=3)
+    for t in range(3):
+        c.append_layers(0, t, n_layers=3)
+    assert [c.page_table(l)[2] for l in range(3)] == [[0, 1, 2]] * 3
+    c.append(2, 3)  # layer 2 is one frame ahead
+    with pytest.raises(kv.KVError) as e:
+        c.append_layers(0, 3, n_layers=3)
+    assert e.value.status == kv.KV_ERR_STATE
+    assert [c.page_table(l)[2] for l in range(2)] == [[0, 1, 2]] * 2  # no layer changed
+    c.append_layers(0, 3, n_layers=2)
+    assert [c.page_table(l)[2] for l in range(3)] == [[0, 1, 2, 3]] * 3
+    with pytest.raises(kv.KVError) as e:
+        c.append_layers(1, 4, n_layers=3)  # layers 1..3 of a 3-layer pool
+    assert e.value.status == kv.KV_ERR_ARG
