@@ -332,7 +332,10 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
     if (pool->splits_override > 0) {
       splits = pool->splits_override;
     } else {
-      const int64_t target = 1024;  // workgroups: two rounds of 256 CUs x 2 resident workgroups
+      // one full round of resident workgroups (256 CUs x 2): split counts that
+      // leave a partial round run measurably slower, and fewer splits write
+      // fewer partials for the combine
+      const int64_t target = 512;
       splits = (int32_t)std::max<int64_t>(1, (target + base / 2) / base);
     }
     splits = std::min<int32_t>(splits, pool->cfg.max_splits);
