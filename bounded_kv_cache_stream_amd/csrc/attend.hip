@@ -13,9 +13,13 @@
 //     MFMAs (LDS reads, LDS staging and HBM->LDS traffic per flop are halved
 //     against one block per wave);
 //   * KV streamed in 64-token tiles, double-buffered in LDS with the next
-//     tile's global loads in flight during the current tile (K as [key][d], V
-//     as [d][key] -- the page already stores V transposed, so both LDS reads
-//     that feed the MFMAs are single 16-byte reads);
+//     tile's global loads in flight during the current tile; K and V are both
+//     [key][d] in the page and in LDS.  The K operand is one 16-byte LDS read;
+//     the V^T operand of the PV product (8 consecutive keys of one d per lane)
+//     comes from two ds_read_b64_tr_b16 transposing reads: within each group
+//     of 16 lanes, lane i receives element i%4 of the 8-byte pieces addressed
+//     by lanes 4j + i/4 (j = 0..3), so lanes that address 4 key rows x 16
+//     columns receive 4 keys of one column each;
 //   * scores are computed transposed, S^T = K Q^T, so each lane's accumulator
 //     column is one query: the row max needs one cross-lane exchange (lane l
 //     with l^32), the O rescale is lane-local, and the accumulator registers
@@ -46,12 +50,19 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
 constexpr int BM = kAttendRows;  // query rows per workgroup (4 waves x 64)
 constexpr int BN = kTile;    // keys per tile
 constexpr int LDS_LD = 72;   // bf16 per LDS row (64 + 8 pad)
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Transposing LDS read (ds_read_b64_tr_b16) of four bf16.
+__device__ inline bf16x4 lds_read_tr4(const bf16* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
 
 __device__ inline int perm_key(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
@@ -71,7 +82,7 @@ __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 // two waves per SIMD: 256 VGPRs per lane for the two query blocks' accumulators
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * LDS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * LDS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * LDS_LD];
 
   const int H = g.heads;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -127,8 +138,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
-  const int64_t head_k = (int64_t)h * g.ts * D;
-  const int64_t head_v = (int64_t)h * D * g.ts;
+  const int64_t head_off = (int64_t)h * g.ts * D;
 
   bf16x8 kreg[2], vreg[2];
   auto load_tile = [&](int t) -> int {
@@ -137,23 +147,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int row0 = (t - en.tile_start) * BN;
     const int nvalid = min(BN, en.len - row0);
     const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
-    const bf16* kt = reinterpret_cast<const bf16*>(page + g.k_off) + head_k + (int64_t)row0 * D;
-    const bf16* vt = reinterpret_cast<const bf16*>(page + g.v_off) + head_v + row0;
+    const bf16* kt = reinterpret_cast<const bf16*>(page + g.k_off) + head_off + (int64_t)row0 * D;
+    const bf16* vt = reinterpret_cast<const bf16*>(page + g.v_off) + head_off + (int64_t)row0 * D;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int r = lrow + 32 * pp;
       kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + r * D + lchunk * 8);
-      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + (int64_t)r * g.ts + lchunk * 8);
+      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + r * D + lchunk * 8);
     }
     return nvalid;
   };
   auto stage = [&](int b, int nvalid) {
     if (nvalid < BN) {
+      // keys past the page's length: zero V rows (their probabilities are 0)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (lchunk * 8 + i >= nvalid) vreg[pp][i] = (bf16)0.f;
+        if (lrow + 32 * pp >= nvalid) vreg[pp] = bf16x8{};
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
@@ -166,6 +175,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
   const f32x16 zero = {};
   const int krow0 = perm_key(ql);
+  // V^T operand of lane l for one MFMA step: keys 8*(l/32) + 0..7, column l%32.
+  // Transposing-read addresses: lane L names key row 8*(L/32) + (L/4)%4 and
+  // columns 16*((L/16)%2) + 4*(L%4) + 0..3; a second read 4 rows lower gives
+  // keys 4..7.
+  const int vtr_row = 8 * (lane >> 5) + ((lane >> 2) & 3);
+  const int vtr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int nv_cur = BN, nv_nxt = BN;
   if (t_begin < t_end) {
     nv_cur = load_tile(t_begin);
@@ -243,7 +258,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[b][(32 * db + ql) * LDS_LD + 32 * kb + 16 * s + 8 * grp]);
+          const bf16* vp = &Vs[b][(32 * kb + 16 * s + vtr_row) * LDS_LD + 32 * db + vtr_col];
+          const bf16x8 a = __builtin_shufflevector(lds_read_tr4(vp), lds_read_tr4(vp + 4 * LDS_LD), 0, 1, 2, 3, 4,
+                                                   5, 6, 7);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][kb][s], oacc[qb][db], 0, 0, 0);
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(PageGeom g, AttendParam
     const DevEntry en = p.table[e];
     const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
     const float* kt = reinterpret_cast<const float*>(page + g.k_off) + (int64_t)h * g.ts * D;
-    const float* vt = reinterpret_cast<const float*>(page + g.v_off) + ((int64_t)h * D + lane) * g.ts;
+    const float* vt = reinterpret_cast<const float*>(page + g.v_off) + (int64_t)h * g.ts * D;
     for (int j = 0; j < en.len; ++j) {
       float s = qv * kt[(int64_t)j * D + lane];
 #pragma unroll
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(PageGeom g, AttendParam
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       const float pv = __builtin_amdgcn_exp2f(x - m_new);
       l_run = l_run * alpha + pv;
-      o = o * alpha + pv * vt[j];
+      o = o * alpha + pv * vt[(int64_t)j * D + lane];
       m_run = m_new;
     }
   }

@@ -20,10 +20,11 @@
 //            bits over the 64-bit pattern, which orders non-negative doubles);
 //   mark     per page: count of s_hat above / equal to the threshold;
 //   plan     per page: rank base among ties (index order), kept count, offset;
-//   compact  one workgroup per (page, K head | V head | token ids): gather the
-//            kept slots to the page's front, in chunks whose reads all finish
-//            before their writes (every source slot is at or after its
-//            destination, so no chunk overwrites data a later chunk reads).
+//   compact  per page: one workgroup per K head, one per V head and one for
+//            the token ids; each gathers the kept slots to the page's front
+//            in chunks whose reads all finish before their writes (every
+//            source slot is at or after its destination, so no chunk
+//            overwrites data a later chunk reads).
 
 #include <hip/hip_runtime.h>
 
@@ -422,110 +423,73 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   if (tid == 0) a.first_drop[e] = first_drop;
 }
 
-constexpr int kStageBytes = 16384;  // LDS staging of V^T rows in the compaction kernel
-constexpr int kVSplit = 2;          // workgroups per V head (each takes 64 / kVSplit rows)
+// Wait for this thread's outstanding vector-memory loads (vmcnt = 0).  Placed
+// before the barrier that separates a chunk's reads from its in-place writes,
+// so no other wave's write can overtake a read still in flight.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One workgroup per (page, K head | V head part | token ids): move the kept slots
-// of the page to its front.  Slots before the first dropped one stay.
+typedef int V16 __attribute__((ext_vector_type(4)));  // a native vector: a struct copy would go through scratch
+
+// Left-pack the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes
+// each): row i <- row kidx[i] for fd <= i < nl.  8 threads per row; every
+// thread holds 16 vectors, so one step moves 512 bf16 rows (256 fp32 rows)
+// with a single barrier between its reads and its writes.  A step's sources lie
+// at or after its first output, so no earlier step writes them, and no barrier
+// is needed after the writes.
+template <typename T>
+__device__ inline void compact_rows(V16* rows, const uint16_t* gk, int fd, int nl, int tid) {
+  constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
+  constexpr int TPR = 8;                    // threads per row
+  constexpr int UPR = VPR / TPR;            // vectors per thread per row
+  constexpr int G = 16 / UPR;               // row groups per step
+  constexpr int RPS = kThreads / TPR * G;   // rows per step
+  const int r = tid / TPR, c = tid % TPR;
+  for (int i0 = fd; i0 < nl; i0 += RPS) {
+    // rows past nl load slot 0 (in bounds, never stored), so every load is
+    // unconditional and the block stays in registers
+    V16 v[G][UPR];
+    int src[G];
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq) {
+      const int i = i0 + gq * (kThreads / TPR) + r;
+      src[gq] = i < nl ? gk[i] : 0;
+    }
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq)
+#pragma unroll
+      for (int u = 0; u < UPR; ++u) v[gq][u] = rows[src[gq] * VPR + c + TPR * u];
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq) {
+      const int i = i0 + gq * (kThreads / TPR) + r;
+      if (i < nl)
+#pragma unroll
+        for (int u = 0; u < UPR; ++u) rows[i * VPR + c + TPR * u] = v[gq][u];
+    }
+  }
+}
+
+// Move the kept slots of each page to its front; slots before the first
+// dropped one stay.  Grid (page, part): part < H is the K block of head
+// `part`, H <= part < 2H the V block of head part - H, part 2H the token ids.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   if (*a.flag) return;
-  __shared__ uint16_t kidx[kMaxPageTokensScored];
-  __shared__ __attribute__((aligned(16))) char stage_buf[kStageBytes];
   const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
   const int H = a.g.heads;
   const DevEntry en = a.entries[e];
   const int len = en.len, nl = a.new_len[e];
-  const bool ids_part = part == (1 + kVSplit) * H;
+  const bool ids_part = part == 2 * H;
   if (!ids_part && nl == len) return;  // nothing dropped: K and V stay
   const int fd = a.first_drop[e];     // slots [0, fd) are kept in place
   const uint16_t* gk = a.kidx + (int64_t)e * a.g.ts;
-  for (int i = fd + tid; i < nl; i += kThreads) kidx[i] = gk[i];
-  __syncthreads();
-
   char* page = a.pool + (int64_t)en.phys * a.g.page_bytes;
-  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte vector
-  typedef int4 V16;
-  if (part < H) {
-    // K rows of head `part`: out row i <- row kidx[i]; 8 threads per row,
-    // 8 row groups in flight per thread (256 rows per step)
-    constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
-    constexpr int TPR = 8;                    // threads per row
-    constexpr int UPR = VPR / TPR;            // vectors per thread per row
-    constexpr int G = 8;
-    constexpr int RPS = kThreads / TPR * G;
-    V16* rows = reinterpret_cast<V16*>(page + a.g.k_off) + (int64_t)part * a.g.ts * VPR;
-    const int r = tid / TPR, c = tid % TPR;
-    for (int i0 = fd; i0 < nl; i0 += RPS) {
-      V16 v[G][UPR];
-#pragma unroll
-      for (int gq = 0; gq < G; ++gq) {
-        const int i = i0 + gq * (kThreads / TPR) + r;
-        if (i < nl)
-#pragma unroll
-          for (int u = 0; u < UPR; ++u) v[gq][u] = rows[(int64_t)kidx[i] * VPR + c + TPR * u];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int gq = 0; gq < G; ++gq) {
-        const int i = i0 + gq * (kThreads / TPR) + r;
-        if (i < nl)
-#pragma unroll
-          for (int u = 0; u < UPR; ++u) rows[(int64_t)i * VPR + c + TPR * u] = v[gq][u];
-      }
-      __syncthreads();
-    }
-  } else if (part < (1 + kVSplit) * H) {
-    // V^T rows (one per d) of one head, 64 / kVSplit of them per workgroup:
-    // stage whole rows in LDS (the in-place hazard is per row), then write
-    // out[i] = row[kidx[i]] for i >= fd as 16-byte vectors.  A row of up to
-    // 8192 bf16 (4096 fp32) fits the staging buffer; a longer fp32 row takes
-    // the chunked gather path below.
-    const int h = (part - H) / kVSplit, dpart = (part - H) % kVSplit;
-    constexpr int DR = kHeadDim / kVSplit;
-    T* vt = reinterpret_cast<T*>(page + a.g.v_off) + ((int64_t)h * kHeadDim + dpart * DR) * a.g.ts;
-    const int rowv = (len + VEC - 1) / VEC;             // vectors to stage per row
-    const int rows_per = max(1, kStageBytes / (rowv * 16));
-    const int v0 = fd / VEC;                            // first output vector that changes
-    const int v1 = (nl + VEC - 1) / VEC;
-    T* stage = reinterpret_cast<T*>(stage_buf);
-    if (rowv * 16 <= kStageBytes) {
-      for (int d0 = 0; d0 < DR; d0 += rows_per) {
-        const int nr = min(rows_per, DR - d0);
-        for (int x = tid; x < nr * rowv; x += kThreads) {
-          const int rr = x / rowv, cv = x % rowv;
-          reinterpret_cast<V16*>(stage)[rr * rowv + cv] =
-              reinterpret_cast<const V16*>(vt + (int64_t)(d0 + rr) * a.g.ts)[cv];
-        }
-        __syncthreads();
-        const int nvo = v1 - v0;
-        for (int x = tid; x < nr * nvo; x += kThreads) {
-          const int rr = x / nvo, cv = v0 + x % nvo;
-          T o[VEC];
-#pragma unroll
-          for (int u = 0; u < VEC; ++u) {
-            const int i = cv * VEC + u;
-            o[u] = stage[rr * rowv * VEC + (i < fd ? i : (i < nl ? kidx[i] : min(i, len - 1)))];
-          }
-          *reinterpret_cast<V16*>(vt + (int64_t)(d0 + rr) * a.g.ts + cv * VEC) = *reinterpret_cast<V16*>(o);
-        }
-        __syncthreads();
-      }
-    } else {
-      // a row longer than the staging buffer: gather in output chunks; every
-      // source of a chunk lies at or after its outputs, so reading the whole
-      // chunk's sources before writing it is safe
-      for (int d = 0; d < DR; ++d) {
-        T* row = vt + (int64_t)d * a.g.ts;
-        for (int i0 = fd; i0 < nl; i0 += kThreads) {
-          const int i = i0 + tid;
-          T x = i < nl ? row[kidx[i]] : T(0.f);
-          __syncthreads();
-          if (i < nl) row[i] = x;
-          __syncthreads();
-        }
-      }
-    }
+  if (!ids_part) {
+    constexpr int VPR = 64 * sizeof(T) / 16;
+    const int h = part < H ? part : part - H;
+    V16* rows = reinterpret_cast<V16*>(page + (part < H ? a.g.k_off : a.g.v_off)) + (int64_t)h * a.g.ts * VPR;
+    compact_rows<T>(rows, gk, fd, nl, tid);
   } else {
     // token ids, and the list of kept ids in table order
     int32_t* ids = reinterpret_cast<int32_t*>(page + a.g.id_off);
@@ -533,13 +497,13 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     for (int i0 = 0; i0 < nl; i0 += kThreads) {
       const int i = i0 + tid;
       int32_t id = 0;
-      if (i < nl) id = ids[i < fd ? i : kidx[i]];
+      if (i < nl) id = ids[i < fd ? i : gk[i]];
+      wait_vmem();
       __syncthreads();
       if (i < nl) {
         if (i >= fd) ids[i] = id;
         if (a.keep_ids_out) a.keep_ids_out[kb + i] = id;
       }
-      __syncthreads();
     }
   }
 }
@@ -637,7 +601,7 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   CompactArgs ca{entries, reinterpret_cast<uint16_t*>(ws + z.kidx), reinterpret_cast<int32_t*>(ws + z.first_drop),
                  shat, sel_state + 8, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
-  dim3 cg((unsigned)P, (unsigned)((1 + kVSplit) * a.geom.heads + 1));
+  dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
   if (a.geom.esize == 2)
     compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
   else

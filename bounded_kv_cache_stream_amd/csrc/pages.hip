@@ -3,11 +3,10 @@
 // Page write (LingBot-Map 20 FPS explainer, "Page-Aligned Tensor Layout":
 // a frame's tokens go straight into a page-aligned layout, no padding between
 // frames, no extra copies).  A frame's K and V arrive as [T][H][D]; the page
-// stores K as [H][Ts][D] and V transposed as [H][D][Ts] (Ts = T rounded up to
-// 64), plus the global token id of every slot.  One workgroup moves a
-// 64-token x 64-dim block of one head: K rows are copied with 16-byte
-// accesses, V goes through LDS to be transposed so that both the HBM reads
-// and the HBM writes are whole 128-byte rows.  Slots T..Ts-1 are zero-filled.
+// stores each as [H][Ts][D] (Ts = T rounded up to 64), plus the global token
+// id of every slot.  One workgroup moves a 64-token block of one head: 128-byte
+// rows (bf16) copied with 16-byte accesses on both sides.  Slots T..Ts-1 are
+// zero-filled.
 
 #include <hip/hip_runtime.h>
 
@@ -18,46 +17,37 @@ namespace {
 
 constexpr int D = kHeadDim;
 
-template <typename T>
-struct Vec8 {
-  T v[8];
-};
-
 // One workgroup: tokens t0..t0+63 of head h of one frame into one page.
 template <typename T>
 __device__ void append_block(const PageGeom& g, char* page, const T* __restrict__ k, const T* __restrict__ v,
                              int n_tokens, int64_t first_id, int h, int t0) {
-  __shared__ T vt[64][D + 1];
+  typedef int V16 __attribute__((ext_vector_type(4)));
+  constexpr int VPR = D * sizeof(T) / 16;  // 16-byte vectors per row: 8 (bf16) or 16 (fp32)
+  constexpr int RPP = 256 / VPR;           // rows per pass
   const int H = g.heads;
   const int tid = threadIdx.x;
-  const int r = tid >> 3;      // 0..31
-  const int c = tid & 7;       // chunk of 8 elements
-  T* kdst = reinterpret_cast<T*>(page + g.k_off) + (int64_t)h * g.ts * D;
-  T* vdst = reinterpret_cast<T*>(page + g.v_off) + (int64_t)h * D * g.ts;
-
+  const int r = tid / VPR, c = tid % VPR;
+  V16* kdst = reinterpret_cast<V16*>(page + g.k_off) + (int64_t)h * g.ts * VPR;
+  V16* vdst = reinterpret_cast<V16*>(page + g.v_off) + (int64_t)h * g.ts * VPR;
+  const V16* ksrc = reinterpret_cast<const V16*>(k);
+  const V16* vsrc = reinterpret_cast<const V16*>(v);
+  V16 kk[64 / RPP], vv[64 / RPP];
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    const int t = t0 + r + 32 * pp;
-    Vec8<T> kk, vv;
+  for (int pp = 0; pp < 64 / RPP; ++pp) {
+    const int t = t0 + r + RPP * pp;
     if (t < n_tokens) {
-      kk = *reinterpret_cast<const Vec8<T>*>(k + ((int64_t)t * H + h) * D + c * 8);
-      vv = *reinterpret_cast<const Vec8<T>*>(v + ((int64_t)t * H + h) * D + c * 8);
+      kk[pp] = ksrc[((int64_t)t * H + h) * VPR + c];
+      vv[pp] = vsrc[((int64_t)t * H + h) * VPR + c];
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { kk.v[i] = (T)0.f; vv.v[i] = (T)0.f; }
+      kk[pp] = V16{};
+      vv[pp] = V16{};
     }
-    *reinterpret_cast<Vec8<T>*>(kdst + (int64_t)t * D + c * 8) = kk;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vt[r + 32 * pp][c * 8 + i] = vv.v[i];
   }
-  __syncthreads();
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    const int d = r + 32 * pp;
-    Vec8<T> o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o.v[i] = vt[c * 8 + i][d];
-    *reinterpret_cast<Vec8<T>*>(vdst + (int64_t)d * g.ts + t0 + c * 8) = o;
+  for (int pp = 0; pp < 64 / RPP; ++pp) {
+    const int t = t0 + r + RPP * pp;
+    kdst[(int64_t)t * VPR + c] = kk[pp];
+    vdst[(int64_t)t * VPR + c] = vv[pp];
   }
   if (h == 0 && tid < 64) {
     const int t = t0 + tid;

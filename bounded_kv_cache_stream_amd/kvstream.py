@@ -300,7 +300,7 @@ class KVCache:
 
     # -- reading pages back (tests) -------------------------------------------
     def page_view(self, layer, page_id):
-        """(K [H, Ts, D], V^T [H, D, Ts], ids [Ts]) views of one page in the pool."""
+        """(K [H, Ts, D], V [H, Ts, D], ids [Ts]) views of one page in the pool."""
         torch = self.torch
         L = self.layout
         base = self.pool_ptr - self.pool_buf.data_ptr() + \
@@ -309,6 +309,6 @@ class KVCache:
         dt = torch.bfloat16 if self.cfg.dtype == KV_BF16 else torch.float32
         H, D, Ts, E = self.cfg.num_heads, self.cfg.head_dim, L["token_stride"], L["elem_bytes"]
         k = raw[L["k_offset"]: L["k_offset"] + H * Ts * D * E].view(dt).view(H, Ts, D)
-        v = raw[L["v_offset"]: L["v_offset"] + H * D * Ts * E].view(dt).view(H, D, Ts)
+        v = raw[L["v_offset"]: L["v_offset"] + H * Ts * D * E].view(dt).view(H, Ts, D)
         ids = raw[L["id_offset"]: L["id_offset"] + Ts * 4].view(torch.int32)
         return k, v, ids

@@ -98,7 +98,7 @@ typedef struct {
  * page, with E = element size, Ts = token_stride (page_tokens rounded up to
  * 64), H heads and D = 64:
  *   K   at k_offset: [H][Ts][D]  -- token rows of each head, in slot order
- *   V   at v_offset: [H][D][Ts]  -- each head's V stored transposed
+ *   V   at v_offset: [H][Ts][D]  -- the same layout as K
  *   ids at id_offset: int32 [Ts] -- global token id frame*page_tokens + slot
  * Slots >= the page's length hold no data of the cache. */
 typedef struct {

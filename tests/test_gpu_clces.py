@@ -26,11 +26,11 @@ def _cfg(layers, T, pages, H=16, window=5, scale_frames=0, max_queries=None, dty
 def _page_bytes_equal(cache, layer, page_id, n, k_rows, v_rows, ids):
     """Compare the first n slots of a page with expected [n,H,D] K/V rows (CPU tensors) and ids, bit-exact."""
     torch = cache.torch
-    k, vt, pid = cache.page_view(layer, page_id)
+    k, v, pid = cache.page_view(layer, page_id)
     ek = k_rows.permute(1, 0, 2).contiguous()          # [H, n, D]
-    ev = v_rows.permute(1, 2, 0).contiguous()          # [H, D, n]
+    ev = v_rows.permute(1, 0, 2).contiguous()          # [H, n, D]
     gk = k[:, :n, :].cpu()
-    gv = vt[:, :, :n].cpu()
+    gv = v[:, :n, :].cpu()
     assert torch.equal(gk.view(torch.int16), ek.view(torch.int16)), f"K bytes of page {page_id}"
     assert torch.equal(gv.view(torch.int16), ev.view(torch.int16)), f"V bytes of page {page_id}"
     assert pid[:n].cpu().numpy().tolist() == list(ids), f"token ids of page {page_id}"

@@ -217,3 +217,34 @@ def test_multi_layer_append_matches_single_layer_append():
             for x, y in zip(a.page_view(l, pid), b.page_view(l, pid)):
                 assert torch.equal(x.cpu().view(torch.uint8) if x.dtype != torch.int32 else x.cpu(),
                                    y.cpu().view(torch.uint8) if y.dtype != torch.int32 else y.cpu())
+
+
+@pytest.mark.parametrize("dtype,T,H", [("bf16", 1004, 16), ("fp32", 100, 2)])
+def test_page_write_bytes(dtype, T, H):
+    # a page holds the frame's K and V as [H][Ts][D] bit for bit, zero pad slots
+    # and the global token ids frame*T + slot (-1 in pad slots); a non-keyframe
+    # goes to the layer's transient page (id pages_per_layer)
+    torch = torch_cuda()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cfg = kv.make_config(num_layers=2, num_heads=H, page_tokens=T, dtype=kv.KV_BF16 if dtype == "bf16" else kv.KV_FP32,
+                         scale_frames=1, sliding_window=2, keyframe_interval=2, pages_per_layer=4, max_queries=T,
+                         max_splits=4)
+    c = kv.KVCache(cfg, device="cuda")
+    Ts = c.layout["token_stride"]
+    assert Ts == (T + 63) // 64 * 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    for t in range(3):  # frames 0 (scale), 1 (keyframe), 2 (transient)
+        k = torch.randn(T, H, 64, device="cuda", generator=g).to(tdt)
+        v = torch.randn(T, H, 64, device="cuda", generator=g).to(tdt)
+        c.append(1, t, k, v)
+        c.evict(1)
+        pid = c.page_table(1)[0][-1] if t < 2 else cfg.pages_per_layer
+        pk, pv, ids = c.page_view(1, pid)
+        torch.cuda.synchronize()
+        iv = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(pk[:, :T].cpu().view(iv), k.permute(1, 0, 2).cpu().view(iv)), f"K of frame {t}"
+        assert torch.equal(pv[:, :T].cpu().view(iv), v.permute(1, 0, 2).cpu().view(iv)), f"V of frame {t}"
+        assert not pk[:, T:].cpu().view(iv).any() and not pv[:, T:].cpu().view(iv).any(), f"pad of frame {t}"
+        expect = [t * T + i for i in range(T)] + [-1] * (Ts - T)
+        assert ids.cpu().numpy().tolist() == expect, f"ids of frame {t}"
