@@ -27,10 +27,16 @@
 //     row m of the K read is taken from key pi(m) with
 //     pi(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3), which makes the
 //     8 probabilities a lane holds for one 16-key MFMA step 8 consecutive keys;
-//   * online softmax in the log2 domain (exp2 on v_exp_f32); the running max
-//     is only raised when a tile exceeds it by more than 8 (probabilities stay
-//     below 2^8, O and l are rescaled rarely); the row sum is accumulated with
-//     v_dot2_f32_bf16 over the same bf16 probabilities that enter the PV MFMA;
+//   * online softmax in the log2 domain (exp2 on v_exp_f32) without a per-tile
+//     max: probabilities are taken against the running max, and the tile's
+//     row sum (v_dot2_f32_bf16 over the same bf16 probabilities that enter the
+//     PV MFMA) flags a tile whose largest probability would pass 2^16 (and the
+//     first tile, whose max is still -inf).  Only such a tile takes its max,
+//     raises the running max, rescales O and l and is redone.  On gfx950 VALU
+//     work does not overlap MFMA work on a SIMD, so every VALU instruction
+//     taken out of the tile loop is time saved;
+//   * the page table is walked with scalar loads (constant address space) and
+//     tile addresses are formed in SGPRs;
 //   * the KV axis is split across workgroups (split-KV); partial (O, m, l) are
 //     merged by attend_combine.  Workgroup ids are remapped so that all query
 //     tiles of one (head, split) land on the same XCD and share its L2.
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int lo = 0, hi = p.n_entries - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (p.table[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
+      if (((const __attribute__((address_space(4))) DevEntry*)p.table)[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
     }
     e = lo;
   }
@@ -141,19 +147,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t head_off = (int64_t)h * g.ts * D;
 
   bf16x8 kreg[2], vreg[2];
+  // The page table is read-only for the kernel's lifetime: read it through the
+  // constant address space so that the walk runs on scalar loads and SALU, and
+  // the tile's base address stays in SGPRs (each load is base + 32-bit lane offset).
+  typedef const __attribute__((address_space(4))) DevEntry* ConstTable;
+  const ConstTable tab = (ConstTable)p.table;
+  const uint32_t lane_off = (uint32_t)((lrow * D + lchunk * 8) * sizeof(bf16));
   auto load_tile = [&](int t) -> int {
-    while (t >= p.table[e].tile_start + ((p.table[e].len + BN - 1) / BN)) ++e;
-    const DevEntry en = p.table[e];
-    const int row0 = (t - en.tile_start) * BN;
-    const int nvalid = min(BN, en.len - row0);
-    const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
-    const bf16* kt = reinterpret_cast<const bf16*>(page + g.k_off) + head_off + (int64_t)row0 * D;
-    const bf16* vt = reinterpret_cast<const bf16*>(page + g.v_off) + head_off + (int64_t)row0 * D;
+    while (t >= tab[e].tile_start + ((tab[e].len + BN - 1) / BN)) ++e;
+    const int row0 = (t - tab[e].tile_start) * BN;
+    const int nvalid = min(BN, tab[e].len - row0);
+    const char* base = p.pool + (int64_t)tab[e].phys * g.page_bytes + (head_off + (int64_t)row0 * D) * (int64_t)sizeof(bf16);
+    const char* kt = base + g.k_off;
+    const char* vt = base + g.v_off;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const int r = lrow + 32 * pp;
-      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + r * D + lchunk * 8);
-      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + r * D + lchunk * 8);
+      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * 32 * D * sizeof(bf16));
+      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * 32 * D * sizeof(bf16));
     }
     return nvalid;
   };
@@ -213,28 +223,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int qb = 0; qb < 2; ++qb) {
       // key of accumulator register r of block kb: 32*kb + 16*(r>>3) + 8*grp + (r&7)
       if (nvalid < BN) {
+        // partial tile: keys at or past nvalid do not exist.  The empty asm
+        // keeps the comparisons inside this branch (otherwise they are
+        // speculated into every tile).
+        int nv_lane = nvalid - 8 * grp;
+        asm volatile("" : "+v"(nv_lane));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + 16 * (r >> 3) + 8 * grp + (r & 7) >= nvalid) sc[qb][kb][r] = -INFINITY;
+            if (32 * kb + 16 * (r >> 3) + (r & 7) >= nv_lane) sc[qb][kb][r] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mt = mx * p.scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + 8.f) != 0) {
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { oacc[qb][0][i] *= alpha; oacc[qb][1][i] *= alpha; }
-      }
-      const float nm = -m_run[qb];
+      // Probabilities against the running max; the tile's row sum (v_dot2
+      // over the bf16 probabilities) flags a tile whose largest probability
+      // would pass 2^16 (or the first tile, where the max is still -inf and
+      // the sum is inf or NaN).  Only then is the tile max taken, the max
+      // raised, O and l rescaled and the tile redone.
+      float nm = -m_run[qb];
+      float lt = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -247,8 +253,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             bf16x2 pr = {pb[qb][kb][s][2 * j], pb[qb][kb][s][2 * j + 1]};
-            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
+            lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
           }
+      if (__builtin_amdgcn_ballot_w64(!(lt <= 65536.f)) != 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run[qb], mx * p.scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { oacc[qb][0][i] *= alpha; oacc[qb][1][i] *= alpha; }
+        nm = -m_new;
+        lt = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pb[qb][kb][r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[qb][kb][r], p.scale_log2, nm));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bf16x2 pr = {pb[qb][kb][s][2 * j], pb[qb][kb][s][2 * j + 1]};
+              lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
+            }
+      }
+      l_run[qb] += lt;
     }
 
     // O^T += V^T P^T for both query blocks; each V operand feeds two MFMAs

@@ -430,19 +430,23 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef int V16 __attribute__((ext_vector_type(4)));  // a native vector: a struct copy would go through scratch
 
+constexpr int kCompactThreads = 1024;
+
 // Left-pack the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes
-// each): row i <- row kidx[i] for fd <= i < nl.  8 threads per row; every
-// thread holds 16 vectors, so one step moves 512 bf16 rows (256 fp32 rows)
-// with a single barrier between its reads and its writes.  A step's sources lie
-// at or after its first output, so no earlier step writes them, and no barrier
-// is needed after the writes.
+// each): row i <- row kidx[i] for fd <= i < nl.  8 threads per row and 8
+// vectors per thread, so one step of the 1024-thread workgroup moves 1024 bf16
+// rows (512 fp32 rows): a whole page of up to 1024 tokens is read in one burst,
+// then written, with a single barrier in between.  A step's sources lie at or
+// after its first output, so no earlier step writes them, and no barrier is
+// needed after the writes.  The moved rows are not read again by this kernel,
+// so loads and stores are nontemporal.
 template <typename T>
 __device__ inline void compact_rows(V16* rows, const uint16_t* gk, int fd, int nl, int tid) {
   constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
   constexpr int TPR = 8;                    // threads per row
   constexpr int UPR = VPR / TPR;            // vectors per thread per row
-  constexpr int G = 16 / UPR;               // row groups per step
-  constexpr int RPS = kThreads / TPR * G;   // rows per step
+  constexpr int G = 8 / UPR;               // row groups per step
+  constexpr int RPS = kCompactThreads / TPR * G;   // rows per step
   const int r = tid / TPR, c = tid % TPR;
   for (int i0 = fd; i0 < nl; i0 += RPS) {
     // rows past nl load slot 0 (in bounds, never stored), so every load is
@@ -451,21 +455,21 @@ __device__ inline void compact_rows(V16* rows, const uint16_t* gk, int fd, int n
     int src[G];
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      const int i = i0 + gq * (kThreads / TPR) + r;
+      const int i = i0 + gq * (kCompactThreads / TPR) + r;
       src[gq] = i < nl ? gk[i] : 0;
     }
 #pragma unroll
     for (int gq = 0; gq < G; ++gq)
 #pragma unroll
-      for (int u = 0; u < UPR; ++u) v[gq][u] = rows[src[gq] * VPR + c + TPR * u];
+      for (int u = 0; u < UPR; ++u) v[gq][u] = __builtin_nontemporal_load(&rows[src[gq] * VPR + c + TPR * u]);
     wait_vmem();
     __syncthreads();
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      const int i = i0 + gq * (kThreads / TPR) + r;
+      const int i = i0 + gq * (kCompactThreads / TPR) + r;
       if (i < nl)
 #pragma unroll
-        for (int u = 0; u < UPR; ++u) rows[i * VPR + c + TPR * u] = v[gq][u];
+        for (int u = 0; u < UPR; ++u) __builtin_nontemporal_store(v[gq][u], &rows[i * VPR + c + TPR * u]);
     }
   }
 }
@@ -474,7 +478,7 @@ __device__ inline void compact_rows(V16* rows, const uint16_t* gk, int fd, int n
 // dropped one stay.  Grid (page, part): part < H is the K block of head
 // `part`, H <= part < 2H the V block of head part - H, part 2H the token ids.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
   if (*a.flag) return;
   const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
   const int H = a.g.heads;
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     // token ids, and the list of kept ids in table order
     int32_t* ids = reinterpret_cast<int32_t*>(page + a.g.id_off);
     const int32_t kb = a.keep_base[e];
-    for (int i0 = 0; i0 < nl; i0 += kThreads) {
+    for (int i0 = 0; i0 < nl; i0 += kCompactThreads) {
       const int i = i0 + tid;
       int32_t id = 0;
       if (i < nl) id = ids[i < fd ? i : gk[i]];
@@ -603,9 +607,9 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
   if (a.geom.esize == 2)
-    compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
+    compact_kernel<__bf16><<<cg, dim3(kCompactThreads), 0, s>>>(ca);
   else
-    compact_kernel<float><<<cg, dim3(kThreads), 0, s>>>(ca);
+    compact_kernel<float><<<cg, dim3(kCompactThreads), 0, s>>>(ca);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(new_lens_host, plan + 2 * P, sizeof(int32_t) * (size_t)P, hipMemcpyDeviceToHost, s);

@@ -6,7 +6,8 @@
 // stores each as [H][Ts][D] (Ts = T rounded up to 64), plus the global token
 // id of every slot.  One workgroup moves a 64-token block of one head: 128-byte
 // rows (bf16) copied with 16-byte accesses on both sides.  Slots T..Ts-1 are
-// zero-filled.
+// zero-filled.  Each byte is touched once by this kernel, so loads and stores
+// are nontemporal (streamed past the caches).
 
 #include <hip/hip_runtime.h>
 
@@ -36,8 +37,8 @@ __device__ void append_block(const PageGeom& g, char* page, const T* __restrict_
   for (int pp = 0; pp < 64 / RPP; ++pp) {
     const int t = t0 + r + RPP * pp;
     if (t < n_tokens) {
-      kk[pp] = ksrc[((int64_t)t * H + h) * VPR + c];
-      vv[pp] = vsrc[((int64_t)t * H + h) * VPR + c];
+      kk[pp] = __builtin_nontemporal_load(&ksrc[((int64_t)t * H + h) * VPR + c]);
+      vv[pp] = __builtin_nontemporal_load(&vsrc[((int64_t)t * H + h) * VPR + c]);
     } else {
       kk[pp] = V16{};
       vv[pp] = V16{};
@@ -46,8 +47,8 @@ __device__ void append_block(const PageGeom& g, char* page, const T* __restrict_
 #pragma unroll
   for (int pp = 0; pp < 64 / RPP; ++pp) {
     const int t = t0 + r + RPP * pp;
-    kdst[(int64_t)t * VPR + c] = kk[pp];
-    vdst[(int64_t)t * VPR + c] = vv[pp];
+    __builtin_nontemporal_store(kk[pp], &kdst[(int64_t)t * VPR + c]);
+    __builtin_nontemporal_store(vv[pp], &vdst[(int64_t)t * VPR + c]);
   }
   if (h == 0 && tid < 64) {
     const int t = t0 + tid;
