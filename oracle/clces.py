@@ -28,15 +28,21 @@ Readings taken where the pages are silent (listed in the design doc):
 * population variance (divide by n); fixed summation order: oldest window
   layer first; every step in float64 with no fused multiply-add;
 * keep order: s_hat descending, then index ascending; K tokens kept;
-* compaction is page-local and stable: each page keeps its kept rows in their
-  original order at its front; pages left empty are released.
+* compaction is page-local: with n kept rows, kept rows already in slots
+  [0, n) stay where they are and the kept rows in slots [n, len) fill the
+  dropped slots of [0, n), both taken in ascending slot order; pages left
+  empty are released.  (The pages fix no order inside a page and attention
+  does not depend on it; this placement moves the fewest rows.)
 
 Pinned by ``tests/test_oracle_clces.py``: ranks against an O(N^2) brute-force
 count, the two-token-order hand example in ``tests/golden/clces_hand_example.txt``,
 the closed forms Cons = 1 for identical rank trajectories and s_hat = s for
 lambda = 0, Cons = 0 for alternating extreme ranks, the range [0, 1], top-k
-against a brute-force full sort with deliberate ties, and compaction against a
-row-by-row copy.
+against a brute-force full sort with deliberate ties, and compaction against
+the hand example in ``tests/golden/compaction_hand_example.txt`` and the
+properties that fix the placement (the result is a permutation of the kept
+rows, kept rows below n are fixed points, and exactly the kept rows at or past
+n move, the fewest any compaction to a prefix can move).
 """
 
 from __future__ import annotations
@@ -129,5 +135,27 @@ def topk_keep(s_hat: np.ndarray, k: int) -> np.ndarray:
 
 
 def compact_page(rows: np.ndarray, keep: np.ndarray) -> np.ndarray:
-    """Stable left-pack of one page: the kept rows, in order, then nothing."""
-    return np.asarray(rows)[np.asarray(keep, dtype=bool)]
+    """The first n = keep.sum() slots of one page after compaction.
+
+    Slot j < n keeps its own row if that row is kept; otherwise it is a hole,
+    and the holes, in ascending order, take the kept rows found at slots >= n,
+    in ascending order."""
+    rows = np.asarray(rows)
+    keep = np.asarray(keep, dtype=bool)
+    n = int(keep.sum())
+    holes = [j for j in range(n) if not keep[j]]
+    fillers = [j for j in range(n, len(keep)) if keep[j]]
+    assert len(holes) == len(fillers)
+    src = list(range(n))
+    for h, f in zip(holes, fillers):
+        src[h] = f
+    return rows[np.array(src, dtype=np.int64)] if n else rows[:0]
+
+
+def compaction_moves(keep: np.ndarray) -> list[tuple[int, int]]:
+    """(source slot, destination slot) of every row that compaction moves, by destination."""
+    keep = np.asarray(keep, dtype=bool)
+    n = int(keep.sum())
+    holes = [j for j in range(n) if not keep[j]]
+    fillers = [j for j in range(n, len(keep)) if keep[j]]
+    return list(zip(fillers, holes))

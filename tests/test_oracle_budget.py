@@ -16,6 +16,9 @@ def _scores(n_tokens, n_layers, seed):
 
 
 def test_paged_policy_matches_flat_list():
+    # the paged cache keeps the same token set as a flat list that applies the
+    # top-k directly; the scores are continuous, so s_hat has no ties and the
+    # set does not depend on the order of tokens inside a page
     T, B, frames, L, W = 8, 20, 12, 6, 5
     table = _scores(T * frames, L, seed=1)
     for layer in range(L):
@@ -29,21 +32,23 @@ def test_paged_policy_matches_flat_list():
                 assert ran
                 lw = clces.window_layers(layer, W)
                 res = clces.clces(np.stack([table[flat, l] for l in lw]), 0.5)
+                assert len(np.unique(res["s_hat"])) == len(flat)
                 flat = flat[clces.topk_keep(res["s_hat"], B)]
+                np.testing.assert_array_equal(np.sort(c.last["keep_ids"]), np.sort(flat))
             else:
                 assert not ran
-            np.testing.assert_array_equal(c.all_ids(), flat)
+            np.testing.assert_array_equal(np.sort(c.all_ids()), np.sort(flat))
             assert len(c.all_ids()) <= max(B, T)
             # bookkeeping: unique ids, no empty page, free + used = pool
             pids = [p for p, _, _ in c.page_table()]
             assert len(set(pids)) == len(pids)
             assert all(n > 0 for _, _, n in c.page_table())
             assert set(pids) | c.free == set(range(frames))
-            # page order follows frame order and ids inside a page stay sorted
+            # page order follows frame order; a page holds only its frame's tokens
             fr = [f for _, f, _ in c.page_table()]
             assert fr == sorted(fr)
             for _, f, ids in c.table:
-                assert (np.diff(ids) > 0).all() and (ids // T == f).all()
+                assert len(set(ids.tolist())) == len(ids) and (ids // T == f).all()
 
 
 def test_scale_frames_are_never_scored():

@@ -147,14 +147,47 @@ def test_bad_scores_rejected():
         clces.clces(np.array([[1.0, -1e-30]], dtype=np.float32), 0.5)
 
 
-def test_compaction_matches_row_copy():
+def _hand_cases():
+    path = os.path.join(os.path.dirname(__file__), "golden", "compaction_hand_example.txt")
+    lines = [ln.rstrip("\n") for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    cases = []
+    for i in range(0, len(lines), 3):
+        keep = [int(x) for x in lines[i].split(":", 1)[1].split()]
+        out = [int(x) for x in lines[i + 1].split(":", 1)[1].split()]
+        moves = [tuple(int(y) for y in m.split("->")) for m in lines[i + 2].split(":", 1)[1].split()]
+        cases.append((keep, out, moves))
+    return cases
+
+
+def test_compaction_hand_examples():
+    cases = _hand_cases()
+    assert len(cases) == 5
+    for keep, out, moves in cases:
+        slots = np.arange(len(keep))
+        np.testing.assert_array_equal(clces.compact_page(slots, np.array(keep, bool)), out)
+        assert clces.compaction_moves(np.array(keep, bool)) == moves
+
+
+def test_compaction_properties():
+    # whatever the placement, compaction to a prefix must move every kept row
+    # that lies at or past n; this rule moves exactly those, keeps every other
+    # kept row where it is, and loses or duplicates nothing
     rng = np.random.default_rng(6)
-    rows = rng.standard_normal((64, 3, 4)).astype(np.float32)
-    keep = rng.random(64) < 0.4
-    out = clces.compact_page(rows, keep)
-    expect = []
-    for i in range(64):
-        if keep[i]:
-            expect.append(rows[i].copy())
-    np.testing.assert_array_equal(out, np.array(expect))
-    assert clces.compact_page(rows, np.zeros(64, bool)).shape[0] == 0
+    for trial in range(200):
+        L = int(rng.integers(1, 130))
+        rows = rng.standard_normal((L, 3)).astype(np.float32)
+        keep = rng.random(L) < rng.random()
+        n = int(keep.sum())
+        out = clces.compact_page(rows, keep)
+        assert out.shape == (n, 3)
+        kept_rows = rows[keep]
+        np.testing.assert_array_equal(np.sort(out, axis=0), np.sort(kept_rows, axis=0))
+        for j in range(n):
+            if keep[j]:
+                np.testing.assert_array_equal(out[j], rows[j])
+        moves = clces.compaction_moves(keep)
+        assert sorted(src for src, _ in moves) == [j for j in range(n, L) if keep[j]]
+        assert sorted(dst for _, dst in moves) == [j for j in range(n) if not keep[j]]
+        for src, dst in moves:
+            np.testing.assert_array_equal(out[dst], rows[src])
+    assert clces.compact_page(np.zeros((64, 2)), np.zeros(64, bool)).shape[0] == 0
