@@ -43,9 +43,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["stream", "clces", "append"], default="stream",
+    ap.add_argument("--workload", choices=["stream", "clces", "append", "long", "budget"], default="stream",
                     help="stream: the attention step (default); clces: score_and_compact on the 24-layer "
-                         "cache; append: one frame's page write for 24 layers in one launch")
+                         "cache; append: one frame's page write for 24 layers in one launch; long: the "
+                         "10,000-frame keyframe-interval-4 stream, sustained; budget: the 24-layer "
+                         "token-budget stack (append, attend, score_and_compact per layer)")
+    ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -93,12 +96,11 @@ def cpu_baseline(frames_kv, q_frame, attended):
 
 
 def moved_tokens(keep_mask_pages):
-    """Tokens a page-local left-pack moves: kept slots after the page's first dropped slot."""
+    """Rows the page compaction moves: with n kept slots in a page, the kept slots at or past n."""
     n = 0
     for m in keep_mask_pages:
-        drop = [i for i, k in enumerate(m) if not k]
-        if drop:
-            n += sum(1 for i in range(drop[0], len(m)) if m[i])
+        kept = sum(1 for k in m if k)
+        n += sum(1 for i in range(kept, len(m)) if m[i])
     return n
 
 
@@ -197,12 +199,143 @@ def run_append(args):
     }), flush=True)
 
 
+def run_long(args):
+    """The 10,000-frame stream with keyframe interval 4: append+evict+attend for every frame, timed whole.
+
+    Inputs come from a ring of 64 AR(1) frames generated in HBM before the clock starts (the values do
+    not change the work; the policy, page table and attended set follow the frame index)."""
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+    from bounded_kv_cache_stream_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[2]
+    T, H, D, S, Wf, k = w["tokens"], w["heads"], w["head_dim"], w["scale_frames"], w["window"], w["keyframe_interval"]
+    F = args.frames or w["frames"]
+    cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
+                         keyframe_interval=k, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=16)
+    cache = kv.KVCache(cfg, device=dev)
+    ar = synth.AR1Stream(2, 0, (T, H, D), device=dev)
+    ring = [ar.next() for _ in range(64)]
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    out_scale = torch.empty((S * T, H, D), dtype=torch.bfloat16, device=dev)
+    scale_q = [ring[t][0] for t in range(S)]
+    q_scale = torch.cat(scale_q)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for t in range(F):
+        q, kk, vv = ring[t % 64]
+        cache.append(0, t, kk, vv)
+        cache.evict(0)
+        if t == S - 1:
+            cache.attend(0, q_scale, 1.0, out=out_scale)
+        elif t >= S:
+            cache.attend(0, q, 1.0, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1)
+    info = cache.info(0)
+    print(json.dumps({
+        "metric": "frames/sec sustained over the keyframe-interval-4 stream (append+evict+attend, 1 layer)",
+        "value": F / (ms / 1e3), "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "frames": F,
+        "ms_per_frame": ms / F, "dtype": "bf16", "data": "synthetic (ring of 64 seeded AR(1) frames, bf16)",
+        "config": {"workload": w["name"], "tokens_per_frame": T, "heads": H, "head_dim": D, "scale_frames": S,
+                   "sliding_window": Wf, "keyframe_interval": k},
+        "final_persisted_frames": info["persisted_frames"], "wall_s": wall}), flush=True)
+
+
+def run_budget(args):
+    """The 24-layer token-budget stack: per frame and layer append -> attend -> score_and_compact.
+
+    Frames 0..warmup-1 fill the cache (the budget of 128,512 tokens is reached at frame 128); the next
+    `steps` frames are timed, with HIP events around each call for the per-kernel split.  K/V/Q come
+    from a ring of 8 AR(1) frames per layer in HBM; the raw-score table covers every token id."""
+    import numpy as np
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+    from bounded_kv_cache_stream_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[4]
+    T, H, D, L, B = w["tokens"], w["heads"], w["head_dim"], w["layers"], w["budget"]
+    warm = max(args.warmup, 140)
+    F = warm + args.steps
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=0,
+                         keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16,
+                         max_window=w["clces_window"])
+    cache = kv.KVCache(cfg, device=dev)
+    table = torch.from_numpy(synth.raw_scores(4, F * T, L)).to(dev)
+    rings = []
+    for l in range(L):
+        ar = synth.AR1Stream(4, l, (T, H, D), device=dev)
+        rings.append([ar.next() for _ in range(8)])
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [] for name in ("append", "attend", "score")}
+
+    def frame(t, timed):
+        for l in range(L):
+            q, k, v = rings[l][t % 8]
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+            if timed:
+                marks[0].record(stream)
+            cache.append(l, t, k, v)
+            if timed:
+                marks[1].record(stream)
+            cache.attend(l, q, w["sm_scale"], out=out)
+            if timed:
+                marks[2].record(stream)
+            cache.score_and_compact(l, table, w["clces_window"], w["lam"], B)
+            if timed:
+                marks[3].record(stream)
+                ev["append"].append((marks[0], marks[1]))
+                ev["attend"].append((marks[1], marks[2]))
+                ev["score"].append((marks[2], marks[3]))
+
+    for t in range(warm):
+        frame(t, False)
+    torch.cuda.synchronize()
+    n_tok = cache.info(0)["tokens"]
+    wall0 = time.perf_counter()
+    for t in range(warm, F):
+        frame(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    split = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3 for name, pairs in ev.items()}
+    attended = n_tok + T
+    flops = 4.0 * H * D * T * attended
+    print(json.dumps({
+        "metric": "frames/sec of the 24-layer token-budget stack (append, attend, score_and_compact per layer)",
+        "value": args.steps / wall, "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps,
+        "warmup": warm, "ms_per_frame": wall / args.steps * 1e3, "dtype": "bf16",
+        "data": "synthetic (ring of 8 seeded AR(1) frames per layer, chi-square raw scores)",
+        "config": {"workload": w["name"], "layers": L, "tokens_per_frame": T, "heads": H, "head_dim": D,
+                   "budget": B, "attended_tokens": attended, "clces_window": w["clces_window"], "lam": w["lam"]},
+        "us_per_layer": split,
+        "attend_tflops": flops / (split["attend"] * 1e-6) / 1e12,
+        "attend_frac_bf16_peak": flops / (split["attend"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "clces":
         return run_clces(args)
     if args.workload == "append":
         return run_append(args)
+    if args.workload == "long":
+        return run_long(args)
+    if args.workload == "budget":
+        return run_budget(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "

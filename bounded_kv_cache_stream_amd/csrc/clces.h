@@ -11,6 +11,7 @@ namespace kvs {
 
 constexpr int32_t kClcesErrNan = 1;    // a raw score is NaN or negative
 constexpr int32_t kClcesErrRow = 2;    // a token id is outside the score table
+constexpr int32_t kClcesErrCount = 4;  // a page's kept count disagrees with its planned length
 constexpr int32_t kRankTile = 2048;    // keys per radix-sort workgroup
 constexpr int32_t kMaxPageTokensScored = 8192;
 
@@ -19,7 +20,7 @@ struct ClcesSizes {
   int64_t n_max;
   int32_t p_max, w_max, nblk_max;
   size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts, plan,
-      kidx, first_drop, flag, total;
+      move_src, move_dst, n_moves, flag, total;
 };
 
 ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_max);

@@ -20,11 +20,12 @@
 //            bits over the 64-bit pattern, which orders non-negative doubles);
 //   mark     per page: count of s_hat above / equal to the threshold;
 //   plan     per page: rank base among ties (index order), kept count, offset;
+//   index    per page: the kept token ids in slot order, and the moves: with
+//            n kept, kept slots below n stay and the dropped slots below n
+//            take the kept slots at or past n (both ascending);
 //   compact  per page: one workgroup per K head, one per V head and one for
-//            the token ids; each gathers the kept slots to the page's front
-//            in chunks whose reads all finish before their writes (every
-//            source slot is at or after its destination, so no chunk
-//            overwrites data a later chunk reads).
+//            the token ids; sources (>= n) and destinations (< n) are
+//            disjoint, so every row moves independently.
 
 #include <hip/hip_runtime.h>
 
@@ -368,8 +369,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 
 struct CompactArgs {
   const DevEntry* entries;
-  uint16_t* kidx;        // [P][ts] kept slots per page
-  int32_t* first_drop;   // [P]
+  uint16_t* move_src;    // [P][ts] kept slots at or past the new length, ascending
+  uint16_t* move_dst;    // [P][ts] dropped slots below the new length, ascending
+  int32_t* n_moves;      // [P]
   const unsigned long long* shat;
   const SelState* final_state;
   const int32_t* eq_base;
@@ -379,136 +381,129 @@ struct CompactArgs {
   PageGeom g;
   int32_t* keep_ids_out;
   const int32_t* flag;
+  int32_t* flag_rw;
 };
 
-// Per page: the kept slots in order (kidx[0..new_len)) and the first dropped
-// slot.  Ties at the threshold are kept in index order: the page's tie rank
-// base comes from the plan step.
+// Per page: which slots are kept (ties at the threshold in index order, from
+// the plan step's tie rank base), the kept token ids in slot order, and the
+// moves of the compaction.  With n = new length, kept slots below n stay; the
+// dropped slots below n (the holes, ascending) take the kept slots at or past
+// n (ascending).  Sources and destinations are disjoint, so the moves can run
+// in any order.
 __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   if (*a.flag) return;
   __shared__ int32_t scan[kThreads];
-  __shared__ int32_t first_drop;
+  __shared__ uint16_t kept[kMaxPageTokensScored];
   const int e = blockIdx.x, tid = threadIdx.x;
   const DevEntry en = a.entries[e];
   const int len = en.len;
+  const int nl = a.new_len[e];
   const SelState st = *a.final_state;
   const int per = (len + kThreads - 1) / kThreads;
   const int b = tid * per, end = min(b + per, len);
   const unsigned long long* sh = a.shat + en.tok_start;
-  if (tid == 0) first_drop = len;
   int32_t n_eq = 0;
   for (int j = b; j < end; ++j) n_eq += sh[j] == st.prefix;
   const int32_t eq_start = a.eq_base[e] + block_excl_scan<kThreads>(n_eq, scan, nullptr);
   int32_t eq_rank = eq_start;
-  int32_t n_keep = 0;
-  int my_drop = len;
+  int32_t n_keep = 0, n_hole = 0;
   for (int j = b; j < end; ++j) {
     const unsigned long long k = sh[j];
     bool keep = k > st.prefix;
     if (k == st.prefix) keep = eq_rank++ < st.k_rem;
     n_keep += keep;
-    if (!keep && j < my_drop) my_drop = j;
+    n_hole += !keep && j < nl;
   }
-  if (my_drop < len) atomicMin(&first_drop, my_drop);
-  int32_t pos = block_excl_scan<kThreads>(n_keep, scan, nullptr);
-  uint16_t* kidx = a.kidx + (int64_t)e * a.g.ts;
+  int32_t kept_total = 0, holes = 0;
+  int32_t pos = block_excl_scan<kThreads>(n_keep, scan, &kept_total);
+  int32_t hpos = block_excl_scan<kThreads>(n_hole, scan, &holes);
+  if (kept_total != nl) {  // cannot happen when the plan and this pass agree; never move on a mismatch
+    if (tid == 0) {
+      atomicOr(a.flag_rw, kClcesErrCount);
+      a.n_moves[e] = 0;
+    }
+    return;
+  }
+  uint16_t* dst = a.move_dst + (int64_t)e * a.g.ts;
   eq_rank = eq_start;
   for (int j = b; j < end; ++j) {
     const unsigned long long k = sh[j];
     bool keep = k > st.prefix;
     if (k == st.prefix) keep = eq_rank++ < st.k_rem;
-    if (keep) kidx[pos++] = (uint16_t)j;
+    if (keep)
+      kept[pos++] = (uint16_t)j;
+    else if (j < nl)
+      dst[hpos++] = (uint16_t)j;
   }
   __syncthreads();
-  if (tid == 0) a.first_drop[e] = first_drop;
+  // fillers: the kept slots at or past nl are the last `holes` entries of the kept list
+  uint16_t* src = a.move_src + (int64_t)e * a.g.ts;
+  for (int k = tid; k < holes; k += kThreads) src[k] = kept[nl - holes + k];
+  if (a.keep_ids_out) {
+    const int32_t* ids = reinterpret_cast<const int32_t*>(a.pool + (int64_t)en.phys * a.g.page_bytes + a.g.id_off);
+    const int32_t kb = a.keep_base[e];
+    for (int i = tid; i < nl; i += kThreads) a.keep_ids_out[kb + i] = ids[kept[i]];
+  }
+  if (tid == 0) a.n_moves[e] = holes;
 }
-
-// Wait for this thread's outstanding vector-memory loads (vmcnt = 0).  Placed
-// before the barrier that separates a chunk's reads from its in-place writes,
-// so no other wave's write can overtake a read still in flight.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef int V16 __attribute__((ext_vector_type(4)));  // a native vector: a struct copy would go through scratch
 
-constexpr int kCompactThreads = 1024;
-
-// Left-pack the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes
-// each): row i <- row kidx[i] for fd <= i < nl.  8 threads per row and 8
-// vectors per thread, so one step of the 1024-thread workgroup moves 1024 bf16
-// rows (512 fp32 rows): a whole page of up to 1024 tokens is read in one burst,
-// then written, with a single barrier in between.  A step's sources lie at or
-// after its first output, so no earlier step writes them, and no barrier is
-// needed after the writes.  The moved rows are not read again by this kernel,
-// so loads and stores are nontemporal.
+// Move the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes each)
+// from the move sources to the move destinations.  8 threads per row and 8
+// vectors per thread: one pass moves 256 bf16 rows (128 fp32 rows), all loads
+// issued before the stores.  Sources and destinations are disjoint, so no
+// barrier is needed; the rows are touched once, so accesses are nontemporal.
 template <typename T>
-__device__ inline void compact_rows(V16* rows, const uint16_t* gk, int fd, int nl, int tid) {
+__device__ inline void move_rows(V16* rows, const uint16_t* src, const uint16_t* dst, int nm, int tid) {
   constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
   constexpr int TPR = 8;                    // threads per row
   constexpr int UPR = VPR / TPR;            // vectors per thread per row
-  constexpr int G = 8 / UPR;               // row groups per step
-  constexpr int RPS = kCompactThreads / TPR * G;   // rows per step
+  constexpr int G = 8 / UPR;                // row groups per pass
+  constexpr int RPP = kThreads / TPR;       // rows per group
   const int r = tid / TPR, c = tid % TPR;
-  for (int i0 = fd; i0 < nl; i0 += RPS) {
-    // rows past nl load slot 0 (in bounds, never stored), so every load is
-    // unconditional and the block stays in registers
+  for (int i0 = 0; i0 < nm; i0 += RPP * G) {
     V16 v[G][UPR];
-    int src[G];
+    int s[G], d[G];
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      const int i = i0 + gq * (kCompactThreads / TPR) + r;
-      src[gq] = i < nl ? gk[i] : 0;
+      const int i = i0 + gq * RPP + r;
+      s[gq] = i < nm ? src[i] : 0;  // past the end: load slot 0 (in bounds, never stored)
+      d[gq] = i < nm ? dst[i] : -1;
     }
 #pragma unroll
     for (int gq = 0; gq < G; ++gq)
 #pragma unroll
-      for (int u = 0; u < UPR; ++u) v[gq][u] = __builtin_nontemporal_load(&rows[src[gq] * VPR + c + TPR * u]);
-    wait_vmem();
-    __syncthreads();
+      for (int u = 0; u < UPR; ++u) v[gq][u] = __builtin_nontemporal_load(&rows[s[gq] * VPR + c + TPR * u]);
 #pragma unroll
-    for (int gq = 0; gq < G; ++gq) {
-      const int i = i0 + gq * (kCompactThreads / TPR) + r;
-      if (i < nl)
+    for (int gq = 0; gq < G; ++gq)
+      if (d[gq] >= 0)
 #pragma unroll
-        for (int u = 0; u < UPR; ++u) __builtin_nontemporal_store(v[gq][u], &rows[i * VPR + c + TPR * u]);
-    }
+        for (int u = 0; u < UPR; ++u) __builtin_nontemporal_store(v[gq][u], &rows[d[gq] * VPR + c + TPR * u]);
   }
 }
 
-// Move the kept slots of each page to its front; slots before the first
-// dropped one stay.  Grid (page, part): part < H is the K block of head
-// `part`, H <= part < 2H the V block of head part - H, part 2H the token ids.
+// Grid (page, part): part < H moves the K rows of head `part`, H <= part < 2H
+// the V rows of head part - H, part 2H the token ids.
 template <typename T>
-__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
+__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   if (*a.flag) return;
   const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int nm = a.n_moves[e];
+  if (nm == 0) return;
   const int H = a.g.heads;
   const DevEntry en = a.entries[e];
-  const int len = en.len, nl = a.new_len[e];
-  const bool ids_part = part == 2 * H;
-  if (!ids_part && nl == len) return;  // nothing dropped: K and V stay
-  const int fd = a.first_drop[e];     // slots [0, fd) are kept in place
-  const uint16_t* gk = a.kidx + (int64_t)e * a.g.ts;
+  const uint16_t* src = a.move_src + (int64_t)e * a.g.ts;
+  const uint16_t* dst = a.move_dst + (int64_t)e * a.g.ts;
   char* page = a.pool + (int64_t)en.phys * a.g.page_bytes;
-  if (!ids_part) {
+  if (part < 2 * H) {
     constexpr int VPR = 64 * sizeof(T) / 16;
     const int h = part < H ? part : part - H;
     V16* rows = reinterpret_cast<V16*>(page + (part < H ? a.g.k_off : a.g.v_off)) + (int64_t)h * a.g.ts * VPR;
-    compact_rows<T>(rows, gk, fd, nl, tid);
+    move_rows<T>(rows, src, dst, nm, tid);
   } else {
-    // token ids, and the list of kept ids in table order
     int32_t* ids = reinterpret_cast<int32_t*>(page + a.g.id_off);
-    const int32_t kb = a.keep_base[e];
-    for (int i0 = 0; i0 < nl; i0 += kCompactThreads) {
-      const int i = i0 + tid;
-      int32_t id = 0;
-      if (i < nl) id = ids[i < fd ? i : gk[i]];
-      wait_vmem();
-      __syncthreads();
-      if (i < nl) {
-        if (i >= fd) ids[i] = id;
-        if (a.keep_ids_out) a.keep_ids_out[kb + i] = id;
-      }
-    }
+    for (int i = tid; i < nm; i += kThreads) ids[dst[i]] = ids[src[i]];
   }
 }
 
@@ -540,8 +535,9 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.entries = take((size_t)p_max * sizeof(DevEntry));
   z.counts = take((size_t)p_max * 2 * 4);
   z.plan = take((size_t)p_max * 3 * 4);
-  z.kidx = take((size_t)p_max * ts_max * 2);
-  z.first_drop = take((size_t)p_max * 4);
+  z.move_src = take((size_t)p_max * ts_max * 2);
+  z.move_dst = take((size_t)p_max * ts_max * 2);
+  z.n_moves = take((size_t)p_max * 4);
   z.flag = take(4);
   z.total = off;
   return z;
@@ -602,14 +598,17 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
   PlanArgs pa{counts, counts + P, sel_state + 8, plan, plan + P, plan + 2 * P, P, flag};
   plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(pa);
-  CompactArgs ca{entries, reinterpret_cast<uint16_t*>(ws + z.kidx), reinterpret_cast<int32_t*>(ws + z.first_drop),
-                 shat, sel_state + 8, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag};
+  CompactArgs ca{entries,
+                 reinterpret_cast<uint16_t*>(ws + z.move_src),
+                 reinterpret_cast<uint16_t*>(ws + z.move_dst),
+                 reinterpret_cast<int32_t*>(ws + z.n_moves),
+                 shat, sel_state + 8, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag, flag};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
   if (a.geom.esize == 2)
-    compact_kernel<__bf16><<<cg, dim3(kCompactThreads), 0, s>>>(ca);
+    compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
   else
-    compact_kernel<float><<<cg, dim3(kCompactThreads), 0, s>>>(ca);
+    compact_kernel<float><<<cg, dim3(kThreads), 0, s>>>(ca);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(new_lens_host, plan + 2 * P, sizeof(int32_t) * (size_t)P, hipMemcpyDeviceToHost, s);

@@ -179,12 +179,14 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
  *   r_w   = R_w / (N-1);  mu, sigma = mean and population std. deviation of r
  *   Cons  = max(0, 1 - sigma*sqrt(12));  s_hat = s_layer * (1 + lambda*Cons)
  * (float64, fixed order, no fused multiply-add), keep the keep_count
- * candidates first in (s_hat descending, index ascending) order, and pack
- * each page's kept rows of K, V and token ids to the front of that page in
- * their order; emptied pages are released.
+ * candidates first in (s_hat descending, index ascending) order, and compact
+ * each page in place: with n of its slots kept, kept slots below n stay and
+ * the dropped slots below n take the kept slots at or past n (both in
+ * ascending slot order), moving K, V and token ids; emptied pages are
+ * released.  The order of tokens inside a page is not part of the method.
  * score_table_dev: fp32 [score_rows][num_layers], row = global token id.
  * keep_ids_out_dev: optional int32 [keep_count], kept global token ids in
- * table order.  ranks_out_dev: optional int32 [n_window][N], oldest window
+ * candidate order (table order, then slot order before compaction).  ranks_out_dev: optional int32 [n_window][N], oldest window
  * layer first.  n_kept: optional host int64.
  * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
  * for a token id >= score_rows or a bad parameter.  Synchronises the stream
