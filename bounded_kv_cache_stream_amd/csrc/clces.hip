@@ -9,18 +9,21 @@
 // explainer ("Rolling Memory", "Prune and roll the memory").
 //
 // Pipeline (one launch each, all on the caller's stream, one final sync):
+//   prep     the page table (first chunk) and the counters set to zero;
 //   gather   raw scores of every candidate at every window layer (by global
 //            token id), validate them, write 32-bit order keys;
 //   rank     stable LSD radix sort, 4 passes of 8 bits, all window layers at
 //            once (histogram / scan / scatter; the scatter is made stable
 //            with wave ballots); the last pass writes rank[token] directly;
 //   fuse     float64 mean, population variance, Cons and s_hat with a fixed
-//            operation order and no contraction (bit-exact reproducible);
+//            operation order and no contraction (bit-exact reproducible),
+//            plus the histogram of the first select digit;
 //   select   radix select of the keep_count-th largest s_hat (8 passes of 8
-//            bits over the 64-bit pattern, which orders non-negative doubles);
+//            bits over the 64-bit pattern, which orders non-negative doubles;
+//            the first histogram comes from fuse, the last step from mark);
 //   mark     per page: count of s_hat above / equal to the threshold;
-//   plan     per page: rank base among ties (index order), kept count, offset;
-//   index    per page: the kept token ids in slot order, and the moves: with
+//   index    per page: its kept count and offsets (from all pages' counts),
+//            the kept token ids in slot order, and the moves: with
 //            n kept, kept slots below n stay and the dropped slots below n
 //            take the kept slots at or past n (both ascending);
 //   compact  per page: one workgroup per K head, one per V head and one for
@@ -53,8 +56,13 @@ __device__ inline uint32_t order_key(float s) {
   return b == 0x80000000u ? 0u : b;  // -0.0 ranks as +0.0
 }
 
-__global__ void zero_kernel(uint32_t* sel_hist, int32_t* counts, int n_counts, int32_t* flag) {
+// First launch of a step: the first page-table chunk, and the counters that
+// later kernels accumulate into set to zero (select histograms, per-page
+// counts, the error flag).
+__global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* sel_hist, int32_t* counts, int n_counts,
+                            int32_t* flag) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < chunk.count) entries[chunk.first + i] = chunk.e[i];
   if (i < 8 * 256) sel_hist[i] = 0;
   if (i < n_counts) counts[i] = 0;
   if (i == 0) *flag = 0;
@@ -111,6 +119,19 @@ __device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
   return incl - v;
 }
 
+// Add one to cnt[d] for every active lane with `valid`, aggregating lanes of
+// the wave that share the first lane's digit into one atomic (digits are often
+// nearly uniform: the top bytes of similar floats).
+__device__ inline void hist_add(uint32_t* cnt, uint32_t d, bool valid) {
+  const unsigned long long act = __ballot(valid);
+  if (act == 0) return;
+  const int first = __ffsll((long long)act) - 1;
+  const uint32_t lead = __shfl(d, first, 64);
+  const unsigned long long same = __ballot(valid && d == lead);
+  if ((threadIdx.x & 63) == first) atomicAdd(&cnt[lead], (uint32_t)__popcll(same));
+  if (valid && d != lead) atomicAdd(&cnt[d], 1u);
+}
+
 __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* hist, int N, int nblk,
                                                              int shift, const int32_t* flag) {
   if (*flag) return;
@@ -121,46 +142,62 @@ __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* key
   const uint32_t* k = keys + (int64_t)w * N;
   for (int j = 0; j < kItems; ++j) {
     const int i = blk * kRankTile + j * kThreads + tid;
-    if (i < N) atomicAdd(&cnt[(k[i] >> shift) & 255u], 1u);
+    hist_add(cnt, i < N ? (k[i] >> shift) & 255u : 0u, i < N);
   }
   __syncthreads();
-  hist[((int64_t)w * 256 + tid) * nblk + blk] = cnt[tid];
+  hist[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];  // [window][block][digit]
 }
 
+// One stable LSD pass over this block's kRankTile keys (kItems per thread;
+// key i = blk*kRankTile + j*kThreads + tid, so index order is (item j, wave,
+// lane)).  Every wave matches the digits of each of its items with ballots,
+// giving each key its rank among equal digits of its (item, wave) group and
+// each group's digit counts; one pass per digit then turns the counts into
+// exclusive offsets in index order, and every key goes to
+// base[digit] + offset[group][digit] + rank.  Four barriers in all.
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
                                                                 uint32_t* keys_out, uint32_t* vals_out,
                                                                 int32_t* ranks, const uint32_t* hist, int N,
                                                                 int nblk, int shift, int last, const int32_t* flag) {
   if (*flag) return;
-  __shared__ uint32_t base[256], run[256], wcnt[4][256];
+  constexpr int kWaves = kThreads / 64;
+  __shared__ uint32_t cnt[kItems][kWaves][256];
   __shared__ int32_t scan[kThreads];
   const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   // offset of this block's digit-tid keys: keys of smaller digits in the whole
   // segment, plus keys of digit tid in the blocks before this one
+  uint32_t run;
   {
-    const uint32_t* hrow = hist + ((int64_t)w * 256 + tid) * nblk;
+    const uint32_t* hcol = hist + (int64_t)w * nblk * 256 + tid;
     uint32_t tot = 0, before = 0;
     for (int bb = 0; bb < nblk; ++bb) {
-      const uint32_t v = hrow[bb];
+      const uint32_t v = hcol[(int64_t)bb * 256];
       tot += v;
       before += bb < blk ? v : 0u;
     }
-    const int32_t digit_base = block_excl_scan<kThreads>((int32_t)tot, scan, nullptr);
-    base[tid] = (uint32_t)digit_base + before;
+    run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
   }
-  run[tid] = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
-  __syncthreads();
+  for (int j = 0; j < kItems; ++j)
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) cnt[j][q][tid] = 0;
   const int64_t seg = (int64_t)w * N;
   const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t key[kItems], val[kItems], rnk[kItems];
+#pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int i = blk * kRankTile + j * kThreads + tid;
     const bool valid = i < N;
-    const uint32_t key = valid ? keys_in[seg + i] : 0u;
-    const uint32_t d = (key >> shift) & 255u;
-    const uint32_t val = valid ? (vals_in ? vals_in[seg + i] : (uint32_t)i) : 0u;
+    key[j] = valid ? keys_in[seg + i] : 0u;
+    val[j] = valid ? (vals_in ? vals_in[seg + i] : (uint32_t)i) : 0u;
+  }
+  __syncthreads();  // counters zeroed
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int i = blk * kRankTile + j * kThreads + tid;
+    const bool valid = i < N;
+    const uint32_t d = (key[j] >> shift) & 255u;
     unsigned long long m = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
@@ -168,34 +205,52 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* 
       const unsigned long long bb = __ballot(on);
       m &= on ? bb : ~bb;
     }
-    const uint32_t rnk = (uint32_t)__popcll(m & lt);
-    if (valid && rnk == 0) wcnt[wave][d] = (uint32_t)__popcll(m);
-    __syncthreads();
-    if (valid) {
-      uint32_t off = base[d] + run[d] + rnk;
-      for (int q = 0; q < wave; ++q) off += wcnt[q][d];
+    rnk[j] = (uint32_t)__popcll(m & lt);
+    if (valid && rnk[j] == 0) cnt[j][wave][d] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // thread tid owns digit tid: exclusive offsets over the groups in index order
+#pragma unroll
+  for (int j = 0; j < kItems; ++j)
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      const uint32_t c = cnt[j][q][tid];
+      cnt[j][q][tid] = run;
+      run += c;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int i = blk * kRankTile + j * kThreads + tid;
+    if (i < N) {
+      const uint32_t d = (key[j] >> shift) & 255u;
+      const uint32_t off = cnt[j][wave][d] + rnk[j];
       if (last) {
-        ranks[seg + val] = (int32_t)off;
+        ranks[seg + val[j]] = (int32_t)off;
       } else {
-        keys_out[seg + off] = key;
-        vals_out[seg + off] = val;
+        keys_out[seg + off] = key[j];
+        vals_out[seg + off] = val[j];
       }
     }
-    __syncthreads();
-    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
-    __syncthreads();
   }
 }
 
+// Also the first select pass: the histogram of the top byte of s_hat, and
+// the state before it (nothing fixed, keep_count to find).
 __global__ __launch_bounds__(kThreads) void fuse_kernel(const int32_t* ranks, const float* scur,
                                                         unsigned long long* shat, int N, int n_win, double lambda,
-                                                        double sqrt12, const int32_t* flag) {
+                                                        double sqrt12, uint32_t* sel_hist, SelState* states,
+                                                        long long keep, const int32_t* flag) {
 #pragma clang fp contract(off)
   if (*flag) return;
+  __shared__ uint32_t cnt[256];
+  cnt[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) states[0] = SelState{0ull, keep};
+  __syncthreads();
   const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= N) return;
+  const bool valid = i < N;
+  unsigned long long bits = 0;
+  if (valid) {
   const double denom = (double)(N - 1);
   double r[8];
   double acc = 0.0;
@@ -220,7 +275,12 @@ __global__ __launch_bounds__(kThreads) void fuse_kernel(const int32_t* ranks, co
   const double c = 1.0 - sigma * sqrt12;
   const double cons = c > 0.0 ? c : 0.0;
   const double sh = (double)scur[i] * (1.0 + lambda * cons) + 0.0;
-  shat[i] = (unsigned long long)__double_as_longlong(sh);
+  bits = (unsigned long long)__double_as_longlong(sh);
+  shat[i] = bits;
+  }
+  hist_add(cnt, (uint32_t)(bits >> 56), valid);
+  __syncthreads();
+  if (cnt[threadIdx.x]) atomicAdd(&sel_hist[threadIdx.x], cnt[threadIdx.x]);
 }
 
 // One select step: from the state before pass p and that pass's digit
@@ -281,10 +341,9 @@ __global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned lo
   const unsigned long long hi = p == 0 ? 0ull : (~0ull << (shift + 8));
   for (int j = 0; j < kItems; ++j) {
     const int i = blockIdx.x * kRankTile + j * kThreads + threadIdx.x;
-    if (i < N) {
-      const unsigned long long k = keys[i];
-      if ((k & hi) == st.prefix) atomicAdd(&cnt[(k >> shift) & 255ull], 1u);
-    }
+    const unsigned long long k = i < N ? keys[i] : 0ull;
+    const bool match = i < N && (k & hi) == st.prefix;
+    hist_add(cnt, (uint32_t)((k >> shift) & 255ull), match);
   }
   __syncthreads();
   if (cnt[threadIdx.x]) atomicAdd(&sel_hist[p * 256 + threadIdx.x], cnt[threadIdx.x]);
@@ -329,44 +388,6 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
   }
 }
 
-struct PlanArgs {
-  const int32_t* n_gt;
-  const int32_t* n_eq;
-  const SelState* final_state;  // states[8]
-  int32_t* eq_base;
-  int32_t* keep_base;
-  int32_t* new_len;
-  int n_entries;
-  const int32_t* flag;
-};
-
-__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
-  if (*a.flag) return;
-  __shared__ int32_t lds[1024];
-  const int tid = threadIdx.x;
-  const long long k_rem = a.final_state->k_rem;
-  const int per = (a.n_entries + 1023) / 1024;
-  const int b = tid * per, e = min(b + per, a.n_entries);
-  int32_t s_eq = 0;
-  for (int i = b; i < e; ++i) s_eq += a.n_eq[i];
-  int32_t eq_run = block_excl_scan<1024>(s_eq, lds, nullptr);
-  int32_t s_keep = 0;
-  for (int i = b; i < e; ++i) {
-    long long take = k_rem - eq_run;
-    take = take < 0 ? 0 : (take > a.n_eq[i] ? a.n_eq[i] : take);
-    a.eq_base[i] = eq_run;
-    const int32_t kc = a.n_gt[i] + (int32_t)take;
-    a.new_len[i] = kc;
-    s_keep += kc;
-    eq_run += a.n_eq[i];
-  }
-  int32_t keep_run = block_excl_scan<1024>(s_keep, lds, nullptr);
-  for (int i = b; i < e; ++i) {
-    a.keep_base[i] = keep_run;
-    keep_run += a.new_len[i];
-  }
-}
-
 struct CompactArgs {
   const DevEntry* entries;
   uint16_t* move_src;    // [P][ts] kept slots at or past the new length, ascending
@@ -374,9 +395,10 @@ struct CompactArgs {
   int32_t* n_moves;      // [P]
   const unsigned long long* shat;
   const SelState* final_state;
-  const int32_t* eq_base;
-  const int32_t* keep_base;
-  const int32_t* new_len;
+  const int32_t* n_gt;   // [P] keys above the threshold, per page
+  const int32_t* n_eq;   // [P] keys equal to the threshold, per page
+  int32_t* new_len;      // [P] written here: kept slots per page
+  int32_t n_entries;
   char* pool;
   PageGeom g;
   int32_t* keep_ids_out;
@@ -397,14 +419,30 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   const int e = blockIdx.x, tid = threadIdx.x;
   const DevEntry en = a.entries[e];
   const int len = en.len;
-  const int nl = a.new_len[e];
   const SelState st = *a.final_state;
+  // This page's plan.  Keys equal to the threshold are kept in index order
+  // until k_rem of them are, so the pages before this one keep
+  // sum(n_gt) + min(k_rem, sum(n_eq)) keys, and this page's ties are ranked
+  // from sum(n_eq) over those pages.
+  int32_t gt_before = 0, eq_before = 0;
+  for (int i = tid; i < e; i += kThreads) {
+    gt_before += a.n_gt[i];
+    eq_before += a.n_eq[i];
+  }
+  int32_t gt_tot = 0, eq_tot = 0;
+  block_excl_scan<kThreads>(gt_before, scan, &gt_tot);
+  block_excl_scan<kThreads>(eq_before, scan, &eq_tot);
+  const long long k_rem = st.k_rem;
+  const long long eq_take = k_rem - eq_tot;
+  const int32_t nl = a.n_gt[e] + (int32_t)(eq_take < 0 ? 0 : (eq_take > a.n_eq[e] ? a.n_eq[e] : eq_take));
+  const int32_t keep_base = gt_tot + (int32_t)(k_rem < eq_tot ? (k_rem < 0 ? 0 : k_rem) : eq_tot);
+  if (tid == 0) a.new_len[e] = nl;
   const int per = (len + kThreads - 1) / kThreads;
   const int b = tid * per, end = min(b + per, len);
   const unsigned long long* sh = a.shat + en.tok_start;
   int32_t n_eq = 0;
   for (int j = b; j < end; ++j) n_eq += sh[j] == st.prefix;
-  const int32_t eq_start = a.eq_base[e] + block_excl_scan<kThreads>(n_eq, scan, nullptr);
+  const int32_t eq_start = eq_tot + block_excl_scan<kThreads>(n_eq, scan, nullptr);
   int32_t eq_rank = eq_start;
   int32_t n_keep = 0, n_hole = 0;
   for (int j = b; j < end; ++j) {
@@ -441,8 +479,7 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   for (int k = tid; k < holes; k += kThreads) src[k] = kept[nl - holes + k];
   if (a.keep_ids_out) {
     const int32_t* ids = reinterpret_cast<const int32_t*>(a.pool + (int64_t)en.phys * a.g.page_bytes + a.g.id_off);
-    const int32_t kb = a.keep_base[e];
-    for (int i = tid; i < nl; i += kThreads) a.keep_ids_out[kb + i] = ids[kept[i]];
+    for (int i = tid; i < nl; i += kThreads) a.keep_ids_out[keep_base + i] = ids[kept[i]];
   }
   if (tid == 0) a.n_moves[e] = holes;
 }
@@ -450,17 +487,18 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
 typedef int V16 __attribute__((ext_vector_type(4)));  // a native vector: a struct copy would go through scratch
 
 // Move the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes each)
-// from the move sources to the move destinations.  8 threads per row and 8
-// vectors per thread: one pass moves 256 bf16 rows (128 fp32 rows), all loads
-// issued before the stores.  Sources and destinations are disjoint, so no
+// from the move sources to the move destinations.  8 threads per row and 4
+// vectors per thread (bf16): one pass of a 1024-thread workgroup moves 512 rows,
+// all loads issued before the stores.  The host takes 1024 threads when many
+// tokens drop (long move lists per page) and 256 when few do.  Sources and destinations are disjoint, so no
 // barrier is needed; the rows are touched once, so accesses are nontemporal.
-template <typename T>
+template <typename T, int NT>
 __device__ inline void move_rows(V16* rows, const uint16_t* src, const uint16_t* dst, int nm, int tid) {
   constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
   constexpr int TPR = 8;                    // threads per row
   constexpr int UPR = VPR / TPR;            // vectors per thread per row
-  constexpr int G = 8 / UPR;                // row groups per pass
-  constexpr int RPP = kThreads / TPR;       // rows per group
+  constexpr int G = 4 / UPR;                // row groups per pass
+  constexpr int RPP = NT / TPR;              // rows per group
   const int r = tid / TPR, c = tid % TPR;
   for (int i0 = 0; i0 < nm; i0 += RPP * G) {
     V16 v[G][UPR];
@@ -485,8 +523,8 @@ __device__ inline void move_rows(V16* rows, const uint16_t* src, const uint16_t*
 
 // Grid (page, part): part < H moves the K rows of head `part`, H <= part < 2H
 // the V rows of head part - H, part 2H the token ids.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void compact_kernel(CompactArgs a) {
   if (*a.flag) return;
   const int e = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
   const int nm = a.n_moves[e];
@@ -500,10 +538,10 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     constexpr int VPR = 64 * sizeof(T) / 16;
     const int h = part < H ? part : part - H;
     V16* rows = reinterpret_cast<V16*>(page + (part < H ? a.g.k_off : a.g.v_off)) + (int64_t)h * a.g.ts * VPR;
-    move_rows<T>(rows, src, dst, nm, tid);
+    move_rows<T, NT>(rows, src, dst, nm, tid);
   } else {
     int32_t* ids = reinterpret_cast<int32_t*>(page + a.g.id_off);
-    for (int i = tid; i < nm; i += kThreads) ids[dst[i]] = ids[src[i]];
+    for (int i = tid; i < nm; i += NT) ids[dst[i]] = ids[src[i]];
   }
 }
 
@@ -564,10 +602,18 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   if (P > z.p_max || (int64_t)N > z.n_max || W > z.w_max || a.geom.ts > kMaxPageTokensScored)
     return hipErrorInvalidValue;
 
-  hipError_t e = launch_table_upload(entries, a.entries_host, P, s);
+  {
+    TableChunk c;
+    c.first = 0;
+    c.count = std::min(P, kUploadChunk);
+    for (int i = 0; i < c.count; ++i) c.e[i] = a.entries_host[i];
+    const int nz = std::max(8 * 256, 2 * P);
+    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, sel_hist, counts, 2 * P, flag);
+  }
+  hipError_t e = P > kUploadChunk ? launch_table_upload(entries + kUploadChunk, a.entries_host + kUploadChunk,
+                                                        P - kUploadChunk, s)
+                                  : hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nz = std::max(8 * 256, 2 * P);
-  zero_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(sel_hist, counts, 2 * P, flag);
 
   GatherArgs g{entries, a.pool, a.geom.page_bytes, a.geom.id_off, a.score_table, a.score_rows, a.score_cols,
                a.first_layer, W, N, keys_a, scur, flag};
@@ -588,27 +634,34 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
     vout = vout == vals_b ? vals_a : vals_b;
   }
   fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
-      ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), flag);
+      ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
   if (a.keep > 0) {
-    for (int p = 0; p < 8; ++p)
+    for (int p = 1; p < 8; ++p)
       select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, a.keep, p,
                                                                          flag);
   }
   MarkArgs m{entries, shat, sel_hist, a.keep, counts, counts + P, sel_state, flag};
   mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
-  PlanArgs pa{counts, counts + P, sel_state + 8, plan, plan + P, plan + 2 * P, P, flag};
-  plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(pa);
   CompactArgs ca{entries,
                  reinterpret_cast<uint16_t*>(ws + z.move_src),
                  reinterpret_cast<uint16_t*>(ws + z.move_dst),
                  reinterpret_cast<int32_t*>(ws + z.n_moves),
-                 shat, sel_state + 8, plan, plan + P, plan + 2 * P, a.pool, a.geom, a.keep_ids_out, flag, flag};
+                 shat, sel_state + 8, counts, counts + P, plan + 2 * P, P, a.pool, a.geom, a.keep_ids_out, flag,
+                 flag};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
-  if (a.geom.esize == 2)
-    compact_kernel<__bf16><<<cg, dim3(kThreads), 0, s>>>(ca);
-  else
-    compact_kernel<float><<<cg, dim3(kThreads), 0, s>>>(ca);
+  const bool many = (int64_t)(N - a.keep) * 10 > (int64_t)N;  // more than 10% of the tokens drop
+  if (a.geom.esize == 2) {
+    if (many)
+      compact_kernel<__bf16, 1024><<<cg, dim3(1024), 0, s>>>(ca);
+    else
+      compact_kernel<__bf16, 256><<<cg, dim3(256), 0, s>>>(ca);
+  } else {
+    if (many)
+      compact_kernel<float, 1024><<<cg, dim3(1024), 0, s>>>(ca);
+    else
+      compact_kernel<float, 256><<<cg, dim3(256), 0, s>>>(ca);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(new_lens_host, plan + 2 * P, sizeof(int32_t) * (size_t)P, hipMemcpyDeviceToHost, s);
