@@ -49,6 +49,7 @@ def parse():
                          "10,000-frame keyframe-interval-4 stream, sustained; budget: the 24-layer "
                          "token-budget stack (append, attend, score_and_compact per layer)")
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
+    ap.add_argument("--merge", action="store_true", help="budget workload: merge ragged pages after each compaction")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -281,12 +282,12 @@ def run_budget(args):
     out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = {name: [] for name in ("append", "attend", "score")}
+    ev = {name: [] for name in ("append", "attend", "score", "merge")}
 
     def frame(t, timed):
         for l in range(L):
             q, k, v = rings[l][t % 8]
-            marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
             if timed:
                 marks[0].record(stream)
             cache.append(l, t, k, v)
@@ -298,9 +299,14 @@ def run_budget(args):
             cache.score_and_compact(l, table, w["clces_window"], w["lam"], B)
             if timed:
                 marks[3].record(stream)
+            if args.merge:
+                cache.merge_pages(l)
+            if timed:
+                marks[4].record(stream)
                 ev["append"].append((marks[0], marks[1]))
                 ev["attend"].append((marks[1], marks[2]))
                 ev["score"].append((marks[2], marks[3]))
+                ev["merge"].append((marks[3], marks[4]))
 
     for t in range(warm):
         frame(t, False)
@@ -314,13 +320,19 @@ def run_budget(args):
     split = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3 for name, pairs in ev.items()}
     attended = n_tok + T
     flops = 4.0 * H * D * T * attended
+    pages = [cache.info(l)["persisted_frames"] for l in range(L)]
+    ids, lens, _ = cache.page_table(L - 1)
+    tiles = sum((n + 63) // 64 for n in lens) + (T + 63) // 64
     print(json.dumps({
-        "metric": "frames/sec of the 24-layer token-budget stack (append, attend, score_and_compact per layer)",
+        "metric": "frames/sec of the 24-layer token-budget stack (append, attend, score_and_compact"
+                  + (", merge_pages" if args.merge else "") + " per layer)",
         "value": args.steps / wall, "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps,
         "warmup": warm, "ms_per_frame": wall / args.steps * 1e3, "dtype": "bf16",
         "data": "synthetic (ring of 8 seeded AR(1) frames per layer, chi-square raw scores)",
         "config": {"workload": w["name"], "layers": L, "tokens_per_frame": T, "heads": H, "head_dim": D,
                    "budget": B, "attended_tokens": attended, "clces_window": w["clces_window"], "lam": w["lam"]},
+        "page_merge": bool(args.merge), "pages_per_layer_mean": float(np.mean(pages)),
+        "attend_tiles_layer23": tiles, "attend_tile_fill": attended / (64.0 * tiles),
         "us_per_layer": split,
         "attend_tflops": flops / (split["attend"] * 1e-6) / 1e12,
         "attend_frac_bf16_peak": flops / (split["attend"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}), flush=True)

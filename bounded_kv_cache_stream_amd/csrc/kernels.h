@@ -50,6 +50,20 @@ hipError_t launch_append_layers(const PageGeom& g, char* pool, const AppendLayer
                                 const void* k, const void* v, int n_tokens, int64_t first_token_id,
                                 hipStream_t s);
 
+// Page merges of one launch: item i moves count tokens (all heads of K and V,
+// and their ids) from the start of page src to slots dst_off.. of page dst
+// (byte offsets of the pages in the pool).
+constexpr int kMergeChunk = 128;
+struct MergeItem {
+  int64_t src_offset, dst_offset;
+  int32_t dst_off, count;
+};
+struct MergeChunk {
+  int32_t n;
+  MergeItem item[kMergeChunk];
+};
+hipError_t launch_merge(const PageGeom& g, char* pool, const MergeChunk& c, hipStream_t s);
+
 struct AttendParams {
   const void* q;
   void* out;

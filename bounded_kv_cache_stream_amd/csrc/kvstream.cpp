@@ -431,6 +431,35 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   return ok();
 }
 
+kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (pool->cfg.sliding_window > 0)
+    return fail(KV_ERR_STATE, "layer %d: page merge needs one frame per page no more (sliding_window must be 0)",
+                layer);
+  auto& L = pool->layers[(size_t)layer];
+  const std::vector<kvs::MergeMove> mv = L.plan_merges();
+  if (!pool->meta_only) {
+    const int64_t pb = pool->lay.geom.page_bytes;
+    for (size_t c0 = 0; c0 < mv.size(); c0 += kvs::kMergeChunk) {
+      kvs::MergeChunk c;
+      c.n = (int32_t)std::min<size_t>(kvs::kMergeChunk, mv.size() - c0);
+      for (int32_t i = 0; i < c.n; ++i) {
+        const auto& m = mv[c0 + (size_t)i];
+        c.item[i].src_offset = phys_page(pool, layer, m.src) * pb;
+        c.item[i].dst_offset = phys_page(pool, layer, m.dst) * pb;
+        c.item[i].dst_off = m.dst_off;
+        c.item[i].count = m.count;
+      }
+      hipError_t e = kvs::launch_merge(pool->lay.geom, pool->pool, c, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "page merge launch");
+    }
+  }
+  L.commit_merges(mv);
+  if (n_merged) *n_merged = (int32_t)mv.size();
+  return ok();
+}
+
 kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
@@ -445,6 +474,7 @@ kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) 
   out->evictions = L.evictions;
   out->compactions = L.compactions;
   out->last_keep_count = L.last_keep;
+  out->merges = L.merges;
   return ok();
 }
 

@@ -1,4 +1,4 @@
-// Page write and page-table upload, gfx950.
+// Page write, page merge and page-table upload, gfx950.
 //
 // Page write (LingBot-Map 20 FPS explainer, "Page-Aligned Tensor Layout":
 // a frame's tokens go straight into a page-aligned layout, no padding between
@@ -74,6 +74,45 @@ __global__ __launch_bounds__(256) void append_layers_kernel(PageGeom g, char* po
                   blockIdx.y, blockIdx.x * 64);
 }
 
+// Page merge: block (item, part) appends the rows of one head of K (part < H)
+// or V (H <= part < 2H), or the token ids (part 2H), of page src after the
+// dst_off rows already in page dst.  Source and destination are different
+// pages, so every row moves independently.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(PageGeom g, char* pool, MergeChunk c) {
+  typedef int V16 __attribute__((ext_vector_type(4)));
+  constexpr int VPR = D * sizeof(T) / 16;  // 16-byte vectors per row
+  constexpr int RPP = 256 / VPR;           // rows per pass
+  const MergeItem it = c.item[blockIdx.x];
+  const int part = blockIdx.y, H = g.heads, tid = threadIdx.x;
+  const char* src = pool + it.src_offset;
+  char* dst = pool + it.dst_offset;
+  if (part < 2 * H) {
+    const int h = part < H ? part : part - H;
+    const int64_t off = (part < H ? g.k_off : g.v_off);
+    const V16* s = reinterpret_cast<const V16*>(src + off) + (int64_t)h * g.ts * VPR;
+    V16* d = reinterpret_cast<V16*>(dst + off) + ((int64_t)h * g.ts + it.dst_off) * VPR;
+    const int r = tid / VPR, cc = tid % VPR;
+    for (int r0 = 0; r0 < it.count; r0 += 4 * RPP) {
+      V16 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = r0 + u * RPP + r;
+        v[u] = row < it.count ? __builtin_nontemporal_load(&s[row * VPR + cc]) : V16{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = r0 + u * RPP + r;
+        if (row < it.count) __builtin_nontemporal_store(v[u], &d[row * VPR + cc]);
+      }
+    }
+  } else {
+    const int32_t* si = reinterpret_cast<const int32_t*>(src + g.id_off);
+    int32_t* di = reinterpret_cast<int32_t*>(dst + g.id_off) + it.dst_off;
+    for (int i = tid; i < it.count; i += 256) di[i] = si[i];
+  }
+}
+
 __global__ void table_upload_kernel(DevEntry* dst, TableChunk chunk) {
   const int i = threadIdx.x;
   if (i < chunk.count) dst[chunk.first + i] = chunk.e[i];
@@ -91,6 +130,16 @@ hipError_t launch_append_layers(const PageGeom& g, char* pool, const AppendLayer
   else
     append_layers_kernel<float><<<grid, dim3(256), 0, s>>>(g, pool, al, static_cast<const float*>(k),
                                                             static_cast<const float*>(v), n_tokens, first_token_id);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const PageGeom& g, char* pool, const MergeChunk& c, hipStream_t s) {
+  if (c.n <= 0) return hipSuccess;
+  dim3 grid((unsigned)c.n, (unsigned)(2 * g.heads + 1));
+  if (g.esize == 2)
+    merge_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, pool, c);
+  else
+    merge_kernel<float><<<grid, dim3(256), 0, s>>>(g, pool, c);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Host-side cache policy of one layer: keyframe rule, page allocation,
-// sliding-window eviction, and application of compaction results.
+// sliding-window eviction, application of compaction results, and the merge
+// of ragged pages.
 //
 // Pages: GCTStream explainer ("KV Cache Lifecycle Management": skip-append of
 // non-keyframes; "Sliding Window Eviction": the oldest blocks go once the
@@ -13,6 +14,7 @@
 
 #include <stdint.h>
 
+#include <map>
 #include <set>
 #include <vector>
 
@@ -21,7 +23,13 @@ namespace kvs {
 struct PageEntry {
   int32_t page;   // layer-local page id
   int32_t len;    // valid tokens in the page
-  int64_t frame;  // frame index
+  int64_t frame;  // frame index (of the first frame a merged page holds)
+};
+
+// One page merge: the `count` tokens of page `src` go to slots
+// dst_off .. dst_off + count - 1 of page `dst`.
+struct MergeMove {
+  int32_t src, dst, dst_off, count;
 };
 
 class LayerPolicy {
@@ -46,6 +54,7 @@ class LayerPolicy {
     evictions = 0;
     compactions = 0;
     last_keep = 0;
+    merges = 0;
   }
 
   bool is_keyframe(int64_t t) const { return t < S_ || (t - S_) % k_ == 0; }
@@ -120,6 +129,49 @@ class LayerPolicy {
     last_keep = kept;
   }
 
+  // Page merge (defragmentation of the ragged pages compaction leaves): walk
+  // the table in order from the first non-scale entry; a page whose length
+  // fits after the page before it (sum <= page_tokens) is appended to it.
+  // Returns the moves; the table is unchanged until commit_merges.
+  std::vector<MergeMove> plan_merges() const {
+    std::vector<MergeMove> mv;
+    size_t f = first_candidate();
+    if (f >= table.size()) return mv;
+    int32_t cur = table[f].page, cur_len = table[f].len;
+    for (size_t i = f + 1; i < table.size(); ++i) {
+      if (cur_len + table[i].len <= T_) {
+        mv.push_back(MergeMove{table[i].page, cur, cur_len, table[i].len});
+        cur_len += table[i].len;
+      } else {
+        cur = table[i].page;
+        cur_len = table[i].len;
+      }
+    }
+    return mv;
+  }
+
+  void commit_merges(const std::vector<MergeMove>& mv) {
+    std::set<int32_t> gone;
+    std::map<int32_t, int32_t> grow;
+    for (const auto& m : mv) {
+      gone.insert(m.src);
+      grow[m.dst] += m.count;
+    }
+    std::vector<PageEntry> out;
+    for (const auto& e0 : table) {
+      if (gone.count(e0.page)) {
+        free_ids.insert(e0.page);
+        continue;
+      }
+      PageEntry e = e0;
+      auto it = grow.find(e.page);
+      if (it != grow.end()) e.len += it->second;
+      out.push_back(e);
+    }
+    table.swap(out);
+    merges += (int64_t)mv.size();
+  }
+
   int64_t tokens() const {
     int64_t n = 0;
     for (const auto& e : table) n += e.len;
@@ -137,6 +189,7 @@ class LayerPolicy {
   int64_t evictions = 0;
   int64_t compactions = 0;
   int64_t last_keep = 0;
+  int64_t merges = 0;
 
  private:
   int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0;

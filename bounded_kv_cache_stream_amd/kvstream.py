@@ -21,7 +21,7 @@ KV_TRANSIENT = 1
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
     "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
-    "kv_get_page_table", "kv_set_attend_splits", "kv_last_error",
+    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_last_error",
 )
 
 
@@ -40,7 +40,7 @@ class kv_cache_info(ctypes.Structure):
     _fields_ = [("persisted_frames", ctypes.c_int32), ("pages_used", ctypes.c_int32),
                 ("pages_free", ctypes.c_int32), ("transient_pending", ctypes.c_int32),
                 ("tokens", ctypes.c_int64), ("bytes", ctypes.c_int64), ("evictions", ctypes.c_int64),
-                ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64)]
+                ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64), ("merges", ctypes.c_int64)]
 
 
 class kv_pool_layout(ctypes.Structure):
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
             "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
             "kv_set_attend_splits": [P, I32],
+            "kv_merge_pages": [P, I32, ctypes.POINTER(I32), P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -159,6 +160,12 @@ def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_coun
     n = ctypes.c_int64()
     _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
                                    ctypes.byref(n), stream))
+    return n.value
+
+
+def kv_merge_pages(pool, layer, stream=None) -> int:
+    n = ctypes.c_int32()
+    _check(lib().kv_merge_pages(pool, layer, ctypes.byref(n), stream))
     return n.value
 
 
@@ -285,6 +292,9 @@ class KVCache:
                                  window, lam, keep_count,
                                  None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),
                                  None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream())
+
+    def merge_pages(self, layer) -> int:
+        return kv_merge_pages(self.handle, layer, self._stream())
 
     def page_table(self, layer):
         return kv_get_page_table(self.handle, layer)

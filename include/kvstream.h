@@ -89,6 +89,7 @@ typedef struct {
   int64_t evictions;        /* pages evicted by the window since the last reset   */
   int64_t compactions;      /* score_and_compact steps that dropped tokens        */
   int64_t last_keep_count;  /* tokens kept by the last such step                  */
+  int64_t merges;           /* pages released by kv_merge_pages                   */
 } kv_cache_info;
 
 /* Device memory layout of the pool, for callers that read pages directly.
@@ -195,6 +196,21 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
                             int64_t score_rows, const kv_clces_params* params,
                             int32_t* keep_ids_out_dev, int32_t* ranks_out_dev, int64_t* n_kept,
                             void* stream);
+
+/* Page merge: defragments the ragged pages that compaction leaves in a
+ * token-budget layer (no passage of the pages covers it; it keeps the number of
+ * live pages near 2*tokens/page_tokens over unbounded streams instead of one
+ * page per frame ever seen).  Walks the layer's table in order from its first
+ * non-scale page: a page whose length fits after the page before it (lengths
+ * summing to at most page_tokens) is appended to that page -- its K and V rows
+ * of every head and its token ids go to the slots after the earlier page's
+ * rows -- and its page id is released.  The token sequence in table order is
+ * unchanged, so scores, keep sets and attention see the same tokens in the
+ * same order.  Device work (one launch per 128 merges) is enqueued on
+ * `stream`; no sync.  n_merged: optional host int32, pages released.
+ * KV_ERR_STATE if sliding_window > 0 (window eviction removes whole frames,
+ * so its pages must hold one frame each). */
+kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void* stream);
 
 /* Statistics of a layer ([GCT] "Cache Monitoring"). */
 kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out);

@@ -20,9 +20,18 @@ Readings taken where the pages are silent (listed in the design doc):
 * compaction is page-local (see ``oracle.clces.compact_page``); pages left
   empty are released and leave the table; the table order never changes.
 
+Page merge (``merge_pages``) is not on the pages: it defragments the ragged
+pages that compaction leaves.  Walking the table from its first non-scale
+page, a page whose length fits after the page before it (sum at most one
+frame's tokens) is appended to that page and its id is released; the token
+sequence in table order is unchanged.
+
 Pinned by ``tests/test_oracle_budget.py``: the kept set equals a direct top-K
 over the flat candidate list (a second formulation without pages), the size
-bound after every frame, and id bookkeeping invariants.
+bound after every frame, id bookkeeping invariants, and for the merge the
+hand example in ``tests/golden/merge_hand_example.txt``, the unchanged token
+sequence, and the greedy properties (every adjacent pair left sums past one
+page, so fewer than 2N/T + 1 pages remain).
 """
 
 from __future__ import annotations
@@ -56,6 +65,25 @@ class BudgetCache:
         ids = t * self.T + np.arange(self.T, dtype=np.int64)
         self.table.append([pid, t, ids])
         return pid
+
+    def merge_pages(self) -> list[tuple[int, int, int, int]]:
+        """Append each page that fits after the page before it; return the moves.
+
+        Moves are ``(src_page, dst_page, dst_slot, count)`` in table order."""
+        moves = []
+        out = []
+        for entry in self.table:
+            pid, f, ids = entry
+            if f < self.S or not out or out[-1][1] < self.S or len(out[-1][2]) + len(ids) > self.T:
+                out.append([pid, f, ids])
+                continue
+            dst = out[-1]
+            moves.append((pid, dst[0], len(dst[2]), len(ids)))
+            dst[2] = np.concatenate([dst[2], ids])
+            self.free.add(pid)
+        self.table = out
+        self.merges = getattr(self, "merges", 0) + len(moves)
+        return moves
 
     def candidate_ids(self) -> np.ndarray:
         parts = [ids for _, f, ids in self.table if f >= self.S]

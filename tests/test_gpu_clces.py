@@ -113,8 +113,10 @@ def test_clces_scale_frames_protected():
         _page_bytes_equal(cache, 1, pid, len(idv), host[f][0][sl], host[f][1][sl], idv)
 
 
-def test_budget_stream_small_ragged_pages():
-    # per frame: append -> attend over ragged pages -> score_and_compact, every frame checked
+@pytest.mark.parametrize("merge", [False, True])
+def test_budget_stream_small_ragged_pages(merge):
+    # per frame: append -> attend over ragged pages -> score_and_compact (-> page
+    # merge), every frame checked
     torch = torch_cuda()
     T, H, L, B, F = 100, 4, 6, 230, 14
     cache = kv.KVCache(_cfg(L, T, F, H=H, max_queries=T), device="cuda")
@@ -123,6 +125,7 @@ def test_budget_stream_small_ragged_pages():
     sims = [budget.BudgetCache(l, T, B, F) for l in range(L)]
     streams = [synth.AR1Stream(92, l, (T, H, 64), device="cuda") for l in range(L)]
     host = {l: {} for l in range(L)}
+    merged = 0
     for t in range(F):
         for l in range(L):
             q, k, v = streams[l].next()
@@ -144,13 +147,22 @@ def test_budget_stream_small_ragged_pages():
             if ran:
                 assert ranks.cpu().numpy().tolist() == sims[l].last["ranks"].tolist(), (t, l)
                 assert keep.cpu().numpy().tolist() == sims[l].last["keep_ids"].tolist(), (t, l)
+            if merge:
+                m = cache.merge_pages(l)
+                assert m == len(sims[l].merge_pages()), (t, l)
+                merged += m
             pids, lens, fr = cache.page_table(l)
             assert list(zip(pids, fr, lens)) == sims[l].page_table(), (t, l)
-    # bytes of every page of the last layer
+    if merge:
+        assert merged > 0
+        assert cache.info(L - 1)["merges"] == sims[L - 1].merges
+    # bytes of every page of the last layer (a merged page holds several frames' tokens)
     l = L - 1
     for pid, f, idv in sims[l].table:
-        sl = torch.from_numpy(idv - f * T)
-        _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
+        fr_of, sl_of = idv // T, idv % T
+        krows = torch.stack([host[l][int(a)][0][int(b)] for a, b in zip(fr_of, sl_of)])
+        vrows = torch.stack([host[l][int(a)][1][int(b)] for a, b in zip(fr_of, sl_of)])
+        _page_bytes_equal(cache, l, pid, len(idv), krows, vrows, idv)
 
 
 def test_clces_24_layers_72288_tokens_keep_half():

@@ -181,3 +181,19 @@ def test_multi_layer_append_is_all_or_nothing():
     with pytest.raises(kv.KVError) as e:
         c.append_layers(1, 4, n_layers=3)  # layers 1..3 of a 3-layer pool
     assert e.value.status == kv.KV_ERR_ARG
+
+
+def test_page_merge_host_rules():
+    # window pools refuse it (their pages are whole frames the window evicts);
+    # in a budget pool, full pages never fit together, so nothing merges
+    c = _meta_pool(1, 4, 1, 6)
+    c.append(0, 0, None, None)
+    with pytest.raises(kv.KVError) as e:
+        c.merge_pages(0)
+    assert e.value.status == kv.KV_ERR_STATE
+    b = _meta_pool(0, 0, 1, 5)
+    for t in range(4):
+        b.append(0, t, None, None)
+    assert b.merge_pages(0) == 0
+    assert b.page_table(0)[1] == [16] * 4
+    assert b.info(0)["merges"] == 0

@@ -4,6 +4,8 @@ The paged simulation is checked against a second formulation that keeps one
 flat list of token ids (no pages, no compaction), and against the size bound.
 """
 
+import os
+
 import numpy as np
 
 from oracle import budget, clces
@@ -72,3 +74,57 @@ def test_budget_step_keeps_exactly_budget():
         c.append(t)
         c.score_and_compact(table)
         assert len(c.all_ids()) == min((t + 1) * T, B) if (t + 1) * T > B else (t + 1) * T
+
+
+def _merge_case():
+    path = os.path.join(os.path.dirname(__file__), "golden", "merge_hand_example.txt")
+    d = {}
+    for ln in open(path):
+        if ln.strip() and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            d[k.strip()] = [int(x) for x in v.split()]
+    return d
+
+
+def _cache_with_lengths(T, lens, scale_frames=0):
+    c = budget.BudgetCache(0, T, 10 ** 9, num_pages=len(lens), scale_frames=scale_frames)
+    for t, n in enumerate(lens):
+        c.append(t)
+        c.table[-1][2] = c.table[-1][2][:n]
+    return c
+
+
+def test_merge_hand_example():
+    d = _merge_case()
+    c = _cache_with_lengths(d["T"][0], d["lengths"])
+    moves = c.merge_pages()
+    assert [n for _, _, n in c.page_table()] == d["after"]
+    assert sorted(src for src, _, _, _ in moves) == d["released"]
+    assert c.free == set(d["released"])
+
+
+def test_merge_properties():
+    # the token sequence is unchanged; greedy leaves every adjacent pair past
+    # one page, so fewer than 2N/T + 1 pages remain; scale pages never merge
+    rng = np.random.default_rng(8)
+    for trial in range(300):
+        T = int(rng.integers(4, 200))
+        S = int(rng.integers(0, 3))
+        lens = [T] * S + [int(x) for x in rng.integers(1, T + 1, size=int(rng.integers(1, 40)))]
+        c = _cache_with_lengths(T, lens, scale_frames=S)
+        before = c.all_ids().copy()
+        pages_before = {p for p, _, _ in c.page_table()}
+        moves = c.merge_pages()
+        np.testing.assert_array_equal(c.all_ids(), before)
+        tab = c.page_table()
+        assert [n for _, f, n in tab[:S]] == [T] * S and all(f < S for _, f, _ in tab[:S])
+        rest = [n for _, _, n in tab[S:]]
+        assert all(n <= T for n in rest)
+        assert all(a + b > T for a, b in zip(rest, rest[1:]))
+        N = sum(rest)
+        assert len(rest) < 2 * N / T + 1
+        assert {p for p, _, _ in tab} | {m[0] for m in moves} == pages_before
+        assert len(moves) == len(pages_before) - len(tab)
+        # every move appends a whole page right after the destination's rows
+        for src, dst, slot, n in moves:
+            assert 0 < n and slot + n <= T
