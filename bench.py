@@ -50,6 +50,8 @@ def parse():
                          "token-budget stack (append, attend, score_and_compact per layer)")
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
     ap.add_argument("--merge", action="store_true", help="budget workload: merge ragged pages after each compaction")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="stream workload: heads per GPU (default 16; 2 = one GPU's share when 8 GPUs split the heads)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -60,14 +62,17 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per attention call from the committed counter summary, if it matches this kernel source."""
+def recorded_traffic(heads, splits):
+    """HBM bytes per attention call from the committed counter summary, if it was taken with this kernel
+    source, this head count and this split count (0 = the library's choice)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(ATTEND_SOURCE):
+    if rec.get("source_sha256_16") != source_hash(ATTEND_SOURCE) or rec.get("heads") != heads:
+        return None
+    if splits not in (0, rec.get("splits")):
         return None
     return rec.get("bytes_per_call")
 
@@ -247,7 +252,8 @@ def run_long(args):
         "metric": "frames/sec sustained over the keyframe-interval-4 stream (append+evict+attend, 1 layer)",
         "value": F / (ms / 1e3), "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "frames": F,
         "ms_per_frame": ms / F, "dtype": "bf16", "data": "synthetic (ring of 64 seeded AR(1) frames, bf16)",
-        "config": {"workload": w["name"], "tokens_per_frame": T, "heads": H, "head_dim": D, "scale_frames": S,
+        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_"), "tokens_per_frame": T, "heads": H,
+                   "head_dim": D, "scale_frames": S,
                    "sliding_window": Wf, "keyframe_interval": k},
         "final_persisted_frames": info["persisted_frames"], "wall_s": wall}), flush=True)
 
@@ -364,10 +370,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[1]
-    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    T, H, D = w["tokens"], args.heads or w["heads"], w["head_dim"]
     S, Wf = w["scale_frames"], w["window"]
     cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
-                         keyframe_interval=1, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=16)
+                         keyframe_interval=1, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=64)
     cache = kv.KVCache(cfg, device=dev)
     if args.splits:
         cache.set_splits(args.splits)
@@ -449,12 +455,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded AR(1) frame-correlated Q/K/V, bf16)",
-        "config": {"workload": w["name"], "tokens_per_frame": T, "heads": H, "head_dim": D,
+        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_"), "tokens_per_frame": T, "heads": H,
+                   "head_dim": D,
                    "cache_frames": S + Wf, "cached_tokens": n_keys, "scale_frames": S, "sliding_window": Wf,
                    "keyframe_interval": 1, "step": "append+evict+attend", "layers": 1,
                    "stream_frames": total},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(),
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(H, args.splits),
                      "kernel": "stream_attend (attend_bf16_kernel + split-KV combine)",
                      "avg_call_us": attend_avg_s * 1e6, "flop_per_call": flops},
         "wall_s_timed": wall,

@@ -59,8 +59,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
-constexpr int BM = kAttendRows;  // query rows per workgroup (4 waves x 64)
 constexpr int BN = kTile;    // keys per tile
+constexpr int BM = kAttendRows;  // query rows per workgroup (4 waves x 64)
 constexpr int LDS_LD = 72;   // bf16 per LDS row (64 + 8 pad)
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -87,6 +87,8 @@ __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // two waves per SIMD: 256 VGPRs per lane for the two query blocks' accumulators
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
+  constexpr int RPP = 32;          // K/V rows staged per pass (8 threads per 128-byte row)
+  constexpr int PP = BN / RPP;     // passes per tile
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * LDS_LD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * LDS_LD];
 
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lchunk = tid & 7;
   const int64_t head_off = (int64_t)h * g.ts * D;
 
-  bf16x8 kreg[2], vreg[2];
+  bf16x8 kreg[PP], vreg[PP];
   // The page table is read-only for the kernel's lifetime: read it through the
   // constant address space so that the walk runs on scalar loads and SALU, and
   // the tile's base address stays in SGPRs (each load is base + 32-bit lane offset).
@@ -161,9 +163,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const char* kt = base + g.k_off;
     const char* vt = base + g.v_off;
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * 32 * D * sizeof(bf16));
-      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * 32 * D * sizeof(bf16));
+    for (int pp = 0; pp < PP; ++pp) {
+      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * RPP * D * sizeof(bf16));
+      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * RPP * D * sizeof(bf16));
     }
     return nvalid;
   };
@@ -171,12 +173,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (nvalid < BN) {
       // keys past the page's length: zero V rows (their probabilities are 0)
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        if (lrow + 32 * pp >= nvalid) vreg[pp] = bf16x8{};
+      for (int pp = 0; pp < PP; ++pp)
+        if (lrow + RPP * pp >= nvalid) vreg[pp] = bf16x8{};
     }
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int r = lrow + 32 * pp;
+    for (int pp = 0; pp < PP; ++pp) {
+      const int r = lrow + RPP * pp;
       *reinterpret_cast<bf16x8*>(&Ks[b][r * LDS_LD + lchunk * 8]) = kreg[pp];
       *reinterpret_cast<bf16x8*>(&Vs[b][r * LDS_LD + lchunk * 8]) = vreg[pp];
     }
@@ -344,28 +346,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // Merge split-KV partials: O = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s.
+// One wave per row: lanes over the splits give m, the weights and L by wave
+// reductions; then lanes over d accumulate the weighted partial rows, the
+// weight of split s read with v_readlane, the loads of the splits independent.
 template <typename OutT>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p, int H) {
   const int64_t rows = (int64_t)p.n_q * H;
-  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;  // 4 d values each
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= rows) return;
-  float m = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_ml[(s * rows + idx) * 2]);
-  float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.splits; ++s) {
-    const float ms = p.part_ml[(s * rows + idx) * 2];
-    const float w = __builtin_amdgcn_exp2f(ms - m);
-    L += w * p.part_ml[(s * rows + idx) * 2 + 1];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + (s * rows + idx) * D + sub * 4);
-    acc += w * o;
+  const int S = p.splits;  // <= 64
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < S) {
+    ms = p.part_ml[((int64_t)lane * rows + idx) * 2];
+    ls = p.part_ml[((int64_t)lane * rows + idx) * 2 + 1];
   }
-  const float inv = 1.f / L;
-  OutT* out = static_cast<OutT*>(p.out) + idx * D + sub * 4;
+  float m = ms;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = (OutT)(acc[j] * inv);
-  if (p.lse && sub == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float w = lane < S ? __builtin_amdgcn_exp2f(ms - m) : 0.f;
+  float L = w * ls;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  float acc = 0.f;
+  const float* po = p.part_o + idx * D + lane;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+    acc = fmaf(ws, po[(int64_t)s * rows * D], acc);
+  }
+  OutT* out = static_cast<OutT*>(p.out) + idx * D + lane;
+  *out = (OutT)(acc / L);
+  if (p.lse && lane == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
 }
 
 // fp32 caches: one wave per (query, head); lane = d.
@@ -416,7 +428,7 @@ hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hi
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits == 1) return err;
   const int64_t rows = (int64_t)p.n_q * g.heads;
-  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(p, g.heads);
+  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, g.heads);
   return hipGetLastError();
 }
 

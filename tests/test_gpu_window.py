@@ -248,3 +248,32 @@ def test_page_write_bytes(dtype, T, H):
         assert not pk[:, T:].cpu().view(iv).any() and not pv[:, T:].cpu().view(iv).any(), f"pad of frame {t}"
         expect = [t * T + i for i in range(T)] + [-1] * (Ts - T)
         assert ids.cpu().numpy().tolist() == expect, f"ids of frame {t}"
+
+
+def test_two_head_shard_many_splits():
+    # one GPU's share when the heads are split across 8 GPUs: 2 heads of the
+    # 1004-token, 72-frame cache; the library fills the chip with many KV splits
+    torch = torch_cuda()
+    T, H, S, Wf = 1004, 2, 8, 64
+    cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
+                         keyframe_interval=1, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=64)
+    cache = kv.KVCache(cfg, device="cuda")
+    ar = synth.AR1Stream(1, 0, (T, H, 64), device="cuda")
+    host = {}
+    for t in range(S + Wf + 1):
+        q, k, v = ar.next()
+        cache.append(0, t, k, v)
+        cache.evict(0)
+        host[t] = (to32(k), to32(v))
+    att = list(range(S)) + list(range(S + 1, S + Wf + 1))
+    assert cache.page_table(0)[2] == att
+    K = np.concatenate([host[f][0] for f in att]).astype(np.float64)
+    V = np.concatenate([host[f][1] for f in att]).astype(np.float64)
+    ref, ref_lse = attention.attend(to64(q), K, V, 1.0)
+    for splits in (0, 64):
+        cache.set_splits(splits)
+        lse = torch.empty(T * H, dtype=torch.float32, device="cuda")
+        out = cache.attend(0, q, 1.0, lse=lse)
+        ma, rl = assert_close(to64(out), ref, bf16=True, what=f"2-head shard, splits {splits or 'auto'}")
+        assert max_abs(to64(lse).reshape(ref_lse.shape), ref_lse) <= LSE_ABS
+        say(f"2-head shard (splits {splits or 'auto'}): max_abs {ma:.2e} rel_l2 {rl:.2e}")
