@@ -123,15 +123,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  const int t_begin = (int)((int64_t)sp * p.total_tiles / p.splits);
-  const int t_end = (int)((int64_t)(sp + 1) * p.total_tiles / p.splits);
+  // The page table is read-only for the kernel's lifetime: read it through the
+  // constant address space so that the walk runs on scalar loads and SALU, and
+  // the tile's base address stays in SGPRs (each load is base + 32-bit lane offset).
+  typedef const __attribute__((address_space(4))) DevEntry* ConstTable;
+  const ConstTable tab = (ConstTable)(p.table + (int64_t)h * p.head_stride);
+  const int total_tiles = p.head_stride ? tab[p.n_entries].tile_start : p.total_tiles;
+  const int t_begin = (int)((int64_t)sp * total_tiles / p.splits);
+  const int t_end = (int)((int64_t)(sp + 1) * total_tiles / p.splits);
 
   int e = 0;
   {
     int lo = 0, hi = p.n_entries - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (((const __attribute__((address_space(4))) DevEntry*)p.table)[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
+      if (tab[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
     }
     e = lo;
   }
@@ -149,11 +155,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t head_off = (int64_t)h * g.ts * D;
 
   bf16x8 kreg[PP], vreg[PP];
-  // The page table is read-only for the kernel's lifetime: read it through the
-  // constant address space so that the walk runs on scalar loads and SALU, and
-  // the tile's base address stays in SGPRs (each load is base + 32-bit lane offset).
-  typedef const __attribute__((address_space(4))) DevEntry* ConstTable;
-  const ConstTable tab = (ConstTable)p.table;
   const uint32_t lane_off = (uint32_t)((lrow * D + lchunk * 8) * sizeof(bf16));
   auto load_tile = [&](int t) -> int {
     while (t >= tab[e].tile_start + ((tab[e].len + BN - 1) / BN)) ++e;
@@ -391,8 +392,9 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(PageGeom g, AttendParam
   const float* q = static_cast<const float*>(p.q);
   const float qv = q[((int64_t)qrow * H + h) * D + lane];
   float m_run = -INFINITY, l_run = 0.f, o = 0.f;
+  const DevEntry* tb = p.table + (int64_t)h * p.head_stride;
   for (int e = 0; e < p.n_entries; ++e) {
-    const DevEntry en = p.table[e];
+    const DevEntry en = tb[e];
     const char* page = p.pool + (int64_t)en.phys * g.page_bytes;
     const float* kt = reinterpret_cast<const float*>(page + g.k_off) + (int64_t)h * g.ts * D;
     const float* vt = reinterpret_cast<const float*>(page + g.v_off) + (int64_t)h * g.ts * D;

@@ -44,6 +44,12 @@ struct ClcesArgs {
   int32_t* ranks_out;
 };
 
+// Stable ascending rank of every key within each of `segments` segments of N
+// keys (keys_a: [segments][N], overwritten; ranks: [segments][N]), 4 LSD
+// passes of 8 bits; hist holds segments * ceil(N / kRankTile) * 256 counters.
+hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
+                                uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s);
+
 // Enqueues the whole step, then waits for it and returns the new page
 // lengths (one per candidate entry) and the error flags.
 hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s);

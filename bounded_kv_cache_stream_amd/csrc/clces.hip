@@ -37,6 +37,7 @@
 #include <utility>
 
 #include "clces.h"
+#include "rowmove.h"
 
 namespace kvs {
 namespace {
@@ -484,42 +485,6 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   if (tid == 0) a.n_moves[e] = holes;
 }
 
-typedef int V16 __attribute__((ext_vector_type(4)));  // a native vector: a struct copy would go through scratch
-
-// Move the rows of one head of one page ([slot][d], 64 * sizeof(T) bytes each)
-// from the move sources to the move destinations.  8 threads per row and 4
-// vectors per thread (bf16): one pass of a 1024-thread workgroup moves 512 rows,
-// all loads issued before the stores.  The host takes 1024 threads when many
-// tokens drop (long move lists per page) and 256 when few do.  Sources and destinations are disjoint, so no
-// barrier is needed; the rows are touched once, so accesses are nontemporal.
-template <typename T, int NT>
-__device__ inline void move_rows(V16* rows, const uint16_t* src, const uint16_t* dst, int nm, int tid) {
-  constexpr int VPR = 64 * sizeof(T) / 16;  // vectors per row
-  constexpr int TPR = 8;                    // threads per row
-  constexpr int UPR = VPR / TPR;            // vectors per thread per row
-  constexpr int G = 4 / UPR;                // row groups per pass
-  constexpr int RPP = NT / TPR;              // rows per group
-  const int r = tid / TPR, c = tid % TPR;
-  for (int i0 = 0; i0 < nm; i0 += RPP * G) {
-    V16 v[G][UPR];
-    int s[G], d[G];
-#pragma unroll
-    for (int gq = 0; gq < G; ++gq) {
-      const int i = i0 + gq * RPP + r;
-      s[gq] = i < nm ? src[i] : 0;  // past the end: load slot 0 (in bounds, never stored)
-      d[gq] = i < nm ? dst[i] : -1;
-    }
-#pragma unroll
-    for (int gq = 0; gq < G; ++gq)
-#pragma unroll
-      for (int u = 0; u < UPR; ++u) v[gq][u] = __builtin_nontemporal_load(&rows[s[gq] * VPR + c + TPR * u]);
-#pragma unroll
-    for (int gq = 0; gq < G; ++gq)
-      if (d[gq] >= 0)
-#pragma unroll
-        for (int u = 0; u < UPR; ++u) __builtin_nontemporal_store(v[gq][u], &rows[d[gq] * VPR + c + TPR * u]);
-  }
-}
 
 // Grid (page, part): part < H moves the K rows of head `part`, H <= part < 2H
 // the V rows of head part - H, part 2H the token ids.
@@ -581,6 +546,26 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   return z;
 }
 
+hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
+                                uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s) {
+  const int nblk = (N + kRankTile - 1) / kRankTile;
+  uint32_t* kin = keys_a;
+  uint32_t* kout = keys_b;
+  uint32_t* vin = nullptr;
+  uint32_t* vout = vals_b;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift,
+                                                                                          flag);
+    rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(
+        kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
+    std::swap(kin, kout);
+    vin = vout;
+    vout = vout == vals_b ? vals_a : vals_b;
+  }
+  return hipGetLastError();
+}
+
 hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s) {
   const ClcesSizes& z = a.sizes;
   char* ws = a.ws;
@@ -620,19 +605,8 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   gather_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(g);
 
   const int nblk = (N + kRankTile - 1) / kRankTile;
-  uint32_t* kin = keys_a;
-  uint32_t* kout = keys_b;
-  uint32_t* vin = nullptr;
-  uint32_t* vout = vals_b;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift, flag);
-    rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)W), dim3(kThreads), 0, s>>>(
-        kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
-    std::swap(kin, kout);
-    vin = vout;
-    vout = vout == vals_b ? vals_a : vals_b;
-  }
+  e = launch_rank_segments(keys_a, keys_b, vals_a, vals_b, ranks, hist, N, W, flag, s);
+  if (e != hipSuccess) return e;
   fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
       ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
   if (a.keep > 0) {

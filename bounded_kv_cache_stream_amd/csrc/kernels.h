@@ -74,6 +74,11 @@ struct AttendParams {
   const DevEntry* table;
   int32_t n_entries;
   int32_t total_tiles;
+  // 0: one table for every head.  Otherwise head h's table starts at
+  // table + h * head_stride (n_entries entries, zero-length where the head
+  // holds nothing of that page) and entry n_entries of it holds the head's
+  // tile count in tile_start.
+  int32_t head_stride;
   int32_t splits;
   int32_t n_q;
   float scale_log2;  // sm_scale * log2(e)

@@ -51,6 +51,7 @@ size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 struct Layout {
   kvs::PageGeom geom;
   int64_t layer_pages;  // pages per layer including the transient page
+  int64_t table_cap;    // device page-table entries per layer
   size_t pool_bytes;
   // workspace regions (byte offsets)
   size_t tables, part_o, part_ml, clces, ws_bytes;
@@ -94,7 +95,8 @@ Layout make_layout(const kv_pool_config* c) {
 
   size_t off = 0;
   L.tables = off;
-  off = align_up(off + sizeof(kvs::DevEntry) * (size_t)(L.layer_pages * c->num_layers));
+  L.table_cap = (H + 1) * (L.layer_pages + 1);  // entries per layer: room for one table per head
+  off = align_up(off + sizeof(kvs::DevEntry) * (size_t)(L.table_cap * c->num_layers));
   L.part_rows = (int64_t)c->max_splits * std::min(c->max_queries, c->page_tokens);
   L.part_o = off;
   off = align_up(off + (size_t)L.part_rows * H * D * 4);
@@ -135,7 +137,7 @@ int64_t phys_page(const kv_pool_t* p, int32_t layer, int32_t page) {
 }
 
 kvs::DevEntry* dev_table(const kv_pool_t* p, int32_t layer) {
-  return reinterpret_cast<kvs::DevEntry*>(p->ws + p->lay.tables) + (int64_t)layer * p->lay.layer_pages;
+  return reinterpret_cast<kvs::DevEntry*>(p->ws + p->lay.tables) + (int64_t)layer * p->lay.table_cap;
 }
 
 }  // namespace
@@ -303,21 +305,37 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   auto& L = pool->layers[(size_t)layer];
   auto& ent = pool->scratch;
   ent.clear();
-  int32_t tiles = 0, toks = 0;
-  auto add = [&](int32_t page, int32_t len) {
-    if (len <= 0) return;
-    kvs::DevEntry d;
-    d.phys = (int32_t)phys_page(pool, layer, page);
-    d.len = len;
-    d.tile_start = tiles;
-    d.tok_start = toks;
-    tiles += (len + kvs::kTile - 1) / kvs::kTile;
-    toks += len;
-    ent.push_back(d);
-  };
-  for (const auto& e : L.table) add(e.page, e.len);
-  if (L.transient_pending) add(-1, pool->cfg.page_tokens);
-  if (ent.empty()) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
+  const int32_t H = pool->cfg.num_heads;
+  const bool per_head = !L.uniform();
+  // one table for every head, or (once heads keep different tokens) one per
+  // head: entries for every page, zero-length where the head holds nothing,
+  // and a last entry carrying the head's tile count
+  int32_t tiles = 0, min_tiles = INT32_MAX, n_entries = 0;
+  for (int32_t h = 0; h < (per_head ? H : 1); ++h) {
+    int32_t t_h = 0, toks = 0;
+    auto add = [&](int32_t page, int32_t len) {
+      kvs::DevEntry d;
+      d.phys = (int32_t)phys_page(pool, layer, page);
+      d.len = len;
+      d.tile_start = t_h;
+      d.tok_start = toks;
+      t_h += (len + kvs::kTile - 1) / kvs::kTile;
+      toks += len;
+      ent.push_back(d);
+    };
+    const size_t first = ent.size();
+    for (const auto& e : L.table)
+      if (per_head || e.len > 0) add(e.page, per_head ? kvs::head_len(e, h) : e.len);
+    if (L.transient_pending) add(-1, pool->cfg.page_tokens);
+    n_entries = (int32_t)(ent.size() - first);
+    if (per_head) {
+      kvs::DevEntry sentinel{0, 0, t_h, toks};
+      ent.push_back(sentinel);
+    }
+    tiles = std::max(tiles, t_h);
+    min_tiles = std::min(min_tiles, t_h);
+  }
+  if (n_entries == 0 || min_tiles == 0) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   kvs::DevEntry* dt = dev_table(pool, layer);
@@ -339,7 +357,7 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
       splits = (int32_t)std::max<int64_t>(1, (target + base / 2) / base);
     }
     splits = std::min<int32_t>(splits, pool->cfg.max_splits);
-    splits = std::min<int32_t>(splits, tiles);
+    splits = std::min<int32_t>(splits, min_tiles);
     splits = (int32_t)std::min<int64_t>(splits, std::max<int64_t>(1, pool->lay.part_rows / n_q));
     splits = std::max(splits, 1);
   }
@@ -351,8 +369,9 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   ap.part_ml = reinterpret_cast<float*>(pool->ws + pool->lay.part_ml);
   ap.pool = pool->pool;
   ap.table = dt;
-  ap.n_entries = (int32_t)ent.size();
+  ap.n_entries = n_entries;
   ap.total_tiles = tiles;
+  ap.head_stride = per_head ? n_entries + 1 : 0;
   ap.splits = splits;
   ap.n_q = n_q;
   ap.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -373,6 +392,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
   auto& L = pool->layers[(size_t)layer];
+  if (!L.uniform()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   const size_t first = L.first_candidate();
   int64_t N = 0;
   for (size_t i = first; i < L.table.size(); ++i) N += L.table[i].len;
@@ -438,6 +458,7 @@ kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void
     return fail(KV_ERR_STATE, "layer %d: page merge needs one frame per page no more (sliding_window must be 0)",
                 layer);
   auto& L = pool->layers[(size_t)layer];
+  if (!L.uniform()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   const std::vector<kvs::MergeMove> mv = L.plan_merges();
   if (!pool->meta_only) {
     const int64_t pb = pool->lay.geom.page_bytes;

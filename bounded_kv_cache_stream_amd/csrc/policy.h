@@ -22,9 +22,12 @@ namespace kvs {
 
 struct PageEntry {
   int32_t page;   // layer-local page id
-  int32_t len;    // valid tokens in the page
+  int32_t len;    // valid tokens in the page (the largest head length when heads differ)
   int64_t frame;  // frame index (of the first frame a merged page holds)
+  std::vector<int32_t> hlen;  // per-head lengths once heads keep different tokens; empty: every head holds len
 };
+
+inline int32_t head_len(const PageEntry& e, int h) { return e.hlen.empty() ? e.len : e.hlen[(size_t)h]; }
 
 // One page merge: the `count` tokens of page `src` go to slots
 // dst_off .. dst_off + count - 1 of page `dst`.
@@ -55,6 +58,7 @@ class LayerPolicy {
     compactions = 0;
     last_keep = 0;
     merges = 0;
+    prunes = 0;
   }
 
   bool is_keyframe(int64_t t) const { return t < S_ || (t - S_) % k_ == 0; }
@@ -80,7 +84,7 @@ class LayerPolicy {
       return;
     }
     free_ids.erase(page);
-    table.push_back(PageEntry{page, T_, t});
+    table.push_back(PageEntry{page, T_, t, {}});
   }
 
   int32_t evict() {
@@ -119,6 +123,7 @@ class LayerPolicy {
     for (size_t i = f; i < table.size(); ++i) {
       PageEntry e = table[i];
       e.len = new_lens[i - f];
+      e.hlen.clear();
       if (e.len == 0)
         free_ids.insert(e.page);
       else
@@ -172,6 +177,42 @@ class LayerPolicy {
     merges += (int64_t)mv.size();
   }
 
+  // Per-head new lengths for entries first_candidate().. ([entry][head]); a
+  // page whose heads are all empty leaves the table and its id is freed.
+  void apply_head_compaction(const std::vector<int32_t>& new_lens, int heads) {
+    size_t f = first_candidate();
+    std::vector<PageEntry> out(table.begin(), table.begin() + (long)f);
+    for (size_t i = f; i < table.size(); ++i) {
+      PageEntry e = table[i];
+      const int32_t* nl = &new_lens[(i - f) * (size_t)heads];
+      int32_t mx = 0;
+      bool same = true;
+      for (int h = 0; h < heads; ++h) {
+        mx = nl[h] > mx ? nl[h] : mx;
+        same = same && nl[h] == nl[0];
+      }
+      if (mx == 0) {
+        free_ids.insert(e.page);
+        continue;
+      }
+      e.len = mx;
+      if (same)
+        e.hlen.clear();
+      else
+        e.hlen.assign(nl, nl + heads);
+      out.push_back(e);
+    }
+    table.swap(out);
+    ++prunes;
+  }
+
+  // True when every page holds the same tokens in every head.
+  bool uniform() const {
+    for (const auto& e : table)
+      if (!e.hlen.empty()) return false;
+    return true;
+  }
+
   int64_t tokens() const {
     int64_t n = 0;
     for (const auto& e : table) n += e.len;
@@ -190,6 +231,7 @@ class LayerPolicy {
   int64_t compactions = 0;
   int64_t last_keep = 0;
   int64_t merges = 0;
+  int64_t prunes = 0;
 
  private:
   int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0;
