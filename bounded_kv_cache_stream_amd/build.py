@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libkvstream.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attend.hip", "pages.hip", "clces.hip"]
+HIP_SOURCES = ["attend.hip", "pages.hip", "clces.hip", "diversity.hip"]
 # per-file extra flags: keep MFMA accumulators in architectural VGPRs (the
 # softmax reads every score accumulator; AGPR copies would cost VALU slots)
 EXTRA_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

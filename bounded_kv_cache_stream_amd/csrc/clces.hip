@@ -36,6 +36,7 @@
 #include <cmath>
 #include <utility>
 
+#include "blockscan.h"
 #include "clces.h"
 #include "rowmove.h"
 
@@ -100,24 +101,6 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
     g.keys[(int64_t)w * g.N + idx] = order_key(s);
   }
   g.scur[idx] = __uint_as_float(order_key(s));
-}
-
-// Block-wide exclusive scan of one value per thread (1024 threads max).
-template <int NT>
-__device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int32_t t = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += t;
-    __syncthreads();
-  }
-  const int32_t incl = lds[tid];
-  if (total) *total = lds[NT - 1];
-  __syncthreads();
-  return incl - v;
 }
 
 // Add one to cnt[d] for every active lane with `valid`, aggregating lanes of

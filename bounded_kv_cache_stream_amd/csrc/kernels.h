@@ -37,6 +37,13 @@ struct TableChunk {
 
 hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStream_t s);
 
+// Per-head tables out[h][0..n] (stride n + 1) from the shared table base[n]:
+// an entry with tile_start != 0 holds hlen[phys * heads + h] rows of head h,
+// any other holds len in every head; tile_start / tok_start are rebuilt per
+// head and entry n of each holds the head's tile and token totals.
+hipError_t launch_head_tables(DevEntry* out, const DevEntry* base, int n, const int32_t* hlen, int heads,
+                              hipStream_t s);
+
 hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
                          int64_t first_token_id, hipStream_t s);
 

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "clces.h"
+#include "diversity.h"
 #include "kernels.h"
 #include "policy.h"
 
@@ -53,10 +54,12 @@ struct Layout {
   int64_t layer_pages;  // pages per layer including the transient page
   int64_t table_cap;    // device page-table entries per layer
   size_t pool_bytes;
-  // workspace regions (byte offsets)
-  size_t tables, part_o, part_ml, clces, ws_bytes;
+  // workspace regions (byte offsets); the CLCES and diversity steps share one
+  // region (each waits for its own work before it returns)
+  size_t tables, part_o, part_ml, hlens, clces, div, ws_bytes;
   int64_t part_rows;  // capacity in (split x query) rows
   kvs::ClcesSizes cl;
+  kvs::DivSizes dv;
 };
 
 kv_status validate(const kv_pool_config* c) {
@@ -102,10 +105,14 @@ Layout make_layout(const kv_pool_config* c) {
   off = align_up(off + (size_t)L.part_rows * H * D * 4);
   L.part_ml = off;
   off = align_up(off + (size_t)L.part_rows * H * 2 * 4);
+  L.hlens = off;  // per-head lengths of every physical page, int32 [page][H]
+  off = align_up(off + (size_t)(L.layer_pages * c->num_layers) * (size_t)H * 4);
   L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window,
                           (int32_t)ts);
+  L.dv = kvs::div_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, (int32_t)H);
   L.clces = off;
-  off = align_up(off + L.cl.total);
+  L.div = off;
+  off = align_up(off + std::max(L.cl.total, L.dv.total));
   L.ws_bytes = off;
   return L;
 }
@@ -138,6 +145,51 @@ int64_t phys_page(const kv_pool_t* p, int32_t layer, int32_t page) {
 
 kvs::DevEntry* dev_table(const kv_pool_t* p, int32_t layer) {
   return reinterpret_cast<kvs::DevEntry*>(p->ws + p->lay.tables) + (int64_t)layer * p->lay.table_cap;
+}
+
+int32_t* hlens_dev(const kv_pool_t* p) { return reinterpret_cast<int32_t*>(p->ws + p->lay.hlens); }
+
+// The candidate pages of a layer for the diversity steps (every page past the
+// scale frames, in table order; tile_start flags pages whose per-head lengths
+// are in the device array), each head's candidate count, and their largest
+// value and sum.
+struct DivPlan {
+  std::vector<kvs::DevEntry> base;
+  std::vector<int64_t> n_head;
+  int64_t n_max = 0, n_total = 0;
+};
+
+DivPlan div_plan(const kv_pool_t* pool, int32_t layer) {
+  const auto& L = pool->layers[(size_t)layer];
+  const int32_t H = pool->cfg.num_heads;
+  DivPlan d;
+  d.n_head.assign((size_t)H, 0);
+  for (size_t i = L.first_candidate(); i < L.table.size(); ++i) {
+    const auto& e = L.table[i];
+    d.base.push_back(kvs::DevEntry{(int32_t)phys_page(pool, layer, e.page), e.len, e.hlen.empty() ? 0 : 1, 0});
+    for (int32_t h = 0; h < H; ++h) d.n_head[(size_t)h] += kvs::head_len(e, h);
+  }
+  for (int64_t n : d.n_head) {
+    d.n_max = std::max(d.n_max, n);
+    d.n_total += n;
+  }
+  return d;
+}
+
+kvs::DivArgs div_args(const kv_pool_t* pool, const DivPlan& d, int64_t keep, float* scores, int64_t stride) {
+  kvs::DivArgs a{};
+  a.ws = pool->ws + pool->lay.div;
+  a.sizes = pool->lay.dv;
+  a.pool = pool->pool;
+  a.geom = pool->lay.geom;
+  a.base_host = d.base.data();
+  a.P = (int32_t)d.base.size();
+  a.hlen_dev = hlens_dev(pool);
+  a.N = d.n_max;
+  a.keep = keep;
+  a.scores_out = scores;
+  a.score_stride = stride;
+  return a;
 }
 
 }  // namespace
@@ -306,40 +358,51 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   auto& ent = pool->scratch;
   ent.clear();
   const int32_t H = pool->cfg.num_heads;
-  const bool per_head = !L.uniform();
-  // one table for every head, or (once heads keep different tokens) one per
-  // head: entries for every page, zero-length where the head holds nothing,
-  // and a last entry carrying the head's tile count
-  int32_t tiles = 0, min_tiles = INT32_MAX, n_entries = 0;
-  for (int32_t h = 0; h < (per_head ? H : 1); ++h) {
-    int32_t t_h = 0, toks = 0;
-    auto add = [&](int32_t page, int32_t len) {
-      kvs::DevEntry d;
-      d.phys = (int32_t)phys_page(pool, layer, page);
-      d.len = len;
-      d.tile_start = t_h;
-      d.tok_start = toks;
-      t_h += (len + kvs::kTile - 1) / kvs::kTile;
-      toks += len;
-      ent.push_back(d);
-    };
-    const size_t first = ent.size();
-    for (const auto& e : L.table)
-      if (per_head || e.len > 0) add(e.page, per_head ? kvs::head_len(e, h) : e.len);
-    if (L.transient_pending) add(-1, pool->cfg.page_tokens);
-    n_entries = (int32_t)(ent.size() - first);
-    if (per_head) {
-      kvs::DevEntry sentinel{0, 0, t_h, toks};
-      ent.push_back(sentinel);
+  const bool per_head = !L.same_lengths();
+  // The shared table: one entry per page with tokens (the longest head's
+  // length).  Once heads hold different counts, every page stays in it,
+  // flagged (tile_start = 1) where its per-head lengths live in the device
+  // array the prune wrote, and one table per head is built from it on the
+  // device, each ending with an entry that carries the head's tile count.
+  int32_t tiles = 0, toks = 0;
+  auto add = [&](int32_t page, int32_t len, int32_t flag) {
+    kvs::DevEntry d;
+    d.phys = (int32_t)phys_page(pool, layer, page);
+    d.len = len;
+    d.tile_start = per_head ? flag : tiles;
+    d.tok_start = toks;
+    tiles += (len + kvs::kTile - 1) / kvs::kTile;
+    toks += len;
+    ent.push_back(d);
+  };
+  for (const auto& e : L.table)
+    if (per_head || e.len > 0) add(e.page, e.len, e.hlen.empty() ? 0 : 1);
+  if (L.transient_pending) add(-1, pool->cfg.page_tokens, 0);
+  const int32_t n_entries = (int32_t)ent.size();
+  int32_t min_tiles = tiles;
+  if (per_head) {
+    tiles = 0;
+    min_tiles = INT32_MAX;
+    for (int32_t h = 0; h < H; ++h) {
+      int32_t t_h = 0;
+      for (const auto& e : L.table) t_h += (kvs::head_len(e, h) + kvs::kTile - 1) / kvs::kTile;
+      if (L.transient_pending) t_h += (pool->cfg.page_tokens + kvs::kTile - 1) / kvs::kTile;
+      tiles = std::max(tiles, t_h);
+      min_tiles = std::min(min_tiles, t_h);
     }
-    tiles = std::max(tiles, t_h);
-    min_tiles = std::min(min_tiles, t_h);
   }
   if (n_entries == 0 || min_tiles == 0) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   kvs::DevEntry* dt = dev_table(pool, layer);
-  hipError_t e = kvs::launch_table_upload(dt, ent.data(), (int)ent.size(), st);
+  hipError_t e;
+  if (per_head) {
+    kvs::DevEntry* base = dt + (int64_t)H * (pool->lay.layer_pages + 1);
+    e = kvs::launch_table_upload(base, ent.data(), n_entries, st);
+    if (e == hipSuccess) e = kvs::launch_head_tables(dt, base, n_entries, hlens_dev(pool), H, st);
+  } else {
+    e = kvs::launch_table_upload(dt, ent.data(), n_entries, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "table upload launch");
 
   const bool bf16 = pool->cfg.dtype == KV_BF16;
@@ -392,7 +455,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
   auto& L = pool->layers[(size_t)layer];
-  if (!L.uniform()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
+  if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   const size_t first = L.first_candidate();
   int64_t N = 0;
   for (size_t i = first; i < L.table.size(); ++i) N += L.table[i].len;
@@ -458,7 +521,7 @@ kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void
     return fail(KV_ERR_STATE, "layer %d: page merge needs one frame per page no more (sliding_window must be 0)",
                 layer);
   auto& L = pool->layers[(size_t)layer];
-  if (!L.uniform()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
+  if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   const std::vector<kvs::MergeMove> mv = L.plan_merges();
   if (!pool->meta_only) {
     const int64_t pb = pool->lay.geom.page_bytes;
@@ -481,6 +544,102 @@ kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void
   return ok();
 }
 
+kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,
+                             double* mean_diversity, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (!mean_diversity) return fail(KV_ERR_ARG, "mean_diversity is NULL");
+  const DivPlan d = div_plan(pool, layer);
+  if (d.n_total == 0) {
+    *mean_diversity = 0.0;
+    return ok();
+  }
+  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+  if (scores_dev && score_stride < d.n_max)
+    return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)score_stride,
+                (long long)d.n_max);
+  const kvs::DivArgs a = div_args(pool, d, 0, scores_dev, score_stride);
+  double sum = 0.0;
+  int32_t flag = 0;
+  hipError_t e = kvs::run_diversity_score(a, &sum, &flag, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "diversity scoring");
+  if (flag & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layer);
+  *mean_diversity = sum / (double)d.n_total;
+  return ok();
+}
+
+kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
+                             int64_t score_stride, int64_t* kept_per_head, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (keep_per_head < 0) return fail(KV_ERR_ARG, "keep_per_head must be >= 0");
+  const int32_t H = pool->cfg.num_heads;
+  const DivPlan d = div_plan(pool, layer);
+  if (d.n_max > keep_per_head) {
+    if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+    if (scores_dev && score_stride < d.n_max)
+      return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)score_stride,
+                  (long long)d.n_max);
+    const kvs::DivArgs a = div_args(pool, d, keep_per_head, scores_dev, score_stride);
+    std::vector<int32_t> nl(d.base.size() * (size_t)H);
+    double sum = 0.0;
+    int32_t flag = 0;
+    hipError_t e = kvs::run_diversity_prune(a, nl.data(), &sum, &flag, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "diversity prune");
+    if (flag & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layer);
+    for (int32_t h = 0; h < H; ++h) {
+      int64_t kept = 0;
+      for (size_t i = 0; i < d.base.size(); ++i) kept += nl[i * (size_t)H + (size_t)h];
+      if (kept != std::min(keep_per_head, d.n_head[(size_t)h]))
+        return fail(KV_ERR_HIP, "layer %d head %d: kept %lld candidates, expected %lld (pool state undefined)",
+                    layer, h, (long long)kept, (long long)std::min(keep_per_head, d.n_head[(size_t)h]));
+    }
+    pool->layers[(size_t)layer].apply_head_compaction(nl, H);
+  }
+  if (kept_per_head)
+    for (int32_t h = 0; h < H; ++h) kept_per_head[h] = std::min(keep_per_head, d.n_head[(size_t)h]);
+  return ok();
+}
+
+kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, double tau, int64_t total_tokens,
+                           int32_t heads, int64_t* keep_per_head) {
+  if (!mean_diversity || !keep_per_head) return fail(KV_ERR_ARG, "mean_diversity or keep_per_head is NULL");
+  if (n_layers < 1) return fail(KV_ERR_ARG, "n_layers must be >= 1");
+  if (!(tau > 0.0) || !std::isfinite(tau)) return fail(KV_ERR_ARG, "tau must be finite and > 0");
+  if (total_tokens < 0 || total_tokens > ((int64_t)1 << 53)) return fail(KV_ERR_ARG, "total_tokens out of range");
+  if (heads < 1) return fail(KV_ERR_ARG, "heads must be >= 1");
+  std::vector<double> z((size_t)n_layers);
+  double mx = -INFINITY;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    z[(size_t)i] = mean_diversity[i] / tau;
+    if (!std::isfinite(z[(size_t)i])) return fail(KV_ERR_ARG, "mean_diversity[%d] / tau is not finite", i);
+    mx = std::max(mx, z[(size_t)i]);
+  }
+  double sum = 0.0;
+  for (auto& v : z) {
+    v = std::exp(v - mx);
+    sum += v;
+  }
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const double share = std::floor(z[(size_t)i] / sum * (double)total_tokens);
+    keep_per_head[i] = (int64_t)std::floor(share / (double)heads);
+  }
+  return ok();
+}
+
+kv_status kv_get_head_lengths(const kv_pool_t* pool, int32_t layer, int32_t* lens, int32_t cap, int32_t* n_out) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (cap < 0) return fail(KV_ERR_ARG, "negative cap");
+  const auto& L = pool->layers[(size_t)layer];
+  const int32_t n = (int32_t)L.table.size(), H = pool->cfg.num_heads;
+  if (lens)
+    for (int32_t i = 0; i < n && i < cap; ++i)
+      for (int32_t h = 0; h < H; ++h) lens[(int64_t)i * H + h] = kvs::head_len(L.table[(size_t)i], h);
+  if (n_out) *n_out = n;
+  return ok();
+}
+
 kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
@@ -496,6 +655,7 @@ kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) 
   out->compactions = L.compactions;
   out->last_keep_count = L.last_keep;
   out->merges = L.merges;
+  out->prunes = L.prunes;
   return ok();
 }
 

@@ -1,4 +1,4 @@
-// Page write, page merge and page-table upload, gfx950.
+// Page write, page merge, page-table upload and per-head tables, gfx950.
 //
 // Page write (LingBot-Map 20 FPS explainer, "Page-Aligned Tensor Layout":
 // a frame's tokens go straight into a page-aligned layout, no padding between
@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "blockscan.h"
 #include "kernels.h"
 
 namespace kvs {
@@ -118,7 +119,44 @@ __global__ void table_upload_kernel(DevEntry* dst, TableChunk chunk) {
   if (i < chunk.count) dst[chunk.first + i] = chunk.e[i];
 }
 
+// One workgroup per head: head h's table from the shared one.  An entry whose
+// tile_start is nonzero takes its length from hlen[phys * H + h], any other
+// keeps len; tile and token prefixes are rebuilt, and entry n (the sentinel)
+// holds the head's totals.
+__global__ __launch_bounds__(256) void head_tables_kernel(DevEntry* out, const DevEntry* base, int n,
+                                                          const int32_t* hlen, int H) {
+  __shared__ int32_t scan[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  DevEntry* t = out + (int64_t)h * (n + 1);
+  const int per = (n + 255) / 256;
+  const int b = min(tid * per, n), e = min(b + per, n);
+  auto len_of = [&](const DevEntry& be) { return be.tile_start ? hlen[(int64_t)be.phys * H + h] : be.len; };
+  int32_t tiles = 0, toks = 0;
+  for (int i = b; i < e; ++i) {
+    const int32_t len = len_of(base[i]);
+    tiles += (len + kTile - 1) / kTile;
+    toks += len;
+  }
+  int32_t tiles_tot = 0, toks_tot = 0;
+  int32_t t0 = block_excl_scan<256>(tiles, scan, &tiles_tot);
+  int32_t k0 = block_excl_scan<256>(toks, scan, &toks_tot);
+  for (int i = b; i < e; ++i) {
+    const DevEntry be = base[i];
+    const int32_t len = len_of(be);
+    t[i] = DevEntry{be.phys, len, t0, k0};
+    t0 += (len + kTile - 1) / kTile;
+    k0 += len;
+  }
+  if (tid == 0) t[n] = DevEntry{0, 0, tiles_tot, toks_tot};
+}
+
 }  // namespace
+
+hipError_t launch_head_tables(DevEntry* out, const DevEntry* base, int n, const int32_t* hlen, int heads,
+                              hipStream_t s) {
+  head_tables_kernel<<<dim3((unsigned)heads), dim3(256), 0, s>>>(out, base, n, hlen, heads);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_layers(const PageGeom& g, char* pool, const AppendLayers& al, int n_layers,
                                 const void* k, const void* v, int n_tokens, int64_t first_token_id,

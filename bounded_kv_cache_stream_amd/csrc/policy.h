@@ -179,6 +179,8 @@ class LayerPolicy {
 
   // Per-head new lengths for entries first_candidate().. ([entry][head]); a
   // page whose heads are all empty leaves the table and its id is freed.
+  // Every remaining candidate page keeps its per-head lengths: its heads now
+  // hold different tokens even where their counts agree.
   void apply_head_compaction(const std::vector<int32_t>& new_lens, int heads) {
     size_t f = first_candidate();
     std::vector<PageEntry> out(table.begin(), table.begin() + (long)f);
@@ -186,20 +188,13 @@ class LayerPolicy {
       PageEntry e = table[i];
       const int32_t* nl = &new_lens[(i - f) * (size_t)heads];
       int32_t mx = 0;
-      bool same = true;
-      for (int h = 0; h < heads; ++h) {
-        mx = nl[h] > mx ? nl[h] : mx;
-        same = same && nl[h] == nl[0];
-      }
+      for (int h = 0; h < heads; ++h) mx = nl[h] > mx ? nl[h] : mx;
       if (mx == 0) {
         free_ids.insert(e.page);
         continue;
       }
       e.len = mx;
-      if (same)
-        e.hlen.clear();
-      else
-        e.hlen.assign(nl, nl + heads);
+      e.hlen.assign(nl, nl + heads);
       out.push_back(e);
     }
     table.swap(out);
@@ -207,9 +202,17 @@ class LayerPolicy {
   }
 
   // True when every page holds the same tokens in every head.
-  bool uniform() const {
+  bool same_tokens() const {
     for (const auto& e : table)
       if (!e.hlen.empty()) return false;
+    return true;
+  }
+
+  // True when every page holds as many rows in every head.
+  bool same_lengths() const {
+    for (const auto& e : table)
+      for (int32_t n : e.hlen)
+        if (n != e.len) return false;
     return true;
   }
 

@@ -21,7 +21,8 @@ KV_TRANSIENT = 1
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
     "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
-    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_last_error",
+    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score", "kv_layer_budgets",
+    "kv_diversity_prune", "kv_get_head_lengths", "kv_last_error",
 )
 
 
@@ -40,7 +41,8 @@ class kv_cache_info(ctypes.Structure):
     _fields_ = [("persisted_frames", ctypes.c_int32), ("pages_used", ctypes.c_int32),
                 ("pages_free", ctypes.c_int32), ("transient_pending", ctypes.c_int32),
                 ("tokens", ctypes.c_int64), ("bytes", ctypes.c_int64), ("evictions", ctypes.c_int64),
-                ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64), ("merges", ctypes.c_int64)]
+                ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64), ("merges", ctypes.c_int64),
+                ("prunes", ctypes.c_int64)]
 
 
 class kv_pool_layout(ctypes.Structure):
@@ -81,6 +83,11 @@ def lib() -> ctypes.CDLL:
             "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
             "kv_set_attend_splits": [P, I32],
             "kv_merge_pages": [P, I32, ctypes.POINTER(I32), P],
+            "kv_diversity_score": [P, I32, P, I64, ctypes.POINTER(ctypes.c_double), P],
+            "kv_layer_budgets": [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_double, I64, I32,
+                                 ctypes.POINTER(I64)],
+            "kv_diversity_prune": [P, I32, I64, P, I64, ctypes.POINTER(I64), P],
+            "kv_get_head_lengths": [P, I32, P, I32, ctypes.POINTER(I32)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -167,6 +174,35 @@ def kv_merge_pages(pool, layer, stream=None) -> int:
     n = ctypes.c_int32()
     _check(lib().kv_merge_pages(pool, layer, ctypes.byref(n), stream))
     return n.value
+
+
+def kv_diversity_score(pool, layer, scores_ptr=None, score_stride=0, stream=None) -> float:
+    m = ctypes.c_double()
+    _check(lib().kv_diversity_score(pool, layer, scores_ptr, score_stride, ctypes.byref(m), stream))
+    return m.value
+
+
+def kv_layer_budgets(mean_diversity, tau, total_tokens, heads) -> list:
+    n = len(mean_diversity)
+    md = (ctypes.c_double * max(n, 1))(*[float(x) for x in mean_diversity])
+    out = (ctypes.c_int64 * max(n, 1))()
+    _check(lib().kv_layer_budgets(md, n, float(tau), int(total_tokens), int(heads), out))
+    return list(out[:n])
+
+
+def kv_diversity_prune(pool, layer, keep_per_head, heads, scores_ptr=None, score_stride=0, stream=None) -> list:
+    kept = (ctypes.c_int64 * heads)()
+    _check(lib().kv_diversity_prune(pool, layer, keep_per_head, scores_ptr, score_stride, kept, stream))
+    return list(kept)
+
+
+def kv_get_head_lengths(pool, layer, heads) -> list:
+    n = ctypes.c_int32()
+    _check(lib().kv_get_head_lengths(pool, layer, None, 0, ctypes.byref(n)))
+    cap = n.value
+    buf = (ctypes.c_int32 * max(cap * heads, 1))()
+    _check(lib().kv_get_head_lengths(pool, layer, buf, cap, ctypes.byref(n)))
+    return [list(buf[i * heads:(i + 1) * heads]) for i in range(cap)]
 
 
 def kv_get_info(pool, layer) -> dict:
@@ -295,6 +331,28 @@ class KVCache:
 
     def merge_pages(self, layer) -> int:
         return kv_merge_pages(self.handle, layer, self._stream())
+
+    def _scores_arg(self, scores):
+        if scores is None:
+            return None, 0
+        torch = self.torch
+        if scores.dtype != torch.float32 or not scores.is_contiguous() or scores.dim() != 2 \
+                or scores.shape[0] != self.cfg.num_heads:
+            raise ValueError("scores must be a contiguous fp32 [num_heads, stride] tensor")
+        return ctypes.c_void_p(scores.data_ptr()), scores.shape[1]
+
+    def diversity_score(self, layer, scores=None) -> float:
+        """Mean diversity of the layer's candidates; scores: optional fp32 [H, stride] output."""
+        sp, stride = self._scores_arg(scores)
+        return kv_diversity_score(self.handle, layer, sp, stride, self._stream())
+
+    def diversity_prune(self, layer, keep_per_head, scores=None) -> list:
+        """Per-head top-K prune; returns the candidates kept per head."""
+        sp, stride = self._scores_arg(scores)
+        return kv_diversity_prune(self.handle, layer, keep_per_head, self.cfg.num_heads, sp, stride, self._stream())
+
+    def head_lengths(self, layer) -> list:
+        return kv_get_head_lengths(self.handle, layer, self.cfg.num_heads)
 
     def page_table(self, layer):
         return kv_get_page_table(self.handle, layer)

@@ -1,7 +1,8 @@
 /*
  * kvstream.h -- C ABI of the bounded streaming KV cache for one AMD Instinct
  * MI355X (gfx950): paged frame-to-cache attention plus the cache-management
- * step (page write, sliding-window eviction, CLCES scoring, top-k compaction).
+ * step (page write, sliding-window eviction, CLCES scoring, top-k compaction)
+ * and diversity-scored per-head pruning.
  *
  * The operations follow these pages:
  *   [GCT]  "How GCTStream Implements Streaming 3D Reconstruction with KV Cache"
@@ -84,12 +85,13 @@ typedef struct {
   int32_t pages_used;       /* = persisted_frames                                 */
   int32_t pages_free;
   int32_t transient_pending;/* 1 if a transient frame waits for stream_attend     */
-  int64_t tokens;           /* tokens in the table (sum of page lengths)          */
+  int64_t tokens;           /* sum of page lengths (a page's longest head)        */
   int64_t bytes;            /* device bytes of the used pages                     */
   int64_t evictions;        /* pages evicted by the window since the last reset   */
   int64_t compactions;      /* score_and_compact steps that dropped tokens        */
   int64_t last_keep_count;  /* tokens kept by the last such step                  */
   int64_t merges;           /* pages released by kv_merge_pages                   */
+  int64_t prunes;           /* kv_diversity_prune steps that dropped tokens       */
 } kv_cache_info;
 
 /* Device memory layout of the pool, for callers that read pages directly.
@@ -101,7 +103,10 @@ typedef struct {
  *   K   at k_offset: [H][Ts][D]  -- token rows of each head, in slot order
  *   V   at v_offset: [H][Ts][D]  -- the same layout as K
  *   ids at id_offset: int32 [Ts] -- global token id frame*page_tokens + slot
- * Slots >= the page's length hold no data of the cache. */
+ * Slots >= the page's length hold no data of the cache.  After
+ * kv_diversity_prune the heads of a pruned page hold different tokens and
+ * different counts (kv_get_head_lengths): the id row then describes none of
+ * them, and rows past a head's own length hold no data. */
 typedef struct {
   int64_t page_bytes;
   int64_t k_offset, v_offset, id_offset;
@@ -162,7 +167,8 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted);
  * "Scale-Frame Phase"): for each query row i and head h,
  *   out[i,h,:] = sum_j softmax_j(sm_scale * q[i,h,:] . k[j,h,:]) v[j,h,:]
  * over every token j of the layer's table in table order, plus the pending
- * transient frame (which is consumed).  No token mask: a frame sees all of
+ * transient frame (which is consumed); after kv_diversity_prune, over the
+ * rows head h holds in each page.  No token mask: a frame sees all of
  * its own tokens and, in the scale phase, the other scale frames.
  * q_dev, out_dev: [n_q][H][D] in the pool's dtype, 1 <= n_q <= max_queries.
  * lse_dev: optional fp32 [n_q][H] = natural log of the softmax denominator
@@ -187,8 +193,10 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
  * released.  The order of tokens inside a page is not part of the method.
  * score_table_dev: fp32 [score_rows][num_layers], row = global token id.
  * keep_ids_out_dev: optional int32 [keep_count], kept global token ids in
- * candidate order (table order, then slot order before compaction).  ranks_out_dev: optional int32 [n_window][N], oldest window
- * layer first.  n_kept: optional host int64.
+ * candidate order (table order, then slot order before compaction).
+ * ranks_out_dev: optional int32 [n_window][N], oldest window layer first.
+ * n_kept: optional host int64.  KV_ERR_STATE on a layer that
+ * kv_diversity_prune has pruned (its heads hold different tokens).
  * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
  * for a token id >= score_rows or a bad parameter.  Synchronises the stream
  * once to read the new page lengths. */
@@ -209,8 +217,56 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
  * same order.  Device work (one launch per 128 merges) is enqueued on
  * `stream`; no sync.  n_merged: optional host int32, pages released.
  * KV_ERR_STATE if sliding_window > 0 (window eviction removes whole frames,
- * so its pages must hold one frame each). */
+ * so its pages must hold one frame each), and on a layer that
+ * kv_diversity_prune has pruned (as for score_and_compact). */
 kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void* stream);
+
+/* Diversity scores of a layer's candidates ([INF] "Building Blocks",
+ * "Cosine Similarity", step-by-step recipe steps 2-4).  Candidates: per head,
+ * the rows of every page past the scale frames (the anchor), in table order,
+ * then slot order (N_h of them).  With k_hat = k / |k| (0 for a zero key) and
+ * m_h the mean of head h's k_hat,
+ *   score = -(k_hat . m_h) / |m_h|     (every score 0 when m_h = 0),
+ * computed in float64 from the stored keys with fixed-order sums.
+ * scores_dev: optional fp32 [H][score_stride] (score_stride >= max N_h), the
+ * float64 score rounded to fp32, candidate order; entries past N_h untouched.
+ * *mean_diversity (host, required): the mean of the float64 scores over
+ * every head and candidate (0 with no candidate).  KV_ERR_NAN if a candidate
+ * key is not finite.  Synchronises the stream. */
+kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,
+                             double* mean_diversity, void* stream);
+
+/* Per-layer budgets ([INF] "Building Blocks", recipe step 5): with
+ * p = softmax(mean_diversity / tau) over the n_layers layers,
+ *   keep_per_head[l] = floor(floor(p_l * total_tokens) / heads).
+ * Host arithmetic in float64 (exp of the values minus their maximum); no
+ * device work.  KV_ERR_ARG for tau <= 0, a non-finite mean / tau, heads < 1,
+ * or total_tokens outside 0 .. 2^53. */
+kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, double tau,
+                           int64_t total_tokens, int32_t heads, int64_t* keep_per_head);
+
+/* Diversity prune ([INF] recipe step 6, "Rolling Memory"): scores the
+ * candidates as kv_diversity_score does, keeps each head's keep_per_head
+ * candidates first in (score descending, candidate index ascending) order,
+ * the scores taken as rounded to fp32, and compacts every page and head in
+ * place with the rule of score_and_compact (kept slots below the head's new
+ * count n stay, the dropped slots below n take the kept slots at or past n,
+ * both ascending), moving the K and V rows of that head; the id row does not
+ * move.  A page whose heads are all empty is released; the scale frames
+ * (anchor) are never touched.  Heads with N_h <= keep_per_head keep
+ * everything; if every head does, nothing happens.  Afterwards heads hold
+ * different tokens: stream_attend follows each head's rows, and
+ * score_and_compact and kv_merge_pages refuse the layer (KV_ERR_STATE).
+ * scores_dev / score_stride as for kv_diversity_score.  kept_per_head:
+ * optional host int64 [H] = min(keep_per_head, N_h).  KV_ERR_NAN (state
+ * unchanged) if a candidate key is not finite.  Synchronises the stream. */
+kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
+                             int64_t score_stride, int64_t* kept_per_head, void* stream);
+
+/* Per-head lengths of the layer's pages, int32 [entry][H] in table order, cap
+ * entries at most; *n_out = table size.  Equal to the page length in every
+ * head unless kv_diversity_prune has run.  lens may be NULL. */
+kv_status kv_get_head_lengths(const kv_pool_t* pool, int32_t layer, int32_t* lens, int32_t cap, int32_t* n_out);
 
 /* Statistics of a layer ([GCT] "Cache Monitoring"). */
 kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out);

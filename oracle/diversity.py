@@ -26,7 +26,9 @@ Readings taken where the pages are silent (listed in the design doc):
 * score = -(k_hat . m) / |m| with m the mean of the normalised candidate keys,
   in float64 from the stored key values;
 * per-head top-K: the K highest scores, ties by candidate index (table order,
-  then slot order); K >= the candidate count keeps everything;
+  then slot order); K >= the candidate count keeps everything; the pages fix
+  no precision for this decision, so ``prune`` can take it on the scores
+  rounded to a given type (float32 is the kernel's);
 * layer budgets: p = softmax(mean_diversity / tau) over the layers;
   K_l = floor(floor(p_l * total) / heads) tokens per head of layer l;
   a layer's average diversity is the mean of its scores over heads and
@@ -122,10 +124,12 @@ class DiversityCache:
         n = sum(len(x) for x in s)
         return float(sum(x.sum() for x in s) / n) if n else 0.0
 
-    def prune(self, key_of, k_per_head: int) -> list[np.ndarray]:
-        """Keep each head's k_per_head most diverse candidates; return the per-head keep masks."""
+    def prune(self, key_of, k_per_head: int, rank_dtype=np.float64) -> list[np.ndarray]:
+        """Keep each head's k_per_head most diverse candidates; return the per-head keep masks.
+
+        The top-K is taken on the scores rounded to ``rank_dtype``."""
         masks = []
-        sc = self.scores(key_of)
+        sc = [np.asarray(x, dtype=rank_dtype) for x in self.scores(key_of)]
         for h in range(self.H):
             masks.append(topk_desc(sc[h], k_per_head) if len(sc[h]) > k_per_head else np.ones(len(sc[h]), bool))
         pos = [0] * self.H

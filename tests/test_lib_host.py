@@ -197,3 +197,67 @@ def test_page_merge_host_rules():
     assert b.merge_pages(0) == 0
     assert b.page_table(0)[1] == [16] * 4
     assert b.info(0)["merges"] == 0
+
+
+def test_layer_budgets_match_oracle():
+    # host arithmetic of the library against the oracle's softmax budgets; the
+    # two evaluate exp with different libraries, so a floor may differ only
+    # where its argument sits within rounding of an integer
+    import numpy as np
+    from oracle import diversity
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        L = int(rng.integers(1, 40))
+        heads = int(rng.integers(1, 33))
+        tau = float(rng.uniform(0.005, 2.0))
+        total = int(rng.integers(0, 10 ** 9))
+        md = rng.uniform(-1.0, 0.0, L)
+        got = np.array(kv.kv_layer_budgets(md, tau, total, heads))
+        want = diversity.layer_budgets(md, tau, total, heads)
+        d = md / tau
+        p = np.exp(d - d.max())
+        p = p / p.sum()
+        for g, w, share in zip(got, want, p * total):
+            if g != w:
+                assert abs(g - w) == 1
+                edge = min(abs(share - round(share)), abs(np.floor(share) / heads - round(np.floor(share) / heads)))
+                assert edge < 1e-6 * max(1.0, share)
+    # the explainer's worked numbers: 12 layers of equal diversity share a
+    # total of 98,304 head-tokens as 512 per head of 16 heads
+    gold = {}
+    for ln in open(os.path.join(ROOT, "tests", "golden", "diversity_budget_example.txt")):
+        if ln.strip() and not ln.startswith("#"):
+            k, v = ln.split(":")
+            gold[k.strip()] = int(v)
+    got = kv.kv_layer_budgets([-0.25] * gold["layers"], 0.7, gold["total"], gold["heads"])
+    assert got == [gold["per_head_budget"]] * gold["layers"]
+    for bad in [dict(tau=0.0), dict(tau=float("nan")), dict(heads=0), dict(total=-1)]:
+        a = dict(md=[-0.1, -0.2], tau=1.0, total=100, heads=2)
+        a.update(bad)
+        with pytest.raises(kv.KVError) as e:
+            kv.kv_layer_budgets(a["md"], a["tau"], a["total"], a["heads"])
+        assert e.value.status == kv.KV_ERR_ARG
+    with pytest.raises(kv.KVError):
+        kv.kv_layer_budgets([1.0, 0.0], 1e-310, 100, 2)  # mean / tau overflows
+
+
+def test_diversity_host_rules():
+    # no candidate: mean 0 without device work; every head within its budget:
+    # nothing to do; otherwise a metadata-only pool refuses the device step
+    c = _meta_pool(1, 0, 1, 6)
+    c.append(0, 0, None, None)
+    assert c.diversity_score(0) == 0.0
+    assert c.diversity_prune(0, 0) == [0, 0]
+    for t in range(1, 4):
+        c.append(0, t, None, None)
+    assert c.diversity_prune(0, 48) == [48, 48]
+    assert c.diversity_prune(0, 100) == [48, 48]
+    for call in (lambda: c.diversity_prune(0, 47), lambda: c.diversity_score(0)):
+        with pytest.raises(kv.KVError) as e:
+            call()
+        assert e.value.status == kv.KV_ERR_STATE
+    with pytest.raises(kv.KVError) as e:
+        c.diversity_prune(0, -1)
+    assert e.value.status == kv.KV_ERR_ARG
+    assert c.head_lengths(0) == [[16, 16]] * 4
+    assert c.info(0)["prunes"] == 0
