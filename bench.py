@@ -43,11 +43,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["stream", "clces", "append", "long", "budget"], default="stream",
+    ap.add_argument("--workload", choices=["stream", "clces", "append", "long", "budget", "diversity"],
+                    default="stream",
                     help="stream: the attention step (default); clces: score_and_compact on the 24-layer "
                          "cache; append: one frame's page write for 24 layers in one launch; long: the "
                          "10,000-frame keyframe-interval-4 stream, sustained; budget: the 24-layer "
-                         "token-budget stack (append, attend, score_and_compact per layer)")
+                         "token-budget stack (append, attend, score_and_compact per layer); diversity: the "
+                         "stack with diversity-scored per-head pruning and softmax layer budgets")
+    ap.add_argument("--layers", type=int, default=0, help="diversity workload: layers (default 24)")
+    ap.add_argument("--per-head", type=int, default=0,
+                    help="diversity workload: mean tokens kept per head and layer (default 128,512)")
+    ap.add_argument("--tau", type=float, default=1.0, help="diversity workload: softmax temperature")
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
     ap.add_argument("--merge", action="store_true", help="budget workload: merge ragged pages after each compaction")
     ap.add_argument("--heads", type=int, default=0,
@@ -364,6 +370,137 @@ def run_budget(args):
         "attend_frac_bf16_peak": flops / (split["attend"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}), flush=True)
 
 
+def run_diversity(args):
+    """The diversity-pruned stack: per frame, append the frame to every layer (one launch), score every
+    layer (its mean diversity), split the total budget over the layers with the tempered softmax, prune
+    every layer to its per-head top-K, then attend every layer over the pages each head kept.
+
+    Frame 0 is the anchor (scale_frames = 1).  The total budget is layers x heads x per_head tokens; the
+    untimed frames run until every layer has pruned at least 8 times.  K/V/Q come from a ring of 8 AR(1)
+    frames per layer in HBM.  HIP events bracket each phase; kv_diversity_score and kv_diversity_prune
+    wait for their own work (they read back the mean, the new lengths and the error flag)."""
+    import numpy as np
+    import torch
+
+    from bounded_kv_cache_stream_amd import kvstream as kv
+    from bounded_kv_cache_stream_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, per_head, tau = args.layers or 24, args.per_head or 128512, args.tau
+    T, H, D = synth.TOKENS_PER_FRAME, 16, 64
+    total = L * H * per_head
+    warm = max(args.warmup, 2 * ((per_head + T - 1) // T) + 9)
+    F = warm + args.steps
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=1, sliding_window=0,
+                         keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16)
+    cache = kv.KVCache(cfg, device=dev)
+    rings_q, rings_k, rings_v = [], [], []
+    ars = [synth.AR1Stream(5, l, (T, H, D), device=dev) for l in range(L)]
+    for i in range(8):
+        fr = [a.next() for a in ars]
+        rings_q.append([f[0] for f in fr])
+        rings_k.append(torch.stack([f[1] for f in fr]).contiguous())
+        rings_v.append(torch.stack([f[2] for f in fr]).contiguous())
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    cand = np.zeros((L, H), dtype=np.int64)  # candidates per head after the frame's append
+    kept = np.zeros((L, H), dtype=np.int64)
+    log = {"score": [], "prune": [], "attend": [], "append": [], "cand": [], "kept": [], "budgets": []}
+
+    def frame(t, timed):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        marks[0].record(stream)
+        cache.append_layers(0, t, rings_k[t % 8], rings_v[t % 8])
+        marks[1].record(stream)
+        cand[:] = kept + (T if t > 0 else 0)
+        means = [cache.diversity_score(l) for l in range(L)]
+        marks[2].record(stream)
+        budgets = kv.kv_layer_budgets(means, tau, total, H)
+        for l in range(L):
+            kept[l] = cache.diversity_prune(l, budgets[l])
+        marks[3].record(stream)
+        for l in range(L):
+            cache.attend(l, rings_q[t % 8][l], 1.0, out=out)
+        marks[4].record(stream)
+        if timed:
+            log["append"].append((marks[0], marks[1]))
+            log["score"].append((marks[1], marks[2]))
+            log["prune"].append((marks[2], marks[3]))
+            log["attend"].append((marks[3], marks[4]))
+            log["cand"].append(cand.copy())
+            log["kept"].append(kept.copy())
+            log["budgets"].append(budgets)
+
+    for t in range(warm):
+        frame(t, False)
+    torch.cuda.synchronize()
+    assert min(cache.info(l)["prunes"] for l in range(L)) >= 8, "the untimed frames must reach every budget"
+    wall0 = time.perf_counter()
+    for t in range(warm, F):
+        frame(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    split = {k: float(np.mean([a.elapsed_time(b) for a, b in log[k]])) * 1e3
+             for k in ("append", "score", "prune", "attend")}
+    cand_rows = float(np.mean([c.sum() for c in log["cand"]]))  # candidate rows (head x token) per frame
+    kept_rows = float(np.mean([k.sum() for k in log["kept"]]))
+    score_bytes = 2.0 * cand_rows * D * 2  # two passes over every candidate key row, bf16
+    attn_flops = float(np.mean([4.0 * D * T * (k.sum() + L * H * T) for k in log["kept"]]))
+    pages = [cache.info(l)["persisted_frames"] for l in range(L)]
+    hl = np.array(cache.head_lengths(L // 2))
+    tiles = ((hl + 63) // 64).sum(axis=0)
+    result = {
+        "metric": f"frames/sec of the {L}-layer diversity-pruned stack (append, score, budgets, prune, attend)",
+        "value": args.steps / wall, "unit": "frames/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": warm, "ms_per_frame": wall / args.steps * 1e3, "dtype": "bf16",
+        "data": "synthetic (ring of 8 seeded AR(1) frames per layer)",
+        "config": {"workload": f"diversity_l{L}_h{H}_d{D}_t{T}_k{per_head}_tau{tau:g}", "layers": L,
+                   "tokens_per_frame": T, "heads": H, "head_dim": D, "per_head_budget_mean": per_head,
+                   "total_budget": total, "tau": tau, "anchor_frames": 1},
+        "us_per_frame": split,
+        "candidates_per_frame": cand_rows, "kept_per_frame": kept_rows,
+        "budget_spread": [int(min(log["budgets"][-1])), int(max(log["budgets"][-1]))],
+        "pages_per_layer_mean": float(np.mean(pages)),
+        "attend_tile_fill_mid_layer": float(hl.sum(axis=0).mean() / (64.0 * tiles.mean())),
+        "roofline": {"bound": "hbm", "achieved": score_bytes / (split["score"] * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": score_bytes / (split["score"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "kernel": "kv_diversity_score over all layers (div_sum + div_score, two "
+                                                "reads of every candidate key; includes the small kernels "
+                                                "and one read-back per layer)",
+                     "bytes_per_frame": score_bytes},
+        "attend_tflops": attn_flops / (split["attend"] * 1e-6) / 1e12,
+        "attend_frac_bf16_peak": attn_flops / (split["attend"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = diversity_cpu_baseline(L, T, H, per_head)
+    print(json.dumps(result), flush=True)
+
+
+def diversity_cpu_baseline(L, T, H, per_head):
+    """The oracle's diversity step for one layer (scores of every candidate of every head in float64, the
+    per-head top-K and the per-page, per-head compaction of the token ids) at the state where the
+    candidates first exceed the budget: the anchor plus ceil(per_head / T) + 1 frames."""
+    import os as _os
+
+    import numpy as np
+
+    from oracle import diversity
+    n_frames = (per_head + T - 1) // T + 2
+    rng = np.random.default_rng(5)
+    keys = {f: rng.standard_normal((T, H, 64)).astype(np.float32) for f in range(n_frames)}
+    c = diversity.DiversityCache(H, T, n_frames)
+    for f in range(n_frames):
+        c.append(f)
+    t0 = time.perf_counter()
+    c.prune(lambda f, h: keys[f][:, h, :], per_head, rank_dtype=np.float32)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / (L * dt), "unit": "frames/s", "cores": len(_os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"one layer's score + top-K + compaction ({H} heads x {(n_frames - 1) * T} candidates, "
+                      f"{dt:.1f} s), scaled to {L} layers; attention and page writes not included"}
+
+
 def main():
     args = parse()
     if args.workload == "clces":
@@ -374,6 +511,8 @@ def main():
         return run_long(args)
     if args.workload == "budget":
         return run_budget(args)
+    if args.workload == "diversity":
+        return run_diversity(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "
