@@ -377,8 +377,9 @@ def run_diversity(args):
 
     Frame 0 is the anchor (scale_frames = 1).  The total budget is layers x heads x per_head tokens; the
     untimed frames run until every layer has pruned at least 8 times.  K/V/Q come from a ring of 8 AR(1)
-    frames per layer in HBM.  HIP events bracket each phase; kv_diversity_score and kv_diversity_prune
-    wait for their own work (they read back the mean, the new lengths and the error flag)."""
+    frames per layer in HBM.  HIP events bracket each phase; the batched scoring and prune each wait once
+    for all layers (they read back the means, the new lengths and the error flags); the prune reuses the
+    keys of the scoring."""
     import numpy as np
     import torch
 
@@ -415,11 +416,10 @@ def run_diversity(args):
         cache.append_layers(0, t, rings_k[t % 8], rings_v[t % 8])
         marks[1].record(stream)
         cand[:] = kept + (T if t > 0 else 0)
-        means = [cache.diversity_score(l) for l in range(L)]
+        means = cache.diversity_score_layers(0, L)
         marks[2].record(stream)
         budgets = kv.kv_layer_budgets(means, tau, total, H)
-        for l in range(L):
-            kept[l] = cache.diversity_prune(l, budgets[l])
+        kept[:] = cache.diversity_prune_layers(0, budgets)
         marks[3].record(stream)
         for l in range(L):
             cache.attend(l, rings_q[t % 8][l], 1.0, out=out)
@@ -466,9 +466,9 @@ def run_diversity(args):
         "attend_tile_fill_mid_layer": float(hl.sum(axis=0).mean() / (64.0 * tiles.mean())),
         "roofline": {"bound": "hbm", "achieved": score_bytes / (split["score"] * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": score_bytes / (split["score"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": None, "kernel": "kv_diversity_score over all layers (div_sum + div_score, two "
+                     "traffic": None, "kernel": "kv_diversity_score_layers (div_sum + div_score per layer, two "
                                                 "reads of every candidate key; includes the small kernels "
-                                                "and one read-back per layer)",
+                                                "and the one read-back)",
                      "bytes_per_frame": score_bytes},
         "attend_tflops": attn_flops / (split["attend"] * 1e-6) / 1e12,
         "attend_frac_bf16_peak": attn_flops / (split["attend"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,

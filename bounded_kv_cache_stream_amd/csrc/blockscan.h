@@ -1,4 +1,5 @@
-// Workgroup-wide exclusive scan shared by the compaction kernels.
+// Workgroup-wide helpers shared by the scoring and compaction kernels: an
+// exclusive scan and a digit histogram in LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +24,19 @@ __device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
   if (total) *total = lds[NT - 1];
   __syncthreads();
   return incl - v;
+}
+
+// Add one to cnt[d] for every active lane with `valid`, aggregating lanes of
+// the wave that share the first lane's digit into one atomic (digits are often
+// nearly uniform: the top bytes of similar floats).
+__device__ inline void hist_add(uint32_t* cnt, uint32_t d, bool valid) {
+  const unsigned long long act = __ballot(valid);
+  if (act == 0) return;
+  const int first = __ffsll((long long)act) - 1;
+  const uint32_t lead = __shfl(d, first, 64);
+  const unsigned long long same = __ballot(valid && d == lead);
+  if ((threadIdx.x & 63) == first) atomicAdd(&cnt[lead], (uint32_t)__popcll(same));
+  if (valid && d != lead) atomicAdd(&cnt[d], 1u);
 }
 
 }  // namespace kvs

@@ -103,19 +103,6 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   g.scur[idx] = __uint_as_float(order_key(s));
 }
 
-// Add one to cnt[d] for every active lane with `valid`, aggregating lanes of
-// the wave that share the first lane's digit into one atomic (digits are often
-// nearly uniform: the top bytes of similar floats).
-__device__ inline void hist_add(uint32_t* cnt, uint32_t d, bool valid) {
-  const unsigned long long act = __ballot(valid);
-  if (act == 0) return;
-  const int first = __ffsll((long long)act) - 1;
-  const uint32_t lead = __shfl(d, first, 64);
-  const unsigned long long same = __ballot(valid && d == lead);
-  if ((threadIdx.x & 63) == first) atomicAdd(&cnt[lead], (uint32_t)__popcll(same));
-  if (valid && d != lead) atomicAdd(&cnt[d], 1u);
-}
-
 __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* hist, int N, int nblk,
                                                              int shift, const int32_t* flag) {
   if (*flag) return;

@@ -11,42 +11,65 @@ namespace kvs {
 
 constexpr int32_t kDivErrNan = 1;  // a key is not finite (its score is NaN)
 
-// Byte offsets of the diversity buffers inside its workspace region.
-struct DivSizes {
-  int64_t n_max;  // candidates per head
-  int32_t p_max, h_max, nblk_max;
-  size_t entries, partial, mean, spart, total_sum, keys_a, keys_b, vals_a, vals_b, ranks, hist, new_len, flag,
-      total;
+// One layer of a call (device copy, one per slot).
+struct DivLayer {
+  int64_t keys_off;  // the layer's keys start at key store + keys_off: [H][N]
+  int64_t N;         // key stride per head: the layer's largest candidate count
+  int64_t keep;      // candidates kept per head (prune)
+  int32_t P;         // candidate pages
+  int32_t rescore;   // 1: score the layer in this call
 };
 
-DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads);
+// Byte offsets of the diversity buffers inside its workspace region, sized
+// for `layers` slots (one per layer of a call).  params and bases are one
+// contiguous block that the host fills with a single copy.
+struct DivSizes {
+  int64_t n_max;  // candidates per head
+  int32_t p_max, h_max, layers;
+  size_t params, bases, tabs, partial, mean, spart, totals, flags, dhist, dstate, lt_cnt, eq_cnt, new_len, total;
+};
 
-struct DivArgs {
+DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers);
+
+// Host layout of the params + bases block for n slots: DivLayer [n] at 0,
+// then candidate pages [n][p_max] at bases - params (phys = physical page,
+// len = rows of every head, tile_start != 0 when the page's per-head lengths
+// are in the head-length array).
+size_t div_staging_bytes(const DivSizes& z, int n);
+inline DivLayer* div_staging_layers(char* staging) { return reinterpret_cast<DivLayer*>(staging); }
+inline DevEntry* div_staging_bases(const DivSizes& z, char* staging, int slot) {
+  return reinterpret_cast<DevEntry*>(staging + (z.bases - z.params)) + (int64_t)slot * z.p_max;
+}
+
+struct DivCall {
   char* ws;  // start of the diversity workspace region
   DivSizes sizes;
   char* pool;
   PageGeom geom;
-  // The layer's candidate pages, in table order: phys = physical page, len =
-  // rows of every head, tile_start != 0 when the page's per-head lengths are
-  // in hlen_dev (see launch_head_tables); P of them.
-  const DevEntry* base_host;
-  int32_t P;
-  int32_t* hlen_dev;  // [physical page][heads] per-head lengths; the prune writes its pages' new lengths
-  int64_t N;          // the largest per-head candidate count
-  int64_t keep;       // candidates kept per head (prune only)
-  float* scores_out;  // optional [heads][score_stride], candidate order
+  int32_t* hlen_dev;      // [physical page][heads] per-head lengths; a prune writes its pages' new lengths
+  uint32_t* keys_dev;     // the key store (each layer's keys at its keys_off)
+  const char* staging;    // host block of div_staging_bytes(sizes, n) bytes
+  int32_t n;              // slots
+  int32_t max_P;          // the largest P over the slots
+  int64_t max_N;          // the largest N over the slots
+  bool any_rescore;       // some slot scores
+  bool prune;             // select and compact after the scoring
+  float* scores_out;      // optional [heads][score_stride] of slot 0, candidate order
   int64_t score_stride;
 };
 
-// Scores every candidate of every head; waits, and returns the sum of the
-// float64 scores over heads and candidates, and the error flags.
-hipError_t run_diversity_score(const DivArgs& a, double* score_sum_host, int32_t* err_flag_host, hipStream_t s);
+// Enqueues one call: the per-head candidate tables of every slot, the
+// scoring of the slots with rescore (keys into the key store, the float64
+// score sum into the totals), and for a prune the per-head top-K and the
+// compaction of every page and head.  Error flags: one word per slot, then
+// one for the call; no row moves once the call's word is set.
+hipError_t enqueue_diversity(const DivCall& c, hipStream_t s);
 
-// Scores, keeps each head's `keep` most diverse candidates and compacts every
-// page and head in place; waits, and returns the new lengths ([P][heads]),
-// the score sum before the prune, and the error flags (on an error nothing
-// moves).
-hipError_t run_diversity_prune(const DivArgs& a, int32_t* new_len_host, double* score_sum_host,
-                               int32_t* err_flag_host, hipStream_t s);
+// Device addresses of the per-slot outputs.
+inline double* div_totals(const DivCall& c) { return reinterpret_cast<double*>(c.ws + c.sizes.totals); }
+inline int32_t* div_flags(const DivCall& c) { return reinterpret_cast<int32_t*>(c.ws + c.sizes.flags); }
+inline int32_t* div_new_len(const DivCall& c, int slot) {  // [P][heads]
+  return reinterpret_cast<int32_t*>(c.ws + c.sizes.new_len) + (int64_t)slot * c.sizes.p_max * c.sizes.h_max;
+}
 
 }  // namespace kvs

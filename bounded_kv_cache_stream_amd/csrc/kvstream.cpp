@@ -56,7 +56,7 @@ struct Layout {
   size_t pool_bytes;
   // workspace regions (byte offsets); the CLCES and diversity steps share one
   // region (each waits for its own work before it returns)
-  size_t tables, part_o, part_ml, hlens, clces, div, ws_bytes;
+  size_t tables, part_o, part_ml, hlens, dkeys, clces, div, ws_bytes;
   int64_t part_rows;  // capacity in (split x query) rows
   kvs::ClcesSizes cl;
   kvs::DivSizes dv;
@@ -107,9 +107,14 @@ Layout make_layout(const kv_pool_config* c) {
   off = align_up(off + (size_t)L.part_rows * H * 2 * 4);
   L.hlens = off;  // per-head lengths of every physical page, int32 [page][H]
   off = align_up(off + (size_t)(L.layer_pages * c->num_layers) * (size_t)H * 4);
+  // diversity keys of every layer, uint32 [layer][H][pages_per_layer * page_tokens]:
+  // 4 bytes per (token, head) against the 256 of its K and V rows
+  L.dkeys = off;
+  off = align_up(off + (size_t)c->num_layers * (size_t)H * (size_t)c->pages_per_layer * (size_t)c->page_tokens * 4);
   L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window,
                           (int32_t)ts);
-  L.dv = kvs::div_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, (int32_t)H);
+  L.dv = kvs::div_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, (int32_t)H,
+                        c->num_layers);
   L.clces = off;
   L.div = off;
   off = align_up(off + std::max(L.cl.total, L.dv.total));
@@ -127,6 +132,7 @@ struct kv_pool {
   bool meta_only = false;
   int32_t splits_override = 0;
   std::vector<kvs::LayerPolicy> layers;
+  std::vector<int64_t> scored_gen;  // per layer: the table generation its diversity keys belong to (-1: none)
   std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
 };
 
@@ -176,20 +182,165 @@ DivPlan div_plan(const kv_pool_t* pool, int32_t layer) {
   return d;
 }
 
-kvs::DivArgs div_args(const kv_pool_t* pool, const DivPlan& d, int64_t keep, float* scores, int64_t stride) {
-  kvs::DivArgs a{};
-  a.ws = pool->ws + pool->lay.div;
-  a.sizes = pool->lay.dv;
-  a.pool = pool->pool;
-  a.geom = pool->lay.geom;
-  a.base_host = d.base.data();
-  a.P = (int32_t)d.base.size();
-  a.hlen_dev = hlens_dev(pool);
-  a.N = d.n_max;
-  a.keep = keep;
-  a.scores_out = scores;
-  a.score_stride = stride;
-  return a;
+kv_status check_layers(const kv_pool_t* p, int32_t first, int32_t n) {
+  if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+  if (n < 1 || first < 0 || first + n > p->cfg.num_layers)
+    return fail(KV_ERR_ARG, "layers %d..%d out of range", first, first + n - 1);
+  return KV_OK;
+}
+
+// One diversity call over a set of layers (slots in order): the host staging
+// block (per-layer parameters and candidate tables) and the launch arguments.
+struct DivBatch {
+  std::vector<char> staging;
+  std::vector<int32_t> layer;  // slot -> layer
+  kvs::DivCall call{};
+};
+
+DivBatch div_batch(const kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
+                   const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, float* scores,
+                   int64_t stride) {
+  DivBatch b;
+  const kvs::DivSizes& z = pool->lay.dv;
+  const int n = (int)layers.size();
+  b.layer = layers;
+  b.staging.assign(kvs::div_staging_bytes(z, n), 0);
+  kvs::DivCall& c = b.call;
+  c.ws = pool->ws + pool->lay.div;
+  c.sizes = z;
+  c.pool = pool->pool;
+  c.geom = pool->lay.geom;
+  c.hlen_dev = hlens_dev(pool);
+  c.keys_dev = reinterpret_cast<uint32_t*>(pool->ws + pool->lay.dkeys);
+  c.staging = b.staging.data();
+  c.n = n;
+  c.prune = prune;
+  c.scores_out = scores;
+  c.score_stride = stride;
+  const int64_t per_layer = (int64_t)pool->cfg.num_heads * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
+  for (int i = 0; i < n; ++i) {
+    const DivPlan& d = *plans[(size_t)i];
+    kvs::DivLayer& L = kvs::div_staging_layers(b.staging.data())[i];
+    L.keys_off = (int64_t)layers[(size_t)i] * per_layer;
+    L.N = d.n_max;
+    L.keep = keep[(size_t)i];
+    L.P = (int32_t)d.base.size();
+    L.rescore = rescore[(size_t)i];
+    std::copy(d.base.begin(), d.base.end(), kvs::div_staging_bases(z, b.staging.data(), i));
+    c.max_P = std::max(c.max_P, L.P);
+    c.max_N = std::max(c.max_N, L.N);
+    c.any_rescore = c.any_rescore || L.rescore;
+  }
+  return b;
+}
+
+// Scores layers first .. first+n-1, one wait for all of them.
+kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, float* scores_dev, int64_t stride,
+                                double* means, hipStream_t st) {
+  std::vector<DivPlan> plans((size_t)n);
+  std::vector<int32_t> layers;
+  std::vector<const DivPlan*> pl;
+  for (int32_t i = 0; i < n; ++i) {
+    plans[(size_t)i] = div_plan(pool, first + i);
+    means[i] = 0.0;
+    if (plans[(size_t)i].n_total > 0) {
+      layers.push_back(first + i);
+      pl.push_back(&plans[(size_t)i]);
+    }
+  }
+  if (layers.empty()) return ok();
+  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+  if (scores_dev && stride < plans[0].n_max)
+    return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)stride,
+                (long long)plans[0].n_max);
+  const size_t m = layers.size();
+  DivBatch b = div_batch(pool, layers, pl, std::vector<int64_t>(m, 0), std::vector<char>(m, 1), false, scores_dev,
+                         stride);
+  for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
+  hipError_t e = kvs::enqueue_diversity(b.call, st);
+  if (e != hipSuccess) return hip_fail(e, "diversity scoring launch");
+  std::vector<double> sums(m);
+  std::vector<int32_t> flags(m + 1);
+  e = hipMemcpyAsync(sums.data(), kvs::div_totals(b.call), sizeof(double) * m, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(flags.data(), kvs::div_flags(b.call), sizeof(int32_t) * (m + 1), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "diversity scoring");
+  for (size_t i = 0; i < m; ++i)
+    if (flags[i] & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layers[i]);
+  for (size_t i = 0; i < m; ++i) {
+    const int32_t l = layers[i];
+    means[l - first] = sums[i] / (double)pl[i]->n_total;
+    pool->scored_gen[(size_t)l] = pool->layers[(size_t)l].gen;
+  }
+  return ok();
+}
+
+// Prunes layers first .. first+n-1 to keep[i] candidates per head, one wait
+// for all of them.  Layers whose keys are not from a scoring of their
+// current state are scored in the same call, before any row moves, so a key
+// that is not finite in any layer leaves every layer unchanged.
+kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const int64_t* keep, float* scores_dev,
+                                int64_t stride, int64_t* kept, hipStream_t st) {
+  const int32_t H = pool->cfg.num_heads;
+  for (int32_t i = 0; i < n; ++i)
+    if (keep[i] < 0) return fail(KV_ERR_ARG, "keep_per_head[%d] must be >= 0", i);
+  std::vector<DivPlan> plans((size_t)n);
+  std::vector<int32_t> layers;
+  std::vector<const DivPlan*> pl;
+  std::vector<int64_t> kp;
+  std::vector<char> rescore;
+  for (int32_t i = 0; i < n; ++i) {
+    plans[(size_t)i] = div_plan(pool, first + i);
+    if (plans[(size_t)i].n_max > keep[i]) {
+      const int32_t l = first + i;
+      layers.push_back(l);
+      pl.push_back(&plans[(size_t)i]);
+      kp.push_back(keep[i]);
+      rescore.push_back(scores_dev || pool->scored_gen[(size_t)l] != pool->layers[(size_t)l].gen);
+    }
+  }
+  if (!layers.empty()) {
+    if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+    if (scores_dev && stride < plans[0].n_max)
+      return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)stride,
+                  (long long)plans[0].n_max);
+    const size_t m = layers.size();
+    DivBatch b = div_batch(pool, layers, pl, kp, rescore, true, scores_dev, stride);
+    for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
+    hipError_t e = kvs::enqueue_diversity(b.call, st);
+    if (e != hipSuccess) return hip_fail(e, "diversity prune launch");
+    std::vector<int32_t> flags(m + 1);
+    std::vector<std::vector<int32_t>> nl(m);
+    e = hipMemcpyAsync(flags.data(), kvs::div_flags(b.call), sizeof(int32_t) * (m + 1), hipMemcpyDeviceToHost, st);
+    for (size_t i = 0; i < m && e == hipSuccess; ++i) {
+      nl[i].resize(pl[i]->base.size() * (size_t)H);
+      e = hipMemcpyAsync(nl[i].data(), kvs::div_new_len(b.call, (int)i), sizeof(int32_t) * nl[i].size(),
+                         hipMemcpyDeviceToHost, st);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "diversity prune");
+    for (size_t i = 0; i < m; ++i)
+      if (flags[i] & kvs::kDivErrNan)
+        return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite (no layer changed)", layers[i]);
+    for (size_t i = 0; i < m; ++i) {
+      if (flags[i]) return fail(KV_ERR_HIP, "layer %d: diversity prune consistency check failed (flag %d, pool "
+                                            "state undefined)", layers[i], flags[i]);
+      for (int32_t h = 0; h < H; ++h) {
+        int64_t k = 0;
+        for (size_t j = 0; j < pl[i]->base.size(); ++j) k += nl[i][j * (size_t)H + (size_t)h];
+        if (k != std::min(kp[i], pl[i]->n_head[(size_t)h]))
+          return fail(KV_ERR_HIP, "layer %d head %d: kept %lld candidates, expected %lld (pool state undefined)",
+                      layers[i], h, (long long)k, (long long)std::min(kp[i], pl[i]->n_head[(size_t)h]));
+      }
+    }
+    for (size_t i = 0; i < m; ++i) pool->layers[(size_t)layers[i]].apply_head_compaction(nl[i], H);
+  }
+  if (kept)
+    for (int32_t i = 0; i < n; ++i)
+      for (int32_t h = 0; h < H; ++h)
+        kept[(int64_t)i * H + h] = std::min(keep[i], plans[(size_t)i].n_head[(size_t)h]);
+  return ok();
 }
 
 }  // namespace
@@ -243,6 +394,7 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   p->ws = static_cast<char*>(workspace_dev);
   p->meta_only = meta;
   p->layers.resize((size_t)cfg->num_layers);
+  p->scored_gen.assign((size_t)cfg->num_layers, -1);
   for (auto& l : p->layers)
     l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens);
   *out = p;
@@ -549,56 +701,34 @@ kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, 
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
   if (!mean_diversity) return fail(KV_ERR_ARG, "mean_diversity is NULL");
-  const DivPlan d = div_plan(pool, layer);
-  if (d.n_total == 0) {
-    *mean_diversity = 0.0;
-    return ok();
-  }
-  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
-  if (scores_dev && score_stride < d.n_max)
-    return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)score_stride,
-                (long long)d.n_max);
-  const kvs::DivArgs a = div_args(pool, d, 0, scores_dev, score_stride);
-  double sum = 0.0;
-  int32_t flag = 0;
-  hipError_t e = kvs::run_diversity_score(a, &sum, &flag, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "diversity scoring");
-  if (flag & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layer);
-  *mean_diversity = sum / (double)d.n_total;
-  return ok();
+  return diversity_score_range(pool, layer, 1, scores_dev, score_stride, mean_diversity,
+                               static_cast<hipStream_t>(stream));
+}
+
+kv_status kv_diversity_score_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, double* mean_diversity,
+                                    void* stream) {
+  kv_status s = check_layers(pool, first_layer, n_layers);
+  if (s != KV_OK) return s;
+  if (!mean_diversity) return fail(KV_ERR_ARG, "mean_diversity is NULL");
+  return diversity_score_range(pool, first_layer, n_layers, nullptr, 0, mean_diversity,
+                               static_cast<hipStream_t>(stream));
 }
 
 kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
                              int64_t score_stride, int64_t* kept_per_head, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
-  if (keep_per_head < 0) return fail(KV_ERR_ARG, "keep_per_head must be >= 0");
-  const int32_t H = pool->cfg.num_heads;
-  const DivPlan d = div_plan(pool, layer);
-  if (d.n_max > keep_per_head) {
-    if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
-    if (scores_dev && score_stride < d.n_max)
-      return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)score_stride,
-                  (long long)d.n_max);
-    const kvs::DivArgs a = div_args(pool, d, keep_per_head, scores_dev, score_stride);
-    std::vector<int32_t> nl(d.base.size() * (size_t)H);
-    double sum = 0.0;
-    int32_t flag = 0;
-    hipError_t e = kvs::run_diversity_prune(a, nl.data(), &sum, &flag, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "diversity prune");
-    if (flag & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layer);
-    for (int32_t h = 0; h < H; ++h) {
-      int64_t kept = 0;
-      for (size_t i = 0; i < d.base.size(); ++i) kept += nl[i * (size_t)H + (size_t)h];
-      if (kept != std::min(keep_per_head, d.n_head[(size_t)h]))
-        return fail(KV_ERR_HIP, "layer %d head %d: kept %lld candidates, expected %lld (pool state undefined)",
-                    layer, h, (long long)kept, (long long)std::min(keep_per_head, d.n_head[(size_t)h]));
-    }
-    pool->layers[(size_t)layer].apply_head_compaction(nl, H);
-  }
-  if (kept_per_head)
-    for (int32_t h = 0; h < H; ++h) kept_per_head[h] = std::min(keep_per_head, d.n_head[(size_t)h]);
-  return ok();
+  return diversity_prune_range(pool, layer, 1, &keep_per_head, scores_dev, score_stride, kept_per_head,
+                               static_cast<hipStream_t>(stream));
+}
+
+kv_status kv_diversity_prune_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers,
+                                    const int64_t* keep_per_head, int64_t* kept_per_head, void* stream) {
+  kv_status s = check_layers(pool, first_layer, n_layers);
+  if (s != KV_OK) return s;
+  if (!keep_per_head) return fail(KV_ERR_ARG, "keep_per_head is NULL");
+  return diversity_prune_range(pool, first_layer, n_layers, keep_per_head, nullptr, 0, kept_per_head,
+                               static_cast<hipStream_t>(stream));
 }
 
 kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, double tau, int64_t total_tokens,

@@ -48,6 +48,7 @@ class LayerPolicy {
   }
 
   void reset() {
+    ++gen;
     table.clear();
     free_ids.clear();
     for (int32_t i = 0; i < pages_; ++i) free_ids.insert(i);
@@ -85,6 +86,7 @@ class LayerPolicy {
     }
     free_ids.erase(page);
     table.push_back(PageEntry{page, T_, t, {}});
+    ++gen;
   }
 
   int32_t evict() {
@@ -105,6 +107,7 @@ class LayerPolicy {
       ++n;
     }
     evictions += n;
+    if (n) ++gen;
     return n;
   }
 
@@ -132,6 +135,7 @@ class LayerPolicy {
     table.swap(out);
     ++compactions;
     last_keep = kept;
+    ++gen;
   }
 
   // Page merge (defragmentation of the ragged pages compaction leaves): walk
@@ -175,6 +179,7 @@ class LayerPolicy {
     }
     table.swap(out);
     merges += (int64_t)mv.size();
+    if (!mv.empty()) ++gen;
   }
 
   // Per-head new lengths for entries first_candidate().. ([entry][head]); a
@@ -199,6 +204,7 @@ class LayerPolicy {
     }
     table.swap(out);
     ++prunes;
+    ++gen;
   }
 
   // True when every page holds the same tokens in every head.
@@ -235,6 +241,7 @@ class LayerPolicy {
   int64_t last_keep = 0;
   int64_t merges = 0;
   int64_t prunes = 0;
+  int64_t gen = 0;  // changes whenever the table does (never reset, so a stale copy never matches)
 
  private:
   int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0;

@@ -21,8 +21,8 @@ KV_TRANSIENT = 1
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
     "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
-    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score", "kv_layer_budgets",
-    "kv_diversity_prune", "kv_get_head_lengths", "kv_last_error",
+    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score", "kv_diversity_score_layers",
+    "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers", "kv_get_head_lengths", "kv_last_error",
 )
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
             "kv_layer_budgets": [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_double, I64, I32,
                                  ctypes.POINTER(I64)],
             "kv_diversity_prune": [P, I32, I64, P, I64, ctypes.POINTER(I64), P],
+            "kv_diversity_score_layers": [P, I32, I32, ctypes.POINTER(ctypes.c_double), P],
+            "kv_diversity_prune_layers": [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), P],
             "kv_get_head_lengths": [P, I32, P, I32, ctypes.POINTER(I32)],
         }
         for name, args in sig.items():
@@ -194,6 +196,20 @@ def kv_diversity_prune(pool, layer, keep_per_head, heads, scores_ptr=None, score
     kept = (ctypes.c_int64 * heads)()
     _check(lib().kv_diversity_prune(pool, layer, keep_per_head, scores_ptr, score_stride, kept, stream))
     return list(kept)
+
+
+def kv_diversity_score_layers(pool, first_layer, n_layers, stream=None) -> list:
+    out = (ctypes.c_double * n_layers)()
+    _check(lib().kv_diversity_score_layers(pool, first_layer, n_layers, out, stream))
+    return list(out)
+
+
+def kv_diversity_prune_layers(pool, first_layer, keep_per_head, heads, stream=None) -> list:
+    n = len(keep_per_head)
+    keep = (ctypes.c_int64 * max(n, 1))(*[int(k) for k in keep_per_head])
+    kept = (ctypes.c_int64 * max(n * heads, 1))()
+    _check(lib().kv_diversity_prune_layers(pool, first_layer, n, keep, kept, stream))
+    return [list(kept[i * heads:(i + 1) * heads]) for i in range(n)]
 
 
 def kv_get_head_lengths(pool, layer, heads) -> list:
@@ -350,6 +366,15 @@ class KVCache:
         """Per-head top-K prune; returns the candidates kept per head."""
         sp, stride = self._scores_arg(scores)
         return kv_diversity_prune(self.handle, layer, keep_per_head, self.cfg.num_heads, sp, stride, self._stream())
+
+    def diversity_score_layers(self, first_layer, n_layers) -> list:
+        """Mean diversity of each of n_layers layers, one wait."""
+        return kv_diversity_score_layers(self.handle, first_layer, n_layers, self._stream())
+
+    def diversity_prune_layers(self, first_layer, keep_per_head) -> list:
+        """Per-head top-K prune of len(keep_per_head) layers, one wait; kept per layer and head."""
+        return kv_diversity_prune_layers(self.handle, first_layer, keep_per_head, self.cfg.num_heads,
+                                         self._stream())
 
     def head_lengths(self, layer) -> list:
         return kv_get_head_lengths(self.handle, layer, self.cfg.num_heads)

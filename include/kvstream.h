@@ -236,6 +236,15 @@ kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void
 kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,
                              double* mean_diversity, void* stream);
 
+/* kv_diversity_score for layers first_layer .. first_layer+n_layers-1 with
+ * one wait for all of them (no score output); mean_diversity: host double
+ * [n_layers].  KV_ERR_NAN names the first layer with a key that is not
+ * finite.  Each layer keeps its keys in its own workspace slot, so a
+ * kv_diversity_prune(_layers) of a layer that has not changed since reuses
+ * them instead of scoring again. */
+kv_status kv_diversity_score_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers,
+                                    double* mean_diversity, void* stream);
+
 /* Per-layer budgets ([INF] "Building Blocks", recipe step 5): with
  * p = softmax(mean_diversity / tau) over the n_layers layers,
  *   keep_per_head[l] = floor(floor(p_l * total_tokens) / heads).
@@ -262,6 +271,15 @@ kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, doubl
  * unchanged) if a candidate key is not finite.  Synchronises the stream. */
 kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
                              int64_t score_stride, int64_t* kept_per_head, void* stream);
+
+/* kv_diversity_prune for layers first_layer .. first_layer+n_layers-1 with
+ * one wait for all of them (no score output): keep_per_head is host int64
+ * [n_layers] (one budget per layer, e.g. from kv_layer_budgets);
+ * kept_per_head, optional, host int64 [n_layers][H].  A layer not scored in
+ * its current state is scored first; every layer is scored before any row
+ * moves, so on KV_ERR_NAN no layer changes. */
+kv_status kv_diversity_prune_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers,
+                                    const int64_t* keep_per_head, int64_t* kept_per_head, void* stream);
 
 /* Per-head lengths of the layer's pages, int32 [entry][H] in table order, cap
  * entries at most; *n_out = table size.  Equal to the page length in every

@@ -211,7 +211,9 @@ def test_diversity_stream_every_frame(dname):
 
 
 def test_diversity_budgets_three_layers():
-    # the whole step: mean diversity of every layer, softmax budgets, prune
+    # the whole step with the batched calls: mean diversity of every layer
+    # (one wait), softmax budgets, prune of every layer (one wait, reusing
+    # the keys of the scoring)
     torch = torch_cuda()
     T, H, F, L = 128, 4, 6, 3
     cache = kv.KVCache(_cfg(T, F + 1, H, kv.KV_BF16, layers=L), device="cuda")
@@ -223,18 +225,52 @@ def test_diversity_budgets_three_layers():
             if l == 2:
                 k = (k.float() + 2.0 * (l + 1)).to(torch.bfloat16)  # a shared offset: low diversity
             s.append(t, k.contiguous(), v)
-    means = [cache.diversity_score(l) for l in range(L)]
+    means = cache.diversity_score_layers(0, L)
+    assert means == [cache.diversity_score(l) for l in range(L)]  # same kernels, same order: same bits
     want = [s.sim.mean_diversity(s.key_of) for s in streams]
     assert np.allclose(means, want, rtol=0, atol=1e-12), (means, want)
     assert means[2] < min(means[:2])
     total = 3 * H * 400
     budgets = kv.kv_layer_budgets(means, 0.1, total, H)
     assert budgets == diversity.layer_budgets(want, 0.1, total, H).tolist()
+    kept = cache.diversity_prune_layers(0, budgets)
     for l, s in enumerate(streams):
-        cache.diversity_prune(l, budgets[l])
+        assert kept[l] == [min(budgets[l], len(s.sim.candidates(h))) for h in range(H)]
         s.sim.prune(s.key_of, budgets[l], rank_dtype=np.float32)
         s.check_pages(f"layer {l}")
     say(f"budgets {budgets} from mean diversity {np.round(means, 5).tolist()}")
+    # unchanged layers: a second batched prune to the same budgets moves nothing
+    assert cache.diversity_prune_layers(0, budgets) == kept
+    for s in streams:
+        s.check_pages("second prune")
+
+
+def test_diversity_batched_prune_all_or_nothing():
+    # a key that is not finite in one layer: the batched prune scores every
+    # layer before any row moves, so no layer changes
+    torch = torch_cuda()
+    T, H, F, L = 64, 2, 5, 3
+    cache = kv.KVCache(_cfg(T, F + 1, H, kv.KV_BF16, layers=L), device="cuda")
+    streams = [Stream(cache, T, H, F + 1, wid=102, layer=l) for l in range(L)]
+    for s in streams:
+        for t in range(F):
+            s.append(t)
+    k, _, _ = cache.page_view(2, 4)
+    k[0, 3, 9] = float("inf")
+    with pytest.raises(kv.KVError) as e:
+        cache.diversity_prune_layers(0, [100, 100, 100])
+    assert e.value.status == kv.KV_ERR_NAN and "layer 2" in str(e.value)
+    with pytest.raises(kv.KVError) as e:
+        cache.diversity_score_layers(0, L)
+    assert e.value.status == kv.KV_ERR_NAN and "layer 2" in str(e.value)
+    for s in streams[:2]:
+        s.check_pages("after the refused prune")
+    assert all(cache.head_lengths(l) == [[T, T]] * F for l in range(L))
+    # the first two layers alone prune normally
+    cache.diversity_prune_layers(0, [100, 100])
+    for s in streams[:2]:
+        s.sim.prune(s.key_of, 100, rank_dtype=np.float32)
+        s.check_pages("after the prune of layers 0-1")
 
 
 def test_diversity_full_size_16_heads():

@@ -261,3 +261,18 @@ def test_diversity_host_rules():
     assert e.value.status == kv.KV_ERR_ARG
     assert c.head_lengths(0) == [[16, 16]] * 4
     assert c.info(0)["prunes"] == 0
+    # batched forms: range checks, and the same host rules per layer
+    m = _meta_pool(1, 0, 1, 6, layers=3)
+    assert m.diversity_score_layers(0, 3) == [0.0, 0.0, 0.0]
+    m.append(1, 0, None, None)
+    m.append(1, 1, None, None)
+    assert m.diversity_prune_layers(0, [5, 16, 0]) == [[0, 0], [16, 16], [0, 0]]
+    for call in (lambda: m.diversity_prune_layers(1, [5, 5]), lambda: m.diversity_score_layers(0, 3)):
+        with pytest.raises(kv.KVError) as e:
+            call()
+        assert e.value.status == kv.KV_ERR_STATE
+    for call in (lambda: m.diversity_score_layers(1, 3), lambda: m.diversity_prune_layers(2, [1, 1]),
+                 lambda: m.diversity_score_layers(0, 0), lambda: m.diversity_prune_layers(0, [1, -1])):
+        with pytest.raises(kv.KVError) as e:
+            call()
+        assert e.value.status == kv.KV_ERR_ARG
