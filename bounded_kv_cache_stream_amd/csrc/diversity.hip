@@ -30,7 +30,8 @@
 //   select  per (head, slot), 4 radix passes of 8 bits (most significant
 //           first) find the K-th smallest key t and how many keys equal to t
 //           are kept: the first ones in candidate order, as a stable sort
-//           would keep them;
+//           would keep them (a histogram pass over the keys, then one
+//           workgroup per (head, slot) fixes the digit);
 //   mark    per (page, head, slot): keys below t and equal to t;
 //   compact per (page, head, slot): the page's new length n follows from the
 //           counts; kept = key < t, or key == t within the tie quota; the
@@ -184,12 +185,22 @@ __device__ inline void load_rows(const char* rows, int j0, int r, int c, int len
   }
 }
 
-// Sum over the 8 lanes of a row; every lane ends with the same bits (each
-// level adds the same two operands, in either order).
+// A double moved across lanes by one DPP pattern (both halves).
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over the 8 lanes of a row (an aligned group of 8 lanes): quad
+// permutes swap lanes 1 apart and 2 apart, then the half-row mirror pairs
+// each lane of one quad with a lane of the other.  Every lane ends with the
+// same bits (each level adds the same two operands, in either order).
 __device__ inline double row_sum(double v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
+  v += dpp_f64<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
   return v;
 }
 
@@ -407,25 +418,32 @@ __device__ inline DSel* sel_state(const DivK& a, int slot, int p, int h) {
   return a.dstate + ((int64_t)slot * 5 + p) * a.H + h;
 }
 
-// Pass p: histogram of digit p over head h's keys that match the digits fixed
-// so far.  The state before pass p comes from the previous pass's state and
-// histogram; workgroup 0 of the (head, slot) stores it.
+// One workgroup per (head, slot): the state before pass p (p = 0: nothing
+// fixed, min(keep, candidates) to keep; p = 1..4: pass p-1's state advanced
+// by its histogram; state 4 is the final one).
+__global__ __launch_bounds__(kThreads) void div_advance_kernel(DivK a, int p) {
+  if (a.flags[a.n]) return;
+  const int h = blockIdx.x, slot = blockIdx.y;
+  const DSel st = p == 0 ? DSel{0u, 0, (long long)min<int64_t>(a.layers[slot].keep, head_count(a, slot, h))}
+                         : select_advance(*sel_state(a, slot, p - 1, h), sel_hist(a, slot, p - 1, h), p - 1);
+  if (threadIdx.x == 0) *sel_state(a, slot, p, h) = st;
+}
+
+// Pass p: histogram of digit p over head h's keys that match the digits
+// fixed so far.
 __global__ __launch_bounds__(kThreads) void div_select_kernel(DivK a, int p) {
   if (a.flags[a.n]) return;
   __shared__ uint32_t cnt[256];
   const int h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
-  const DivLayer L = a.layers[slot];
   const int64_t nh = head_count(a, slot, h);
-  if (blockIdx.x > 0 && (int64_t)blockIdx.x * kSelTile >= nh) return;  // past the head's keys
-  const DSel st = p == 0 ? DSel{0u, 0, (long long)min<int64_t>(L.keep, nh)}
-                         : select_advance(*sel_state(a, slot, p - 1, h), sel_hist(a, slot, p - 1, h), p - 1);
-  if (blockIdx.x == 0 && tid == 0) *sel_state(a, slot, p, h) = st;
+  if ((int64_t)blockIdx.x * kSelTile >= nh) return;  // past the head's keys
+  const DSel st = *sel_state(a, slot, p, h);
   if (st.k_rem == 0) return;
   cnt[tid] = 0;
   __syncthreads();
   const int shift = 24 - 8 * p;
   const uint32_t hi = p == 0 ? 0u : (~0u << (32 - 8 * p));
-  const uint32_t* kk = head_keys(a, L, h);
+  const uint32_t* kk = head_keys(a, a.layers[slot], h);
 #pragma unroll
   for (int j = 0; j < kSelItems; ++j) {
     const int64_t i = (int64_t)blockIdx.x * kSelTile + j * kThreads + tid;
@@ -436,16 +454,14 @@ __global__ __launch_bounds__(kThreads) void div_select_kernel(DivK a, int p) {
   if (cnt[tid]) atomicAdd(&sel_hist(a, slot, p, h)[tid], cnt[tid]);
 }
 
-// The final state (threshold t = its prefix, k_rem keys equal to t kept) and,
-// per (page, head, slot), the keys below t and equal to t.
+// Per (page, head, slot): the keys below the threshold t and equal to it.
 __global__ __launch_bounds__(kThreads) void div_mark_kernel(DivK a) {
   if (a.flags[a.n]) return;
   __shared__ int32_t s_lt, s_eq;
   const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
   const DivLayer L = a.layers[slot];
   if (p >= L.P) return;
-  const DSel st = select_advance(*sel_state(a, slot, 3, h), sel_hist(a, slot, 3, h), 3);
-  if (p == 0 && tid == 0) *sel_state(a, slot, 4, h) = st;
+  const uint32_t t = sel_state(a, slot, 4, h)->prefix;
   if (tid == 0) {
     s_lt = 0;
     s_eq = 0;
@@ -456,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void div_mark_kernel(DivK a) {
   int32_t lt = 0, eq = 0;
   for (int j = tid; j < en.len; j += kThreads) {
     const uint32_t key = kk[j];
-    lt += key < st.prefix;
-    eq += key == st.prefix;
+    lt += key < t;
+    eq += key == t;
   }
   for (int off = 32; off > 0; off >>= 1) {
     lt += __shfl_xor(lt, off, 64);
@@ -494,14 +510,18 @@ __global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
   const int len = en.len;
   const DSel st = *sel_state(a, slot, 4, h);
   const int64_t cnt_at = ((int64_t)slot * a.H + h) * a.p_max;
+  const int32_t eq = a.eq_cnt[cnt_at + p];
+  // keys equal to t in the earlier pages: only a page holding such a key
+  // needs them (its share of the tie quota), and such pages are rare
   if (tid == 0) s_eqb = 0;
   __syncthreads();
-  int32_t e = 0;
-  for (int i = tid; i < p; i += kThreads) e += a.eq_cnt[cnt_at + i];
-  if (e) atomicAdd(&s_eqb, e);
-  __syncthreads();
+  if (eq > 0) {
+    int32_t e = 0;
+    for (int i = tid; i < p; i += kThreads) e += a.eq_cnt[cnt_at + i];
+    if (e) atomicAdd(&s_eqb, e);
+    __syncthreads();
+  }
   const long long eq_before = s_eqb;
-  const int32_t eq = a.eq_cnt[cnt_at + p];
   const long long quota = st.k_rem - eq_before;
   const int32_t n = a.lt_cnt[cnt_at + p] + (int32_t)(quota < 0 ? 0 : (quota > eq ? eq : quota));
   if (tid == 0) {
@@ -656,8 +676,12 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   }
   if (c.prune) {
     const unsigned nblk = (unsigned)((c.max_N + kSelTile - 1) / kSelTile);
-    for (int p = 0; p < 4; ++p)
+    const dim3 heads((unsigned)H, (unsigned)c.n);
+    for (int p = 0; p < 4; ++p) {
+      div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, p);
       div_select_kernel<<<dim3(nblk, (unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k, p);
+    }
+    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, 4);
     div_mark_kernel<<<pages, dim3(kThreads), 0, s>>>(k);
     if (c.geom.esize == 2)
       div_compact_kernel<__bf16><<<pages, dim3(kThreads), 0, s>>>(k);

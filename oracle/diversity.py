@@ -40,7 +40,7 @@ Readings taken where the pages are silent (listed in the design doc):
 Pinned by ``tests/test_oracle_diversity.py``: closed forms (identical
 directions score -1; an orthonormal set scores -1/sqrt(n); scores are
 invariant to positive scaling of a key; the mean of the scores of n keys is
--|m|), a brute-force cosine written with explicit angles on small inputs, the
+-|m|), a brute-force cosine with exactly rounded component sums on small inputs, the
 worked budget example in ``tests/golden/diversity_budget_example.txt``, and the
 softmax budgets' limits (equal averages split evenly, a cold temperature gives
 everything to the most diverse layer).
