@@ -28,7 +28,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
 Pinned by ``tests/test_oracle_window.py``: the closed form below is checked
 against the allocator simulation (two independent formulations), the hand-made
 page-table fixture ``tests/golden/config0_page_tables.txt``, the occupancy bound
-and the frames/k growth claim.
+and the frames/k growth claim.  The special-token variant is pinned by the
+hand-worked fixture ``tests/golden/special_tokens_hand_example.txt``, by an
+independent closed form of the held special ids on 60 random policies, by the
+fill rule of its pages, and by reducing to the plain policy with no special
+tokens.
 """
 
 from __future__ import annotations
@@ -120,3 +124,84 @@ class WindowCache:
 
     def page_ids(self) -> list[int]:
         return [p for p, _ in self.table]
+
+
+class SpecialWindowCache(WindowCache):
+    """The window policy with cross-frame special-token persistence.
+
+    GCTStream explainer, "Special Token Persistence": with
+    ``kv_cache_cross_frame_special`` the special tokens of a frame survive the
+    eviction that discards the rest of its KV.  Readings (listed in the design doc):
+
+    * the special tokens are the first ``special`` slots of every frame;
+    * at each eviction (oldest victim first) the victim's special token ids
+      go, in slot order, to the end of the layer's last special page; a new
+      special page is taken (lowest free id, while the victim still holds its
+      own id) when they do not fit in ``tokens_per_frame`` slots; then the
+      victim's id is freed;
+    * special pages sit after the scale frames, in the order they were
+      opened, and are never evicted; they count as no frame of the window.
+
+    ``table`` keeps the ``(page_id, frame)`` pairs of the frame pages;
+    ``special_pages`` holds ``[page_id, [token ids]]`` lists.
+    """
+
+    def __init__(self, scale_frames: int, window: int, keyframe_interval: int, num_pages: int, special: int,
+                 tokens_per_frame: int):
+        super().__init__(scale_frames, window, keyframe_interval, num_pages)
+        self.special = special
+        self.T = tokens_per_frame
+        self.special_pages: list[list] = []
+
+    def evict(self) -> int:
+        n = 0
+        if self.W <= 0:
+            return 0
+        while sum(1 for _, f in self.table if f >= self.S) > self.W:
+            idx = next(i for i, (_, f) in enumerate(self.table) if f >= self.S)
+            pid, f = self.table[idx]
+            if self.special > 0:
+                if not self.special_pages or len(self.special_pages[-1][1]) + self.special > self.T:
+                    if not self.free:
+                        raise PoolExhausted(f"no free page for the special tokens of frame {f}")
+                    sp = min(self.free)
+                    self.free.remove(sp)
+                    self.special_pages.append([sp, []])
+                self.special_pages[-1][1].extend(f * self.T + j for j in range(self.special))
+            self.table.pop(idx)
+            self.free.add(pid)
+            n += 1
+        self.evictions += n
+        return n
+
+    def attended_tokens(self) -> list[int]:
+        """Token ids of the next attention call in table order (scale frames, special pages, window frames,
+        then the transient frame, which is consumed)."""
+        scale = [f for _, f in self.table if f < self.S]
+        rest = [f for _, f in self.table if f >= self.S]
+        ids = [f * self.T + j for f in scale for j in range(self.T)]
+        for _, toks in self.special_pages:
+            ids.extend(toks)
+        ids.extend(f * self.T + j for f in rest for j in range(self.T))
+        if self.transient is not None:
+            ids.extend(self.transient * self.T + j for j in range(self.T))
+            self.transient = None
+        return ids
+
+    def page_table(self) -> list[tuple[int, int, int]]:
+        """``(page_id, frame, length)`` per entry in table order; a special page reports ``-1 - f`` with ``f``
+        the first frame whose special tokens it holds."""
+        scale = [(p, f, self.T) for p, f in self.table if f < self.S]
+        rest = [(p, f, self.T) for p, f in self.table if f >= self.S]
+        special = [(p, -1 - toks[0] // self.T, len(toks)) for p, toks in self.special_pages]
+        return scale + special + rest
+
+
+def special_token_ids(t: int, scale_frames: int, window: int, keyframe_interval: int, special: int,
+                      tokens_per_frame: int) -> list[int]:
+    """Closed form: the special token ids held after frame ``t`` was appended and evicted -- the first
+    ``special`` slots of every keyframe past the scale frames that is no longer persisted, oldest first."""
+    kept = set(persisted_frames(t, scale_frames, window, keyframe_interval))
+    gone = [f for f in range(scale_frames, t + 1)
+            if is_keyframe(f, scale_frames, keyframe_interval) and f not in kept]
+    return [f * tokens_per_frame + j for f in gone for j in range(special)]

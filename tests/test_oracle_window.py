@@ -9,6 +9,7 @@ import itertools
 import os
 import random
 
+import numpy as np
 import pytest
 
 from oracle import window
@@ -124,3 +125,64 @@ def test_keyframe_rule():
     for S, k in itertools.product(range(0, 9, 4), (1, 2, 4)):
         for t in range(S, 50):
             assert window.is_keyframe(t, S, k) == ((t - S) % k == 0)
+
+
+def _special_fixture():
+    rows = {}
+    for ln in open(os.path.join(os.path.dirname(__file__), "golden", "special_tokens_hand_example.txt")):
+        if ln.strip() and not ln.startswith("#"):
+            t, rest = ln.split(":", 1)
+            tab, ids, free = rest.split("|")
+            rows[int(t[1:])] = ([tuple(int(x) for x in e.split(":")) for e in tab.split()],
+                                [int(x) for x in ids.split()], {int(x) for x in free.split()})
+    return rows
+
+
+def test_special_tokens_hand_example():
+    gold = _special_fixture()
+    c = window.SpecialWindowCache(1, 2, 1, 6, special=1, tokens_per_frame=4)
+    for t in range(8):
+        c.append(t)
+        c.evict()
+        tab, ids, free = gold[t]
+        assert c.page_table() == tab, t
+        assert [i for _, toks in c.special_pages for i in toks] == ids, t
+        assert c.free == free, t
+
+
+def test_special_tokens_closed_form_and_fill():
+    # the held special ids equal the first slots of every evicted keyframe
+    # (an independent closed form); every special page but the last is filled
+    # to floor(T / special) frames; the attended set is scale + specials +
+    # window + transient; special = 0 is the plain window policy
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        S, W, k = int(rng.integers(0, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 4))
+        T = int(rng.integers(2, 12))
+        sp = int(rng.integers(1, T + 1))
+        frames = int(rng.integers(5, 80))
+        c = window.SpecialWindowCache(S, W, k, S + W + 1 + frames, special=sp, tokens_per_frame=T)
+        plain = window.WindowCache(S, W, k, S + W + 1 + frames)
+        for t in range(frames):
+            c.append(t)
+            c.evict()
+            plain.append(t)
+            plain.evict()
+            assert c.persisted() == plain.persisted() == window.persisted_frames(t, S, W, k)
+            held = [i for _, toks in c.special_pages for i in toks]
+            assert held == window.special_token_ids(t, S, W, k, sp, T)
+            per_page = (T // sp) * sp
+            lens = [len(toks) for _, toks in c.special_pages]
+            assert all(n == per_page for n in lens[:-1]) and (not lens or 0 < lens[-1] <= per_page)
+            att = c.attended_tokens()
+            fr = window.attended_frames(t, S, W, k) if t >= S else window.persisted_frames(t, S, W, k)
+            want = [f * T + j for f in fr if f < S for j in range(T)] + held + \
+                [f * T + j for f in fr if f >= S for j in range(T)]
+            assert att == want
+            pids = [p for p, _, _ in c.page_table()]
+            assert len(set(pids)) == len(pids) and not (set(pids) & c.free)
+    c = window.SpecialWindowCache(1, 4, 1, 6, special=0, tokens_per_frame=16)
+    p = window.WindowCache(1, 4, 1, 6)
+    for t in range(12):
+        c.append(t), c.evict(), p.append(t), p.evict()
+        assert [(a, b) for a, b, _ in c.page_table()] == list(zip(p.page_ids(), p.persisted()))
