@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--per-head", type=int, default=0,
                     help="diversity workload: mean tokens kept per head and layer (default 128,512)")
     ap.add_argument("--tau", type=float, default=1.0, help="diversity workload: softmax temperature")
+    ap.add_argument("--special", type=int, default=0,
+                    help="stream / long workloads: special tokens per frame kept across evictions (0 = off)")
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
     ap.add_argument("--merge", action="store_true", help="budget workload: merge ragged pages after each compaction")
     ap.add_argument("--heads", type=int, default=0,
@@ -246,8 +248,11 @@ def run_long(args):
     w = synth.WORKLOADS[2]
     T, H, D, S, Wf, k = w["tokens"], w["heads"], w["head_dim"], w["scale_frames"], w["window"], w["keyframe_interval"]
     F = args.frames or w["frames"]
+    sp = args.special
+    special_pages = (F * sp + (T // max(sp, 1)) * max(sp, 1) - 1) // ((T // max(sp, 1)) * max(sp, 1)) + 1 if sp else 0
     cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
-                         keyframe_interval=k, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=16)
+                         keyframe_interval=k, pages_per_layer=S + Wf + 1 + special_pages, max_queries=S * T,
+                         max_splits=16, special_tokens=sp)
     cache = kv.KVCache(cfg, device=dev)
     ar = synth.AR1Stream(2, 0, (T, H, D), device=dev)
     ring = [ar.next() for _ in range(64)]
@@ -278,10 +283,11 @@ def run_long(args):
         "metric": "frames/sec sustained over the keyframe-interval-4 stream (append+evict+attend, 1 layer)",
         "value": F / (ms / 1e3), "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "frames": F,
         "ms_per_frame": ms / F, "dtype": "bf16", "data": "synthetic (ring of 64 seeded AR(1) frames, bf16)",
-        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_"), "tokens_per_frame": T, "heads": H,
-                   "head_dim": D, "scale_frames": S,
-                   "sliding_window": Wf, "keyframe_interval": k},
-        "final_persisted_frames": info["persisted_frames"], "wall_s": wall}), flush=True)
+        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_") + (f"_sp{sp}" if sp else ""),
+                   "tokens_per_frame": T, "heads": H, "head_dim": D, "scale_frames": S,
+                   "sliding_window": Wf, "keyframe_interval": k, "special_tokens": sp},
+        "final_persisted_frames": info["persisted_frames"], "final_special_tokens": info["special_tokens"],
+        "wall_s": wall}), flush=True)
 
 
 def run_budget(args):
@@ -531,8 +537,10 @@ def main():
     w = synth.WORKLOADS[1]
     T, H, D = w["tokens"], args.heads or w["heads"], w["head_dim"]
     S, Wf = w["scale_frames"], w["window"]
+    sp = args.special
     cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=Wf,
-                         keyframe_interval=1, pages_per_layer=S + Wf + 1, max_queries=S * T, max_splits=64)
+                         keyframe_interval=1, pages_per_layer=S + Wf + 1 + (8 if sp else 0), max_queries=S * T,
+                         max_splits=64, special_tokens=sp)
     cache = kv.KVCache(cfg, device=dev)
     if args.splits:
         cache.set_splits(args.splits)
@@ -586,12 +594,14 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     info = cache.info(0)
-    assert info["persisted_frames"] == S + Wf and info["tokens"] == (S + Wf) * T
+    assert info["persisted_frames"] == S + Wf and info["tokens"] == (S + Wf) * T + info["special_tokens"]
 
     attend_ms = [a.elapsed_time(b) for a, b in ev]
     attend_avg_s = sum(attend_ms) / len(attend_ms) / 1e3
     attend_sorted = sorted(attend_ms)
-    n_keys = (S + Wf) * T
+    # every timed step evicts one frame (keyframe interval 1), so the special tokens attended grow by `sp`
+    # per step: the mean over the timed steps is the last count less sp * (steps - 1) / 2
+    n_keys = (S + Wf) * T + info["special_tokens"] - sp * (args.steps - 1) / 2.0
     flops = 4.0 * H * D * T * n_keys
     achieved = flops / attend_avg_s / 1e12
 
@@ -615,13 +625,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded AR(1) frame-correlated Q/K/V, bf16)",
-        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_"), "tokens_per_frame": T, "heads": H,
-                   "head_dim": D,
+        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_") + (f"_sp{sp}" if sp else ""),
+                   "tokens_per_frame": T, "heads": H, "head_dim": D, "special_tokens": sp,
                    "cache_frames": S + Wf, "cached_tokens": n_keys, "scale_frames": S, "sliding_window": Wf,
                    "keyframe_interval": 1, "step": "append+evict+attend", "layers": 1,
                    "stream_frames": total},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(H, args.splits),
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None if sp else recorded_traffic(H, args.splits),
                      "kernel": "stream_attend (attend_bf16_kernel + split-KV combine)",
                      "avg_call_us": attend_avg_s * 1e6, "flop_per_call": flops,
                      "median_call_us": attend_sorted[len(attend_sorted) // 2] * 1e3,

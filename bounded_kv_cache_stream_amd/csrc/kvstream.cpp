@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -78,6 +79,8 @@ kv_status validate(const kv_pool_config* c) {
   if (c->max_queries < 1) return fail(KV_ERR_ARG, "max_queries must be >= 1");
   if (c->max_splits < 1 || c->max_splits > 64) return fail(KV_ERR_ARG, "max_splits must be 1..64");
   if (c->max_window < 1 || c->max_window > 8) return fail(KV_ERR_ARG, "max_window must be 1..8");
+  if (c->special_tokens < 0 || c->special_tokens > c->page_tokens)
+    return fail(KV_ERR_ARG, "special_tokens %d out of 0..page_tokens", c->special_tokens);
   return KV_OK;
 }
 
@@ -396,7 +399,8 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   p->layers.resize((size_t)cfg->num_layers);
   p->scored_gen.assign((size_t)cfg->num_layers, -1);
   for (auto& l : p->layers)
-    l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens);
+    l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens,
+           cfg->special_tokens);
   *out = p;
   return ok();
 }
@@ -482,10 +486,45 @@ kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n
   return ok();
 }
 
-kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted) {
+kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
-  int32_t n = pool->layers[(size_t)layer].evict();
+  auto& L = pool->layers[(size_t)layer];
+  const kvs::LayerPolicy saved = L;
+  std::vector<kvs::MergeMove> mv;
+  const int32_t n = L.evict(&mv);
+  if (n < 0)
+    return fail(KV_ERR_NO_PAGES, "layer %d: no free page id for the special tokens of an evicted frame", layer);
+  if (!pool->meta_only && !mv.empty()) {
+    // special rows of the victims to the special pages; a copy whose
+    // destination is the source of an earlier copy in the same launch (a
+    // victim's freed id reused as a special page) starts a new launch, which
+    // the stream orders after it
+    const int64_t pb = pool->lay.geom.page_bytes;
+    kvs::MergeChunk c;
+    c.n = 0;
+    std::set<int32_t> sources;
+    hipError_t e = hipSuccess;
+    auto flush = [&]() {
+      if (c.n > 0 && e == hipSuccess) e = kvs::launch_merge(pool->lay.geom, pool->pool, c, static_cast<hipStream_t>(stream));
+      c.n = 0;
+      sources.clear();
+    };
+    for (const auto& m : mv) {
+      if (c.n == kvs::kMergeChunk || sources.count(m.dst)) flush();
+      c.item[c.n].src_offset = phys_page(pool, layer, m.src) * pb;
+      c.item[c.n].dst_offset = phys_page(pool, layer, m.dst) * pb;
+      c.item[c.n].dst_off = m.dst_off;
+      c.item[c.n].count = m.count;
+      ++c.n;
+      sources.insert(m.src);
+    }
+    flush();
+    if (e != hipSuccess) {
+      L = saved;
+      return hip_fail(e, "special-token copy launch");
+    }
+  }
   if (n_evicted) *n_evicted = n;
   return ok();
 }
@@ -775,7 +814,7 @@ kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) 
   if (s != KV_OK) return s;
   if (!out) return fail(KV_ERR_ARG, "out is NULL");
   const auto& L = pool->layers[(size_t)layer];
-  out->persisted_frames = (int32_t)L.table.size();
+  out->persisted_frames = (int32_t)L.table.size() - L.special_pages();
   out->pages_used = (int32_t)L.table.size();
   out->pages_free = (int32_t)L.free_ids.size();
   out->transient_pending = L.transient_pending ? 1 : 0;
@@ -786,6 +825,8 @@ kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out) 
   out->last_keep_count = L.last_keep;
   out->merges = L.merges;
   out->prunes = L.prunes;
+  out->special_pages = L.special_pages();
+  out->special_tokens = L.special_tokens();
   return ok();
 }
 
@@ -799,7 +840,7 @@ kv_status kv_get_page_table(const kv_pool_t* pool, int32_t layer, int32_t* page_
   for (int32_t i = 0; i < n && i < cap; ++i) {
     if (page_ids) page_ids[i] = L.table[(size_t)i].page;
     if (page_lens) page_lens[i] = L.table[(size_t)i].len;
-    if (frame_ids) frame_ids[i] = L.table[(size_t)i].frame;
+    if (frame_ids) frame_ids[i] = L.table[(size_t)i].special ? -1 - L.table[(size_t)i].frame : L.table[(size_t)i].frame;
   }
   if (n_out) *n_out = n;
   return ok();

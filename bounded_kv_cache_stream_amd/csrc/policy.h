@@ -4,12 +4,17 @@
 //
 // Pages: GCTStream explainer ("KV Cache Lifecycle Management": skip-append of
 // non-keyframes; "Sliding Window Eviction": the oldest blocks go once the
-// cache is over the window); LingBot-Map 20 FPS explainer ("Sliding-Window
-// Eviction Strategy": the window counts frames, the first scale frames are
-// kept).  Readings: the window counts persisted non-scale frames; frame t is
-// a keyframe iff t < S or (t - S) % k == 0; page ids come from a per-layer
-// pool, lowest free id first; a frame's page is allocated before the
-// eviction of the same frame; freed ids are free at once.
+// cache is over the window; "Special Token Persistence": special tokens
+// survive the eviction of their frame); LingBot-Map 20 FPS explainer
+// ("Sliding-Window Eviction Strategy": the window counts frames, the first
+// scale frames are kept).  Readings: the window counts persisted non-scale
+// frames; frame t is a keyframe iff t < S or (t - S) % k == 0; page ids come
+// from a per-layer pool, lowest free id first; a frame's page is allocated
+// before the eviction of the same frame; freed ids are free at once.  Special
+// tokens are a frame's first slots; at each eviction (oldest victim first)
+// they go to the end of the last special page, a new one being taken (lowest
+// free id, the victim still holding its own) when they do not fit; special
+// pages sit after the scale frames and count as no frame of the window.
 #pragma once
 
 #include <stdint.h>
@@ -25,6 +30,7 @@ struct PageEntry {
   int32_t len;    // valid tokens in the page (the largest head length when heads differ)
   int64_t frame;  // frame index (of the first frame a merged page holds)
   std::vector<int32_t> hlen;  // per-head lengths once heads keep different tokens; empty: every head holds len
+  bool special = false;       // holds the special tokens of evicted frames (frame = the first of them)
 };
 
 inline int32_t head_len(const PageEntry& e, int h) { return e.hlen.empty() ? e.len : e.hlen[(size_t)h]; }
@@ -37,13 +43,14 @@ struct MergeMove {
 
 class LayerPolicy {
  public:
-  void init(int32_t pages, int32_t scale_frames, int32_t window, int32_t keyframe_interval,
-            int32_t page_tokens) {
+  void init(int32_t pages, int32_t scale_frames, int32_t window, int32_t keyframe_interval, int32_t page_tokens,
+            int32_t special_tokens) {
     pages_ = pages;
     S_ = scale_frames;
     W_ = window;
     k_ = keyframe_interval;
     T_ = page_tokens;
+    SP_ = special_tokens;
     reset();
   }
 
@@ -85,36 +92,78 @@ class LayerPolicy {
       return;
     }
     free_ids.erase(page);
-    table.push_back(PageEntry{page, T_, t, {}});
+    table.push_back(PageEntry{page, T_, t, {}, false});
     ++gen;
   }
 
-  int32_t evict() {
+  bool is_window_frame(const PageEntry& e) const { return e.frame >= S_ && !e.special; }
+
+  // Window eviction.  With special tokens on, each victim's first SP_ rows go
+  // to the last special page (the copies are returned for the device); a
+  // special page that cannot be had leaves everything unchanged and returns
+  // -1.  Otherwise returns the number of frames evicted.
+  int32_t evict(std::vector<MergeMove>* copies) {
     if (W_ <= 0) return 0;
+    std::vector<PageEntry> tab = table;
+    std::set<int32_t> free_set = free_ids;
+    std::vector<MergeMove> mv;
     int32_t n = 0;
     for (;;) {
       int32_t nonscale = 0;
-      for (const auto& e : table)
-        if (e.frame >= S_) ++nonscale;
+      for (const auto& e : tab)
+        if (is_window_frame(e)) ++nonscale;
       if (nonscale <= W_) break;
-      for (size_t i = 0; i < table.size(); ++i) {
-        if (table[i].frame >= S_) {
-          free_ids.insert(table[i].page);
-          table.erase(table.begin() + (long)i);
-          break;
+      size_t idx = 0;
+      while (!is_window_frame(tab[idx])) ++idx;
+      const PageEntry victim = tab[idx];
+      if (SP_ > 0) {
+        // the special block follows the scale frames
+        size_t end = 0;
+        while (end < tab.size() && !is_window_frame(tab[end])) ++end;
+        size_t last = end;
+        for (size_t i = 0; i < end; ++i)
+          if (tab[i].special) last = i;
+        if (last == end || tab[last].len + SP_ > T_) {
+          if (free_set.empty()) return -1;
+          const int32_t id = *free_set.begin();
+          free_set.erase(free_set.begin());
+          tab.insert(tab.begin() + (long)end, PageEntry{id, 0, victim.frame, {}, true});
+          last = end;
+          ++idx;
         }
+        mv.push_back(MergeMove{victim.page, tab[last].page, tab[last].len, SP_});
+        tab[last].len += SP_;
       }
+      free_set.insert(victim.page);
+      tab.erase(tab.begin() + (long)idx);
       ++n;
     }
+    table.swap(tab);
+    free_ids.swap(free_set);
     evictions += n;
     if (n) ++gen;
+    if (copies) *copies = mv;
     return n;
   }
 
-  // Index of the first table entry that is not a scale frame.
+  int32_t special_pages() const {
+    int32_t n = 0;
+    for (const auto& e : table) n += e.special;
+    return n;
+  }
+
+  int64_t special_tokens() const {
+    int64_t n = 0;
+    for (const auto& e : table)
+      if (e.special) n += e.len;
+    return n;
+  }
+
+  // Index of the first table entry that is neither a scale frame nor a
+  // special page (those lead the table).
   size_t first_candidate() const {
     size_t i = 0;
-    while (i < table.size() && table[i].frame < S_) ++i;
+    while (i < table.size() && !is_window_frame(table[i])) ++i;
     return i;
   }
 
@@ -244,7 +293,7 @@ class LayerPolicy {
   int64_t gen = 0;  // changes whenever the table does (never reset, so a stale copy never matches)
 
  private:
-  int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0;
+  int32_t pages_ = 0, S_ = 0, W_ = 0, k_ = 1, T_ = 0, SP_ = 0;
 };
 
 }  // namespace kvs

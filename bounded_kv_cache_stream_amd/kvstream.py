@@ -29,7 +29,7 @@ EXPORTED = (
 class kv_pool_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_layers", "num_heads", "head_dim", "page_tokens", "dtype", "scale_frames", "sliding_window",
-        "keyframe_interval", "pages_per_layer", "max_queries", "max_splits", "max_window")]
+        "keyframe_interval", "pages_per_layer", "max_queries", "max_splits", "max_window", "special_tokens")]
 
 
 class kv_clces_params(ctypes.Structure):
@@ -42,7 +42,7 @@ class kv_cache_info(ctypes.Structure):
                 ("pages_free", ctypes.c_int32), ("transient_pending", ctypes.c_int32),
                 ("tokens", ctypes.c_int64), ("bytes", ctypes.c_int64), ("evictions", ctypes.c_int64),
                 ("compactions", ctypes.c_int64), ("last_keep_count", ctypes.c_int64), ("merges", ctypes.c_int64),
-                ("prunes", ctypes.c_int64)]
+                ("prunes", ctypes.c_int64), ("special_pages", ctypes.c_int64), ("special_tokens", ctypes.c_int64)]
 
 
 class kv_pool_layout(ctypes.Structure):
@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
             "kv_reset": [P],
             "kv_append_frame": [P, I32, I64, P, P, I32, U32, P],
             "kv_append_frame_layers": [P, I32, I32, I64, P, P, I32, U32, P],
-            "kv_evict": [P, I32, ctypes.POINTER(I32)],
+            "kv_evict": [P, I32, ctypes.POINTER(I32), P],
             "stream_attend": [P, I32, P, I32, F32, P, P, P],
             "score_and_compact": [P, I32, P, I64, ctypes.POINTER(kv_clces_params), P, P, ctypes.POINTER(I64), P],
             "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
@@ -112,9 +112,9 @@ def _check(status: int) -> None:
 
 def make_config(num_layers=1, num_heads=16, head_dim=64, page_tokens=1004, dtype=KV_BF16, scale_frames=8,
                 sliding_window=64, keyframe_interval=1, pages_per_layer=73, max_queries=8032, max_splits=16,
-                max_window=5) -> kv_pool_config:
+                max_window=5, special_tokens=0) -> kv_pool_config:
     return kv_pool_config(num_layers, num_heads, head_dim, page_tokens, dtype, scale_frames, sliding_window,
-                          keyframe_interval, pages_per_layer, max_queries, max_splits, max_window)
+                          keyframe_interval, pages_per_layer, max_queries, max_splits, max_window, special_tokens)
 
 
 def kv_pool_required_bytes(cfg: kv_pool_config) -> tuple[int, int]:
@@ -153,9 +153,9 @@ def kv_append_frame_layers(pool, first_layer, n_layers, frame_idx, k_ptr, v_ptr,
                                         stream))
 
 
-def kv_evict(pool, layer) -> int:
+def kv_evict(pool, layer, stream=None) -> int:
     n = ctypes.c_int32()
-    _check(lib().kv_evict(pool, layer, ctypes.byref(n)))
+    _check(lib().kv_evict(pool, layer, ctypes.byref(n), stream))
     return n.value
 
 
@@ -316,7 +316,7 @@ class KVCache:
                                ctypes.c_void_p(v.data_ptr()), k.shape[1], flags, self._stream())
 
     def evict(self, layer) -> int:
-        return kv_evict(self.handle, layer)
+        return kv_evict(self.handle, layer, self._stream())
 
     def attend(self, layer, q, sm_scale, out=None, lse=None):
         torch = self.torch

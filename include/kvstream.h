@@ -68,6 +68,9 @@ typedef struct {
   int32_t max_queries;       /* largest n_q of stream_attend, >= 1                 */
   int32_t max_splits;        /* split-KV partitions of one attention call, 1..64   */
   int32_t max_window;        /* largest CLCES layer window, 1..8                   */
+  int32_t special_tokens;    /* 0 = off; else the first special_tokens slots of    */
+                             /* every frame survive its window eviction ([GCT]     */
+                             /* "Special Token Persistence"), 0..page_tokens       */
 } kv_pool_config;
 
 /* Parameters of one CLCES step ([SCV] 2.1.1-2.1.3): window W = 5 layers,
@@ -81,8 +84,8 @@ typedef struct {
 
 /* Cache statistics ([GCT] "Cache Monitoring", get_kv_cache_info()). */
 typedef struct {
-  int32_t persisted_frames; /* pages in the layer's table                         */
-  int32_t pages_used;       /* = persisted_frames                                 */
+  int32_t persisted_frames; /* frames in the layer's table                        */
+  int32_t pages_used;       /* = persisted_frames + special_pages                 */
   int32_t pages_free;
   int32_t transient_pending;/* 1 if a transient frame waits for stream_attend     */
   int64_t tokens;           /* sum of page lengths (a page's longest head)        */
@@ -92,6 +95,8 @@ typedef struct {
   int64_t last_keep_count;  /* tokens kept by the last such step                  */
   int64_t merges;           /* pages released by kv_merge_pages                   */
   int64_t prunes;           /* kv_diversity_prune steps that dropped tokens       */
+  int64_t special_pages;    /* pages holding special tokens of evicted frames     */
+  int64_t special_tokens;   /* special tokens held (included in tokens)           */
 } kv_cache_info;
 
 /* Device memory layout of the pool, for callers that read pages directly.
@@ -160,8 +165,17 @@ kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n
  * "Sliding-Window Eviction Strategy", _apply_kv_cache_eviction_causal):
  * while the layer holds more than sliding_window persisted non-scale frames,
  * release the oldest one (whole page).  Scale frames are never evicted.
- * Host metadata only, no device work.  n_evicted may be NULL. */
-kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted);
+ * With special_tokens > 0 ([GCT] "Special Token Persistence"), the first
+ * special_tokens rows of the victim (K and V of every head, and their ids)
+ * are first appended to the layer's last special page; a new special page
+ * (lowest free id, taken while the victim still holds its own) opens when
+ * they do not fit in page_tokens slots.  Special pages follow the scale
+ * frames in the table, are attended like any page, and are never evicted,
+ * scored, pruned or merged.  Without special tokens this is host metadata
+ * only; with them the copies are enqueued on `stream`.  KV_ERR_NO_PAGES
+ * (nothing changes) if a special page is needed and no id is free.
+ * n_evicted may be NULL. */
+kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* stream);
 
 /* Frame-to-cache attention ([GCT] "Frame-by-Frame Causal Processing" and
  * "Scale-Frame Phase"): for each query row i and head h,
@@ -291,7 +305,8 @@ kv_status kv_get_info(const kv_pool_t* pool, int32_t layer, kv_cache_info* out);
 
 /* The layer's persisted table in logical order: page ids (layer-local),
  * lengths and frame indices, cap entries at most; *n_out = table size (may
- * exceed cap).  Any output pointer may be NULL. */
+ * exceed cap).  A special page reports -1 - f, f the first frame whose special
+ * tokens it holds.  Any output pointer may be NULL. */
 kv_status kv_get_page_table(const kv_pool_t* pool, int32_t layer, int32_t* page_ids,
                             int32_t* page_lens, int64_t* frame_ids, int32_t cap, int32_t* n_out);
 

@@ -277,3 +277,57 @@ def test_two_head_shard_many_splits():
         ma, rl = assert_close(to64(out), ref, bf16=True, what=f"2-head shard, splits {splits or 'auto'}")
         assert max_abs(to64(lse).reshape(ref_lse.shape), ref_lse) <= LSE_ABS
         say(f"2-head shard (splits {splits or 'auto'}): max_abs {ma:.2e} rel_l2 {rl:.2e}")
+
+
+@pytest.mark.parametrize("dname,T,sp,k", [("bf16", 40, 5, 2), ("fp32", 20, 3, 1)])
+def test_special_tokens_stream_every_frame(dname, T, sp, k):
+    # window eviction with cross-frame special-token persistence: every frame
+    # the page table matches the oracle, attention covers scale frames +
+    # special tokens of every evicted frame + window + transient, and the
+    # special pages hold the evicted frames' first rows bit-exactly
+    torch = torch_cuda()
+    S, W, H, F = 2, 4, 4, 40
+    per_page = (T // sp) * sp
+    pages = S + W + 1 + (F * sp) // per_page + 2
+    dt = torch.bfloat16 if dname == "bf16" else torch.float32
+    cfg = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, dtype=kv.KV_BF16 if dname == "bf16" else kv.KV_FP32,
+                         scale_frames=S, sliding_window=W, keyframe_interval=k, pages_per_layer=pages,
+                         max_queries=S * T, max_splits=8, special_tokens=sp)
+    cache = kv.KVCache(cfg, device="cuda")
+    sim = window.SpecialWindowCache(S, W, k, pages, special=sp, tokens_per_frame=T)
+    host = {}
+    pending = []
+    for t in range(F):
+        q, kk, v = synth.iid_frame(103, 0, t, (T, H, 64), device="cuda", dtype=dt)
+        host[t] = (kk.cpu(), v.cpu())
+        cache.append(0, t, kk, v)
+        sim.append(t)
+        assert cache.evict(0) == sim.evict()
+        ids, lens, fr = cache.page_table(0)
+        assert list(zip(ids, fr, lens)) == sim.page_table(), t
+        if t < S - 1:
+            pending.append(q)
+            continue
+        if t == S - 1:
+            q = torch.cat(pending + [q])
+            pending = []
+        toks = np.array(sim.attended_tokens())
+        out = cache.attend(0, q.contiguous(), 0.125)
+        K = attention.gather_tokens(lambda f: host[f][0].double().numpy(), toks, T)
+        V = attention.gather_tokens(lambda f: host[f][1].double().numpy(), toks, T)
+        ref, _ = attention.attend(to64(q), K, V, 0.125)
+        assert_close(to64(out), ref, bf16=dname == "bf16", what=f"{dname} frame {t}")
+    assert len(sim.special_pages) >= 2
+    bits = torch.int16 if dname == "bf16" else torch.int32
+    for pid, toks in sim.special_pages:
+        k_pg, v_pg, id_pg = cache.page_view(0, pid)
+        n = len(toks)
+        fr, sl = np.array(toks) // T, np.array(toks) % T
+        ek = torch.stack([host[int(a)][0][int(b)] for a, b in zip(fr, sl)]).permute(1, 0, 2).contiguous()
+        ev = torch.stack([host[int(a)][1][int(b)] for a, b in zip(fr, sl)]).permute(1, 0, 2).contiguous()
+        assert torch.equal(k_pg[:, :n].cpu().view(bits), ek.view(bits)), f"K of special page {pid}"
+        assert torch.equal(v_pg[:, :n].cpu().view(bits), ev.view(bits)), f"V of special page {pid}"
+        assert id_pg[:n].cpu().numpy().tolist() == list(toks)
+    info = cache.info(0)
+    assert info["special_tokens"] == sum(len(x) for _, x in sim.special_pages)
+    say(f"{dname}: {len(sim.special_pages)} special pages, {info['special_tokens']} special tokens attended")

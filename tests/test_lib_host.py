@@ -276,3 +276,51 @@ def test_diversity_host_rules():
         with pytest.raises(kv.KVError) as e:
             call()
         assert e.value.status == kv.KV_ERR_ARG
+
+
+@pytest.mark.parametrize("S,W,k,T,sp,frames", [(1, 2, 1, 4, 1, 8), (8, 64, 4, 1004, 5, 3000), (0, 3, 2, 16, 5, 200),
+                                             (2, 5, 1, 12, 12, 60), (1, 4, 3, 10, 3, 400)])
+def test_special_tokens_page_tables_match_oracle(S, W, k, T, sp, frames):
+    # window eviction with special-token persistence through the C ABI, frame
+    # by frame: page ids, frame ids (-1 - f for a special page), lengths,
+    # free count and the special counters equal the oracle's
+    n_special = (frames * sp + (T // sp) * sp - 1) // ((T // sp) * sp) + 1
+    pages = S + W + 1 + n_special
+    cfg = kv.make_config(num_layers=1, num_heads=2, page_tokens=T, dtype=kv.KV_FP32, scale_frames=S,
+                         sliding_window=W, keyframe_interval=k, pages_per_layer=pages, max_queries=64,
+                         special_tokens=sp)
+    c = kv.KVCache(cfg, device=None)
+    sim = window.SpecialWindowCache(S, W, k, pages, special=sp, tokens_per_frame=T)
+    for t in range(frames):
+        if not window.is_keyframe(t, S, k):
+            continue  # a metadata-only pool cannot consume a transient frame (no attention)
+        c.append(0, t)
+        sim.append(t)
+        assert c.evict(0) == sim.evict()
+        ids, lens, fr = c.page_table(0)
+        assert list(zip(ids, fr, lens)) == sim.page_table(), t
+        info = c.info(0)
+        assert info["special_pages"] == len(sim.special_pages)
+        assert info["special_tokens"] == sum(len(x) for _, x in sim.special_pages)
+        assert info["pages_free"] == len(sim.free)
+        assert info["persisted_frames"] == len(sim.table)
+    assert len(sim.special_pages) > 0
+
+
+def test_special_tokens_need_a_free_page():
+    # no id left for a special page: the eviction fails and nothing changes
+    cfg = kv.make_config(num_layers=1, num_heads=2, page_tokens=4, dtype=kv.KV_FP32, scale_frames=1,
+                         sliding_window=2, keyframe_interval=1, pages_per_layer=4, max_queries=8, special_tokens=1)
+    c = kv.KVCache(cfg, device=None)
+    for t in range(3):
+        c.append(0, t)
+        c.evict(0)
+    c.append(0, 3)
+    before = c.page_table(0)
+    with pytest.raises(kv.KVError) as e:
+        c.evict(0)
+    assert e.value.status == kv.KV_ERR_NO_PAGES
+    assert c.page_table(0) == before
+    for bad in (-1, 5):
+        with pytest.raises(kv.KVError):
+            kv.KVCache(kv.make_config(page_tokens=4, special_tokens=bad), device=None)
