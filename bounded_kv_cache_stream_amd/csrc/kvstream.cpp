@@ -288,6 +288,9 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   const int32_t H = pool->cfg.num_heads;
   for (int32_t i = 0; i < n; ++i)
     if (keep[i] < 0) return fail(KV_ERR_ARG, "keep_per_head[%d] must be >= 0", i);
+  if (pool->cfg.special_tokens > 0)
+    return fail(KV_ERR_STATE, "a prune would move the special tokens out of a frame's first slots "
+                              "(special_tokens > 0)");
   std::vector<DivPlan> plans((size_t)n);
   std::vector<int32_t> layers;
   std::vector<const DivPlan*> pl;
@@ -647,6 +650,9 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
   auto& L = pool->layers[(size_t)layer];
   if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
+  if (pool->cfg.special_tokens > 0)
+    return fail(KV_ERR_STATE, "compaction would move the special tokens out of a frame's first slots "
+                              "(special_tokens > 0)");
   const size_t first = L.first_candidate();
   int64_t N = 0;
   for (size_t i = first; i < L.table.size(); ++i) N += L.table[i].len;

@@ -210,7 +210,9 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
  * candidate order (table order, then slot order before compaction).
  * ranks_out_dev: optional int32 [n_window][N], oldest window layer first.
  * n_kept: optional host int64.  KV_ERR_STATE on a layer that
- * kv_diversity_prune has pruned (its heads hold different tokens).
+ * kv_diversity_prune has pruned (its heads hold different tokens), and on a
+ * pool with special_tokens > 0 (compaction would move the special tokens out
+ * of a frame's first slots).
  * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
  * for a token id >= score_rows or a bad parameter.  Synchronises the stream
  * once to read the new page lengths. */
@@ -280,6 +282,7 @@ kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, doubl
  * everything; if every head does, nothing happens.  Afterwards heads hold
  * different tokens: stream_attend follows each head's rows, and
  * score_and_compact and kv_merge_pages refuse the layer (KV_ERR_STATE).
+ * KV_ERR_STATE on a pool with special_tokens > 0 (as for score_and_compact).
  * scores_dev / score_stride as for kv_diversity_score.  kept_per_head:
  * optional host int64 [H] = min(keep_per_head, N_h).  KV_ERR_NAN (state
  * unchanged) if a candidate key is not finite.  Synchronises the stream. */

@@ -324,3 +324,9 @@ def test_special_tokens_need_a_free_page():
     for bad in (-1, 5):
         with pytest.raises(kv.KVError):
             kv.KVCache(kv.make_config(page_tokens=4, special_tokens=bad), device=None)
+    # compaction and pruning would move the special tokens out of the first
+    # slots: a pool with special tokens refuses both
+    for call in (lambda: kv.score_and_compact(c.handle, 0, None, 1, 5, 0.5, 1), lambda: c.diversity_prune(0, 1)):
+        with pytest.raises(kv.KVError) as e:
+            call()
+        assert e.value.status == kv.KV_ERR_STATE
