@@ -12,7 +12,7 @@ namespace kvs {
 constexpr int32_t kClcesErrNan = 1;    // a raw score is NaN or negative
 constexpr int32_t kClcesErrRow = 2;    // a token id is outside the score table
 constexpr int32_t kClcesErrCount = 4;  // a page's kept count disagrees with its planned length
-constexpr int32_t kRankTile = 2048;    // keys per radix-sort workgroup
+constexpr int32_t kRankTile = 512;     // keys per radix-sort workgroup
 constexpr int32_t kMaxPageTokensScored = 8192;
 
 // Byte offsets of the CLCES buffers inside its workspace region.
@@ -46,7 +46,8 @@ struct ClcesArgs {
 
 // Stable ascending rank of every key within each of `segments` segments of N
 // keys (keys_a: [segments][N], overwritten; ranks: [segments][N]), 4 LSD
-// passes of 8 bits; hist holds segments * ceil(N / kRankTile) * 256 counters.
+// passes of 8 bits; hist holds segments * (nblk + ceil(nblk / 16)) * 256
+// counters, nblk = ceil(N / kRankTile).
 hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
                                 uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s);
 

@@ -44,7 +44,7 @@ namespace kvs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = kRankTile / kThreads;  // 8
+constexpr int kItems = kRankTile / kThreads;  // 2
 
 struct SelState {
   unsigned long long prefix;
@@ -119,36 +119,72 @@ __global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* key
   hist[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];  // [window][block][digit]
 }
 
+// Digit offsets of one pass, written over the histogram ([segment][block]
+// [digit]): for block b and digit d, the keys of smaller digits in the whole
+// segment plus the keys of digit d in the blocks before b.  Blocks are taken
+// in chunks of kChunk so that the work spreads over many workgroups: one
+// kernel sums each chunk's column (thread = digit), the next turns the chunk
+// sums into each chunk's start and walks its kChunk blocks.
+constexpr int kChunk = 16;
+
+__global__ __launch_bounds__(kThreads) void rank_chunk_kernel(const uint32_t* hist, uint32_t* ctot, int nblk,
+                                                              int nchunk, const int32_t* flag) {
+  if (*flag) return;
+  const int c = blockIdx.x, w = blockIdx.y, d = threadIdx.x;
+  const uint32_t* col = hist + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + d;
+  const int nb = min(kChunk, nblk - c * kChunk);
+  uint32_t v[kChunk];
+#pragma unroll
+  for (int b = 0; b < kChunk; ++b) v[b] = b < nb ? col[(int64_t)b * 256] : 0u;
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 0; b < kChunk; ++b) t += v[b];
+  ctot[((int64_t)w * nchunk + c) * 256 + d] = t;
+}
+
+__global__ __launch_bounds__(kThreads) void rank_offsets_kernel(uint32_t* hist, const uint32_t* ctot, int nblk,
+                                                                int nchunk, const int32_t* flag) {
+  if (*flag) return;
+  __shared__ int32_t scan[kThreads];
+  const int c = blockIdx.x, w = blockIdx.y, d = threadIdx.x;
+  const uint32_t* ct = ctot + (int64_t)w * nchunk * 256 + d;
+  uint32_t tot = 0, before = 0;
+  for (int cc = 0; cc < nchunk; ++cc) {
+    const uint32_t x = ct[(int64_t)cc * 256];
+    tot += x;
+    before += cc < c ? x : 0u;
+  }
+  uint32_t run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
+  uint32_t* col = hist + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + d;
+  const int nb = min(kChunk, nblk - c * kChunk);
+  uint32_t v[kChunk];
+#pragma unroll
+  for (int b = 0; b < kChunk; ++b) v[b] = b < nb ? col[(int64_t)b * 256] : 0u;
+#pragma unroll
+  for (int b = 0; b < kChunk; ++b) {
+    if (b < nb) col[(int64_t)b * 256] = run;
+    run += v[b];
+  }
+}
+
 // One stable LSD pass over this block's kRankTile keys (kItems per thread;
 // key i = blk*kRankTile + j*kThreads + tid, so index order is (item j, wave,
 // lane)).  Every wave matches the digits of each of its items with ballots,
 // giving each key its rank among equal digits of its (item, wave) group and
 // each group's digit counts; one pass per digit then turns the counts into
 // exclusive offsets in index order, and every key goes to
-// base[digit] + offset[group][digit] + rank.  Four barriers in all.
+// offset[block][digit] + offset[group][digit] + rank.  Three barriers.
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
                                                                 uint32_t* keys_out, uint32_t* vals_out,
-                                                                int32_t* ranks, const uint32_t* hist, int N,
+                                                                int32_t* ranks, const uint32_t* offsets, int N,
                                                                 int nblk, int shift, int last, const int32_t* flag) {
   if (*flag) return;
   constexpr int kWaves = kThreads / 64;
   __shared__ uint32_t cnt[kItems][kWaves][256];
-  __shared__ int32_t scan[kThreads];
   const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  // offset of this block's digit-tid keys: keys of smaller digits in the whole
-  // segment, plus keys of digit tid in the blocks before this one
-  uint32_t run;
-  {
-    const uint32_t* hcol = hist + (int64_t)w * nblk * 256 + tid;
-    uint32_t tot = 0, before = 0;
-    for (int bb = 0; bb < nblk; ++bb) {
-      const uint32_t v = hcol[(int64_t)bb * 256];
-      tot += v;
-      before += bb < blk ? v : 0u;
-    }
-    run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
-  }
+  // where this block's keys of digit tid start in the segment
+  uint32_t run = offsets[((int64_t)w * nblk + blk) * 256 + tid];
 #pragma unroll
   for (int j = 0; j < kItems; ++j)
 #pragma unroll
@@ -502,7 +538,7 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.ranks = take(wn * 4);
   z.scur = take((size_t)n_max * 4);
   z.shat = take((size_t)n_max * 8);
-  z.hist = take((size_t)w_max * 256 * z.nblk_max * 4);
+  z.hist = take((size_t)w_max * 256 * (z.nblk_max + (z.nblk_max + kChunk - 1) / kChunk) * 4);  // + chunk sums
   z.sel_hist = take(8 * 256 * 4);
   z.sel_state = take(9 * sizeof(SelState));
   z.entries = take((size_t)p_max * sizeof(DevEntry));
@@ -519,6 +555,8 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
 hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
                                 uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s) {
   const int nblk = (N + kRankTile - 1) / kRankTile;
+  const int nchunk = (nblk + kChunk - 1) / kChunk;
+  uint32_t* ctot = hist + (int64_t)segments * nblk * 256;  // chunk sums after the histograms
   uint32_t* kin = keys_a;
   uint32_t* kout = keys_b;
   uint32_t* vin = nullptr;
@@ -527,6 +565,10 @@ hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* va
     const int shift = 8 * pass;
     rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift,
                                                                                           flag);
+    rank_chunk_kernel<<<dim3((unsigned)nchunk, (unsigned)segments), dim3(kThreads), 0, s>>>(hist, ctot, nblk, nchunk,
+                                                                                             flag);
+    rank_offsets_kernel<<<dim3((unsigned)nchunk, (unsigned)segments), dim3(kThreads), 0, s>>>(hist, ctot, nblk,
+                                                                                               nchunk, flag);
     rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(
         kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
     std::swap(kin, kout);
