@@ -46,10 +46,12 @@ struct ClcesArgs {
 
 // Stable ascending rank of every key within each of `segments` segments of N
 // keys (keys_a: [segments][N], overwritten; ranks: [segments][N]), 4 LSD
-// passes of 8 bits; hist holds segments * (nblk + ceil(nblk / 16)) * 256
-// counters, nblk = ceil(N / kRankTile).
+// passes of 8 bits.  counts holds rank_counters(N, segments) counters; its
+// first part (the chunk sums, which accumulate with atomics) is set to zero
+// beforehand by the caller's first kernel.
+int64_t rank_counters(int N, int segments);
 hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
-                                uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s);
+                                uint32_t* counts, int N, int segments, const int32_t* flag, hipStream_t s);
 
 // Enqueues the whole step, then waits for it and returns the new page
 // lengths (one per candidate entry) and the error flags.

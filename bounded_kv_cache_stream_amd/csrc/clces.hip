@@ -59,16 +59,41 @@ __device__ inline uint32_t order_key(float s) {
 }
 
 // First launch of a step: the first page-table chunk, and the counters that
-// later kernels accumulate into set to zero (select histograms, per-page
-// counts, the error flag).
-__global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* sel_hist, int32_t* counts, int n_counts,
-                            int32_t* flag) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// later kernels accumulate into set to zero (the rank chunk sums of every
+// pass, select histograms, per-page counts, the error flag).
+__global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* rank_counts, int64_t n_rank,
+                            uint32_t* sel_hist, int32_t* counts, int n_counts, int32_t* flag) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < chunk.count) entries[chunk.first + i] = chunk.e[i];
+  if (i < n_rank) rank_counts[i] = 0;
   if (i < 8 * 256) sel_hist[i] = 0;
   if (i < n_counts) counts[i] = 0;
   if (i == 0) *flag = 0;
 }
+
+constexpr int kChunk = 16;  // rank blocks per chunk of the digit-offset scan
+
+// Counts of one rank pass: [segment][block][digit] and the chunk sums
+// [segment][chunk][digit].  The chunk sums of all 4 passes come first in the
+// counter array (they accumulate with atomics, so only they are zeroed), then
+// the block counts of all 4 passes (stored outright).
+struct RankCounts {
+  uint32_t* blk;
+  uint32_t* chunk;
+  int nblk, nchunk;
+};
+
+__host__ __device__ inline int64_t rank_chunk_counters(int segments, int nblk) {
+  return 4 * (int64_t)segments * ((nblk + kChunk - 1) / kChunk) * 256;
+}
+
+__device__ inline RankCounts rank_counts(uint32_t* base, int pass, int segments, int nblk) {
+  const int nchunk = (nblk + kChunk - 1) / kChunk;
+  return RankCounts{base + rank_chunk_counters(segments, nblk) + (int64_t)pass * segments * nblk * 256,
+                    base + (int64_t)pass * segments * nchunk * 256, nblk, nchunk};
+}
+
+
 
 struct GatherArgs {
   const DevEntry* entries;
@@ -103,68 +128,27 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   g.scur[idx] = __uint_as_float(order_key(s));
 }
 
-__global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* hist, int N, int nblk,
-                                                             int shift, const int32_t* flag) {
+// Digit histogram of one block of one pass, counted in LDS (wave-aggregated:
+// the top bytes of similar scores are nearly uniform), stored as the block's
+// counts and added into its chunk's sums (at most kChunk workgroups add to
+// one counter).
+__global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* counts, int N, int nblk,
+                                                             int pass, const int32_t* flag) {
   if (*flag) return;
   __shared__ uint32_t cnt[256];
-  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x, segments = gridDim.y;
   cnt[tid] = 0;
   __syncthreads();
   const uint32_t* k = keys + (int64_t)w * N;
+  const int shift = 8 * pass;
   for (int j = 0; j < kItems; ++j) {
     const int i = blk * kRankTile + j * kThreads + tid;
     hist_add(cnt, i < N ? (k[i] >> shift) & 255u : 0u, i < N);
   }
   __syncthreads();
-  hist[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];  // [window][block][digit]
-}
-
-// Digit offsets of one pass, written over the histogram ([segment][block]
-// [digit]): for block b and digit d, the keys of smaller digits in the whole
-// segment plus the keys of digit d in the blocks before b.  Blocks are taken
-// in chunks of kChunk so that the work spreads over many workgroups: one
-// kernel sums each chunk's column (thread = digit), the next turns the chunk
-// sums into each chunk's start and walks its kChunk blocks.
-constexpr int kChunk = 16;
-
-__global__ __launch_bounds__(kThreads) void rank_chunk_kernel(const uint32_t* hist, uint32_t* ctot, int nblk,
-                                                              int nchunk, const int32_t* flag) {
-  if (*flag) return;
-  const int c = blockIdx.x, w = blockIdx.y, d = threadIdx.x;
-  const uint32_t* col = hist + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + d;
-  const int nb = min(kChunk, nblk - c * kChunk);
-  uint32_t v[kChunk];
-#pragma unroll
-  for (int b = 0; b < kChunk; ++b) v[b] = b < nb ? col[(int64_t)b * 256] : 0u;
-  uint32_t t = 0;
-#pragma unroll
-  for (int b = 0; b < kChunk; ++b) t += v[b];
-  ctot[((int64_t)w * nchunk + c) * 256 + d] = t;
-}
-
-__global__ __launch_bounds__(kThreads) void rank_offsets_kernel(uint32_t* hist, const uint32_t* ctot, int nblk,
-                                                                int nchunk, const int32_t* flag) {
-  if (*flag) return;
-  __shared__ int32_t scan[kThreads];
-  const int c = blockIdx.x, w = blockIdx.y, d = threadIdx.x;
-  const uint32_t* ct = ctot + (int64_t)w * nchunk * 256 + d;
-  uint32_t tot = 0, before = 0;
-  for (int cc = 0; cc < nchunk; ++cc) {
-    const uint32_t x = ct[(int64_t)cc * 256];
-    tot += x;
-    before += cc < c ? x : 0u;
-  }
-  uint32_t run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
-  uint32_t* col = hist + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + d;
-  const int nb = min(kChunk, nblk - c * kChunk);
-  uint32_t v[kChunk];
-#pragma unroll
-  for (int b = 0; b < kChunk; ++b) v[b] = b < nb ? col[(int64_t)b * 256] : 0u;
-#pragma unroll
-  for (int b = 0; b < kChunk; ++b) {
-    if (b < nb) col[(int64_t)b * 256] = run;
-    run += v[b];
-  }
+  const RankCounts rc = rank_counts(counts, pass, segments, nblk);
+  rc.blk[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];
+  if (cnt[tid]) atomicAdd(&rc.chunk[((int64_t)w * rc.nchunk + blk / kChunk) * 256 + tid], cnt[tid]);
 }
 
 // One stable LSD pass over this block's kRankTile keys (kItems per thread;
@@ -173,18 +157,37 @@ __global__ __launch_bounds__(kThreads) void rank_offsets_kernel(uint32_t* hist, 
 // giving each key its rank among equal digits of its (item, wave) group and
 // each group's digit counts; one pass per digit then turns the counts into
 // exclusive offsets in index order, and every key goes to
-// offset[block][digit] + offset[group][digit] + rank.  Three barriers.
+// offset[block][digit] + offset[group][digit] + rank.
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
                                                                 uint32_t* keys_out, uint32_t* vals_out,
-                                                                int32_t* ranks, const uint32_t* offsets, int N,
-                                                                int nblk, int shift, int last, const int32_t* flag) {
+                                                                int32_t* ranks, uint32_t* counts, int N,
+                                                                int nblk, int pass, const int32_t* flag) {
   if (*flag) return;
   constexpr int kWaves = kThreads / 64;
   __shared__ uint32_t cnt[kItems][kWaves][256];
   const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  // where this block's keys of digit tid start in the segment
-  uint32_t run = offsets[((int64_t)w * nblk + blk) * 256 + tid];
+  const int segments = gridDim.y, shift = 8 * pass, last = pass == 3;
+  __shared__ int32_t scan[kThreads];
+  // where this block's keys of digit tid start in the segment: keys of smaller
+  // digits in the whole segment (the chunk sums added over chunks, scanned
+  // over digits), plus keys of digit tid in the chunks before this block's
+  // chunk and in the blocks before it within its chunk
+  uint32_t run;
+  {
+    const RankCounts rc = rank_counts(counts, pass, segments, nblk);
+    const int c = blk / kChunk;
+    const uint32_t* ct = rc.chunk + (int64_t)w * rc.nchunk * 256 + tid;
+    uint32_t tot = 0, before = 0;
+    for (int cc = 0; cc < rc.nchunk; ++cc) {
+      const uint32_t x = ct[(int64_t)cc * 256];
+      tot += x;
+      before += cc < c ? x : 0u;
+    }
+    const uint32_t* col = rc.blk + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + tid;
+    for (int b = c * kChunk; b < blk; ++b) before += col[(int64_t)(b - c * kChunk) * 256];
+    run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
+  }
 #pragma unroll
   for (int j = 0; j < kItems; ++j)
 #pragma unroll
@@ -538,7 +541,7 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.ranks = take(wn * 4);
   z.scur = take((size_t)n_max * 4);
   z.shat = take((size_t)n_max * 8);
-  z.hist = take((size_t)w_max * 256 * (z.nblk_max + (z.nblk_max + kChunk - 1) / kChunk) * 4);  // + chunk sums
+  z.hist = take((size_t)rank_counters((int)n_max, w_max) * 4);  // rank counts of the 4 passes
   z.sel_hist = take(8 * 256 * 4);
   z.sel_state = take(9 * sizeof(SelState));
   z.entries = take((size_t)p_max * sizeof(DevEntry));
@@ -552,25 +555,23 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   return z;
 }
 
-hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
-                                uint32_t* hist, int N, int segments, const int32_t* flag, hipStream_t s) {
+int64_t rank_counters(int N, int segments) {
   const int nblk = (N + kRankTile - 1) / kRankTile;
-  const int nchunk = (nblk + kChunk - 1) / kChunk;
-  uint32_t* ctot = hist + (int64_t)segments * nblk * 256;  // chunk sums after the histograms
+  return rank_chunk_counters(segments, nblk) + 4 * (int64_t)segments * nblk * 256;
+}
+
+hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
+                                uint32_t* counts, int N, int segments, const int32_t* flag, hipStream_t s) {
+  const int nblk = (N + kRankTile - 1) / kRankTile;
   uint32_t* kin = keys_a;
   uint32_t* kout = keys_b;
   uint32_t* vin = nullptr;
   uint32_t* vout = vals_b;
   for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(kin, hist, N, nblk, shift,
+    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(kin, counts, N, nblk, pass,
                                                                                           flag);
-    rank_chunk_kernel<<<dim3((unsigned)nchunk, (unsigned)segments), dim3(kThreads), 0, s>>>(hist, ctot, nblk, nchunk,
-                                                                                             flag);
-    rank_offsets_kernel<<<dim3((unsigned)nchunk, (unsigned)segments), dim3(kThreads), 0, s>>>(hist, ctot, nblk,
-                                                                                               nchunk, flag);
     rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(
-        kin, vin, kout, vout, ranks, hist, N, nblk, shift, pass == 3, flag);
+        kin, vin, kout, vout, ranks, counts, N, nblk, pass, flag);
     std::swap(kin, kout);
     vin = vout;
     vout = vout == vals_b ? vals_a : vals_b;
@@ -604,8 +605,10 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
     c.first = 0;
     c.count = std::min(P, kUploadChunk);
     for (int i = 0; i < c.count; ++i) c.e[i] = a.entries_host[i];
-    const int nz = std::max(8 * 256, 2 * P);
-    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, sel_hist, counts, 2 * P, flag);
+    const int64_t n_rank = rank_chunk_counters(W, (N + kRankTile - 1) / kRankTile);  // the chunk sums
+    const int64_t nz = std::max<int64_t>(std::max(8 * 256, 2 * P), n_rank);
+    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, hist, n_rank, sel_hist, counts,
+                                                                          2 * P, flag);
   }
   hipError_t e = P > kUploadChunk ? launch_table_upload(entries + kUploadChunk, a.entries_host + kUploadChunk,
                                                         P - kUploadChunk, s)
