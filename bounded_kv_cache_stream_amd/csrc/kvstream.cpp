@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <set>
 #include <string>
@@ -493,7 +494,10 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
   auto& L = pool->layers[(size_t)layer];
-  const kvs::LayerPolicy saved = L;
+  // the special-token copies are launched after the policy changed: keep the
+  // old state to restore if a launch fails (only then is there device work)
+  std::unique_ptr<kvs::LayerPolicy> saved;
+  if (pool->cfg.special_tokens > 0 && !pool->meta_only) saved.reset(new kvs::LayerPolicy(L));
   std::vector<kvs::MergeMove> mv;
   const int32_t n = L.evict(&mv);
   if (n < 0)
@@ -524,7 +528,7 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
     }
     flush();
     if (e != hipSuccess) {
-      L = saved;
+      L = *saved;
       return hip_fail(e, "special-token copy launch");
     }
   }

@@ -104,6 +104,24 @@ class LayerPolicy {
   // -1.  Otherwise returns the number of frames evicted.
   int32_t evict(std::vector<MergeMove>* copies) {
     if (W_ <= 0) return 0;
+    if (SP_ == 0) {  // no special tokens: whole pages go, nothing can fail, edit in place
+      int32_t n = 0;
+      for (;;) {
+        int32_t nonscale = 0;
+        for (const auto& e : table)
+          if (is_window_frame(e)) ++nonscale;
+        if (nonscale <= W_) break;
+        size_t idx = 0;
+        while (!is_window_frame(table[idx])) ++idx;
+        free_ids.insert(table[idx].page);
+        table.erase(table.begin() + (long)idx);
+        ++n;
+      }
+      evictions += n;
+      if (n) ++gen;
+      if (copies) copies->clear();
+      return n;
+    }
     std::vector<PageEntry> tab = table;
     std::set<int32_t> free_set = free_ids;
     std::vector<MergeMove> mv;

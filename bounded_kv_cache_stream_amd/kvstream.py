@@ -316,7 +316,8 @@ class KVCache:
                                ctypes.c_void_p(v.data_ptr()), k.shape[1], flags, self._stream())
 
     def evict(self, layer) -> int:
-        return kv_evict(self.handle, layer, self._stream())
+        # device work (and so a stream) only when special tokens persist
+        return kv_evict(self.handle, layer, self._stream() if self.cfg.special_tokens else None)
 
     def attend(self, layer, q, sm_scale, out=None, lse=None):
         torch = self.torch
