@@ -47,6 +47,11 @@ hipError_t launch_head_tables(DevEntry* out, const DevEntry* base, int n, const 
 hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
                          int64_t first_token_id, hipStream_t s);
 
+// launch_append and launch_table_upload(dst, src, n) in one launch (table
+// entries past the first kUploadChunk go in further upload launches).
+hipError_t launch_append_table(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
+                               int64_t first_token_id, DevEntry* dst, const DevEntry* src, int n, hipStream_t s);
+
 // Destination pages of one multi-layer append launch (byte offsets into the pool).
 constexpr int kAppendLayersChunk = 128;
 struct AppendLayers {

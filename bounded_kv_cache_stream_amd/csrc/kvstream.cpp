@@ -490,6 +490,39 @@ kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n
   return ok();
 }
 
+namespace {
+
+// Copies of the special rows of evicted frames into the special pages.  A
+// copy whose destination is the source of an earlier copy in the same launch
+// (a victim's freed id reused as a special page) starts a new launch, which
+// the stream orders after it.
+kv_status launch_special_copies(kv_pool_t* pool, int32_t layer, const std::vector<kvs::MergeMove>& mv,
+                                hipStream_t st) {
+  const int64_t pb = pool->lay.geom.page_bytes;
+  kvs::MergeChunk c;
+  c.n = 0;
+  std::set<int32_t> sources;
+  hipError_t e = hipSuccess;
+  auto flush = [&]() {
+    if (c.n > 0 && e == hipSuccess) e = kvs::launch_merge(pool->lay.geom, pool->pool, c, st);
+    c.n = 0;
+    sources.clear();
+  };
+  for (const auto& m : mv) {
+    if (c.n == kvs::kMergeChunk || sources.count(m.dst)) flush();
+    c.item[c.n].src_offset = phys_page(pool, layer, m.src) * pb;
+    c.item[c.n].dst_offset = phys_page(pool, layer, m.dst) * pb;
+    c.item[c.n].dst_off = m.dst_off;
+    c.item[c.n].count = m.count;
+    ++c.n;
+    sources.insert(m.src);
+  }
+  flush();
+  return e == hipSuccess ? KV_OK : hip_fail(e, "special-token copy launch");
+}
+
+}  // namespace
+
 kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
@@ -503,33 +536,10 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
   if (n < 0)
     return fail(KV_ERR_NO_PAGES, "layer %d: no free page id for the special tokens of an evicted frame", layer);
   if (!pool->meta_only && !mv.empty()) {
-    // special rows of the victims to the special pages; a copy whose
-    // destination is the source of an earlier copy in the same launch (a
-    // victim's freed id reused as a special page) starts a new launch, which
-    // the stream orders after it
-    const int64_t pb = pool->lay.geom.page_bytes;
-    kvs::MergeChunk c;
-    c.n = 0;
-    std::set<int32_t> sources;
-    hipError_t e = hipSuccess;
-    auto flush = [&]() {
-      if (c.n > 0 && e == hipSuccess) e = kvs::launch_merge(pool->lay.geom, pool->pool, c, static_cast<hipStream_t>(stream));
-      c.n = 0;
-      sources.clear();
-    };
-    for (const auto& m : mv) {
-      if (c.n == kvs::kMergeChunk || sources.count(m.dst)) flush();
-      c.item[c.n].src_offset = phys_page(pool, layer, m.src) * pb;
-      c.item[c.n].dst_offset = phys_page(pool, layer, m.dst) * pb;
-      c.item[c.n].dst_off = m.dst_off;
-      c.item[c.n].count = m.count;
-      ++c.n;
-      sources.insert(m.src);
-    }
-    flush();
-    if (e != hipSuccess) {
+    s = launch_special_copies(pool, layer, mv, static_cast<hipStream_t>(stream));
+    if (s != KV_OK) {
       L = *saved;
-      return hip_fail(e, "special-token copy launch");
+      return s;
     }
   }
   if (n_evicted) *n_evicted = n;
@@ -543,16 +553,32 @@ kv_status kv_set_attend_splits(kv_pool_t* pool, int32_t splits) {
   return ok();
 }
 
-kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q, float sm_scale,
-                        void* out_dev, float* lse_dev, void* stream) {
-  kv_status s = check_layer(pool, layer);
-  if (s != KV_OK) return s;
+namespace {
+
+kv_status check_attend_args(const kv_pool_t* pool, const void* q_dev, int32_t n_q, float sm_scale,
+                            const void* out_dev) {
   if (n_q < 1 || n_q > pool->cfg.max_queries)
     return fail(KV_ERR_SHAPE, "n_q %d out of 1..max_queries (%d)", n_q, pool->cfg.max_queries);
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_ERR_ARG, "sm_scale must be finite and > 0");
   if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
   if (!q_dev || !out_dev) return fail(KV_ERR_ARG, "q or out is NULL");
-  auto& L = pool->layers[(size_t)layer];
+  return KV_OK;
+}
+
+// A page write that rides in the table-upload launch of the attention.
+struct PageWrite {
+  const void* k;
+  const void* v;
+  char* page;
+  int64_t first_id;
+};
+
+// Uploads the table of L (the layer's policy, possibly a not yet committed
+// copy) and launches the attention over it; with `write`, the frame's page
+// write and the table upload are one launch, ordered before the attention.
+// Changes no host state.
+kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& L, const void* q_dev, int32_t n_q,
+                        float sm_scale, void* out_dev, float* lse_dev, hipStream_t st, const PageWrite* write) {
   auto& ent = pool->scratch;
   ent.clear();
   const int32_t H = pool->cfg.num_heads;
@@ -591,17 +617,17 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   }
   if (n_entries == 0 || min_tiles == 0) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
   kvs::DevEntry* dt = dev_table(pool, layer);
   hipError_t e;
-  if (per_head) {
-    kvs::DevEntry* base = dt + (int64_t)H * (pool->lay.layer_pages + 1);
-    e = kvs::launch_table_upload(base, ent.data(), n_entries, st);
-    if (e == hipSuccess) e = kvs::launch_head_tables(dt, base, n_entries, hlens_dev(pool), H, st);
-  } else {
-    e = kvs::launch_table_upload(dt, ent.data(), n_entries, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "table upload launch");
+  // per-head tables are built on the device from the shared one, uploaded after them
+  kvs::DevEntry* up = per_head ? dt + (int64_t)H * (pool->lay.layer_pages + 1) : dt;
+  if (write)
+    e = kvs::launch_append_table(pool->lay.geom, write->page, write->k, write->v, pool->cfg.page_tokens,
+                                 write->first_id, up, ent.data(), n_entries, st);
+  else
+    e = kvs::launch_table_upload(up, ent.data(), n_entries, st);
+  if (e == hipSuccess && per_head) e = kvs::launch_head_tables(dt, up, n_entries, hlens_dev(pool), H, st);
+  if (e != hipSuccess) return hip_fail(e, write ? "page write and table upload launch" : "table upload launch");
 
   const bool bf16 = pool->cfg.dtype == KV_BF16;
   int32_t splits = 1;
@@ -638,7 +664,67 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   ap.scale_log2 = sm_scale * 1.4426950408889634f;
   e = kvs::launch_attend(pool->lay.geom, ap, bf16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return KV_OK;
+}
+
+}  // namespace
+
+kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q, float sm_scale,
+                        void* out_dev, float* lse_dev, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  s = check_attend_args(pool, q_dev, n_q, sm_scale, out_dev);
+  if (s != KV_OK) return s;
+  auto& L = pool->layers[(size_t)layer];
+  s = attend_launch(pool, layer, L, q_dev, n_q, sm_scale, out_dev, lse_dev, static_cast<hipStream_t>(stream),
+                    nullptr);
+  if (s != KV_OK) return s;
   L.transient_pending = false;
+  return ok();
+}
+
+kv_status kv_append_attend(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev, const void* v_dev,
+                           int32_t n_tokens, uint32_t flags, const void* q_dev, int32_t n_q, float sm_scale,
+                           void* out_dev, float* lse_dev, int32_t* n_evicted, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  if (n_tokens != pool->cfg.page_tokens)
+    return fail(KV_ERR_SHAPE, "n_tokens %d != page_tokens %d", n_tokens, pool->cfg.page_tokens);
+  if (frame_idx < 0) return fail(KV_ERR_ARG, "negative frame index");
+  if (frame_idx > (int64_t)(INT32_MAX / pool->cfg.page_tokens) - 1)
+    return fail(KV_ERR_ARG, "frame index %lld too large for 32-bit token ids", (long long)frame_idx);
+  if (flags & ~KV_TRANSIENT) return fail(KV_ERR_ARG, "unknown flags 0x%x", flags);
+  s = check_attend_args(pool, q_dev, n_q, sm_scale, out_dev);
+  if (s != KV_OK) return s;
+  if (!k_dev || !v_dev) return fail(KV_ERR_ARG, "k or v is NULL");
+  auto& L = pool->layers[(size_t)layer];
+  int32_t page = 0;
+  int rc = L.plan_append(frame_idx, (flags & KV_TRANSIENT) != 0, &page);
+  if (rc == 1)
+    return fail(KV_ERR_STATE, "layer %d: frame %lld after frame %lld%s", layer, (long long)frame_idx,
+                (long long)L.last_frame, L.transient_pending ? " (a transient frame is still pending)" : "");
+  if (rc == 2) return fail(KV_ERR_NO_PAGES, "layer %d: all %d page ids in use", layer, pool->cfg.pages_per_layer);
+
+  // the append and the eviction act on a copy that replaces the layer's
+  // policy only once every launch is enqueued
+  kvs::LayerPolicy next = L;
+  next.commit_append(frame_idx, page);
+  std::vector<kvs::MergeMove> mv;
+  const int32_t n_ev = next.evict(&mv);
+  if (n_ev < 0)
+    return fail(KV_ERR_NO_PAGES, "layer %d: no free page id for the special tokens of an evicted frame", layer);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!mv.empty()) {
+    s = launch_special_copies(pool, layer, mv, st);
+    if (s != KV_OK) return s;
+  }
+  const PageWrite w{k_dev, v_dev, pool->pool + phys_page(pool, layer, page) * pool->lay.geom.page_bytes,
+                    frame_idx * pool->cfg.page_tokens};
+  s = attend_launch(pool, layer, next, q_dev, n_q, sm_scale, out_dev, lse_dev, st, &w);
+  if (s != KV_OK) return s;
+  next.transient_pending = false;
+  L = std::move(next);
+  if (n_evicted) *n_evicted = n_ev;
   return ok();
 }
 

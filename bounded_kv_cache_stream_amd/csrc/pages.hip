@@ -64,6 +64,20 @@ __global__ __launch_bounds__(256) void append_kernel(PageGeom g, char* page, con
   append_block<T>(g, page, k, v, n_tokens, first_id, blockIdx.y, blockIdx.x * 64);
 }
 
+// A frame's page write that also uploads (the first chunk of) a layer's
+// attention table: the block after the page's 64-token blocks copies it.
+template <typename T>
+__global__ __launch_bounds__(256) void append_table_kernel(PageGeom g, char* page, const T* __restrict__ k,
+                                                           const T* __restrict__ v, int n_tokens, int64_t first_id,
+                                                           DevEntry* dst, TableChunk chunk) {
+  if (blockIdx.x == gridDim.x - 1) {
+    const int i = threadIdx.x;
+    if (blockIdx.y == 0 && i < chunk.count) dst[chunk.first + i] = chunk.e[i];
+    return;
+  }
+  append_block<T>(g, page, k, v, n_tokens, first_id, blockIdx.y, blockIdx.x * 64);
+}
+
 // Several layers' frames in one launch: blockIdx.z = layer within the chunk.
 template <typename T>
 __global__ __launch_bounds__(256) void append_layers_kernel(PageGeom g, char* pool, AppendLayers al,
@@ -192,6 +206,26 @@ hipError_t launch_table_upload(DevEntry* dst, const DevEntry* src, int n, hipStr
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_append_table(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,
+                               int64_t first_token_id, DevEntry* dst, const DevEntry* src, int n, hipStream_t s) {
+  TableChunk c;
+  c.first = 0;
+  c.count = n < kUploadChunk ? n : kUploadChunk;
+  for (int i = 0; i < c.count; ++i) c.e[i] = src[i];
+  dim3 grid((unsigned)(g.ts / 64 + 1), (unsigned)g.heads);
+  if (g.esize == 2)
+    append_table_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, page, static_cast<const __bf16*>(k),
+                                                            static_cast<const __bf16*>(v), n_tokens, first_token_id,
+                                                            dst, c);
+  else
+    append_table_kernel<float><<<grid, dim3(256), 0, s>>>(g, page, static_cast<const float*>(k),
+                                                           static_cast<const float*>(v), n_tokens, first_token_id,
+                                                           dst, c);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n <= kUploadChunk) return err;
+  return launch_table_upload(dst + kUploadChunk, src + kUploadChunk, n - kUploadChunk, s);
 }
 
 hipError_t launch_append(const PageGeom& g, char* page, const void* k, const void* v, int n_tokens,

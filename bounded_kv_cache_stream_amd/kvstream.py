@@ -20,9 +20,10 @@ KV_TRANSIENT = 1
 
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
-    "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "score_and_compact", "kv_get_info",
-    "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score", "kv_diversity_score_layers",
-    "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers", "kv_get_head_lengths", "kv_last_error",
+    "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "kv_append_attend", "score_and_compact",
+    "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score",
+    "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
+    "kv_get_head_lengths", "kv_last_error",
 )
 
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "kv_append_frame_layers": [P, I32, I32, I64, P, P, I32, U32, P],
             "kv_evict": [P, I32, ctypes.POINTER(I32), P],
             "stream_attend": [P, I32, P, I32, F32, P, P, P],
+            "kv_append_attend": [P, I32, I64, P, P, I32, U32, P, I32, F32, P, P, ctypes.POINTER(I32), P],
             "score_and_compact": [P, I32, P, I64, ctypes.POINTER(kv_clces_params), P, P, ctypes.POINTER(I64), P],
             "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
             "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
@@ -161,6 +163,14 @@ def kv_evict(pool, layer, stream=None) -> int:
 
 def stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr=None, stream=None) -> None:
     _check(lib().stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr, stream))
+
+
+def kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_ptr, n_q, sm_scale, out_ptr,
+                     lse_ptr=None, stream=None) -> int:
+    n = ctypes.c_int32()
+    _check(lib().kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_ptr, n_q, sm_scale,
+                                  out_ptr, lse_ptr, ctypes.byref(n), stream))
+    return n.value
 
 
 def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_count, keep_ids_ptr=None,
@@ -332,6 +342,23 @@ class KVCache:
             lp = ctypes.c_void_p(lse.data_ptr())
         stream_attend(self.handle, layer, qp, q.shape[0], float(sm_scale), op, lp, self._stream())
         return out
+
+    def append_attend(self, layer, frame_idx, k, v, q, sm_scale, transient=False, out=None, lse=None):
+        """append + evict + attend of one frame in one call; returns (out, frames evicted)."""
+        torch = self.torch
+        if out is None:
+            out = torch.empty_like(q)
+        kp, vp = self._tensor(k), self._tensor(v)
+        qp = self._tensor(q)
+        op = self._tensor(out, q.shape[0])
+        lp = None
+        if lse is not None:
+            if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != q.shape[0] * q.shape[1]:
+                raise ValueError("lse must be a contiguous fp32 tensor of n_q * H elements")
+            lp = ctypes.c_void_p(lse.data_ptr())
+        n = kv_append_attend(self.handle, layer, frame_idx, kp, vp, k.shape[0], KV_TRANSIENT if transient else 0,
+                             qp, q.shape[0], float(sm_scale), op, lp, self._stream())
+        return out, n
 
     def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None) -> int:
         torch = self.torch

@@ -191,6 +191,21 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
 kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q,
                         float sm_scale, void* out_dev, float* lse_dev, void* stream);
 
+/* One frame's cache step in one call: kv_append_frame(layer, frame_idx, k_dev,
+ * v_dev, n_tokens, flags), then kv_evict(layer), then stream_attend(layer,
+ * q_dev, n_q, sm_scale, out_dev, lse_dev), with the same arguments, checks,
+ * results and page contents as those three calls in that order ([FPS]
+ * "Page-Aligned Tensor Layout"; [GCT] "Frame-by-Frame Causal Processing").
+ * The page write and the upload of the attention's page table are one
+ * launch, so a frame costs one launch fewer than the three calls.  n_q may
+ * exceed n_tokens (the scale phase: the queries of every scale frame with
+ * the last one's append).  n_evicted may be NULL.  On any error nothing
+ * changes.  Asynchronous on stream. */
+kv_status kv_append_attend(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev,
+                           const void* v_dev, int32_t n_tokens, uint32_t flags, const void* q_dev,
+                           int32_t n_q, float sm_scale, void* out_dev, float* lse_dev, int32_t* n_evicted,
+                           void* stream);
+
 /* One CLCES step on a layer ([SCV] 2.1.1-2.1.4; top-k keep and compaction as
  * in [SCV] section 1 and [INF] "Rolling Memory").  Candidates: the tokens of
  * the layer's table, scale-frame pages excluded, in table order (N of them).

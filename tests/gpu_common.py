@@ -13,7 +13,14 @@ BF16_REL_L2 = 5e-3
 # fp32 caches: fp32 dot products and softmax over at most a few thousand keys
 FP32_MAX_ABS = 1e-4
 FP32_REL_L2 = 1e-5
-LSE_ABS = 1e-3
+# LSE = m + ln l.  The bf16 kernel's l sums the bf16-rounded probabilities that
+# also enter the PV product (each within a relative 2^-8 of its fp32 value, so
+# O stays consistent with its own denominator): |ln l' - ln l| <= -ln(1 - 2^-8)
+# < 3.92e-3, reached only when few keys carry the sum (it averages out over
+# many).  fp32 caches sum fp32 probabilities: about 1e-6 over a few thousand
+# keys, bounded here by 1e-4.
+LSE_ABS_BF16 = 3.92e-3
+LSE_ABS_FP32 = 1e-4
 
 
 def torch_cuda():

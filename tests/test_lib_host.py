@@ -330,3 +330,23 @@ def test_special_tokens_need_a_free_page():
         with pytest.raises(kv.KVError) as e:
             call()
         assert e.value.status == kv.KV_ERR_STATE
+
+
+def test_append_attend_checks_before_changing_anything():
+    # kv_append_attend validates every argument first: a metadata-only pool has
+    # no device memory to attend with, and a frame of the wrong size is refused;
+    # either way the layer is left as it was
+    c = _meta_pool(1, 4, 1, 6)
+    c.append(0, 0)
+    c.evict(0)
+    before = (c.page_table(0), c.info(0))
+    with pytest.raises(kv.KVError) as e:
+        kv.kv_append_attend(c.handle, 0, 1, None, None, 16, 0, None, 16, 1.0, None)
+    assert e.value.status == kv.KV_ERR_STATE
+    with pytest.raises(kv.KVError) as e:
+        kv.kv_append_attend(c.handle, 0, 1, None, None, 15, 0, None, 16, 1.0, None)
+    assert e.value.status == kv.KV_ERR_SHAPE
+    with pytest.raises(kv.KVError) as e:
+        kv.kv_append_attend(c.handle, 0, 1, None, None, 16, 0, None, 65, 1.0, None)
+    assert e.value.status == kv.KV_ERR_SHAPE
+    assert (c.page_table(0), c.info(0)) == before
