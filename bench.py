@@ -532,7 +532,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by head across GPUs "
-                                   "without any exchange, and no multi-GPU run is part of this build",
+                                   "without any exchange (attention, page writes and compaction are per head); there is no multi-GPU mode",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -7,7 +7,7 @@ discard the rest so the size stays bounded) and step "Prune and roll the
 memory"; StreamCacheVGGT article, section 2.1 (the score used here is the
 fused CLCES score, computed by ``oracle.clces``).
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
 
 * one page per appended frame from a per-layer pool, lowest free id first;
 * the candidates of layer ``l`` are the layer's own cached tokens in table

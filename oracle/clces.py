@@ -20,7 +20,7 @@ budget) and the InfiniteVGGT explainer ("Rolling Memory"; step "Prune and roll
 the memory": keep the top-K tokens, discard the rest, the cache size stays
 fixed).
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
 
 * rank direction ascending, ties by index (a stable sort);
 * ``r = R / (N - 1)`` (r = 0 when N = 1);

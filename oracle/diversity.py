@@ -18,7 +18,7 @@ Visual Geometry Grounded Transformer for Endless Streams"):
 * "Concrete mini-example" -- a per-head budget of 512 with 1,200 candidates
   keeps 512 and drops 688.
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
 
 * the anchor is frame 0's page in every layer and head;
 * a zero key normalises to the zero vector; when the mean of the normalised

@@ -14,7 +14,7 @@ Oracle (test infrastructure only).  Sources:
   LingBot-Map handle sequences longer than 10,000 frames": evicts older
   frames while retaining the scale frames.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * the window counts persisted non-scale frames (not stream time);
 * keyframe rule ``t < S or (t - S) % k == 0``;
@@ -131,7 +131,7 @@ class SpecialWindowCache(WindowCache):
 
     GCTStream explainer, "Special Token Persistence": with
     ``kv_cache_cross_frame_special`` the special tokens of a frame survive the
-    eviction that discards the rest of its KV.  Readings (listed in the design doc):
+    eviction that discards the rest of its KV.  Readings taken where the page is silent:
 
     * the special tokens are the first ``special`` slots of every frame;
     * at each eviction (oldest victim first) the victim's special token ids
