@@ -354,38 +354,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // Merge split-KV partials: O = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s.
-// One wave per row: lanes over the splits give m, the weights and L by wave
-// reductions; then lanes over d accumulate the weighted partial rows, the
-// weight of split s read with v_readlane, the loads of the splits independent.
+// 16 lanes per row (4 consecutive d each, one 16-byte load per split), four
+// rows per wave.  Lane j of a row holds splits j, j+16, j+32, j+48: m, the
+// weights and L come from reductions over the row's 16 lanes, and the
+// weighted sum runs over the splits in order, the weight of split s taken
+// from the lane that holds it.
 template <typename OutT>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p, int H) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
   const int64_t rows = (int64_t)p.n_q * H;
-  const int lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (idx >= rows) return;
-  const int S = p.splits;  // <= 64
-  float ms = -INFINITY, ls = 0.f;
-  if (lane < S) {
-    ms = p.part_ml[((int64_t)lane * rows + idx) * 2];
-    ls = p.part_ml[((int64_t)lane * rows + idx) * 2 + 1];
+  const int sub = threadIdx.x & 15;
+  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (idx >= rows) return;  // whole 16-lane groups leave together
+  const int S = p.splits;   // <= 64
+  float ms[4], w[4];
+  float ls[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sj = sub + 16 * j;
+    ms[j] = -INFINITY;
+    ls[j] = 0.f;
+    if (sj < S) {
+      ms[j] = p.part_ml[((int64_t)sj * rows + idx) * 2];
+      ls[j] = p.part_ml[((int64_t)sj * rows + idx) * 2 + 1];
+    }
+    m = fmaxf(m, ms[j]);
   }
-  float m = ms;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const float w = lane < S ? __builtin_amdgcn_exp2f(ms - m) : 0.f;
-  float L = w * ls;
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+  float L = 0.f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
-  float acc = 0.f;
-  const float* po = p.part_o + idx * D + lane;
+  for (int j = 0; j < 4; ++j) {
+    w[j] = sub + 16 * j < S ? __builtin_amdgcn_exp2f(ms[j] - m) : 0.f;
+    L += w[j] * ls[j];
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) L += __shfl_xor(L, off, 16);
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = p.part_o + idx * D + 4 * sub;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
-    acc = fmaf(ws, po[(int64_t)s * rows * D], acc);
+    const float wj = s < 16 ? w[0] : s < 32 ? w[1] : s < 48 ? w[2] : w[3];
+    const float ws = __shfl(wj, s & 15, 16);
+    const f32x4v o = *reinterpret_cast<const f32x4v*>(po + (int64_t)s * rows * D);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = fmaf(ws, o[c], acc[c]);
   }
-  OutT* out = static_cast<OutT*>(p.out) + idx * D + lane;
-  *out = (OutT)(acc / L);
-  if (p.lse && lane == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
+  OutT* out = static_cast<OutT*>(p.out) + idx * D + 4 * sub;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) out[c] = (OutT)(acc[c] / L);
+  if (p.lse && sub == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
 }
 
 // fp32 caches: one wave per (query, head); lane = d.
@@ -437,7 +456,7 @@ hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hi
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits == 1) return err;
   const int64_t rows = (int64_t)p.n_q * g.heads;
-  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(p, g.heads);
+  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(p, g.heads);
   return hipGetLastError();
 }
 
