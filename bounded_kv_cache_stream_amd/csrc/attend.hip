@@ -354,57 +354,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // Merge split-KV partials: O = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s.
-// 16 lanes per row (4 consecutive d each, one 16-byte load per split), four
-// rows per wave.  Lane j of a row holds splits j, j+16, j+32, j+48: m, the
-// weights and L come from reductions over the row's 16 lanes, and the
-// weighted sum runs over the splits in order, the weight of split s taken
-// from the lane that holds it.
-template <typename OutT>
-__global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p, int H) {
+// Lanes take 4 consecutive d each (one 16-byte load per split and row).
+//   G = 1 (up to 16 splits): 16 lanes per row, four rows per wave; lane j of
+//     a row holds split j's m and weight, and sums all splits in order.
+//   G = 4 (17 to 64 splits): one row per wave; lane l holds split l's m and
+//     weight, and the four 16-lane groups sum every fourth split each before
+//     their partial sums are added, which shortens each lane's dependent
+//     chain fourfold for the many splits of a head-split layer.
+// One wave per block, so that few rows still spread over every CU.
+template <typename OutT, int G>
+__global__ __launch_bounds__(64) void attend_combine_kernel(AttendParams p, int H) {
   typedef float f32x4v __attribute__((ext_vector_type(4)));
+  constexpr int W = 16 * G;  // lanes per row
   const int64_t rows = (int64_t)p.n_q * H;
   const int sub = threadIdx.x & 15;
-  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (idx >= rows) return;  // whole 16-lane groups leave together
-  const int S = p.splits;   // <= 64
-  float ms[4], w[4];
-  float ls[4];
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int sj = sub + 16 * j;
-    ms[j] = -INFINITY;
-    ls[j] = 0.f;
-    if (sj < S) {
-      ms[j] = p.part_ml[((int64_t)sj * rows + idx) * 2];
-      ls[j] = p.part_ml[((int64_t)sj * rows + idx) * 2 + 1];
-    }
-    m = fmaxf(m, ms[j]);
+  const int lr = threadIdx.x & (W - 1);  // lane within the row
+  const int64_t idx = (int64_t)blockIdx.x * (4 / G) + threadIdx.x / W;
+  if (idx >= rows) return;  // whole rows leave together
+  const int S = p.splits;
+  float ms = -INFINITY, ls = 0.f;
+  if (lr < S) {
+    ms = p.part_ml[((int64_t)lr * rows + idx) * 2];
+    ls = p.part_ml[((int64_t)lr * rows + idx) * 2 + 1];
   }
+  float m = ms;
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-  float L = 0.f;
+  for (int off = W / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, W));
+  const float w = lr < S ? __builtin_amdgcn_exp2f(ms - m) : 0.f;
+  float L = w * ls;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[j] = sub + 16 * j < S ? __builtin_amdgcn_exp2f(ms[j] - m) : 0.f;
-    L += w[j] * ls[j];
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) L += __shfl_xor(L, off, 16);
+  for (int off = W / 2; off >= 1; off >>= 1) L += __shfl_xor(L, off, W);
   f32x4v acc = {0.f, 0.f, 0.f, 0.f};
   const float* po = p.part_o + idx * D + 4 * sub;
+  const int grp = lr >> 4;
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float wj = s < 16 ? w[0] : s < 32 ? w[1] : s < 48 ? w[2] : w[3];
-    const float ws = __shfl(wj, s & 15, 16);
+  for (int s = grp; s < S; s += G) {
+    const float ws = __shfl(w, s, W);
     const f32x4v o = *reinterpret_cast<const f32x4v*>(po + (int64_t)s * rows * D);
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = fmaf(ws, o[c], acc[c]);
   }
+  if (G > 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[c] += __shfl_xor(acc[c], 16, 64);
+      acc[c] += __shfl_xor(acc[c], 32, 64);
+    }
+    if (grp != 0) return;
+  }
   OutT* out = static_cast<OutT*>(p.out) + idx * D + 4 * sub;
 #pragma unroll
   for (int c = 0; c < 4; ++c) out[c] = (OutT)(acc[c] / L);
-  if (p.lse && sub == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
+  if (p.lse && lr == 0) p.lse[idx] = (m + __builtin_log2f(L)) * kLn2;
 }
 
 // fp32 caches: one wave per (query, head); lane = d.
@@ -456,7 +457,10 @@ hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hi
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits == 1) return err;
   const int64_t rows = (int64_t)p.n_q * g.heads;
-  attend_combine_kernel<__bf16><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(p, g.heads);
+  if (p.splits <= 16)
+    attend_combine_kernel<__bf16, 1><<<dim3((unsigned)((rows + 3) / 4)), dim3(64), 0, s>>>(p, g.heads);
+  else
+    attend_combine_kernel<__bf16, 4><<<dim3((unsigned)rows), dim3(64), 0, s>>>(p, g.heads);
   return hipGetLastError();
 }
 
