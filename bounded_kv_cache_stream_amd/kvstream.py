@@ -307,8 +307,8 @@ class KVCache:
         if self.device is None:
             kv_append_frame(self.handle, layer, frame_idx, None, None, self.cfg.page_tokens, flags, None)
             return
-        kv_append_frame(self.handle, layer, frame_idx, self._tensor(k), self._tensor(v), k.shape[0], flags,
-                        self._stream())
+        kv_append_frame(self.handle, layer, frame_idx, self._tensor(k), self._tensor(v, k.shape[0]), k.shape[0],
+                        flags, self._stream())
 
     def append_layers(self, first_layer, frame_idx, k=None, v=None, n_layers=None, transient=False):
         """k, v: [n_layers, T, H, D] contiguous (one frame of several layers)."""
@@ -348,7 +348,7 @@ class KVCache:
         torch = self.torch
         if out is None:
             out = torch.empty_like(q)
-        kp, vp = self._tensor(k), self._tensor(v)
+        kp, vp = self._tensor(k), self._tensor(v, k.shape[0])
         qp = self._tensor(q)
         op = self._tensor(out, q.shape[0])
         lp = None

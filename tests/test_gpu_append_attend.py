@@ -197,6 +197,10 @@ def test_append_attend_errors_change_nothing():
     with pytest.raises(kv.KVError) as e:  # too many queries
         c.append_attend(0, 1, k, v, torch.cat([q, q]), 0.125)
     assert e.value.status == kv.KV_ERR_SHAPE
+    with pytest.raises(ValueError):  # V shorter than K: refused before any call (it would be read past its end)
+        c.append_attend(0, 1, k, v[:50].contiguous(), q, 0.125)
+    with pytest.raises(ValueError):
+        c.append(0, 1, k, v[:50].contiguous())
     assert (c.page_table(0), c.info(0)) == before
     # the pool needs S + W + 1 = 4 page ids: with 3, the fourth keyframe finds none
     small = kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=1, sliding_window=2,
