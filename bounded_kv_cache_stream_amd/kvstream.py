@@ -368,6 +368,15 @@ class KVCache:
         for t in (keep_ids, ranks):
             if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError("keep_ids / ranks must be contiguous int32 tensors")
+        # the library writes keep_count ids and n_window x N ranks (N = the candidate tokens, pages of the
+        # scale frames excluded); it cannot see the buffers' sizes
+        _, lens, frames = self.page_table(layer)
+        n_cand = sum(n for n, f in zip(lens, frames) if f >= self.cfg.scale_frames)
+        if keep_ids is not None and keep_ids.numel() < min(keep_count, n_cand):
+            raise ValueError(f"keep_ids holds {keep_ids.numel()} ids, the step writes {min(keep_count, n_cand)}")
+        if ranks is not None and ranks.numel() < min(window, layer + 1) * n_cand:
+            raise ValueError(f"ranks holds {ranks.numel()} entries, the step writes "
+                             f"{min(window, layer + 1) * n_cand}")
         return score_and_compact(self.handle, layer, ctypes.c_void_p(score_table.data_ptr()), score_table.shape[0],
                                  window, lam, keep_count,
                                  None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),

@@ -92,6 +92,27 @@ def test_clces_small_edge_cases():
     assert list(zip(ids, fr, lens)) == b.page_table()
 
 
+def test_clces_output_buffers_too_small_are_refused():
+    # the step writes keep_count ids and n_window x N ranks into caller buffers whose sizes the C ABI
+    # cannot see: the binding refuses smaller ones before any device work, and nothing changes
+    torch = torch_cuda()
+    T, H, L = 64, 2, 3
+    cache = kv.KVCache(_cfg(L, T, 6, H=H), device="cuda")
+    for layer in range(L):
+        _fill(cache, layer, 4, T, H, 91)
+    table = torch.from_numpy(synth.raw_scores(91, 4 * T, L)).cuda()
+    before = cache.page_table(2)
+    with pytest.raises(ValueError):
+        cache.score_and_compact(2, table, 5, 0.5, 100, keep_ids=torch.empty(99, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):  # layer 2 with window 5: 3 window layers x 256 candidates
+        cache.score_and_compact(2, table, 5, 0.5, 100,
+                                ranks=torch.empty(3 * 4 * T - 1, dtype=torch.int32, device="cuda"))
+    assert cache.page_table(2) == before
+    ranks = torch.empty(3 * 4 * T, dtype=torch.int32, device="cuda")
+    assert cache.score_and_compact(2, table, 5, 0.5, 100, ranks=ranks) == 100
+    torch.cuda.synchronize()
+
+
 def test_clces_scale_frames_protected():
     torch = torch_cuda()
     T, H = 64, 2
