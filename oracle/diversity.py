@@ -35,7 +35,9 @@ Readings taken where the pages are silent:
   candidates;
 * compaction is per page and head, with the hole-filling rule of
   ``oracle.clces.compact_page``; a page is released once every head of it is
-  empty.
+  empty;
+* ``merge_pages`` (not on the pages) folds a candidate page into the page
+  before it when every head fits, keeping each head's row order.
 
 Pinned by ``tests/test_oracle_diversity.py``: closed forms (identical
 directions score -1; an orthonormal set scores -1/sqrt(n); scores are
@@ -43,7 +45,10 @@ invariant to positive scaling of a key; the mean of the scores of n keys is
 -|m|), a brute-force cosine with exactly rounded component sums on small inputs, the
 worked budget example in ``tests/golden/diversity_budget_example.txt``, and the
 softmax budgets' limits (equal averages split evenly, a cold temperature gives
-everything to the most diverse layer).
+everything to the most diverse layer); for ``merge_pages``, a hand-worked
+example and invariants after pruning (each head's token order unchanged, no
+page over T rows in any head, no adjacent pair of candidate pages left that
+fits, the merged pages' ids freed).
 """
 
 from __future__ import annotations
@@ -149,6 +154,27 @@ class DiversityCache:
                 out.append([pid, f, new_ids])
         self.table = out
         return masks
+
+    def merge_pages(self) -> list[tuple[int, int, tuple, tuple]]:
+        """Append each candidate page to the page before it when, in every head, their lengths sum to at most
+        T; return the moves ``(src_page, dst_page, per-head dst slots, per-head counts)`` in table order.
+
+        A design step, not on the pages: it bounds the ragged pages that per-head pruning leaves.  Rows keep
+        their table-then-slot order in every head, so candidate indices (the top-K tie-break) do not change.
+        The anchor page is neither merged nor merged into; a merged page keeps the frame of its first page."""
+        moves = []
+        out = []
+        for pid, f, ids in self.table:
+            if f == 0 or not out or out[-1][1] == 0 or \
+                    any(len(out[-1][2][h]) + len(ids[h]) > self.T for h in range(self.H)):
+                out.append([pid, f, ids])
+                continue
+            dst = out[-1]
+            moves.append((pid, dst[0], tuple(len(x) for x in dst[2]), tuple(len(x) for x in ids)))
+            dst[2] = [np.concatenate([dst[2][h], ids[h]]) for h in range(self.H)]
+            self.free.add(pid)
+        self.table = out
+        return moves
 
     def page_table(self) -> list[tuple[int, int, tuple]]:
         """(page_id, frame, per-head lengths) per entry, in table order."""

@@ -142,3 +142,53 @@ def test_prune_decides_on_rounded_scores():
     order32 = np.argsort(-sc.astype(np.float32), kind="stable")
     m = c.prune(lambda f, h: keys[f], 2, rank_dtype=np.float32)[0]
     assert m.tolist() == [i in order32[:2] for i in range(3)]
+
+
+def _set_table(c, entries):
+    c.table = [[pid, f, [np.asarray(x, dtype=np.int64) for x in ids]] for pid, f, ids in entries]
+    c.free -= {pid for pid, _, _ in entries}
+
+
+def test_merge_pages_hand_example():
+    # T = 4, two heads.  Page 2 fits after page 1 in both heads (2+1 <= 4, 1+3 <= 4); page 3 does not fit
+    # after the merged page in head 0 (3+2 > 4) and starts a new page; page 4 fits after page 3 (2+1, 0+3).
+    # The anchor (frame 0) takes no part.
+    c = diversity.DiversityCache(2, 4, 6)
+    _set_table(c, [(0, 0, ([0, 1, 2, 3], [0, 1, 2, 3])),
+                   (1, 1, ([4, 5], [6])),
+                   (2, 2, ([9], [8, 10, 11])),
+                   (3, 3, ([12, 13], [])),
+                   (4, 4, ([17], [16, 18, 19]))])
+    before = [c.all_ids(h).tolist() for h in range(2)]
+    moves = c.merge_pages()
+    assert moves == [(2, 1, (2, 1), (1, 3)), (4, 3, (2, 0), (1, 3))]
+    assert c.page_table() == [(0, 0, (4, 4)), (1, 1, (3, 4)), (3, 3, (3, 3))]
+    assert [c.all_ids(h).tolist() for h in range(2)] == before
+    assert c.table[1][2][0].tolist() == [4, 5, 9] and c.table[2][2][1].tolist() == [16, 18, 19]
+    assert c.free == {2, 4, 5}
+    assert c.merge_pages() == []  # nothing left to merge
+
+
+def test_merge_pages_invariants_after_prunes():
+    rng = np.random.default_rng(11)
+    T, H, F = 20, 3, 12
+    keys = {f: rng.standard_normal((H, T, 64)) for f in range(F)}
+    c = diversity.DiversityCache(H, T, F + 1)
+    total_moves = 0
+    for t in range(F):
+        c.append(t)
+        c.prune(lambda f, h: keys[f][h], 45)
+        ids_before = [c.all_ids(h).tolist() for h in range(H)]
+        pages_before, free_before = len(c.table), set(c.free)
+        moves = c.merge_pages()
+        total_moves += len(moves)
+        assert [c.all_ids(h).tolist() for h in range(H)] == ids_before
+        assert len(c.table) == pages_before - len(moves)
+        assert c.free == free_before | {m[0] for m in moves}
+        cand = [e for e in c.table if e[1] > 0]
+        assert all(len(x) <= T for _, _, ids in cand for x in ids)
+        for a, b in zip(cand, cand[1:]):  # the greedy pass leaves no adjacent pair that fits
+            assert any(len(a[2][h]) + len(b[2][h]) > T for h in range(H))
+        for src, dst, off, cnt in moves:
+            assert src not in [e[0] for e in c.table] and len(off) == len(cnt) == H
+    assert total_moves > 0
