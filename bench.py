@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--special", type=int, default=0,
                     help="stream / long workloads: special tokens per frame kept across evictions (0 = off)")
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
-    ap.add_argument("--merge", action="store_true", help="budget workload: merge ragged pages after each compaction")
+    ap.add_argument("--merge", action="store_true",
+                    help="budget / diversity workloads: merge ragged pages after each compaction / prune")
     ap.add_argument("--fused", action="store_true",
                     help="stream/long workloads: one kv_append_attend call per frame (the page write shares the "
                          "table-upload launch) instead of append, evict and attend")
@@ -424,10 +425,11 @@ def run_diversity(args):
     torch.cuda.synchronize()
     cand = np.zeros((L, H), dtype=np.int64)  # candidates per head after the frame's append
     kept = np.zeros((L, H), dtype=np.int64)
-    log = {"score": [], "prune": [], "attend": [], "append": [], "cand": [], "kept": [], "budgets": []}
+    log = {"score": [], "prune": [], "merge": [], "attend": [], "append": [], "cand": [], "kept": [],
+           "budgets": []}
 
     def frame(t, timed):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         marks[0].record(stream)
         cache.append_layers(0, t, rings_k[t % 8], rings_v[t % 8])
         marks[1].record(stream)
@@ -437,14 +439,18 @@ def run_diversity(args):
         budgets = kv.kv_layer_budgets(means, tau, total, H)
         kept[:] = cache.diversity_prune_layers(0, budgets)
         marks[3].record(stream)
+        if args.merge:
+            cache.merge_pages_layers(0, L)
+        marks[4].record(stream)
         for l in range(L):
             cache.attend(l, rings_q[t % 8][l], 1.0, out=out)
-        marks[4].record(stream)
+        marks[5].record(stream)
         if timed:
             log["append"].append((marks[0], marks[1]))
             log["score"].append((marks[1], marks[2]))
             log["prune"].append((marks[2], marks[3]))
-            log["attend"].append((marks[3], marks[4]))
+            log["merge"].append((marks[3], marks[4]))
+            log["attend"].append((marks[4], marks[5]))
             log["cand"].append(cand.copy())
             log["kept"].append(kept.copy())
             log["budgets"].append(budgets)
@@ -459,7 +465,7 @@ def run_diversity(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     split = {k: float(np.mean([a.elapsed_time(b) for a, b in log[k]])) * 1e3
-             for k in ("append", "score", "prune", "attend")}
+             for k in ("append", "score", "prune", "merge", "attend")}
     cand_rows = float(np.mean([c.sum() for c in log["cand"]]))  # candidate rows (head x token) per frame
     kept_rows = float(np.mean([k.sum() for k in log["kept"]]))
     score_bytes = 2.0 * cand_rows * D * 2  # two passes over every candidate key row, bf16
@@ -468,17 +474,20 @@ def run_diversity(args):
     hl = np.array(cache.head_lengths(L // 2))
     tiles = ((hl + 63) // 64).sum(axis=0)
     result = {
-        "metric": f"frames/sec of the {L}-layer diversity-pruned stack (append, score, budgets, prune, attend)",
+        "metric": f"frames/sec of the {L}-layer diversity-pruned stack (append, score, budgets, prune, "
+                  + ("page merge, " if args.merge else "") + "attend)",
         "value": args.steps / wall, "unit": "frames/s", "higher_is_better": True, "n_gpus": 1,
         "steps": args.steps, "warmup": warm, "ms_per_frame": wall / args.steps * 1e3, "dtype": "bf16",
         "data": "synthetic (ring of 8 seeded AR(1) frames per layer)",
-        "config": {"workload": f"diversity_l{L}_h{H}_d{D}_t{T}_k{per_head}_tau{tau:g}", "layers": L,
+        "config": {"workload": f"diversity_l{L}_h{H}_d{D}_t{T}_k{per_head}_tau{tau:g}"
+                               + ("_merge" if args.merge else ""), "layers": L,
                    "tokens_per_frame": T, "heads": H, "head_dim": D, "per_head_budget_mean": per_head,
                    "total_budget": total, "tau": tau, "anchor_frames": 1},
         "us_per_frame": split,
         "candidates_per_frame": cand_rows, "kept_per_frame": kept_rows,
         "budget_spread": [int(min(log["budgets"][-1])), int(max(log["budgets"][-1]))],
         "pages_per_layer_mean": float(np.mean(pages)),
+        "merges_per_layer_mean": float(np.mean([cache.info(l)["merges"] for l in range(L)])),
         "attend_tile_fill_mid_layer": float(hl.sum(axis=0).mean() / (64.0 * tiles.mean())),
         "roofline": {"bound": "hbm", "achieved": score_bytes / (split["score"] * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": score_bytes / (split["score"] * 1e-6) / 1e9 / PEAK_HBM_GBS,

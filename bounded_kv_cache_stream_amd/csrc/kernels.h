@@ -76,6 +76,23 @@ struct MergeChunk {
 };
 hipError_t launch_merge(const PageGeom& g, char* pool, const MergeChunk& c, hipStream_t s);
 
+// Per-head page merges of one launch (pages whose heads hold different rows):
+// item i moves, for every head h, rows 0 .. count-1 of head h of page src to
+// slots off.. of head h of page dst, with (off, count) = hv[2*(i*heads+h)],
+// hv[2*(i*heads+h)+1]; an item with last = 1 also writes off + count, the
+// page's new per-head lengths, to hlen[dst_phys * heads + h].  Token ids are
+// not moved (a pruned page's id row describes none of its heads).
+constexpr int kHeadMergeItems = 16;
+constexpr int kHeadMergeInts = 640;
+struct HeadMergeChunk {
+  int32_t n;
+  int64_t src_offset[kHeadMergeItems], dst_offset[kHeadMergeItems];
+  int32_t dst_phys[kHeadMergeItems];
+  int32_t last[kHeadMergeItems];
+  int32_t hv[kHeadMergeInts];
+};
+hipError_t launch_head_merge(const PageGeom& g, char* pool, int32_t* hlen, const HeadMergeChunk& c, hipStream_t s);
+
 struct AttendParams {
   const void* q;
   void* out;

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <memory>
 #include <new>
@@ -801,34 +802,98 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   return ok();
 }
 
+namespace {
+
+// Page merges of layers first .. first+n-1: each layer's plan (whole pages
+// where every head holds the same rows, per head otherwise), the moves of all
+// layers packed into shared launches (moves carry absolute page offsets; a
+// plan never moves a page it writes), then every layer's table updated.
+kv_status merge_layers(kv_pool_t* pool, int32_t first, int32_t n, int32_t* n_merged, hipStream_t st) {
+  if (pool->cfg.sliding_window > 0)
+    return fail(KV_ERR_STATE, "page merge needs one frame per page no more (sliding_window must be 0)");
+  const int32_t H = pool->cfg.num_heads;
+  std::vector<std::vector<kvs::MergeMove>> whole((size_t)n);
+  std::vector<std::vector<kvs::HeadMergeMove>> heads((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& L = pool->layers[(size_t)(first + i)];
+    if (L.same_tokens()) {
+      whole[(size_t)i] = L.plan_merges();
+    } else {
+      if (2 * H > kvs::kHeadMergeInts)
+        return fail(KV_ERR_ARG, "per-head page merge supports at most %d heads", kvs::kHeadMergeInts / 2);
+      heads[(size_t)i] = L.plan_head_merges(H);
+    }
+  }
+  if (!pool->meta_only) {
+    const int64_t pb = pool->lay.geom.page_bytes;
+    hipError_t e = hipSuccess;
+    kvs::MergeChunk c;
+    c.n = 0;
+    for (int32_t i = 0; i < n && e == hipSuccess; ++i)
+      for (const auto& m : whole[(size_t)i]) {
+        c.item[c.n].src_offset = phys_page(pool, first + i, m.src) * pb;
+        c.item[c.n].dst_offset = phys_page(pool, first + i, m.dst) * pb;
+        c.item[c.n].dst_off = m.dst_off;
+        c.item[c.n].count = m.count;
+        if (++c.n == kvs::kMergeChunk) {
+          e = kvs::launch_merge(pool->lay.geom, pool->pool, c, st);
+          c.n = 0;
+          if (e != hipSuccess) break;
+        }
+      }
+    if (e == hipSuccess && c.n > 0) e = kvs::launch_merge(pool->lay.geom, pool->pool, c, st);
+    // per-head moves; the last move into each destination writes its per-head lengths
+    const int per_chunk = (int)std::min<int64_t>(kvs::kHeadMergeItems, kvs::kHeadMergeInts / (2 * (int64_t)H));
+    kvs::HeadMergeChunk hc;
+    hc.n = 0;
+    std::vector<size_t> last_into((size_t)pool->cfg.pages_per_layer);
+    for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
+      const auto& mv = heads[(size_t)i];
+      for (size_t j = 0; j < mv.size(); ++j) last_into[(size_t)mv[j].dst] = j;
+      for (size_t j = 0; j < mv.size(); ++j) {
+        const auto& m = mv[j];
+        const int k = hc.n;
+        hc.src_offset[k] = phys_page(pool, first + i, m.src) * pb;
+        hc.dst_offset[k] = phys_page(pool, first + i, m.dst) * pb;
+        hc.dst_phys[k] = (int32_t)phys_page(pool, first + i, m.dst);
+        hc.last[k] = last_into[(size_t)m.dst] == j ? 1 : 0;
+        for (int32_t h = 0; h < H; ++h) {
+          hc.hv[2 * (k * H + h)] = m.dst_off[(size_t)h];
+          hc.hv[2 * (k * H + h) + 1] = m.count[(size_t)h];
+        }
+        if (++hc.n == per_chunk) {
+          e = kvs::launch_head_merge(pool->lay.geom, pool->pool, hlens_dev(pool), hc, st);
+          hc.n = 0;
+          if (e != hipSuccess) break;
+        }
+      }
+    }
+    if (e == hipSuccess && hc.n > 0) e = kvs::launch_head_merge(pool->lay.geom, pool->pool, hlens_dev(pool), hc, st);
+    if (e != hipSuccess) return hip_fail(e, "page merge launch");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    auto& L = pool->layers[(size_t)(first + i)];
+    const size_t moved = whole[(size_t)i].size() + heads[(size_t)i].size();
+    if (!whole[(size_t)i].empty()) L.commit_merges(whole[(size_t)i]);
+    if (!heads[(size_t)i].empty()) L.commit_head_merges(heads[(size_t)i], H);
+    if (n_merged) n_merged[i] = (int32_t)moved;
+  }
+  return ok();
+}
+
+}  // namespace
+
 kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
-  if (pool->cfg.sliding_window > 0)
-    return fail(KV_ERR_STATE, "layer %d: page merge needs one frame per page no more (sliding_window must be 0)",
-                layer);
-  auto& L = pool->layers[(size_t)layer];
-  if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
-  const std::vector<kvs::MergeMove> mv = L.plan_merges();
-  if (!pool->meta_only) {
-    const int64_t pb = pool->lay.geom.page_bytes;
-    for (size_t c0 = 0; c0 < mv.size(); c0 += kvs::kMergeChunk) {
-      kvs::MergeChunk c;
-      c.n = (int32_t)std::min<size_t>(kvs::kMergeChunk, mv.size() - c0);
-      for (int32_t i = 0; i < c.n; ++i) {
-        const auto& m = mv[c0 + (size_t)i];
-        c.item[i].src_offset = phys_page(pool, layer, m.src) * pb;
-        c.item[i].dst_offset = phys_page(pool, layer, m.dst) * pb;
-        c.item[i].dst_off = m.dst_off;
-        c.item[i].count = m.count;
-      }
-      hipError_t e = kvs::launch_merge(pool->lay.geom, pool->pool, c, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "page merge launch");
-    }
-  }
-  L.commit_merges(mv);
-  if (n_merged) *n_merged = (int32_t)mv.size();
-  return ok();
+  return merge_layers(pool, layer, 1, n_merged, static_cast<hipStream_t>(stream));
+}
+
+kv_status kv_merge_pages_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, int32_t* n_merged,
+                                void* stream) {
+  kv_status s = check_layers(pool, first_layer, n_layers);
+  if (s != KV_OK) return s;
+  return merge_layers(pool, first_layer, n_layers, n_merged, static_cast<hipStream_t>(stream));
 }
 
 kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,

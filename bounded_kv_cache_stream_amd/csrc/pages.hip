@@ -128,6 +128,46 @@ __global__ __launch_bounds__(256) void merge_kernel(PageGeom g, char* pool, Merg
   }
 }
 
+// Per-head page merge: block (item, part) appends head h's rows of page src
+// after the rows head h already holds in page dst, for K (part < H) or V
+// (H <= part < 2H); part 2H writes the destination's new per-head lengths
+// when this item is the last move into it.  Moves of one launch read pages
+// that no move of it writes, and write disjoint row ranges.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_heads_kernel(PageGeom g, char* pool, int32_t* hlen, HeadMergeChunk c) {
+  typedef int V16 __attribute__((ext_vector_type(4)));
+  constexpr int VPR = D * sizeof(T) / 16;  // 16-byte vectors per row
+  constexpr int RPP = 256 / VPR;           // rows per pass
+  const int it = blockIdx.x, part = blockIdx.y, H = g.heads, tid = threadIdx.x;
+  if (part == 2 * H) {
+    if (c.last[it])
+      for (int h = tid; h < H; h += 256) {
+        const int32_t* v = &c.hv[2 * (it * H + h)];
+        hlen[(int64_t)c.dst_phys[it] * H + h] = v[0] + v[1];
+      }
+    return;
+  }
+  const int h = part < H ? part : part - H;
+  const int off = c.hv[2 * (it * H + h)], count = c.hv[2 * (it * H + h) + 1];
+  const int64_t seg = part < H ? g.k_off : g.v_off;
+  const V16* src = reinterpret_cast<const V16*>(pool + c.src_offset[it] + seg) + (int64_t)h * g.ts * VPR;
+  V16* dst = reinterpret_cast<V16*>(pool + c.dst_offset[it] + seg) + ((int64_t)h * g.ts + off) * VPR;
+  const int r = tid / VPR, cc = tid % VPR;
+  for (int r0 = 0; r0 < count; r0 += 4 * RPP) {
+    V16 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + u * RPP + r;
+      v[u] = row < count ? __builtin_nontemporal_load(&src[row * VPR + cc]) : V16{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + u * RPP + r;
+      if (row < count) __builtin_nontemporal_store(v[u], &dst[row * VPR + cc]);
+    }
+  }
+}
+
 __global__ void table_upload_kernel(DevEntry* dst, TableChunk chunk) {
   const int i = threadIdx.x;
   if (i < chunk.count) dst[chunk.first + i] = chunk.e[i];
@@ -192,6 +232,16 @@ hipError_t launch_merge(const PageGeom& g, char* pool, const MergeChunk& c, hipS
     merge_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, pool, c);
   else
     merge_kernel<float><<<grid, dim3(256), 0, s>>>(g, pool, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_merge(const PageGeom& g, char* pool, int32_t* hlen, const HeadMergeChunk& c, hipStream_t s) {
+  if (c.n < 1) return hipSuccess;
+  dim3 grid((unsigned)c.n, (unsigned)(2 * g.heads + 1));
+  if (g.esize == 2)
+    merge_heads_kernel<__bf16><<<grid, dim3(256), 0, s>>>(g, pool, hlen, c);
+  else
+    merge_heads_kernel<float><<<grid, dim3(256), 0, s>>>(g, pool, hlen, c);
   return hipGetLastError();
 }
 

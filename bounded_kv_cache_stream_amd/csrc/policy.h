@@ -41,6 +41,13 @@ struct MergeMove {
   int32_t src, dst, dst_off, count;
 };
 
+// One per-head page merge: rows 0 .. count[h]-1 of head h of page src go to
+// slots dst_off[h] .. of head h of page dst.
+struct HeadMergeMove {
+  int32_t src, dst;
+  std::vector<int32_t> dst_off, count;
+};
+
 class LayerPolicy {
  public:
   void init(int32_t pages, int32_t scale_frames, int32_t window, int32_t keyframe_interval, int32_t page_tokens,
@@ -242,6 +249,69 @@ class LayerPolicy {
       PageEntry e = e0;
       auto it = grow.find(e.page);
       if (it != grow.end()) e.len += it->second;
+      out.push_back(e);
+    }
+    table.swap(out);
+    merges += (int64_t)mv.size();
+    if (!mv.empty()) ++gen;
+  }
+
+  // Page merge once heads hold different rows: walk the table from the first
+  // candidate; a page whose rows fit after the page before it in every head
+  // (per-head sums <= page_tokens) is appended to it head by head, so each
+  // head keeps its row order.  Returns the moves; the table is unchanged until
+  // commit_head_merges.
+  std::vector<HeadMergeMove> plan_head_merges(int heads) const {
+    std::vector<HeadMergeMove> mv;
+    size_t f = first_candidate();
+    if (f >= table.size()) return mv;
+    int32_t cur = table[f].page;
+    std::vector<int32_t> cur_len((size_t)heads);
+    for (int h = 0; h < heads; ++h) cur_len[(size_t)h] = head_len(table[f], h);
+    for (size_t i = f + 1; i < table.size(); ++i) {
+      bool fits = true;
+      for (int h = 0; h < heads && fits; ++h) fits = cur_len[(size_t)h] + head_len(table[i], h) <= T_;
+      if (fits) {
+        HeadMergeMove m{table[i].page, cur, cur_len, std::vector<int32_t>((size_t)heads)};
+        for (int h = 0; h < heads; ++h) {
+          m.count[(size_t)h] = head_len(table[i], h);
+          cur_len[(size_t)h] += m.count[(size_t)h];
+        }
+        mv.push_back(std::move(m));
+      } else {
+        cur = table[i].page;
+        for (int h = 0; h < heads; ++h) cur_len[(size_t)h] = head_len(table[i], h);
+      }
+    }
+    return mv;
+  }
+
+  void commit_head_merges(const std::vector<HeadMergeMove>& mv, int heads) {
+    std::set<int32_t> gone;
+    std::map<int32_t, std::vector<int32_t>> grow;
+    for (const auto& m : mv) {
+      gone.insert(m.src);
+      auto& g = grow[m.dst];
+      if (g.empty()) g.assign((size_t)heads, 0);
+      for (int h = 0; h < heads; ++h) g[(size_t)h] += m.count[(size_t)h];
+    }
+    std::vector<PageEntry> out;
+    for (const auto& e0 : table) {
+      if (gone.count(e0.page)) {
+        free_ids.insert(e0.page);
+        continue;
+      }
+      PageEntry e = e0;
+      auto it = grow.find(e.page);
+      if (it != grow.end()) {
+        if (e.hlen.empty()) e.hlen.assign((size_t)heads, e.len);
+        int32_t mx = 0;
+        for (int h = 0; h < heads; ++h) {
+          e.hlen[(size_t)h] += it->second[(size_t)h];
+          mx = e.hlen[(size_t)h] > mx ? e.hlen[(size_t)h] : mx;
+        }
+        e.len = mx;
+      }
       out.push_back(e);
     }
     table.swap(out);

@@ -21,7 +21,8 @@ KV_TRANSIENT = 1
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
     "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "kv_append_attend", "score_and_compact",
-    "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_diversity_score",
+    "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_merge_pages_layers",
+    "kv_diversity_score",
     "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
     "kv_get_head_lengths", "kv_last_error",
 )
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
             "kv_set_attend_splits": [P, I32],
             "kv_merge_pages": [P, I32, ctypes.POINTER(I32), P],
+            "kv_merge_pages_layers": [P, I32, I32, ctypes.POINTER(I32), P],
             "kv_diversity_score": [P, I32, P, I64, ctypes.POINTER(ctypes.c_double), P],
             "kv_layer_budgets": [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_double, I64, I32,
                                  ctypes.POINTER(I64)],
@@ -186,6 +188,12 @@ def kv_merge_pages(pool, layer, stream=None) -> int:
     n = ctypes.c_int32()
     _check(lib().kv_merge_pages(pool, layer, ctypes.byref(n), stream))
     return n.value
+
+
+def kv_merge_pages_layers(pool, first_layer, n_layers, stream=None) -> list:
+    n = (ctypes.c_int32 * n_layers)()
+    _check(lib().kv_merge_pages_layers(pool, first_layer, n_layers, n, stream))
+    return list(n)
 
 
 def kv_diversity_score(pool, layer, scores_ptr=None, score_stride=0, stream=None) -> float:
@@ -384,6 +392,10 @@ class KVCache:
 
     def merge_pages(self, layer) -> int:
         return kv_merge_pages(self.handle, layer, self._stream())
+
+    def merge_pages_layers(self, first_layer, n_layers) -> list:
+        """Page merges of n_layers layers in one call; pages released per layer."""
+        return kv_merge_pages_layers(self.handle, first_layer, n_layers, self._stream())
 
     def _scores_arg(self, scores):
         if scores is None:

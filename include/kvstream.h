@@ -247,10 +247,24 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
  * unchanged, so scores, keep sets and attention see the same tokens in the
  * same order.  Device work (one launch per 128 merges) is enqueued on
  * `stream`; no sync.  n_merged: optional host int32, pages released.
- * KV_ERR_STATE if sliding_window > 0 (window eviction removes whole frames,
- * so its pages must hold one frame each), and on a layer that
- * kv_diversity_prune has pruned (as for score_and_compact). */
+ * On a layer that kv_diversity_prune has pruned (heads holding different
+ * rows) the rule is applied per head: a page is appended to the page before
+ * it when every head's two lengths sum to at most page_tokens, each head's
+ * rows going after the rows that head already holds (one launch per 16
+ * merges at 16 heads; at most 320 heads, KV_ERR_ARG beyond).  Each head's
+ * token sequence in table order is unchanged, so the diversity top-K (ties
+ * by candidate index) and attention see the same tokens in the same order.
+ * Token ids are not moved there (such a page's id row describes none of its
+ * heads).  KV_ERR_STATE if sliding_window > 0 (window eviction removes whole
+ * frames, so its pages must hold one frame each). */
 kv_status kv_merge_pages(kv_pool_t* pool, int32_t layer, int32_t* n_merged, void* stream);
+
+/* kv_merge_pages for layers first_layer .. first_layer+n_layers-1 in one call:
+ * the moves of every layer share launches.  n_merged: optional host int32
+ * [n_layers], pages released per layer.  Every layer is checked first; on
+ * an error no layer changes. */
+kv_status kv_merge_pages_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, int32_t* n_merged,
+                                void* stream);
 
 /* Diversity scores of a layer's candidates ([INF] "Building Blocks",
  * "Cosine Similarity", step-by-step recipe steps 2-4).  Candidates: per head,

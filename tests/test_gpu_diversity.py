@@ -132,10 +132,70 @@ def test_diversity_small_ragged(dname):
     assert cache.info(0)["prunes"] == 1
     q = synth.iid_frame(96, 0, 0, (T, H, 64), device="cuda", dtype=dt)[0] * 0.125
     s.check_attention(q.contiguous(), 1.0, f"{dname} attention after the prune")
-    # CLCES and page merge refuse a layer whose heads hold different tokens
+    # CLCES refuses a layer whose heads hold different tokens
     with pytest.raises(kv.KVError) as e:
-        cache.merge_pages(0)
+        cache.score_and_compact(0, torch.ones((F * T, 1), device="cuda"), 5, 0.5, 10)
     assert e.value.status == kv.KV_ERR_STATE
+    # a second prune to 180 per head, then the per-head page merge: pages 2 and 3 go after page 1 (page 2
+    # holds no row of head 0), pages 5 and 6 after page 4, as in the oracle
+    assert cache.diversity_prune(0, 180) == [180] * H
+    s.sim.prune(s.key_of, 180, rank_dtype=np.float32)
+    moves = s.sim.merge_pages()
+    assert [(m[0], m[1]) for m in moves] == [(2, 1), (3, 1), (5, 4), (6, 4)]
+    assert cache.merge_pages(0) == len(moves)
+    assert cache.info(0)["merges"] == len(moves)
+    s.check_pages(f"{dname} per-head merge")
+    s.check_attention(q.contiguous(), 1.0, f"{dname} attention after the merge")
+    assert cache.merge_pages(0) == 0
+
+
+def test_diversity_stream_with_page_merge():
+    # per frame: append, prune to 260 per head, per-head page merge; pages, per-head lengths and attention
+    # against the oracle every frame (merges start at frame 6)
+    torch = torch_cuda()
+    T, H, F, B = 100, 4, 14, 260
+    cache = kv.KVCache(_cfg(T, F + 1, H, kv.KV_BF16), device="cuda")
+    s = Stream(cache, T, H, F + 1, wid=94)
+    merged = 0
+    for t in range(F):
+        s.append(t)
+        cache.diversity_prune(0, B)
+        s.sim.prune(s.key_of, B, rank_dtype=np.float32)
+        n = cache.merge_pages(0)
+        moves = s.sim.merge_pages()
+        assert n == len(moves), t
+        merged += n
+        s.check_pages(f"stream frame {t}")
+        q = synth.iid_frame(93, 0, t, (T, H, 64), device="cuda", dtype=torch.bfloat16)[0]
+        s.check_attention(q, 0.125, f"stream frame {t}")
+    assert merged > 0 and cache.info(0)["merges"] == merged
+    say(f"diversity stream with page merge: {merged} merges, {len(cache.page_table(0)[0])} pages at the end")
+
+
+def test_merge_pages_layers_batched():
+    # one call merges three layers: layers 0 and 1 are pruned (per-head merges), layer 2 is not (its full
+    # pages never fit together); each layer against its own oracle every frame
+    torch = torch_cuda()
+    T, H, F = 100, 4, 12
+    cache = kv.KVCache(_cfg(T, F + 1, H, kv.KV_BF16, layers=3), device="cuda")
+    streams = [Stream(cache, T, H, F + 1, wid=92, layer=l) for l in range(3)]
+    budgets = (230, 300)
+    merged = [0, 0, 0]
+    for t in range(F):
+        for s in streams:
+            s.append(t)
+        for l, b in enumerate(budgets):
+            cache.diversity_prune(l, b)
+            streams[l].sim.prune(streams[l].key_of, b, rank_dtype=np.float32)
+        n = cache.merge_pages_layers(0, 3)
+        for l in range(3):
+            assert n[l] == len(streams[l].sim.merge_pages()), (t, l)
+            merged[l] += n[l]
+            streams[l].check_pages(f"batched merge frame {t} layer {l}")
+    assert merged[0] > 0 and merged[1] > 0 and merged[2] == 0
+    q = synth.iid_frame(91, 0, 0, (T, H, 64), device="cuda", dtype=torch.bfloat16)[0]
+    for s in streams:
+        s.check_attention(q, 0.125, f"after batched merges, layer {s.layer}")
 
 
 def test_diversity_edge_cases():

@@ -197,6 +197,18 @@ def test_page_merge_host_rules():
     assert b.merge_pages(0) == 0
     assert b.page_table(0)[1] == [16] * 4
     assert b.info(0)["merges"] == 0
+    # the batched call: same rules for every layer, and a bad range changes nothing
+    m = _meta_pool(0, 0, 1, 5, layers=3)
+    for l in range(3):
+        m.append(l, 0, None, None)
+    assert m.merge_pages_layers(0, 3) == [0, 0, 0]
+    with pytest.raises(kv.KVError) as e:
+        m.merge_pages_layers(1, 3)
+    assert e.value.status == kv.KV_ERR_ARG
+    w = _meta_pool(1, 4, 1, 6, layers=2)
+    with pytest.raises(kv.KVError) as e:
+        w.merge_pages_layers(0, 2)
+    assert e.value.status == kv.KV_ERR_STATE
 
 
 def test_layer_budgets_match_oracle():
