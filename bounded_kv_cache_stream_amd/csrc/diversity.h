@@ -65,11 +65,9 @@ struct DivCall {
 // one for the call; no row moves once the call's word is set.
 hipError_t enqueue_diversity(const DivCall& c, hipStream_t s);
 
-// Device addresses of the per-slot outputs.
+// Device addresses of the outputs the host reads back: totals, then flags,
+// then the new lengths [slot][p_max][heads], adjacent in that order.
 inline double* div_totals(const DivCall& c) { return reinterpret_cast<double*>(c.ws + c.sizes.totals); }
 inline int32_t* div_flags(const DivCall& c) { return reinterpret_cast<int32_t*>(c.ws + c.sizes.flags); }
-inline int32_t* div_new_len(const DivCall& c, int slot) {  // [P][heads]
-  return reinterpret_cast<int32_t*>(c.ws + c.sizes.new_len) + (int64_t)slot * c.sizes.p_max * c.sizes.h_max;
-}
 
 }  // namespace kvs

@@ -633,12 +633,14 @@ DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers) 
   z.partial = take(L * H * P * kHeadDim * 8);
   z.mean = take(L * H * (kHeadDim + 1) * 8);
   z.spart = take(L * H * P * 8);
-  z.totals = take(L * 8);
-  z.flags = take((L + 1) * 4);
   z.dhist = take(L * 4 * H * 256 * 4);
   z.dstate = take(L * 5 * H * sizeof(DSel));
   z.lt_cnt = take(L * H * P * 4);
   z.eq_cnt = take(L * H * P * 4);
+  // the outputs the host reads back, adjacent: a scoring reads totals and
+  // flags in one copy, a prune flags and new lengths in one copy
+  z.totals = take(L * 8);
+  z.flags = take((L + 1) * 4);
   z.new_len = take(L * P * H * 4);
   z.total = off;
   return z;

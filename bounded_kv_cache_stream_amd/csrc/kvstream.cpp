@@ -139,6 +139,7 @@ struct kv_pool {
   std::vector<kvs::LayerPolicy> layers;
   std::vector<int64_t> scored_gen;  // per layer: the table generation its diversity keys belong to (-1: none)
   std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
+  std::vector<char> div_staging;       // host staging of the diversity calls (reused, never shrunk)
 };
 
 namespace {
@@ -175,11 +176,21 @@ DivPlan div_plan(const kv_pool_t* pool, int32_t layer) {
   const int32_t H = pool->cfg.num_heads;
   DivPlan d;
   d.n_head.assign((size_t)H, 0);
-  for (size_t i = L.first_candidate(); i < L.table.size(); ++i) {
+  const size_t first = L.first_candidate();
+  d.base.reserve(L.table.size() - std::min(first, L.table.size()));
+  int64_t uniform = 0;  // rows of pages whose heads all hold len rows
+  int64_t* nh = d.n_head.data();
+  for (size_t i = first; i < L.table.size(); ++i) {
     const auto& e = L.table[i];
     d.base.push_back(kvs::DevEntry{(int32_t)phys_page(pool, layer, e.page), e.len, e.hlen.empty() ? 0 : 1, 0});
-    for (int32_t h = 0; h < H; ++h) d.n_head[(size_t)h] += kvs::head_len(e, h);
+    if (e.hlen.empty()) {
+      uniform += e.len;
+    } else {
+      const int32_t* hl = e.hlen.data();
+      for (int32_t h = 0; h < H; ++h) nh[h] += hl[h];
+    }
   }
+  for (int32_t h = 0; h < H; ++h) nh[h] += uniform;
   for (int64_t n : d.n_head) {
     d.n_max = std::max(d.n_max, n);
     d.n_total += n;
@@ -197,19 +208,20 @@ kv_status check_layers(const kv_pool_t* p, int32_t first, int32_t n) {
 // One diversity call over a set of layers (slots in order): the host staging
 // block (per-layer parameters and candidate tables) and the launch arguments.
 struct DivBatch {
-  std::vector<char> staging;
   std::vector<int32_t> layer;  // slot -> layer
   kvs::DivCall call{};
 };
 
-DivBatch div_batch(const kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
+DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
                    const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, float* scores,
                    int64_t stride) {
   DivBatch b;
   const kvs::DivSizes& z = pool->lay.dv;
   const int n = (int)layers.size();
   b.layer = layers;
-  b.staging.assign(kvs::div_staging_bytes(z, n), 0);
+  // only the parameters and each slot's first P entries are read on the device
+  if (pool->div_staging.size() < kvs::div_staging_bytes(z, n)) pool->div_staging.resize(kvs::div_staging_bytes(z, n));
+  char* staging = pool->div_staging.data();
   kvs::DivCall& c = b.call;
   c.ws = pool->ws + pool->lay.div;
   c.sizes = z;
@@ -217,7 +229,7 @@ DivBatch div_batch(const kv_pool_t* pool, const std::vector<int32_t>& layers, co
   c.geom = pool->lay.geom;
   c.hlen_dev = hlens_dev(pool);
   c.keys_dev = reinterpret_cast<uint32_t*>(pool->ws + pool->lay.dkeys);
-  c.staging = b.staging.data();
+  c.staging = staging;
   c.n = n;
   c.prune = prune;
   c.scores_out = scores;
@@ -225,13 +237,13 @@ DivBatch div_batch(const kv_pool_t* pool, const std::vector<int32_t>& layers, co
   const int64_t per_layer = (int64_t)pool->cfg.num_heads * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
   for (int i = 0; i < n; ++i) {
     const DivPlan& d = *plans[(size_t)i];
-    kvs::DivLayer& L = kvs::div_staging_layers(b.staging.data())[i];
+    kvs::DivLayer& L = kvs::div_staging_layers(staging)[i];
     L.keys_off = (int64_t)layers[(size_t)i] * per_layer;
     L.N = d.n_max;
     L.keep = keep[(size_t)i];
     L.P = (int32_t)d.base.size();
     L.rescore = rescore[(size_t)i];
-    std::copy(d.base.begin(), d.base.end(), kvs::div_staging_bases(z, b.staging.data(), i));
+    std::copy(d.base.begin(), d.base.end(), kvs::div_staging_bases(z, staging, i));
     c.max_P = std::max(c.max_P, L.P);
     c.max_N = std::max(c.max_N, L.N);
     c.any_rescore = c.any_rescore || L.rescore;
@@ -264,13 +276,17 @@ kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, float
   for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
   hipError_t e = kvs::enqueue_diversity(b.call, st);
   if (e != hipSuccess) return hip_fail(e, "diversity scoring launch");
-  std::vector<double> sums(m);
-  std::vector<int32_t> flags(m + 1);
-  e = hipMemcpyAsync(sums.data(), kvs::div_totals(b.call), sizeof(double) * m, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(flags.data(), kvs::div_flags(b.call), sizeof(int32_t) * (m + 1), hipMemcpyDeviceToHost, st);
+  // one read-back: the float64 score sums, then (adjacent) the error flags
+  const kvs::DivSizes& z = pool->lay.dv;
+  const size_t flags_at = z.flags - z.totals;
+  std::vector<char> rb(flags_at + sizeof(int32_t) * (m + 1));
+  e = hipMemcpyAsync(rb.data(), kvs::div_totals(b.call), rb.size(), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "diversity scoring");
+  std::vector<double> sums(m);
+  std::vector<int32_t> flags(m + 1);
+  std::memcpy(sums.data(), rb.data(), sizeof(double) * m);
+  std::memcpy(flags.data(), rb.data() + flags_at, sizeof(int32_t) * (m + 1));
   for (size_t i = 0; i < m; ++i)
     if (flags[i] & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layers[i]);
   for (size_t i = 0; i < m; ++i) {
@@ -318,31 +334,31 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
     for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
     hipError_t e = kvs::enqueue_diversity(b.call, st);
     if (e != hipSuccess) return hip_fail(e, "diversity prune launch");
-    std::vector<int32_t> flags(m + 1);
-    std::vector<std::vector<int32_t>> nl(m);
-    e = hipMemcpyAsync(flags.data(), kvs::div_flags(b.call), sizeof(int32_t) * (m + 1), hipMemcpyDeviceToHost, st);
-    for (size_t i = 0; i < m && e == hipSuccess; ++i) {
-      nl[i].resize(pl[i]->base.size() * (size_t)H);
-      e = hipMemcpyAsync(nl[i].data(), kvs::div_new_len(b.call, (int)i), sizeof(int32_t) * nl[i].size(),
-                         hipMemcpyDeviceToHost, st);
-    }
+    // one read-back: the error flags, then (adjacent) every slot's new lengths [slot][p_max][H]
+    const kvs::DivSizes& z = pool->lay.dv;
+    const size_t len_at = (z.new_len - z.flags) / sizeof(int32_t);
+    std::vector<int32_t> rb(len_at + m * (size_t)z.p_max * (size_t)H);
+    e = hipMemcpyAsync(rb.data(), kvs::div_flags(b.call), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, "diversity prune");
+    const int32_t* flags = rb.data();
+    auto nl = [&](size_t i) { return rb.data() + len_at + i * (size_t)z.p_max * (size_t)H; };
     for (size_t i = 0; i < m; ++i)
       if (flags[i] & kvs::kDivErrNan)
         return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite (no layer changed)", layers[i]);
     for (size_t i = 0; i < m; ++i) {
       if (flags[i]) return fail(KV_ERR_HIP, "layer %d: diversity prune consistency check failed (flag %d, pool "
                                             "state undefined)", layers[i], flags[i]);
+      const int32_t* li = nl(i);
       for (int32_t h = 0; h < H; ++h) {
         int64_t k = 0;
-        for (size_t j = 0; j < pl[i]->base.size(); ++j) k += nl[i][j * (size_t)H + (size_t)h];
+        for (size_t j = 0; j < pl[i]->base.size(); ++j) k += li[j * (size_t)H + (size_t)h];
         if (k != std::min(kp[i], pl[i]->n_head[(size_t)h]))
           return fail(KV_ERR_HIP, "layer %d head %d: kept %lld candidates, expected %lld (pool state undefined)",
                       layers[i], h, (long long)k, (long long)std::min(kp[i], pl[i]->n_head[(size_t)h]));
       }
     }
-    for (size_t i = 0; i < m; ++i) pool->layers[(size_t)layers[i]].apply_head_compaction(nl[i], H);
+    for (size_t i = 0; i < m; ++i) pool->layers[(size_t)layers[i]].apply_head_compaction(nl(i), H);
   }
   if (kept)
     for (int32_t i = 0; i < n; ++i)

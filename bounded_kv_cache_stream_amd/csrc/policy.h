@@ -287,6 +287,7 @@ class LayerPolicy {
   }
 
   void commit_head_merges(const std::vector<HeadMergeMove>& mv, int heads) {
+    if (mv.empty()) return;
     std::set<int32_t> gone;
     std::map<int32_t, std::vector<int32_t>> grow;
     for (const auto& m : mv) {
@@ -295,13 +296,13 @@ class LayerPolicy {
       if (g.empty()) g.assign((size_t)heads, 0);
       for (int h = 0; h < heads; ++h) g[(size_t)h] += m.count[(size_t)h];
     }
-    std::vector<PageEntry> out;
-    for (const auto& e0 : table) {
-      if (gone.count(e0.page)) {
-        free_ids.insert(e0.page);
+    size_t w = 0;
+    for (size_t i = 0; i < table.size(); ++i) {
+      if (gone.count(table[i].page)) {
+        free_ids.insert(table[i].page);
         continue;
       }
-      PageEntry e = e0;
+      PageEntry& e = table[i];
       auto it = grow.find(e.page);
       if (it != grow.end()) {
         if (e.hlen.empty()) e.hlen.assign((size_t)heads, e.len);
@@ -312,34 +313,37 @@ class LayerPolicy {
         }
         e.len = mx;
       }
-      out.push_back(e);
+      if (w != i) table[w] = std::move(e);
+      ++w;
     }
-    table.swap(out);
+    table.erase(table.begin() + (long)w, table.end());
     merges += (int64_t)mv.size();
-    if (!mv.empty()) ++gen;
+    ++gen;
   }
 
   // Per-head new lengths for entries first_candidate().. ([entry][head]); a
   // page whose heads are all empty leaves the table and its id is freed.
   // Every remaining candidate page keeps its per-head lengths: its heads now
   // hold different tokens even where their counts agree.
-  void apply_head_compaction(const std::vector<int32_t>& new_lens, int heads) {
-    size_t f = first_candidate();
-    std::vector<PageEntry> out(table.begin(), table.begin() + (long)f);
+  void apply_head_compaction(const int32_t* new_lens, int heads) {
+    // in place: entries keep their per-head length vectors (no reallocation)
+    const size_t f = first_candidate();
+    size_t w = f;
     for (size_t i = f; i < table.size(); ++i) {
-      PageEntry e = table[i];
       const int32_t* nl = &new_lens[(i - f) * (size_t)heads];
       int32_t mx = 0;
       for (int h = 0; h < heads; ++h) mx = nl[h] > mx ? nl[h] : mx;
       if (mx == 0) {
-        free_ids.insert(e.page);
+        free_ids.insert(table[i].page);
         continue;
       }
+      PageEntry& e = table[i];
       e.len = mx;
       e.hlen.assign(nl, nl + heads);
-      out.push_back(e);
+      if (w != i) table[w] = std::move(e);
+      ++w;
     }
-    table.swap(out);
+    table.erase(table.begin() + (long)w, table.end());
     ++prunes;
     ++gen;
   }
