@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--frames", type=int, default=0, help="long workload: frames to run (0 = the full 10,000)")
     ap.add_argument("--merge", action="store_true",
                     help="budget / diversity workloads: merge ragged pages after each compaction / prune")
+    ap.add_argument("--defer", action="store_true",
+                    help="budget workload: score_and_compact returns once enqueued (KV_CLCES_DEFER); the next call "
+                         "on the layer applies the new page lengths")
     ap.add_argument("--fused", action="store_true",
                     help="stream/long workloads: one kv_append_attend call per frame (the page write shares the "
                          "table-upload launch) instead of append, evict and attend")
@@ -345,7 +348,7 @@ def run_budget(args):
             cache.attend(l, q, w["sm_scale"], out=out)
             if timed:
                 marks[2].record(stream)
-            cache.score_and_compact(l, table, w["clces_window"], w["lam"], B)
+            cache.score_and_compact(l, table, w["clces_window"], w["lam"], B, defer=args.defer)
             if timed:
                 marks[3].record(stream)
             if args.merge:
@@ -374,7 +377,7 @@ def run_budget(args):
     tiles = sum((n + 63) // 64 for n in lens) + (T + 63) // 64
     print(json.dumps({
         "metric": "frames/sec of the 24-layer token-budget stack (append, attend, score_and_compact"
-                  + (", merge_pages" if args.merge else "") + " per layer)",
+                  + (" deferred" if args.defer else "") + (", merge_pages" if args.merge else "") + " per layer)",
         "value": args.steps / wall, "unit": "frames/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps,
         "warmup": warm, "ms_per_frame": wall / args.steps * 1e3, "dtype": "bf16",
         "data": "synthetic (ring of 8 seeded AR(1) frames per layer, chi-square raw scores)",

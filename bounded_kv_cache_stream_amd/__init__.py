@@ -13,5 +13,5 @@ from .kvstream import (  # noqa: F401
     kv_get_head_lengths, kv_get_info, kv_get_page_table, kv_last_error, kv_layer_budgets, kv_merge_pages,
     kv_merge_pages_layers,
     kv_pool_create, kv_pool_destroy, kv_pool_get_layout, kv_pool_required_bytes, kv_reset, kv_set_attend_splits,
-    make_config, score_and_compact, stream_attend,
+    make_config, score_and_compact, stream_attend, kv_sync, KV_CLCES_DEFER,
 )

@@ -19,7 +19,7 @@ constexpr int32_t kMaxPageTokensScored = 8192;
 struct ClcesSizes {
   int64_t n_max;
   int32_t p_max, w_max, nblk_max;
-  size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts, plan,
+  size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts,
       move_src, move_dst, n_moves, flag, total;
 };
 
@@ -56,5 +56,12 @@ hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* va
 // Enqueues the whole step, then waits for it and returns the new page
 // lengths (one per candidate entry) and the error flags.
 hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s);
+
+// The same step without the wait: enqueues the kernels only.  Its result (the
+// error flag, then the new length of each of the n_entries pages) is at
+// clces_result(a) on the device once the stream reaches this point, until the
+// next step that uses the same workspace.
+hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s);
+int32_t* clces_result(const ClcesArgs& a);
 
 }  // namespace kvs

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <utility>
 
@@ -546,11 +547,10 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.sel_state = take(9 * sizeof(SelState));
   z.entries = take((size_t)p_max * sizeof(DevEntry));
   z.counts = take((size_t)p_max * 2 * 4);
-  z.plan = take((size_t)p_max * 3 * 4);
   z.move_src = take((size_t)p_max * ts_max * 2);
   z.move_dst = take((size_t)p_max * ts_max * 2);
   z.n_moves = take((size_t)p_max * 4);
-  z.flag = take(4);
+  z.flag = take(((size_t)p_max + 1) * 4);  // the error flag, then the new page lengths [p_max]
   z.total = off;
   return z;
 }
@@ -579,7 +579,7 @@ hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* va
   return hipGetLastError();
 }
 
-hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s) {
+hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
   const ClcesSizes& z = a.sizes;
   char* ws = a.ws;
   auto* entries = reinterpret_cast<DevEntry*>(ws + z.entries);
@@ -594,7 +594,6 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
   auto* sel_hist = reinterpret_cast<uint32_t*>(ws + z.sel_hist);
   auto* sel_state = reinterpret_cast<SelState*>(ws + z.sel_state);
   auto* counts = reinterpret_cast<int32_t*>(ws + z.counts);
-  auto* plan = reinterpret_cast<int32_t*>(ws + z.plan);
   auto* flag = reinterpret_cast<int32_t*>(ws + z.flag);
   const int P = a.n_entries, N = a.n_tokens, W = a.n_window;
   if (P > z.p_max || (int64_t)N > z.n_max || W > z.w_max || a.geom.ts > kMaxPageTokensScored)
@@ -635,7 +634,7 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
                  reinterpret_cast<uint16_t*>(ws + z.move_src),
                  reinterpret_cast<uint16_t*>(ws + z.move_dst),
                  reinterpret_cast<int32_t*>(ws + z.n_moves),
-                 shat, sel_state + 8, counts, counts + P, plan + 2 * P, P, a.pool, a.geom, a.keep_ids_out, flag,
+                 shat, sel_state + 8, counts, counts + P, flag + 1, P, a.pool, a.geom, a.keep_ids_out, flag,
                  flag};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
@@ -651,13 +650,22 @@ hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_fl
     else
       compact_kernel<float, 256><<<cg, dim3(256), 0, s>>>(ca);
   }
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+int32_t* clces_result(const ClcesArgs& a) { return reinterpret_cast<int32_t*>(a.ws + a.sizes.flag); }
+
+hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s) {
+  hipError_t e = enqueue_clces(a, s);
   if (e != hipSuccess) return e;
-  e = hipMemcpyAsync(new_lens_host, plan + 2 * P, sizeof(int32_t) * (size_t)P, hipMemcpyDeviceToHost, s);
+  // one read-back: the error flag and, after it, the new page lengths
+  std::vector<int32_t> rb((size_t)a.n_entries + 1);
+  e = hipMemcpyAsync(rb.data(), clces_result(a), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return e;
-  e = hipMemcpyAsync(err_flag_host, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s);
-  if (e != hipSuccess) return e;
-  return hipStreamSynchronize(s);
+  *err_flag_host = rb[0];
+  std::copy(rb.begin() + 1, rb.end(), new_lens_host);
+  return hipSuccess;
 }
 
 }  // namespace kvs

@@ -140,14 +140,66 @@ struct kv_pool {
   std::vector<int64_t> scored_gen;  // per layer: the table generation its diversity keys belong to (-1: none)
   std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
   std::vector<char> div_staging;       // host staging of the diversity calls (reused, never shrunk)
+  // deferred score_and_compact steps (KV_CLCES_DEFER): per layer, whether one
+  // is pending, the event after its read-back, its page count and keep count;
+  // the read-backs land in pinned host memory, (pages_per_layer + 1) ints per
+  // layer (the error flag, then the new page lengths)
+  struct Pending {
+    bool active = false;
+    hipEvent_t done = nullptr;
+    int32_t n_entries = 0;
+    int64_t keep = 0;
+  };
+  std::vector<Pending> pending;
+  int32_t* pinned = nullptr;
 };
 
 namespace {
 
+// Completes the layer's deferred score_and_compact, if one is pending: waits
+// for its read-back and applies the new page lengths to the host table, or
+// returns the step's error (its kernels then moved no row, and the table stays
+// as it was).
+kv_status settle(kv_pool_t* p, int32_t layer) {
+  auto& ps = p->pending[(size_t)layer];
+  if (!ps.active) return KV_OK;
+  ps.active = false;
+  hipError_t e = hipEventSynchronize(ps.done);
+  if (e != hipSuccess) return hip_fail(e, "deferred score_and_compact");
+  const int32_t* rb = p->pinned + (size_t)layer * ((size_t)p->cfg.pages_per_layer + 1);
+  if (rb[0] & kvs::kClcesErrNan)
+    return fail(KV_ERR_NAN, "layer %d: a raw score of the deferred score_and_compact is NaN or negative (nothing "
+                            "changed)", layer);
+  if (rb[0] & kvs::kClcesErrRow)
+    return fail(KV_ERR_ARG, "layer %d: a token id of the deferred score_and_compact is >= score_rows (nothing "
+                            "changed)", layer);
+  if (rb[0]) return fail(KV_ERR_HIP, "layer %d: deferred CLCES consistency check failed (flag %d)", layer, rb[0]);
+  std::vector<int32_t> nl(rb + 1, rb + 1 + ps.n_entries);
+  int64_t kept = 0;
+  for (int32_t v : nl) kept += v;
+  if (kept != ps.keep)
+    return fail(KV_ERR_HIP, "layer %d: deferred step kept %lld tokens, expected %lld", layer, (long long)kept,
+                (long long)ps.keep);
+  p->layers[(size_t)layer].apply_compaction(nl, kept);
+  return KV_OK;
+}
+
+// Waits for a pending read-back and drops its result (reset, destroy).
+void discard_pending(kv_pool_t* p) {
+  for (auto& ps : p->pending)
+    if (ps.active) {
+      (void)hipEventSynchronize(ps.done);
+      ps.active = false;
+    }
+}
+
+// Every entry point that names a layer checks it here, which also completes a
+// deferred step of that layer first (the const getters included: a pool is
+// never created const).
 kv_status check_layer(const kv_pool_t* p, int32_t layer) {
   if (!p) return fail(KV_ERR_ARG, "pool is NULL");
   if (layer < 0 || layer >= p->cfg.num_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
-  return KV_OK;
+  return settle(const_cast<kv_pool_t*>(p), layer);
 }
 
 int64_t phys_page(const kv_pool_t* p, int32_t layer, int32_t page) {
@@ -202,6 +254,10 @@ kv_status check_layers(const kv_pool_t* p, int32_t first, int32_t n) {
   if (!p) return fail(KV_ERR_ARG, "pool is NULL");
   if (n < 1 || first < 0 || first + n > p->cfg.num_layers)
     return fail(KV_ERR_ARG, "layers %d..%d out of range", first, first + n - 1);
+  for (int32_t l = first; l < first + n; ++l) {
+    kv_status s = settle(const_cast<kv_pool_t*>(p), l);
+    if (s != KV_OK) return s;
+  }
   return KV_OK;
 }
 
@@ -419,6 +475,7 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   p->meta_only = meta;
   p->layers.resize((size_t)cfg->num_layers);
   p->scored_gen.assign((size_t)cfg->num_layers, -1);
+  p->pending.resize((size_t)cfg->num_layers);
   for (auto& l : p->layers)
     l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens,
            cfg->special_tokens);
@@ -428,14 +485,41 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
 
 kv_status kv_pool_destroy(kv_pool_t* pool) {
   if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  discard_pending(pool);
+  for (auto& ps : pool->pending)
+    if (ps.done) (void)hipEventDestroy(ps.done);
+  if (pool->pinned) (void)hipHostFree(pool->pinned);
   delete pool;
   return ok();
 }
 
 kv_status kv_reset(kv_pool_t* pool) {
   if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  discard_pending(pool);
   for (auto& l : pool->layers) l.reset();
   return ok();
+}
+
+kv_status kv_sync(kv_pool_t* pool, int32_t layer) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  if (layer == -1) {
+    kv_status first_err = KV_OK;
+    std::string msg;
+    for (int32_t l = 0; l < pool->cfg.num_layers; ++l) {
+      kv_status s = settle(pool, l);
+      if (s != KV_OK && first_err == KV_OK) {
+        first_err = s;
+        msg = g_err;
+      }
+    }
+    if (first_err != KV_OK) {
+      g_err = msg;
+      return first_err;
+    }
+    return ok();
+  }
+  kv_status s = check_layer(pool, layer);
+  return s != KV_OK ? s : ok();
 }
 
 kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, const void* k_dev, const void* v_dev,
@@ -755,6 +839,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
     return fail(KV_ERR_ARG, "window %d out of 1..max_window (%d)", params->window, pool->cfg.max_window);
   if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
+  if (params->flags & ~KV_CLCES_DEFER) return fail(KV_ERR_ARG, "unknown CLCES flags 0x%x", params->flags);
   auto& L = pool->layers[(size_t)layer];
   if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   if (pool->cfg.special_tokens > 0)
@@ -801,6 +886,28 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   a.keep = params->keep_count;
   a.keep_ids_out = keep_ids_out_dev;
   a.ranks_out = ranks_out_dev;
+  if (params->flags & KV_CLCES_DEFER) {
+    // enqueue the step and its read-back; the next call on this layer applies it
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto& ps = pool->pending[(size_t)layer];
+    hipError_t e = hipSuccess;
+    if (!pool->pinned)
+      e = hipHostMalloc(reinterpret_cast<void**>(&pool->pinned),
+                        sizeof(int32_t) * (size_t)pool->cfg.num_layers * ((size_t)pool->cfg.pages_per_layer + 1),
+                        hipHostMallocDefault);
+    if (e == hipSuccess && !ps.done) e = hipEventCreateWithFlags(&ps.done, hipEventDisableTiming);
+    if (e == hipSuccess) e = kvs::enqueue_clces(a, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(pool->pinned + (size_t)layer * ((size_t)pool->cfg.pages_per_layer + 1), kvs::clces_result(a),
+                         sizeof(int32_t) * ((size_t)a.n_entries + 1), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipEventRecord(ps.done, st);
+    if (e != hipSuccess) return hip_fail(e, "deferred CLCES step");
+    ps.active = true;
+    ps.n_entries = a.n_entries;
+    ps.keep = params->keep_count;
+    if (n_kept) *n_kept = params->keep_count;
+    return ok();
+  }
   std::vector<int32_t> new_lens((size_t)a.n_entries);
   int32_t err_flag = 0;
   hipError_t e = kvs::run_clces(a, new_lens.data(), &err_flag, static_cast<hipStream_t>(stream));

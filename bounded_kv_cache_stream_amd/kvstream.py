@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_ERR_ARG, KV_ERR_SHAPE, KV_ERR_NO_PAGES, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_NAN = 0, -1, -2, -3, -4, -5, -6
+KV_CLCES_DEFER = 1
 KV_BF16, KV_FP32 = 0, 1
 KV_TRANSIENT = 1
 
@@ -24,7 +25,7 @@ EXPORTED = (
     "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_merge_pages_layers",
     "kv_diversity_score",
     "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
-    "kv_get_head_lengths", "kv_last_error",
+    "kv_get_head_lengths", "kv_sync", "kv_last_error",
 )
 
 
@@ -35,7 +36,7 @@ class kv_pool_config(ctypes.Structure):
 
 
 class kv_clces_params(ctypes.Structure):
-    _fields_ = [("window", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lambda_", ctypes.c_double),
+    _fields_ = [("window", ctypes.c_int32), ("flags", ctypes.c_uint32), ("lambda_", ctypes.c_double),
                 ("keep_count", ctypes.c_int64)]
 
 
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "kv_diversity_score_layers": [P, I32, I32, ctypes.POINTER(ctypes.c_double), P],
             "kv_diversity_prune_layers": [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), P],
             "kv_get_head_lengths": [P, I32, P, I32, ctypes.POINTER(I32)],
+            "kv_sync": [P, I32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -176,12 +178,16 @@ def kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_pt
 
 
 def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_count, keep_ids_ptr=None,
-                      ranks_ptr=None, stream=None) -> int:
-    prm = kv_clces_params(window, 0, lam, keep_count)
+                      ranks_ptr=None, stream=None, defer=False) -> int:
+    prm = kv_clces_params(window, KV_CLCES_DEFER if defer else 0, lam, keep_count)
     n = ctypes.c_int64()
     _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
                                    ctypes.byref(n), stream))
     return n.value
+
+
+def kv_sync(pool, layer=-1) -> None:
+    _check(lib().kv_sync(pool, layer))
 
 
 def kv_merge_pages(pool, layer, stream=None) -> int:
@@ -368,7 +374,8 @@ class KVCache:
                              qp, q.shape[0], float(sm_scale), op, lp, self._stream())
         return out, n
 
-    def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None) -> int:
+    def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None,
+                          defer=False) -> int:
         torch = self.torch
         if score_table.dtype != torch.float32 or not score_table.is_contiguous() or score_table.dim() != 2 \
                 or score_table.shape[1] != self.cfg.num_layers:
@@ -376,19 +383,25 @@ class KVCache:
         for t in (keep_ids, ranks):
             if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError("keep_ids / ranks must be contiguous int32 tensors")
-        # the library writes keep_count ids and n_window x N ranks (N = the candidate tokens, pages of the
-        # scale frames excluded); it cannot see the buffers' sizes
-        _, lens, frames = self.page_table(layer)
-        n_cand = sum(n for n, f in zip(lens, frames) if f >= self.cfg.scale_frames)
-        if keep_ids is not None and keep_ids.numel() < min(keep_count, n_cand):
-            raise ValueError(f"keep_ids holds {keep_ids.numel()} ids, the step writes {min(keep_count, n_cand)}")
-        if ranks is not None and ranks.numel() < min(window, layer + 1) * n_cand:
-            raise ValueError(f"ranks holds {ranks.numel()} entries, the step writes "
-                             f"{min(window, layer + 1) * n_cand}")
+        # the library writes up to keep_count ids and n_window x N ranks (N = the candidate tokens, pages of
+        # the scale frames excluded); it cannot see the buffers' sizes
+        if keep_ids is not None and keep_ids.numel() < keep_count:
+            raise ValueError(f"keep_ids holds {keep_ids.numel()} ids, the step may write {keep_count}")
+        if ranks is not None:
+            _, lens, frames = self.page_table(layer)
+            n_cand = sum(n for n, f in zip(lens, frames) if f >= self.cfg.scale_frames)
+            if ranks.numel() < min(window, layer + 1) * n_cand:
+                raise ValueError(f"ranks holds {ranks.numel()} entries, the step writes "
+                                 f"{min(window, layer + 1) * n_cand}")
         return score_and_compact(self.handle, layer, ctypes.c_void_p(score_table.data_ptr()), score_table.shape[0],
                                  window, lam, keep_count,
                                  None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),
-                                 None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream())
+                                 None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream(),
+                                 defer)
+
+    def sync(self, layer=-1) -> None:
+        """Complete deferred score_and_compact steps (layer -1: every layer); raises their error, if any."""
+        kv_sync(self.handle, layer)
 
     def merge_pages(self, layer) -> int:
         return kv_merge_pages(self.handle, layer, self._stream())

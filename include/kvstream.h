@@ -73,11 +73,15 @@ typedef struct {
                              /* "Special Token Persistence"), 0..page_tokens       */
 } kv_pool_config;
 
+/* score_and_compact flag: return once the step is enqueued (see there). */
+#define KV_CLCES_DEFER 1u
+
 /* Parameters of one CLCES step ([SCV] 2.1.1-2.1.3): window W = 5 layers,
- * lambda = 0.5 on the pages; keep_count = tokens kept (the budget). */
+ * lambda = 0.5 on the pages; keep_count = tokens kept (the budget); flags =
+ * 0 or KV_CLCES_DEFER. */
 typedef struct {
   int32_t window;
-  int32_t reserved;
+  uint32_t flags;
   double lambda;
   int64_t keep_count;
 } kv_clces_params;
@@ -230,11 +234,25 @@ kv_status kv_append_attend(kv_pool_t* pool, int32_t layer, int64_t frame_idx, co
  * of a frame's first slots).
  * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
  * for a token id >= score_rows or a bad parameter.  Synchronises the stream
- * once to read the new page lengths. */
+ * once to read the new page lengths.
+ * With flags = KV_CLCES_DEFER the call returns once the step and the
+ * read-back of its page lengths (into pinned host memory the pool allocates
+ * on first use) are enqueued, *n_kept = keep_count, and the layer's host table
+ * is brought up to date by the next call that names the layer (or by
+ * kv_sync), which waits for that read-back first.  An error the kernels find
+ * (NaN score, token id out of range) is then returned by that next call, which
+ * does nothing else; the step moved no row and the layer is as it was.  Calls
+ * on other layers do not wait.  Later calls must be issued on the same stream
+ * (or one ordered after it): steps of all layers share the workspace. */
 kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_table_dev,
                             int64_t score_rows, const kv_clces_params* params,
                             int32_t* keep_ids_out_dev, int32_t* ranks_out_dev, int64_t* n_kept,
                             void* stream);
+
+/* Completes the deferred score_and_compact of a layer (layer = -1: of every
+ * layer) and returns its error, if any (the first one for -1).  A no-op where
+ * nothing is pending. */
+kv_status kv_sync(kv_pool_t* pool, int32_t layer);
 
 /* Page merge: defragments the ragged pages that compaction leaves in a
  * token-budget layer (no passage of the pages covers it; it keeps the number of

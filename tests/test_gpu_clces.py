@@ -216,3 +216,66 @@ def test_clces_24_layers_72288_tokens_keep_half():
                 sl = torch.from_numpy(idv - f * T)
                 _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
         say(f"CLCES layer {l}: ranks, {K} kept ids and {len(ids)} page lengths bit-exact")
+
+
+def test_deferred_steps_match_synchronous_ones():
+    # KV_CLCES_DEFER: the step returns once enqueued and the next call naming the layer applies its result.
+    # Three layers through append -> attend -> score_and_compact, one pool synchronous, one deferred:
+    # attention outputs, keep ids, page tables and page bytes equal every frame
+    torch = torch_cuda()
+    T, H, L, F, B = 100, 2, 3, 12, 250
+    a = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+    b = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+    table = torch.from_numpy(synth.raw_scores(89, F * T, L)).cuda()
+    ka = torch.empty(B, dtype=torch.int32, device="cuda")
+    kb = torch.empty(B, dtype=torch.int32, device="cuda")
+    for t in range(F):
+        for l in range(L):
+            q, k, v = synth.iid_frame(89, l, t, (T, H, 64), device="cuda", dtype=torch.bfloat16)
+            a.append(l, t, k, v)
+            b.append(l, t, k, v)
+            oa, ob = a.attend(l, q, 0.125), b.attend(l, q, 0.125)
+            assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), (t, l)
+            na = a.score_and_compact(l, table, 5, 0.5, B, keep_ids=ka)
+            nb = b.score_and_compact(l, table, 5, 0.5, B, keep_ids=kb, defer=True)
+            assert na == nb == min(B, (t + 1) * T)
+            if (t + 1) * T > B:
+                torch.cuda.synchronize()
+                assert torch.equal(ka, kb), (t, l)
+        for l in range(L):
+            ids, lens, fr = a.page_table(l)
+            assert (ids, lens, fr) == b.page_table(l), (t, l)
+            for pid, n in zip(ids, lens):
+                for x, y in zip(a.page_view(l, pid), b.page_view(l, pid)):
+                    assert torch.equal(x[..., :n, :].cpu() if x.dim() == 3 else x[:n].cpu(),
+                                       y[..., :n, :].cpu() if y.dim() == 3 else y[:n].cpu())
+    b.sync()
+    assert a.info(2) == b.info(2)
+
+
+def test_deferred_step_error_surfaces_on_the_next_call():
+    torch = torch_cuda()
+    T, H, L = 64, 2, 2
+    c = kv.KVCache(_cfg(L, T, 6, H=H), device="cuda")
+    for layer in range(L):
+        _fill(c, layer, 4, T, H, 88)
+    table = torch.from_numpy(synth.raw_scores(88, 4 * T, L)).cuda()
+    bad = table.clone()
+    bad[5, 1] = float("nan")
+    before = c.page_table(1)
+    assert c.score_and_compact(1, bad, 5, 0.5, 100, defer=True) == 100  # enqueued: no error yet
+    # a call on another layer does not wait for it, and succeeds
+    assert c.score_and_compact(0, table, 5, 0.5, 100, defer=True) == 100
+    with pytest.raises(kv.KVError) as e:  # the next call naming layer 1 reports the step's error
+        c.page_table(1)
+    assert e.value.status == kv.KV_ERR_NAN
+    assert c.page_table(1) == before  # nothing changed, and the layer works again
+    assert c.score_and_compact(1, table, 5, 0.5, 100, defer=True) == 100
+    c.sync()
+    assert sum(c.page_table(1)[1]) == 100 and sum(c.page_table(0)[1]) == 100
+    # a pending step survives reset and destroy without use
+    assert c.score_and_compact(0, table, 5, 0.5, 50, defer=True) == 50
+    c.reset()
+    assert c.page_table(0) == ([], [], [])
+    c.close()
+    torch.cuda.synchronize()

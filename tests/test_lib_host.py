@@ -362,3 +362,19 @@ def test_append_attend_checks_before_changing_anything():
         kv.kv_append_attend(c.handle, 0, 1, None, None, 16, 0, None, 65, 1.0, None)
     assert e.value.status == kv.KV_ERR_SHAPE
     assert (c.page_table(0), c.info(0)) == before
+
+
+def test_clces_flags_and_sync_on_a_metadata_pool():
+    # unknown flag bits are refused before anything else; kv_sync is a no-op where nothing is pending
+    c = _meta_pool(0, 0, 1, 5)
+    for t in range(3):
+        c.append(0, t, None, None)
+    prm = kv.kv_clces_params(5, 2, 0.5, 10)
+    n = ctypes.c_int64()
+    st = kv.lib().score_and_compact(c.handle, 0, None, 0, ctypes.byref(prm), None, None, ctypes.byref(n), None)
+    assert st == kv.KV_ERR_ARG and "flags" in kv.kv_last_error()
+    kv.kv_sync(c.handle, -1)
+    kv.kv_sync(c.handle, 0)
+    with pytest.raises(kv.KVError):
+        kv.kv_sync(c.handle, 1)
+    assert c.page_table(0)[1] == [16] * 3
