@@ -137,11 +137,15 @@ kv_status kv_pool_get_layout(const kv_pool_config* cfg, kv_pool_layout* out);
 kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_bytes,
                          void* workspace_dev, size_t workspace_bytes, kv_pool_t** out);
 
+/* Release the pool's host state.  Waits for the read-back of any deferred
+ * score_and_compact first and frees the pinned memory and events such steps
+ * used; the caller's device buffers are left untouched. */
 kv_status kv_pool_destroy(kv_pool_t* pool);
 
 /* Drop every cached frame of every layer and reset statistics and frame
  * order ([GCT] "Cache Initialization and Cleanup", clean_kv_cache()).
- * Host-only; device contents are left as they are. */
+ * Host-only; device contents are left as they are.  The result of a pending
+ * deferred score_and_compact is waited for and dropped. */
 kv_status kv_reset(kv_pool_t* pool);
 
 /* Write frame frame_idx of one layer into the cache ([FPS] "Page-Aligned
