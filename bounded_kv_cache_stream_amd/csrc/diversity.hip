@@ -306,12 +306,13 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
   uint32_t* kk = head_keys(a, L, h);
   double ssum = 0.0;
   bool bad = false;
+  static_assert(kUnroll <= kTPR, "one lane of a row group per unrolled row");
   for (int j0 = 0; j0 < en.len; j0 += kRowsPerPass * kUnroll) {
     RowPart<T> raw[kUnroll];
     load_rows<T>(rows, j0, r, c, en.len, raw);
+    double s2u[kUnroll], dotu[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int j = j0 + u * kRowsPerPass + r;
       double x[8];
       widen(raw[u], x);
       double s2 = 0.0, dot = 0.0;
@@ -320,9 +321,22 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
         s2 = s2 + x[i] * x[i];
         dot = dot + x[i] * sv[i];
       }
-      s2 = row_sum(s2);
-      dot = row_sum(dot);
-      if (j < en.len && c == 0) {
+      // every lane of the row group holds the same sums afterwards
+      s2u[u] = row_sum(s2);
+      dotu[u] = row_sum(dot);
+    }
+    // lane u of each row group finishes unrolled row u: the square root and
+    // the division run once for kUnroll rows
+    if (c < kUnroll) {
+      double s2 = s2u[0], dot = dotu[0];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u)
+        if (c == u) {
+          s2 = s2u[u];
+          dot = dotu[u];
+        }
+      const int j = j0 + c * kRowsPerPass + r;
+      if (j < en.len) {
         const double sc = (s2 > 0.0 && sn > 0.0) ? -(dot / (sqrt(s2) * sn)) : 0.0;
         bad = bad || !(s2 <= 1.0e300) || !(sc == sc);  // a NaN or infinite key
         const float f = (float)sc;
