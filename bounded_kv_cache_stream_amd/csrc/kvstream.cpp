@@ -553,9 +553,8 @@ kv_status kv_append_frame(kv_pool_t* pool, int32_t layer, int64_t frame_idx, con
 kv_status kv_append_frame_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_layers, int64_t frame_idx,
                                  const void* k_dev, const void* v_dev, int32_t n_tokens, uint32_t flags,
                                  void* stream) {
-  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
-  if (n_layers < 1 || first_layer < 0 || first_layer + n_layers > pool->cfg.num_layers)
-    return fail(KV_ERR_ARG, "layers %d..%d out of range", first_layer, first_layer + n_layers - 1);
+  kv_status s = check_layers(pool, first_layer, n_layers);  // completes deferred steps of these layers
+  if (s != KV_OK) return s;
   if (n_tokens != pool->cfg.page_tokens)
     return fail(KV_ERR_SHAPE, "n_tokens %d != page_tokens %d", n_tokens, pool->cfg.page_tokens);
   if (frame_idx < 0) return fail(KV_ERR_ARG, "negative frame index");

@@ -253,6 +253,34 @@ def test_deferred_steps_match_synchronous_ones():
     assert a.info(2) == b.info(2)
 
 
+def test_deferred_steps_then_batched_page_writes():
+    # the batched page write names a range of layers: it completes their deferred steps before it adds a page,
+    # so the deferred pool's tables track the synchronous pool's frame by frame
+    torch = torch_cuda()
+    T, H, L, F, B = 100, 2, 3, 10, 250
+    a = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+    b = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+    table = torch.from_numpy(synth.raw_scores(87, F * T, L)).cuda()
+    for t in range(F):
+        frames = [synth.iid_frame(87, l, t, (T, H, 64), device="cuda", dtype=torch.bfloat16) for l in range(L)]
+        k = torch.stack([f[1] for f in frames])
+        v = torch.stack([f[2] for f in frames])
+        a.append_layers(0, t, k, v)
+        b.append_layers(0, t, k, v)  # layers still carry the previous frame's deferred steps
+        for l in range(L):
+            assert a.page_table(l) == b.page_table(l), (t, l)
+        for l in range(L):
+            assert a.score_and_compact(l, table, 5, 0.5, B) == b.score_and_compact(l, table, 5, 0.5, B, defer=True)
+    b.sync()
+    for l in range(L):
+        assert a.page_table(l) == b.page_table(l), l
+        ids, lens, _ = a.page_table(l)
+        for pid, n in zip(ids, lens):
+            for x, y in zip(a.page_view(l, pid), b.page_view(l, pid)):
+                assert torch.equal(x[..., :n, :].cpu() if x.dim() == 3 else x[:n].cpu(),
+                                   y[..., :n, :].cpu() if y.dim() == 3 else y[:n].cpu())
+
+
 def test_deferred_step_error_surfaces_on_the_next_call():
     torch = torch_cuda()
     T, H, L = 64, 2, 2
