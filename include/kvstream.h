@@ -24,6 +24,10 @@
  *     waiting, except where a function says it synchronises.
  *   - Layouts are row-major.  A frame's K, V and Q are [n_tokens][H][D].
  *   - Calls on one pool must not overlap from several host threads.
+ *   - The device work of every call on one pool uses the pool's workspace
+ *     (page-table mirrors, attention partials, CLCES and diversity scratch):
+ *     issue a pool's calls on one stream, or order the streams with events,
+ *     so that no two of its calls run on the GPU at once.
  */
 #ifndef KVSTREAM_H
 #define KVSTREAM_H
