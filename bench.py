@@ -24,7 +24,10 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk/CU)
 PEAK_HBM_GBS = 8000.0
+PEAK_SCLK_MHZ = 2400.0  # the clock the bf16 peak assumes
 ATTEND_SOURCE = os.path.join(ROOT, "bounded_kv_cache_stream_amd", "csrc", "attend.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_traffic.json")
 
@@ -67,6 +71,9 @@ def parse():
                          "table-upload launch) instead of append, evict and attend")
     ap.add_argument("--heads", type=int, default=0,
                     help="stream workload: heads per GPU (default 16; 2 = one GPU's share when 8 GPUs split the heads)")
+    ap.add_argument("--sclk", action="store_true",
+                    help="stream workload: sample the shader clock with rocm-smi during the timed steps (use "
+                         "--steps 20000 or so: one read takes about half a second)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -75,6 +82,43 @@ def parse():
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (rocm-smi's sclk level, read in a child process) in a thread
+    while the timed steps run.  One read takes about half a second, so a timed region of a few seconds is
+    needed for a useful median."""
+
+    PATTERN = re.compile(r"sclk clock level: \S+ \((\d+)Mhz\)")
+
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = self.PATTERN.search(r.stdout)
+            if m:
+                self.samples.append((time.perf_counter(), int(m.group(1))))
+            self._stop.wait(0.05)
+
+    def start(self):
+        self._thread.start()
+
+    def stop(self, t0, t1):
+        """Stops sampling; the summary of the reads that completed between t0 and t1 (perf_counter)."""
+        self._stop.set()
+        self._thread.join()
+        mhz = sorted(v for t, v in self.samples if t0 <= t <= t1)
+        if not mhz:
+            return {"median": None, "samples": 0, "note": "no read completed inside the timed steps"}
+        return {"median": mhz[len(mhz) // 2], "min": mhz[0], "max": mhz[-1], "samples": len(mhz),
+                "source": "rocm-smi current sclk level, read during the timed steps"}
 
 
 def recorded_traffic(heads, splits):
@@ -639,6 +683,9 @@ def main():
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    sampler = ClockSampler() if args.sclk else None
+    if sampler:
+        sampler.start()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
@@ -646,6 +693,7 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    sclk = sampler.stop(wall0, wall0 + wall) if sampler else None
     ms_total = t_start.elapsed_time(t_end)
     info = cache.info(0)
     assert info["persisted_frames"] == S + Wf and info["tokens"] == (S + Wf) * T + info["special_tokens"]
@@ -696,6 +744,13 @@ def main():
                      "p90_call_us": attend_sorted[int(0.9 * (len(attend_sorted) - 1))] * 1e3},
         "wall_s_timed": wall,
     }
+    if sclk is not None:
+        result["sclk_mhz"] = sclk
+        if sclk["median"]:
+            # the same kernel against the bf16 peak at the clock it ran at
+            clk_peak = PEAK_BF16_TFLOPS * sclk["median"] / PEAK_SCLK_MHZ
+            result["roofline"]["peak_at_measured_sclk"] = clk_peak
+            result["roofline"]["frac_at_measured_sclk"] = achieved / clk_peak
     if not args.no_cpu_baseline:
         last = fill + args.warmup + args.steps - 1
         attended = list(range(S)) + list(range(last - Wf + 1, last + 1))
