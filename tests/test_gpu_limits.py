@@ -5,6 +5,7 @@
 - One-token pages: a window stream with transient frames, and a token-budget stream whose compaction
   empties pages.
 - A single query row, and a query count one past a 256-row workgroup tile.
+- An fp32 pool with pages of several tiles and a ragged tail.
 """
 
 import numpy as np
@@ -13,28 +14,30 @@ import pytest
 from bounded_kv_cache_stream_amd import kvstream as kv
 from bounded_kv_cache_stream_amd import synth
 from oracle import attention, budget, window
-from tests.gpu_common import LSE_ABS_BF16, assert_close, max_abs, say, to64, torch_cuda
+from tests.gpu_common import LSE_ABS_BF16, LSE_ABS_FP32, assert_close, max_abs, say, to64, torch_cuda
 from tests.test_gpu_clces import _page_bytes_equal
 from tests.test_gpu_diversity import Stream as DivStream
 
 pytestmark = pytest.mark.gpu
 
 
-def _window_cfg(T, H, S, W, k, pages, max_queries, max_splits=16):
-    return kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=W,
+def _window_cfg(T, H, S, W, k, pages, max_queries, max_splits=16, dtype=kv.KV_BF16):
+    return kv.make_config(num_layers=1, num_heads=H, page_tokens=T, scale_frames=S, sliding_window=W, dtype=dtype,
                           keyframe_interval=k, pages_per_layer=pages, max_queries=max_queries, max_splits=max_splits)
 
 
-def _window_stream(T, H, S, W, k, frames, rows, wid, tau=0.125):
+def _window_stream(T, H, S, W, k, frames, rows, wid, tau=0.125, fp32=False):
     """append -> evict -> attend for `frames` frames; every frame's output rows `rows` (or all) against the
     oracle over the frames the policy attends."""
     torch = torch_cuda()
-    c = kv.KVCache(_window_cfg(T, H, S, W, k, S + W + 1, max(S, 1) * T), device="cuda")
+    dt = kv.KV_FP32 if fp32 else kv.KV_BF16
+    c = kv.KVCache(_window_cfg(T, H, S, W, k, S + W + 1, max(S, 1) * T, dtype=dt), device="cuda")
     host = {}
     pending = []
     rng = np.random.default_rng(wid)
     for t in range(frames):
-        q, kk, vv = synth.iid_frame(wid, 0, t, (T, H, 64), device="cuda", dtype=torch.bfloat16)
+        q, kk, vv = synth.iid_frame(wid, 0, t, (T, H, 64), device="cuda",
+                                    dtype=torch.float32 if fp32 else torch.bfloat16)
         host[t] = (kk.double().cpu().numpy(), vv.double().cpu().numpy())
         c.append(0, t, kk, vv)
         c.evict(0)
@@ -51,8 +54,8 @@ def _window_stream(T, H, S, W, k, frames, rows, wid, tau=0.125):
         K = np.concatenate([host[f][0] for f in att])
         V = np.concatenate([host[f][1] for f in att])
         ref, ref_lse = attention.attend(to64(q)[sel], K, V, tau)
-        ma, rl = assert_close(to64(out)[sel], ref, bf16=True, what=f"T={T} frame {t}")
-        assert max_abs(to64(lse).reshape(-1, H)[sel], ref_lse) <= LSE_ABS_BF16, t
+        ma, rl = assert_close(to64(out)[sel], ref, bf16=not fp32, what=f"T={T} frame {t}")
+        assert max_abs(to64(lse).reshape(-1, H)[sel], ref_lse) <= (LSE_ABS_FP32 if fp32 else LSE_ABS_BF16), t
     return c, host
 
 
@@ -117,6 +120,13 @@ def test_largest_page_diversity_prune():
     q = synth.iid_frame(73, 0, 0, (32, H, 64), device="cuda", dtype=torch.bfloat16)[0]
     s.check_attention(q, 0.125, "8192-token pages, attention after the prune")
     say("8192-token pages: diversity prune matches the oracle")
+
+
+def test_fp32_multi_tile_pages_window_stream():
+    # fp32 pool, 200-token pages (several 64-token tiles and a ragged tail), 3 heads, two scale frames attended
+    # jointly, keyframe interval 2 (every other frame transient): every row of every frame
+    _window_stream(200, 3, 2, 3, 2, 12, None, wid=78, fp32=True)
+    say("fp32 200-token pages: window stream matches the oracle")
 
 
 def test_one_token_pages_window_stream():
