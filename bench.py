@@ -591,7 +591,7 @@ def diversity_cpu_baseline(L, T, H, per_head):
     for f in range(n_frames):
         c.append(f)
     t0 = time.perf_counter()
-    c.prune(lambda f, h: keys[f][:, h, :], per_head, rank_dtype=np.float32)
+    c.prune(lambda f, h: keys[f][:, h, :], per_head)
     dt = time.perf_counter() - t0
     return {"value": 1.0 / (L * dt), "unit": "frames/s", "cores": len(_os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"one layer's score + top-K + compaction ({H} heads x {(n_frames - 1) * T} candidates, "

@@ -47,14 +47,14 @@ struct DivCall {
   char* pool;
   PageGeom geom;
   int32_t* hlen_dev;      // [physical page][heads] per-head lengths; a prune writes its pages' new lengths
-  uint32_t* keys_dev;     // the key store (each layer's keys at its keys_off)
+  uint32_t* keys_dev;     // the key store (each layer's keys at its keys_off: per head a high plane, then a low plane)
   const char* staging;    // host block of div_staging_bytes(sizes, n) bytes
   int32_t n;              // slots
   int32_t max_P;          // the largest P over the slots
   int64_t max_N;          // the largest N over the slots
   bool any_rescore;       // some slot scores
   bool prune;             // select and compact after the scoring
-  float* scores_out;      // optional [heads][score_stride] of slot 0, candidate order
+  double* scores_out;     // optional [heads][score_stride] of slot 0, candidate order
   int64_t score_stride;
 };
 

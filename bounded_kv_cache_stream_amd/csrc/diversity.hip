@@ -23,15 +23,18 @@
 //   sum     float64 sum over a page's rows of k / |k|;
 //   mean    per (head, slot): the pages' sums added in a fixed order = S,
 //           and |S|;
-//   score   float64 score per row, rounded to float32 (the value that is
-//           ranked and reported) and stored as a 32-bit key that orders the
-//           scores descending; float64 score sums per block;
+//   score   float64 score per row (the value that is ranked and reported),
+//           stored as a 64-bit key that orders the scores descending, split
+//           in a high and a low 32-bit plane; float64 score sums per block;
 //   total   per slot, the block sums added in a fixed order;
-//   select  per (head, slot), 4 radix passes of 8 bits (most significant
-//           first) find the K-th smallest key t and how many keys equal to t
-//           are kept: the first ones in candidate order, as a stable sort
-//           would keep them (a histogram pass over the keys, then one
-//           workgroup per (head, slot) fixes the digit);
+//   select  per (head, slot), up to 8 radix passes of 8 bits (most
+//           significant first; the first four read only the high plane)
+//           find the K-th smallest key t and how many keys equal to t are
+//           kept: the first ones in candidate order, as a stable sort would
+//           keep them (a histogram pass over the keys, then one workgroup per
+//           (head, slot) fixes the digit).  Once every key matching the
+//           digits fixed so far is kept, the remaining passes are skipped and
+//           t compares under the mask of the fixed bits;
 //   mark    per (page, head, slot): keys below t and equal to t;
 //   compact per (page, head, slot): the page's new length n follows from the
 //           counts; kept = key < t, or key == t within the tie quota; the
@@ -60,13 +63,18 @@ constexpr int kMaxMoves = kMaxPageTokensScored / 2;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Select state of one head: the key prefix fixed so far and how many of the
-// keys matching it are still to be kept.
+// Select state of one head: the key bits fixed so far (prefix, under mask)
+// and how many of the keys matching them are still to be kept.  done: no
+// further pass is needed (every matching key is kept, or none is to be kept,
+// or all 64 bits are fixed).
 struct DSel {
-  uint32_t prefix;
-  int32_t pad;
+  uint64_t prefix;
+  uint64_t mask;
   long long k_rem;
+  int32_t done;
+  int32_t pad;
 };
+constexpr int kSelPasses = 8;
 
 struct DivK {
   const DivLayer* layers;  // [n]
@@ -80,11 +88,11 @@ struct DivK {
   double* mean;     // [n][H][65]: S, then |S|
   double* spart;    // [n][H][p_max]
   double* totals;   // [n]
-  uint32_t* keys;   // the key store
-  float* scores;    // optional [H][score_stride] of slot 0
+  uint32_t* keys;   // the key store: per layer and head a high plane [N], then a low plane [N]
+  double* scores;   // optional [H][score_stride] of slot 0
   int64_t score_stride;
-  uint32_t* dhist;  // [n][4][H][256] select histograms
-  DSel* dstate;     // [n][5][H] states before each pass, [4] final
+  uint32_t* dhist;  // [n][8][H][256] select histograms
+  DSel* dstate;     // [n][9][H] states before each pass, [8] final
   int32_t* lt_cnt;  // [n][H][p_max] keys below the threshold per page
   int32_t* eq_cnt;  // [n][H][p_max] keys equal to the threshold per page
   int32_t* new_len; // [n][p_max][H]
@@ -98,8 +106,9 @@ __device__ inline const DevEntry& tab(const DivK& a, int slot, int h, int p) {
 __device__ inline int64_t head_count(const DivK& a, int slot, int h) {
   return tab(a, slot, h, a.layers[slot].P).tok_start;
 }
+// High plane of head h's keys; the low plane follows at + L.N.
 __device__ inline uint32_t* head_keys(const DivK& a, const DivLayer& L, int h) {
-  return a.keys + L.keys_off + (int64_t)h * L.N;
+  return a.keys + L.keys_off + (int64_t)h * 2 * L.N;
 }
 
 // One workgroup per (head, slot): head h's table from the layer's shared one
@@ -280,11 +289,11 @@ __global__ __launch_bounds__(kMeanThreads) void div_mean_kernel(DivK a) {
   }
 }
 
-// Rank key of a score: ascending keys = descending scores (-0 as +0).
-__device__ inline uint32_t desc_key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  const uint32_t b = __float_as_uint(f);
-  const uint32_t asc = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+// Rank key of a float64 score: ascending keys = descending scores (-0 as +0).
+__device__ inline uint64_t desc_key(double f) {
+  if (f == 0.0) f = 0.0;
+  const uint64_t b = (uint64_t)__double_as_longlong(f);
+  const uint64_t asc = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
   return ~asc;
 }
 
@@ -339,10 +348,11 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
       if (j < en.len) {
         const double sc = (s2 > 0.0 && sn > 0.0) ? -(dot / (sqrt(s2) * sn)) : 0.0;
         bad = bad || !(s2 <= 1.0e300) || !(sc == sc);  // a NaN or infinite key
-        const float f = (float)sc;
         const int64_t idx = en.tok_start + j;
-        kk[idx] = desc_key(f);
-        if (a.scores && slot == 0) a.scores[(int64_t)h * a.score_stride + idx] = f;
+        const uint64_t key = desc_key(sc);
+        kk[idx] = (uint32_t)(key >> 32);
+        kk[L.N + idx] = (uint32_t)key;
+        if (a.scores && slot == 0) a.scores[(int64_t)h * a.score_stride + idx] = sc;
         ssum = ssum + sc;
       }
     }
@@ -384,18 +394,21 @@ __global__ __launch_bounds__(kThreads) void div_total_kernel(DivK a) {
 constexpr int kSelItems = 8;
 constexpr int kSelTile = kThreads * kSelItems;
 
-// Fix digit p: the smallest digit whose prefix count (over digits in
-// ascending order) reaches k_rem; k_rem drops by the count of smaller digits.
-// Wave 0 scans its 64 lanes (4 digits each); the result goes through LDS.
-// Every thread of the (256-thread) workgroup calls it.
+// Fix digit p (bits 56 - 8p .. 63 - 8p of the key): the smallest digit whose
+// prefix count (over digits in ascending order) reaches k_rem; k_rem drops by
+// the count of smaller digits.  When every key matching the new prefix is to
+// be kept, no later pass can change the outcome (done).  Wave 0 scans its 64
+// lanes (4 digits each); the result goes through LDS.  Every thread of the
+// (256-thread) workgroup calls it.
 __device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
   __shared__ uint32_t cnt[256];
   __shared__ DSel out;
+  if (st.done) return st;
   const int tid = threadIdx.x;
   cnt[tid] = hist[tid];
   if (tid == 0) out = st;
   __syncthreads();
-  if (tid < 64 && st.k_rem > 0) {
+  if (tid < 64) {
     long long own = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) own += cnt[4 * tid + j];
@@ -411,8 +424,11 @@ __device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
       for (int j = 0; j < 4; ++j) {
         const long long c = cnt[4 * tid + j];
         if (cum + c >= st.k_rem) {
-          out.prefix = st.prefix | ((uint32_t)(4 * tid + j) << (24 - 8 * p));
+          const int shift = 56 - 8 * p;
+          out.prefix = st.prefix | ((uint64_t)(4 * tid + j) << shift);
+          out.mask = st.mask | (0xffull << shift);
           out.k_rem = st.k_rem - cum;
+          out.done = out.k_rem == c || p == kSelPasses - 1;
           break;
         }
         cum += c;
@@ -426,25 +442,32 @@ __device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
 }
 
 __device__ inline uint32_t* sel_hist(const DivK& a, int slot, int p, int h) {
-  return a.dhist + (((int64_t)slot * 4 + p) * a.H + h) * 256;
+  return a.dhist + (((int64_t)slot * kSelPasses + p) * a.H + h) * 256;
 }
 __device__ inline DSel* sel_state(const DivK& a, int slot, int p, int h) {
-  return a.dstate + ((int64_t)slot * 5 + p) * a.H + h;
+  return a.dstate + ((int64_t)slot * (kSelPasses + 1) + p) * a.H + h;
 }
 
 // One workgroup per (head, slot): the state before pass p (p = 0: nothing
-// fixed, min(keep, candidates) to keep; p = 1..4: pass p-1's state advanced
-// by its histogram; state 4 is the final one).
+// fixed, min(keep, candidates) to keep; p = 1..8: pass p-1's state advanced
+// by its histogram; state 8 is the final one).
 __global__ __launch_bounds__(kThreads) void div_advance_kernel(DivK a, int p) {
   if (a.flags[a.n]) return;
   const int h = blockIdx.x, slot = blockIdx.y;
-  const DSel st = p == 0 ? DSel{0u, 0, (long long)min<int64_t>(a.layers[slot].keep, head_count(a, slot, h))}
-                         : select_advance(*sel_state(a, slot, p - 1, h), sel_hist(a, slot, p - 1, h), p - 1);
+  DSel st;
+  if (p == 0) {
+    const int64_t nh = head_count(a, slot, h);
+    const long long k0 = (long long)min<int64_t>(a.layers[slot].keep, nh);
+    st = DSel{0ull, 0ull, k0, k0 == 0 || k0 == nh, 0};
+  } else {
+    st = select_advance(*sel_state(a, slot, p - 1, h), sel_hist(a, slot, p - 1, h), p - 1);
+  }
   if (threadIdx.x == 0) *sel_state(a, slot, p, h) = st;
 }
 
 // Pass p: histogram of digit p over head h's keys that match the digits
-// fixed so far.
+// fixed so far.  Passes 0-3 take their digit from the high plane; passes 4-7
+// read a key's low word only when its high word matches.
 __global__ __launch_bounds__(kThreads) void div_select_kernel(DivK a, int p) {
   if (a.flags[a.n]) return;
   __shared__ uint32_t cnt[256];
@@ -452,20 +475,37 @@ __global__ __launch_bounds__(kThreads) void div_select_kernel(DivK a, int p) {
   const int64_t nh = head_count(a, slot, h);
   if ((int64_t)blockIdx.x * kSelTile >= nh) return;  // past the head's keys
   const DSel st = *sel_state(a, slot, p, h);
-  if (st.k_rem == 0) return;
+  if (st.done) return;
   cnt[tid] = 0;
   __syncthreads();
-  const int shift = 24 - 8 * p;
-  const uint32_t hi = p == 0 ? 0u : (~0u << (32 - 8 * p));
-  const uint32_t* kk = head_keys(a, a.layers[slot], h);
+  const DivLayer L = a.layers[slot];
+  const uint32_t* kh = head_keys(a, L, h);
+  const uint32_t* kl = kh + L.N;
+  const uint32_t pre_hi = (uint32_t)(st.prefix >> 32), mask_hi = (uint32_t)(st.mask >> 32);
+  const uint32_t pre_lo = (uint32_t)st.prefix, mask_lo = (uint32_t)st.mask;
+  const int shift = 24 - 8 * (p & 3);
 #pragma unroll
   for (int j = 0; j < kSelItems; ++j) {
     const int64_t i = (int64_t)blockIdx.x * kSelTile + j * kThreads + tid;
-    const uint32_t key = i < nh ? kk[i] : 0u;
-    hist_add(cnt, (key >> shift) & 255u, i < nh && (key & hi) == st.prefix);
+    const bool valid = i < nh;
+    const uint32_t hi = valid ? kh[i] : 0u;
+    bool match = valid && (hi & mask_hi) == pre_hi;
+    uint32_t word = hi;
+    if (p >= 4) {
+      word = match ? kl[i] : 0u;
+      match = match && (word & mask_lo) == pre_lo;
+    }
+    hist_add(cnt, (word >> shift) & 255u, match);
   }
   __syncthreads();
   if (cnt[tid]) atomicAdd(&sel_hist(a, slot, p, h)[tid], cnt[tid]);
+}
+
+// The key of candidate i under the final state's mask (the low plane is read
+// only when the mask reaches it).
+__device__ inline uint64_t masked_key(const uint32_t* kh, const uint32_t* kl, int64_t i, const DSel& st) {
+  const uint64_t hi = (uint64_t)kh[i] << 32;
+  return ((uint32_t)st.mask ? (hi | kl[i]) : hi) & st.mask;
 }
 
 // Per (page, head, slot): the keys below the threshold t and equal to it.
@@ -475,19 +515,20 @@ __global__ __launch_bounds__(kThreads) void div_mark_kernel(DivK a) {
   const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
   const DivLayer L = a.layers[slot];
   if (p >= L.P) return;
-  const uint32_t t = sel_state(a, slot, 4, h)->prefix;
+  const DSel st = *sel_state(a, slot, kSelPasses, h);
   if (tid == 0) {
     s_lt = 0;
     s_eq = 0;
   }
   __syncthreads();
   const DevEntry en = tab(a, slot, h, p);
-  const uint32_t* kk = head_keys(a, L, h) + en.tok_start;
+  const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
+  const uint32_t* kl = kh + L.N;
   int32_t lt = 0, eq = 0;
   for (int j = tid; j < en.len; j += kThreads) {
-    const uint32_t key = kk[j];
-    lt += key < t;
-    eq += key == t;
+    const uint64_t key = masked_key(kh, kl, j, st);
+    lt += key < st.prefix;
+    eq += key == st.prefix;
   }
   for (int off = 32; off > 0; off >>= 1) {
     lt += __shfl_xor(lt, off, 64);
@@ -522,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
   const int wave = tid >> 6, lane = tid & 63;
   const DevEntry en = tab(a, slot, h, p);
   const int len = en.len;
-  const DSel st = *sel_state(a, slot, 4, h);
+  const DSel st = *sel_state(a, slot, kSelPasses, h);
   const int64_t cnt_at = ((int64_t)slot * a.H + h) * a.p_max;
   const int32_t eq = a.eq_cnt[cnt_at + p];
   // keys equal to t in the earlier pages: only a page holding such a key
@@ -543,14 +584,15 @@ __global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
     a.hlen[(int64_t)en.phys * a.H + h] = n;
   }
   if (n == len) return;  // nothing dropped in this page and head
-  const uint32_t* kk = head_keys(a, L, h) + en.tok_start;
+  const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
+  const uint32_t* kl = kh + L.N;
   const unsigned long long below = (1ull << lane) - 1ull;
   long long eq_run = eq_before;
   int32_t h_run = 0, f_run = 0;
   for (int c0 = 0; c0 < len; c0 += kThreads) {
     const int j = c0 + tid;
     const bool valid = j < len;
-    const uint32_t key = valid ? kk[j] : 0xffffffffu;
+    const uint64_t key = valid ? masked_key(kh, kl, j, st) : ~0ull;
     const bool is_eq = valid && key == st.prefix;
     const unsigned long long be = __ballot(is_eq);
     if (lane == 0) wsum[0][wave] = __popcll(be);
@@ -578,14 +620,15 @@ __global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
       chunk_h += wsum[1][w];
       chunk_f += wsum[2][w];
     }
-    if (hole) holes[hp] = (uint16_t)j;
-    if (fill) fills[fp] = (uint16_t)j;
+    // a consistent plan has at most len / 2 moves; the counts are checked below
+    if (hole && hp < kMaxMoves) holes[hp] = (uint16_t)j;
+    if (fill && fp < kMaxMoves) fills[fp] = (uint16_t)j;
     eq_run += chunk_eq;
     h_run += chunk_h;
     f_run += chunk_f;
     __syncthreads();  // wsum is rewritten by the next chunk; the lists are read below
   }
-  if (h_run != f_run) {  // cannot happen when the counts and the walk agree; never move on a mismatch
+  if (h_run != f_run || h_run > kMaxMoves) {  // cannot happen when the counts and the walk agree; never move on a mismatch
     if (tid == 0) atomicOr(&a.flags[slot], kClcesErrCount);
     return;
   }
@@ -647,8 +690,8 @@ DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers) 
   z.partial = take(L * H * P * kHeadDim * 8);
   z.mean = take(L * H * (kHeadDim + 1) * 8);
   z.spart = take(L * H * P * 8);
-  z.dhist = take(L * 4 * H * 256 * 4);
-  z.dstate = take(L * 5 * H * sizeof(DSel));
+  z.dhist = take(L * kSelPasses * H * 256 * 4);
+  z.dstate = take(L * (kSelPasses + 1) * H * sizeof(DSel));
   z.lt_cnt = take(L * H * P * 4);
   z.eq_cnt = take(L * H * P * 4);
   // the outputs the host reads back, adjacent: a scoring reads totals and
@@ -673,7 +716,7 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   const int H = c.geom.heads;
   hipError_t e = hipMemcpyAsync(c.ws + z.params, c.staging, div_staging_bytes(z, c.n), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
-  const int n_hist = c.prune ? c.n * 4 * H * 256 : 0;
+  const int n_hist = c.prune ? c.n * kSelPasses * H * 256 : 0;
   div_zero_kernel<<<dim3((unsigned)((std::max(n_hist, c.n + 1) + 255) / 256)), dim3(256), 0, s>>>(
       k.flags, c.n + 1, reinterpret_cast<int32_t*>(k.dhist), n_hist);
   div_tables_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k);
@@ -693,11 +736,11 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   if (c.prune) {
     const unsigned nblk = (unsigned)((c.max_N + kSelTile - 1) / kSelTile);
     const dim3 heads((unsigned)H, (unsigned)c.n);
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kSelPasses; ++p) {
       div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, p);
       div_select_kernel<<<dim3(nblk, (unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k, p);
     }
-    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, 4);
+    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, kSelPasses);
     div_mark_kernel<<<pages, dim3(kThreads), 0, s>>>(k);
     if (c.geom.esize == 2)
       div_compact_kernel<__bf16><<<pages, dim3(kThreads), 0, s>>>(k);

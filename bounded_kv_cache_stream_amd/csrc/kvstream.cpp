@@ -112,10 +112,11 @@ Layout make_layout(const kv_pool_config* c) {
   off = align_up(off + (size_t)L.part_rows * H * 2 * 4);
   L.hlens = off;  // per-head lengths of every physical page, int32 [page][H]
   off = align_up(off + (size_t)(L.layer_pages * c->num_layers) * (size_t)H * 4);
-  // diversity keys of every layer, uint32 [layer][H][pages_per_layer * page_tokens]:
-  // 4 bytes per (token, head) against the 256 of its K and V rows
+  // diversity keys of every layer, uint32 [layer][H][2][pages_per_layer * page_tokens]
+  // (the high and the low word of each 64-bit order key): 8 bytes per (token,
+  // head) against the 256 of its K and V rows
   L.dkeys = off;
-  off = align_up(off + (size_t)c->num_layers * (size_t)H * (size_t)c->pages_per_layer * (size_t)c->page_tokens * 4);
+  off = align_up(off + (size_t)c->num_layers * (size_t)H * (size_t)c->pages_per_layer * (size_t)c->page_tokens * 8);
   L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window,
                           (int32_t)ts);
   L.dv = kvs::div_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, (int32_t)H,
@@ -269,7 +270,7 @@ struct DivBatch {
 };
 
 DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
-                   const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, float* scores,
+                   const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, double* scores,
                    int64_t stride) {
   DivBatch b;
   const kvs::DivSizes& z = pool->lay.dv;
@@ -290,7 +291,7 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
   c.prune = prune;
   c.scores_out = scores;
   c.score_stride = stride;
-  const int64_t per_layer = (int64_t)pool->cfg.num_heads * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
+  const int64_t per_layer = 2 * (int64_t)pool->cfg.num_heads * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
   for (int i = 0; i < n; ++i) {
     const DivPlan& d = *plans[(size_t)i];
     kvs::DivLayer& L = kvs::div_staging_layers(staging)[i];
@@ -308,7 +309,7 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
 }
 
 // Scores layers first .. first+n-1, one wait for all of them.
-kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, float* scores_dev, int64_t stride,
+kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, double* scores_dev, int64_t stride,
                                 double* means, hipStream_t st) {
   std::vector<DivPlan> plans((size_t)n);
   std::vector<int32_t> layers;
@@ -357,7 +358,7 @@ kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, float
 // for all of them.  Layers whose keys are not from a scoring of their
 // current state are scored in the same call, before any row moves, so a key
 // that is not finite in any layer leaves every layer unchanged.
-kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const int64_t* keep, float* scores_dev,
+kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const int64_t* keep, double* scores_dev,
                                 int64_t stride, int64_t* kept, hipStream_t st) {
   const int32_t H = pool->cfg.num_heads;
   for (int32_t i = 0; i < n; ++i)
@@ -1018,7 +1019,7 @@ kv_status kv_merge_pages_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_
   return merge_layers(pool, first_layer, n_layers, n_merged, static_cast<hipStream_t>(stream));
 }
 
-kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,
+kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, double* scores_dev, int64_t score_stride,
                              double* mean_diversity, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;
@@ -1036,7 +1037,7 @@ kv_status kv_diversity_score_layers(kv_pool_t* pool, int32_t first_layer, int32_
                                static_cast<hipStream_t>(stream));
 }
 
-kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
+kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, double* scores_dev,
                              int64_t score_stride, int64_t* kept_per_head, void* stream) {
   kv_status s = check_layer(pool, layer);
   if (s != KV_OK) return s;

@@ -414,13 +414,13 @@ class KVCache:
         if scores is None:
             return None, 0
         torch = self.torch
-        if scores.dtype != torch.float32 or not scores.is_contiguous() or scores.dim() != 2 \
+        if scores.dtype != torch.float64 or not scores.is_contiguous() or scores.dim() != 2 \
                 or scores.shape[0] != self.cfg.num_heads:
-            raise ValueError("scores must be a contiguous fp32 [num_heads, stride] tensor")
+            raise ValueError("scores must be a contiguous float64 [num_heads, stride] tensor")
         return ctypes.c_void_p(scores.data_ptr()), scores.shape[1]
 
     def diversity_score(self, layer, scores=None) -> float:
-        """Mean diversity of the layer's candidates; scores: optional fp32 [H, stride] output."""
+        """Mean diversity of the layer's candidates; scores: optional float64 [H, stride] output."""
         sp, stride = self._scores_arg(scores)
         return kv_diversity_score(self.handle, layer, sp, stride, self._stream())
 

@@ -299,12 +299,12 @@ kv_status kv_merge_pages_layers(kv_pool_t* pool, int32_t first_layer, int32_t n_
  * m_h the mean of head h's k_hat,
  *   score = -(k_hat . m_h) / |m_h|     (every score 0 when m_h = 0),
  * computed in float64 from the stored keys with fixed-order sums.
- * scores_dev: optional fp32 [H][score_stride] (score_stride >= max N_h), the
- * float64 score rounded to fp32, candidate order; entries past N_h untouched.
+ * scores_dev: optional float64 [H][score_stride] (score_stride >= max N_h),
+ * the scores in candidate order; entries past N_h untouched.
  * *mean_diversity (host, required): the mean of the float64 scores over
  * every head and candidate (0 with no candidate).  KV_ERR_NAN if a candidate
  * key is not finite.  Synchronises the stream. */
-kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, float* scores_dev, int64_t score_stride,
+kv_status kv_diversity_score(kv_pool_t* pool, int32_t layer, double* scores_dev, int64_t score_stride,
                              double* mean_diversity, void* stream);
 
 /* kv_diversity_score for layers first_layer .. first_layer+n_layers-1 with
@@ -327,8 +327,8 @@ kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, doubl
 
 /* Diversity prune ([INF] recipe step 6, "Rolling Memory"): scores the
  * candidates as kv_diversity_score does, keeps each head's keep_per_head
- * candidates first in (score descending, candidate index ascending) order,
- * the scores taken as rounded to fp32, and compacts every page and head in
+ * candidates first in (float64 score descending, candidate index ascending)
+ * order, and compacts every page and head in
  * place with the rule of score_and_compact (kept slots below the head's new
  * count n stay, the dropped slots below n take the kept slots at or past n,
  * both ascending), moving the K and V rows of that head; the id row does not
@@ -341,7 +341,7 @@ kv_status kv_layer_budgets(const double* mean_diversity, int32_t n_layers, doubl
  * scores_dev / score_stride as for kv_diversity_score.  kept_per_head:
  * optional host int64 [H] = min(keep_per_head, N_h).  KV_ERR_NAN (state
  * unchanged) if a candidate key is not finite.  Synchronises the stream. */
-kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, float* scores_dev,
+kv_status kv_diversity_prune(kv_pool_t* pool, int32_t layer, int64_t keep_per_head, double* scores_dev,
                              int64_t score_stride, int64_t* kept_per_head, void* stream);
 
 /* kv_diversity_prune for layers first_layer .. first_layer+n_layers-1 with

@@ -26,9 +26,9 @@ Readings taken where the pages are silent:
 * score = -(k_hat . m) / |m| with m the mean of the normalised candidate keys,
   in float64 from the stored key values;
 * per-head top-K: the K highest scores, ties by candidate index (table order,
-  then slot order); K >= the candidate count keeps everything; the pages fix
-  no precision for this decision, so ``prune`` can take it on the scores
-  rounded to a given type (float32 is the kernel's);
+  then slot order); K >= the candidate count keeps everything; the recipe's
+  step 6 keeps the most diverse tokens and fixes no precision of its own, so
+  the decision is taken on the float64 scores themselves;
 * layer budgets: p = softmax(mean_diversity / tau) over the layers;
   K_l = floor(floor(p_l * total) / heads) tokens per head of layer l;
   a layer's average diversity is the mean of its scores over heads and
@@ -69,7 +69,9 @@ def diversity_scores(keys: np.ndarray) -> np.ndarray:
     mn = np.sqrt((m * m).sum())
     if mn == 0:
         return np.zeros(len(k))
-    return -(khat @ m) / mn
+    # a fixed-order sum per row (not a BLAS product): identical keys score identically, so exact ties
+    # reach the index tie-break of the top-K
+    return -((khat * m).sum(axis=1)) / mn
 
 
 def topk_desc(scores: np.ndarray, k: int) -> np.ndarray:
@@ -129,12 +131,10 @@ class DiversityCache:
         n = sum(len(x) for x in s)
         return float(sum(x.sum() for x in s) / n) if n else 0.0
 
-    def prune(self, key_of, k_per_head: int, rank_dtype=np.float64) -> list[np.ndarray]:
-        """Keep each head's k_per_head most diverse candidates; return the per-head keep masks.
-
-        The top-K is taken on the scores rounded to ``rank_dtype``."""
+    def prune(self, key_of, k_per_head: int) -> list[np.ndarray]:
+        """Keep each head's k_per_head most diverse candidates (float64 scores); return the per-head keep masks."""
         masks = []
-        sc = [np.asarray(x, dtype=rank_dtype) for x in self.scores(key_of)]
+        sc = self.scores(key_of)
         for h in range(self.H):
             masks.append(topk_desc(sc[h], k_per_head) if len(sc[h]) > k_per_head else np.ones(len(sc[h]), bool))
         pos = [0] * self.H

@@ -115,7 +115,7 @@ def test_largest_page_diversity_prune():
     for t in range(F):
         s.append(t)
     assert c.diversity_prune(0, 9000) == [9000] * H
-    s.sim.prune(s.key_of, 9000, rank_dtype=np.float32)
+    s.prune(9000)
     s.check_pages("8192-token pages, prune")
     q = synth.iid_frame(73, 0, 0, (32, H, 64), device="cuda", dtype=torch.bfloat16)[0]
     s.check_attention(q, 0.125, "8192-token pages, attention after the prune")

@@ -219,6 +219,34 @@ def test_multi_layer_append_matches_single_layer_append():
                                    y.cpu().view(torch.uint8) if y.dtype != torch.int32 else y.cpu())
 
 
+def test_batched_page_write_full_shape_bytes():
+    # the 24-layer batched write the append benchmark times (24 layers x 1004 tokens x 16 heads x 64, bf16,
+    # 197 MB per frame): every layer's page holds the caller's K and V as [H][Ts][D] bit for bit, zero pad
+    # slots and the token ids, for two persisted frames and then a transient one
+    torch = torch_cuda()
+    T, H, L = 1004, 16, 24
+    cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=1, sliding_window=1,
+                         keyframe_interval=2, pages_per_layer=3, max_queries=T, max_splits=4)
+    c = kv.KVCache(cfg, device="cuda")
+    Ts = c.layout["token_stride"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    for t in range(3):  # frames 0 (scale) and 1 (keyframe) persist; frame 2 is not a keyframe: transient
+        k = torch.randn(L, T, H, 64, device="cuda", generator=g).bfloat16()
+        v = torch.randn(L, T, H, 64, device="cuda", generator=g).bfloat16()
+        c.append_layers(0, t, k, v)
+        torch.cuda.synchronize()
+        for l in range(L):
+            c.evict(l)
+            pid = c.page_table(l)[0][-1] if t < 2 else cfg.pages_per_layer
+            pk, pv, ids = c.page_view(l, pid)
+            assert torch.equal(pk[:, :T].view(torch.int16), k[l].permute(1, 0, 2).view(torch.int16)), (t, l)
+            assert torch.equal(pv[:, :T].view(torch.int16), v[l].permute(1, 0, 2).view(torch.int16)), (t, l)
+            assert not pk[:, T:].view(torch.int16).any() and not pv[:, T:].view(torch.int16).any(), (t, l)
+            assert ids.cpu().numpy().tolist() == [t * T + i for i in range(T)] + [-1] * (Ts - T), (t, l)
+    say(f"batched page write: {L} layers x {T} tokens x {H} heads bit for bit")
+
+
 @pytest.mark.parametrize("dtype,T,H", [("bf16", 1004, 16), ("fp32", 100, 2)])
 def test_page_write_bytes(dtype, T, H):
     # a page holds the frame's K and V as [H][Ts][D] bit for bit, zero pad slots

@@ -124,24 +124,23 @@ def test_cache_anchor_and_per_head_topk():
     assert all(sum(l) > 0 for _, _, l in tab)
 
 
-def test_prune_decides_on_rounded_scores():
-    # two candidates whose float64 scores differ by less than half an fp32 ulp
-    # tie once rounded to float32, and the lower candidate index wins; in
-    # float64 the larger score wins
+def test_prune_decides_on_float64_scores():
+    # two candidates whose float64 scores differ by 2^-30 (less than half an
+    # fp32 ulp at 0.25): the larger float64 score wins, not the lower index;
+    # an exact tie goes to the lower index
     s64 = np.array([0.25, 0.25 + 2.0 ** -30, 0.1])
-    assert s64[0] != s64[1] and np.float32(s64[0]) == np.float32(s64[1])
     assert diversity.topk_desc(s64, 1).tolist() == [False, True, False]
-    assert diversity.topk_desc(s64.astype(np.float32), 1).tolist() == [True, False, False]
-    # through the cache: the prune keeps the best of the scores rounded to float32
+    assert diversity.topk_desc(np.array([0.3, 0.3, 0.1]), 1).tolist() == [True, False, False]
+    # through the cache: the prune keeps the top 2 of the float64 scores
     c = diversity.DiversityCache(1, 3, 2)
     c.append(0)
     c.append(1)
     rng = np.random.default_rng(5)
     keys = {0: rng.normal(size=(3, 64)), 1: rng.normal(size=(3, 64))}
     sc = c.scores(lambda f, h: keys[f])[0]
-    order32 = np.argsort(-sc.astype(np.float32), kind="stable")
-    m = c.prune(lambda f, h: keys[f], 2, rank_dtype=np.float32)[0]
-    assert m.tolist() == [i in order32[:2] for i in range(3)]
+    order = sorted(range(3), key=lambda i: (-sc[i], i))
+    m = c.prune(lambda f, h: keys[f], 2)[0]
+    assert m.tolist() == [i in order[:2] for i in range(3)]
 
 
 def _set_table(c, entries):
