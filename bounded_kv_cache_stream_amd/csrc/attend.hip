@@ -46,9 +46,17 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace kvs {
+
+// Split-KV partials of stream_attend_scratch, one copy per GPU, held until the
+// process ends.  In host code this name is a host-side stand-in, never a
+// device address: kernels get each GPU's copy from attend_scratch_address.
+static __device__ __align__(256) char scratch[kAttendScratchBytes];
+
 namespace {
 
 typedef __bf16 bf16;
@@ -444,6 +452,24 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(PageGeom g, AttendParam
 }
 
 }  // namespace
+
+hipError_t attend_scratch_address(char** out) {
+  static std::mutex mu;
+  static char* addr[kAttendScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kAttendScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<char*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s) {
   if (!bf16) {

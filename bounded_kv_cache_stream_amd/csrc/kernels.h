@@ -115,4 +115,12 @@ struct AttendParams {
 
 hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s);
 
+// Device scratch of the allocation-free attention entry point: a file-scope
+// array in attend.hip, one copy per GPU, holding the split-KV partials.
+constexpr size_t kAttendScratchBytes = size_t(64) << 20;
+constexpr int kAttendScratchDevices = 64;
+// This GPU's copy (the current device): its address is looked up once per
+// device and kept.
+hipError_t attend_scratch_address(char** out);
+
 }  // namespace kvs

@@ -480,6 +480,8 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   for (auto& l : p->layers)
     l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens,
            cfg->special_tokens);
+  // every page id of a layer plus its transient page: table uploads never grow the staging vector
+  p->scratch.reserve((size_t)cfg->pages_per_layer + 2);
   *out = p;
   return ok();
 }
@@ -679,7 +681,8 @@ struct PageWrite {
 // write and the table upload are one launch, ordered before the attention.
 // Changes no host state.
 kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& L, const void* q_dev, int32_t n_q,
-                        float sm_scale, void* out_dev, float* lse_dev, hipStream_t st, const PageWrite* write) {
+                        float sm_scale, void* out_dev, float* lse_dev, hipStream_t st, const PageWrite* write,
+                        bool static_scratch = false) {
   auto& ent = pool->scratch;
   ent.clear();
   const int32_t H = pool->cfg.num_heads;
@@ -718,18 +721,6 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
   }
   if (n_entries == 0 || min_tiles == 0) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
 
-  kvs::DevEntry* dt = dev_table(pool, layer);
-  hipError_t e;
-  // per-head tables are built on the device from the shared one, uploaded after them
-  kvs::DevEntry* up = per_head ? dt + (int64_t)H * (pool->lay.layer_pages + 1) : dt;
-  if (write)
-    e = kvs::launch_append_table(pool->lay.geom, write->page, write->k, write->v, pool->cfg.page_tokens,
-                                 write->first_id, up, ent.data(), n_entries, st);
-  else
-    e = kvs::launch_table_upload(up, ent.data(), n_entries, st);
-  if (e == hipSuccess && per_head) e = kvs::launch_head_tables(dt, up, n_entries, hlens_dev(pool), H, st);
-  if (e != hipSuccess) return hip_fail(e, write ? "page write and table upload launch" : "table upload launch");
-
   const bool bf16 = pool->cfg.dtype == KV_BF16;
   int32_t splits = 1;
   if (bf16) {
@@ -749,12 +740,39 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
     splits = (int32_t)std::min<int64_t>(splits, std::max<int64_t>(1, pool->lay.part_rows / n_q));
     splits = std::max(splits, 1);
   }
+  // split-KV partials: the pool's workspace, or this GPU's static scratch
+  float* part_o = reinterpret_cast<float*>(pool->ws + pool->lay.part_o);
+  float* part_ml = reinterpret_cast<float*>(pool->ws + pool->lay.part_ml);
+  if (static_scratch && splits > 1) {
+    const size_t o_bytes = align_up((size_t)splits * (size_t)n_q * (size_t)H * kvs::kHeadDim * 4);
+    const size_t need = o_bytes + (size_t)splits * (size_t)n_q * (size_t)H * 2 * 4;
+    if (need > kvs::kAttendScratchBytes)
+      return fail(KV_ERR_SHAPE, "split-KV partials of %zu bytes (%d splits x %d queries x %d heads) exceed the "
+                  "%zu-byte static scratch", need, splits, n_q, H, kvs::kAttendScratchBytes);
+    char* base = nullptr;
+    hipError_t se = kvs::attend_scratch_address(&base);
+    if (se != hipSuccess) return hip_fail(se, "static scratch address");
+    part_o = reinterpret_cast<float*>(base);
+    part_ml = reinterpret_cast<float*>(base + o_bytes);
+  }
+  kvs::DevEntry* dt = dev_table(pool, layer);
+  hipError_t e;
+  // per-head tables are built on the device from the shared one, uploaded after them
+  kvs::DevEntry* up = per_head ? dt + (int64_t)H * (pool->lay.layer_pages + 1) : dt;
+  if (write)
+    e = kvs::launch_append_table(pool->lay.geom, write->page, write->k, write->v, pool->cfg.page_tokens,
+                                 write->first_id, up, ent.data(), n_entries, st);
+  else
+    e = kvs::launch_table_upload(up, ent.data(), n_entries, st);
+  if (e == hipSuccess && per_head) e = kvs::launch_head_tables(dt, up, n_entries, hlens_dev(pool), H, st);
+  if (e != hipSuccess) return hip_fail(e, write ? "page write and table upload launch" : "table upload launch");
+
   kvs::AttendParams ap{};
   ap.q = q_dev;
   ap.out = out_dev;
   ap.lse = lse_dev;
-  ap.part_o = reinterpret_cast<float*>(pool->ws + pool->lay.part_o);
-  ap.part_ml = reinterpret_cast<float*>(pool->ws + pool->lay.part_ml);
+  ap.part_o = part_o;
+  ap.part_ml = part_ml;
   ap.pool = pool->pool;
   ap.table = dt;
   ap.n_entries = n_entries;
@@ -779,6 +797,20 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
   auto& L = pool->layers[(size_t)layer];
   s = attend_launch(pool, layer, L, q_dev, n_q, sm_scale, out_dev, lse_dev, static_cast<hipStream_t>(stream),
                     nullptr);
+  if (s != KV_OK) return s;
+  L.transient_pending = false;
+  return ok();
+}
+
+kv_status stream_attend_scratch(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q, float sm_scale,
+                                void* out_dev, float* lse_dev, void* stream) {
+  kv_status s = check_layer(pool, layer);
+  if (s != KV_OK) return s;
+  s = check_attend_args(pool, q_dev, n_q, sm_scale, out_dev);
+  if (s != KV_OK) return s;
+  auto& L = pool->layers[(size_t)layer];
+  s = attend_launch(pool, layer, L, q_dev, n_q, sm_scale, out_dev, lse_dev, static_cast<hipStream_t>(stream),
+                    nullptr, true);
   if (s != KV_OK) return s;
   L.transient_pending = false;
   return ok();

@@ -21,7 +21,8 @@ KV_TRANSIENT = 1
 
 EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
-    "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "kv_append_attend", "score_and_compact",
+    "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "stream_attend_scratch",
+    "kv_append_attend", "score_and_compact",
     "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_merge_pages_layers",
     "kv_diversity_score",
     "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "kv_append_frame_layers": [P, I32, I32, I64, P, P, I32, U32, P],
             "kv_evict": [P, I32, ctypes.POINTER(I32), P],
             "stream_attend": [P, I32, P, I32, F32, P, P, P],
+            "stream_attend_scratch": [P, I32, P, I32, F32, P, P, P],
             "kv_append_attend": [P, I32, I64, P, P, I32, U32, P, I32, F32, P, P, ctypes.POINTER(I32), P],
             "score_and_compact": [P, I32, P, I64, ctypes.POINTER(kv_clces_params), P, P, ctypes.POINTER(I64), P],
             "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
@@ -167,6 +169,10 @@ def kv_evict(pool, layer, stream=None) -> int:
 
 def stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr=None, stream=None) -> None:
     _check(lib().stream_attend(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr, stream))
+
+
+def stream_attend_scratch(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr=None, stream=None) -> None:
+    _check(lib().stream_attend_scratch(pool, layer, q_ptr, n_q, sm_scale, out_ptr, lse_ptr, stream))
 
 
 def kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_ptr, n_q, sm_scale, out_ptr,
@@ -343,7 +349,9 @@ class KVCache:
         # device work (and so a stream) only when special tokens persist
         return kv_evict(self.handle, layer, self._stream() if self.cfg.special_tokens else None)
 
-    def attend(self, layer, q, sm_scale, out=None, lse=None):
+    def attend(self, layer, q, sm_scale, out=None, lse=None, static_scratch=False):
+        """stream_attend (static_scratch: stream_attend_scratch, the allocation-free variant; out must then
+        be given for the call to allocate nothing)."""
         torch = self.torch
         if out is None:
             out = torch.empty_like(q)
@@ -354,7 +362,8 @@ class KVCache:
             if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != q.shape[0] * q.shape[1]:
                 raise ValueError("lse must be a contiguous fp32 tensor of n_q * H elements")
             lp = ctypes.c_void_p(lse.data_ptr())
-        stream_attend(self.handle, layer, qp, q.shape[0], float(sm_scale), op, lp, self._stream())
+        fn = stream_attend_scratch if static_scratch else stream_attend
+        fn(self.handle, layer, qp, q.shape[0], float(sm_scale), op, lp, self._stream())
         return out
 
     def append_attend(self, layer, frame_idx, k, v, q, sm_scale, transient=False, out=None, lse=None):

@@ -203,6 +203,22 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
 kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q,
                         float sm_scale, void* out_dev, float* lse_dev, void* stream);
 
+/* stream_attend for callers that cannot allocate device memory or grow any
+ * buffer during the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, checks, split
+ * count, kernels and results, bit for bit, but the split-KV partials go to a
+ * static 64 MiB device array of the library (one copy per GPU, held until
+ * the process ends; its address is looked up once per device on the first
+ * call there) instead of the pool's workspace.  Allocates nothing: no
+ * hipMalloc, no host allocation.  KV_ERR_SHAPE (nothing enqueued) when the
+ * partials of the chosen split count, splits * n_q * H * (D + 2) * 4 bytes
+ * plus alignment, exceed 64 MiB (the 1004-query, 16-head, 8-split call
+ * needs 33.9 MB; one split needs none).  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads)
+ * race and corrupt each other's results; serialise them. */
+kv_status stream_attend_scratch(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q,
+                                float sm_scale, void* out_dev, float* lse_dev, void* stream);
+
 /* One frame's cache step in one call: kv_append_frame(layer, frame_idx, k_dev,
  * v_dev, n_tokens, flags), then kv_evict(layer), then stream_attend(layer,
  * q_dev, n_q, sm_scale, out_dev, lse_dev), with the same arguments, checks,
