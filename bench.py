@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--defer", action="store_true",
                     help="budget / clces workloads: score_and_compact returns once enqueued (KV_CLCES_DEFER); the next call "
                          "on the layer applies the new page lengths")
+    ap.add_argument("--reuse-ranks", action="store_true",
+                    help="clces workload: each step ranks only its own layer and reuses the earlier steps' ranks of "
+                         "the other window layers (KV_CLCES_REUSE_RANKS; every layer holds the same whole frames)")
     ap.add_argument("--fused", action="store_true",
                     help="stream/long workloads: one kv_append_attend call per frame (the page write shares the "
                          "table-upload launch) instead of append, evict and attend")
@@ -208,7 +211,8 @@ def run_clces(args):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for l in range(L):
-            cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keeps[l], defer=True)
+            cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keeps[l], defer=True,
+                                    reuse_ranks=args.reuse_ranks)
         e1.record(stream)
         torch.cuda.synchronize()
         cache.sync()
@@ -219,7 +223,8 @@ def run_clces(args):
     else:
         for l in range(L):
             t0 = time.perf_counter()
-            cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep)
+            cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep,
+                                    reuse_ranks=args.reuse_ranks)
             times.append(time.perf_counter() - t0)  # the call synchronises once (new page lengths)
             kept = set(keep.cpu().numpy().tolist())
             moved += moved_tokens([[(t * T + j) in kept for j in range(T)] for t in range(F)])
@@ -231,7 +236,8 @@ def run_clces(args):
         cpu = clces_cpu_baseline(synth.raw_scores(3, N, L), T, F, K, w)
     print(json.dumps({
         "metric": "score_and_compact us per layer (CLCES W=5, lambda=0.5, keep 50%)"
-                  + (", deferred: stream time of 24 back-to-back calls / 24" if args.defer else ""),
+                  + (", deferred: stream time of 24 back-to-back calls / 24" if args.defer else "")
+                  + (", ranks of earlier layers reused" if args.reuse_ranks else ""),
         "value": med * 1e6,
         "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": L, "dtype": "fp64 score / bf16 pages",
         "data": "synthetic (seeded chi-square raw scores, iid N(0,1) K/V)",

@@ -12,15 +12,27 @@ namespace kvs {
 constexpr int32_t kClcesErrNan = 1;    // a raw score is NaN or negative
 constexpr int32_t kClcesErrRow = 2;    // a token id is outside the score table
 constexpr int32_t kClcesErrCount = 4;  // a page's kept count disagrees with its planned length
-constexpr int32_t kRankTile = 512;     // keys per radix-sort workgroup
+constexpr int32_t kRankTile = 2048;    // keys per radix-rank workgroup
 constexpr int32_t kMaxPageTokensScored = 8192;
+constexpr int kMaxWindow = 8;          // largest CLCES layer window
+constexpr int kSelBits = 11;           // bits of the select digits (the last pass takes the 9 left)
+constexpr int kSelPasses = 6;
+
+// Rank arrays of one step: per window slot (rank in) or per ranked segment
+// (rank out), int32 [N] each.
+struct RankIn {
+  const int32_t* w[kMaxWindow];
+};
+struct RankOut {
+  int32_t* seg[kMaxWindow];
+};
 
 // Byte offsets of the CLCES buffers inside its workspace region.
 struct ClcesSizes {
   int64_t n_max;
-  int32_t p_max, w_max, nblk_max;
-  size_t keys_a, keys_b, vals_a, vals_b, ranks, scur, shat, hist, sel_hist, sel_state, entries, counts,
-      move_src, move_dst, n_moves, flag, total;
+  int32_t p_max, w_max;
+  size_t keys_a, keys_b, vals_a, vals_b, blk_cnt, scur, shat, sel_hist, sel_state, entries, counts, move_src,
+      move_dst, n_moves, flag, total;
 };
 
 ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_max);
@@ -41,23 +53,23 @@ struct ClcesArgs {
   double lambda;
   int64_t keep;
   int32_t* keep_ids_out;
-  int32_t* ranks_out;
+  // per window slot (oldest first): where the layer's ranks are (rank_new =
+  // 0: from an earlier step) or go (rank_new = 1: ranked in this step)
+  int32_t* rank_dst[kMaxWindow];
+  uint8_t rank_new[kMaxWindow];
+  int32_t n_rank;      // slots with rank_new set
+  double* s_hat_out;   // optional float64 [N]
 };
 
 // Stable ascending rank of every key within each of `segments` segments of N
-// keys (keys_a: [segments][N], overwritten; ranks: [segments][N]), 4 LSD
-// passes of 8 bits.  counts holds rank_counters(N, segments) counters; its
-// first part (the chunk sums, which accumulate with atomics) is set to zero
-// beforehand by the caller's first kernel.
-int64_t rank_counters(int N, int segments);
-hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
-                                uint32_t* counts, int N, int segments, const int32_t* flag, hipStream_t s);
+// keys (keys_a: [segments][N], overwritten): 4 LSD passes of 8 bits, two
+// launches each (block digit counts into blk_cnt, then the scatter);
+// segment w's ranks go to out.seg[w] ([N]).
+hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b,
+                                uint32_t* blk_cnt, const RankOut& out, int N, int segments, const int32_t* flag,
+                                hipStream_t s);
 
-// Enqueues the whole step, then waits for it and returns the new page
-// lengths (one per candidate entry) and the error flags.
-hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s);
-
-// The same step without the wait: enqueues the kernels only.  Its result (the
+// Enqueues the whole step (kernels only, no wait).  Its result (the
 // error flag, then the new length of each of the n_entries pages) is at
 // clces_result(a) on the device once the stream reaches this point, until the
 // next step that uses the same workspace.

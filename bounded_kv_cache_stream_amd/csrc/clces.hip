@@ -10,17 +10,21 @@
 //
 // Pipeline (one launch each, all on the caller's stream, one final sync):
 //   prep     the page table (first chunk) and the counters set to zero;
-//   gather   raw scores of every candidate at every window layer (by global
-//            token id), validate them, write 32-bit order keys;
-//   rank     stable LSD radix sort, 4 passes of 8 bits, all window layers at
-//            once (histogram / scan / scatter; the scatter is made stable
-//            with wave ballots); the last pass writes rank[token] directly;
+//   gather   raw scores of every candidate at every window layer whose ranks
+//            are not reused from an earlier step (by global token id),
+//            validate them, write 32-bit order keys;
+//   rank     stable LSD radix sort of those layers' keys, 4 passes of 8 bits
+//            over blocks of 2048 keys: the digit counts of every block, then
+//            a scatter whose workgroups add the counts of the blocks before
+//            them (all loads in flight together) and rank their own keys with
+//            wave ballots; the last pass writes rank[token] directly;
 //   fuse     float64 mean, population variance, Cons and s_hat with a fixed
 //            operation order and no contraction (bit-exact reproducible),
 //            plus the histogram of the first select digit;
-//   select   radix select of the keep_count-th largest s_hat (8 passes of 8
-//            bits over the 64-bit pattern, which orders non-negative doubles;
-//            the first histogram comes from fuse, the last step from mark);
+//   select   radix select of the keep_count-th largest s_hat (6 passes of
+//            11, 11, 11, 11, 11 and 9 bits over the 64-bit pattern, which
+//            orders non-negative doubles; the first histogram comes from fuse,
+//            the last step from mark);
 //   mark     per page: count of s_hat above / equal to the threshold;
 //   index    per page: its kept count and offsets (from all pages' counts),
 //            the kept token ids in slot order, and the moves: with
@@ -45,11 +49,20 @@ namespace kvs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = kRankTile / kThreads;  // 2
+constexpr int kItems = 2;                      // keys per thread of the select passes
+constexpr int kSelTile = kThreads * kItems;    // keys per select workgroup
+constexpr int kSelBins = 1 << kSelBits;        // bins of a select digit
 
+// Select state: the key bits fixed so far (prefix, under mask) and how many
+// of the keys matching them are still to be kept.  done: no later pass can
+// change the outcome (every matching key is kept, or nothing is to be kept,
+// or all bits are fixed), so later passes only pass the state on.
 struct SelState {
   unsigned long long prefix;
+  unsigned long long mask;
   long long k_rem;
+  int32_t done;
+  int32_t pad;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -60,41 +73,16 @@ __device__ inline uint32_t order_key(float s) {
 }
 
 // First launch of a step: the first page-table chunk, and the counters that
-// later kernels accumulate into set to zero (the rank chunk sums of every
-// pass, select histograms, per-page counts, the error flag).
-__global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* rank_counts, int64_t n_rank,
-                            uint32_t* sel_hist, int32_t* counts, int n_counts, int32_t* flag) {
+// later kernels accumulate into set to zero (select histograms, per-page
+// counts, the error flag).
+__global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* sel_hist, int n_hist, int32_t* counts,
+                            int n_counts, int32_t* flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < chunk.count) entries[chunk.first + i] = chunk.e[i];
-  if (i < n_rank) rank_counts[i] = 0;
-  if (i < 8 * 256) sel_hist[i] = 0;
+  if (i < n_hist) sel_hist[i] = 0;
   if (i < n_counts) counts[i] = 0;
   if (i == 0) *flag = 0;
 }
-
-constexpr int kChunk = 16;  // rank blocks per chunk of the digit-offset scan
-
-// Counts of one rank pass: [segment][block][digit] and the chunk sums
-// [segment][chunk][digit].  The chunk sums of all 4 passes come first in the
-// counter array (they accumulate with atomics, so only they are zeroed), then
-// the block counts of all 4 passes (stored outright).
-struct RankCounts {
-  uint32_t* blk;
-  uint32_t* chunk;
-  int nblk, nchunk;
-};
-
-__host__ __device__ inline int64_t rank_chunk_counters(int segments, int nblk) {
-  return 4 * (int64_t)segments * ((nblk + kChunk - 1) / kChunk) * 256;
-}
-
-__device__ inline RankCounts rank_counts(uint32_t* base, int pass, int segments, int nblk) {
-  const int nchunk = (nblk + kChunk - 1) / kChunk;
-  return RankCounts{base + rank_chunk_counters(segments, nblk) + (int64_t)pass * segments * nblk * 256,
-                    base + (int64_t)pass * segments * nchunk * 256, nblk, nchunk};
-}
-
-
 
 struct GatherArgs {
   const DevEntry* entries;
@@ -102,9 +90,10 @@ struct GatherArgs {
   int64_t page_bytes, id_off;
   const float* table;
   int64_t rows;
-  int32_t cols, first_layer, n_win, N;
-  uint32_t* keys;  // [n_win][N]
-  float* scur;     // [N]
+  int32_t cols, col_cur, n_seg, N;
+  int32_t seg_col[kMaxWindow];  // score-table column of each segment to rank
+  uint32_t* keys;  // [n_seg][N]
+  float* scur;     // [N] the current layer's raw score
   int32_t* flag;
 };
 
@@ -119,95 +108,133 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
     atomicOr(g.flag, kClcesErrRow);
     return;
   }
-  const float* row = g.table + (int64_t)tok * g.cols + g.first_layer;
-  float s = 0.f;
-  for (int w = 0; w < g.n_win; ++w) {
-    s = row[w];
-    if (!(s >= 0.f)) atomicOr(g.flag, kClcesErrNan);
+  const float* row = g.table + (int64_t)tok * g.cols;
+  bool bad = false;
+  for (int w = 0; w < g.n_seg; ++w) {
+    const float s = row[g.seg_col[w]];
+    bad = bad || !(s >= 0.f);
     g.keys[(int64_t)w * g.N + idx] = order_key(s);
   }
+  const float s = row[g.col_cur];
+  bad = bad || !(s >= 0.f);
+  if (bad) atomicOr(g.flag, kClcesErrNan);
   g.scur[idx] = __uint_as_float(order_key(s));
 }
 
-// Digit histogram of one block of one pass, counted in LDS (wave-aggregated:
-// the top bytes of similar scores are nearly uniform), stored as the block's
-// counts and added into its chunk's sums (at most kChunk workgroups add to
-// one counter).
-__global__ __launch_bounds__(kThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* counts, int N, int nblk,
-                                                             int pass, const int32_t* flag) {
+// One stable LSD pass of 8 bits over every segment to rank (grid: blocks x
+// segments) in two launches.  Block blk of a segment holds keys
+// blk*kRankTile + j*kRankThreads + tid (item-major, so index order is (item
+// j, wave, lane)).
+//   rank_hist_kernel     the digit counts of each block, stored as they are;
+//   rank_scatter_kernel  thread d < 256 adds digit d's counts over every block
+//                        of the segment (total) and over the blocks before
+//                        its own (before), all loads in flight together; the
+//                        keys of digit d go to (keys of smaller digits) +
+//                        (keys of digit d in earlier blocks) + (their rank in
+//                        this block).  Within the block every wave matches
+//                        the digits of each of its items with ballots, giving
+//                        each key its rank among equal digits of its (item,
+//                        wave) group and each group's digit counts; a pass over
+//                        the groups in index order turns those into offsets.
+constexpr int kRankThreads = 1024;
+constexpr int kRankItems = kRankTile / kRankThreads;  // 2
+constexpr int kRankWaves = kRankThreads / 64;
+constexpr int kHistThreads = 256;
+
+__global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* blk_cnt, int N,
+                                                                 int nblk, int pass, const int32_t* flag) {
   if (*flag) return;
   __shared__ uint32_t cnt[256];
-  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x, segments = gridDim.y;
+  const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
   const uint32_t* k = keys + (int64_t)w * N;
   const int shift = 8 * pass;
-  for (int j = 0; j < kItems; ++j) {
-    const int i = blk * kRankTile + j * kThreads + tid;
-    hist_add(cnt, i < N ? (k[i] >> shift) & 255u : 0u, i < N);
+  constexpr int kPer = kRankTile / kHistThreads;  // 8
+  uint32_t d[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = blk * kRankTile + j * kHistThreads + tid;
+    d[j] = i < N ? (k[i] >> shift) & 255u : 0u;
   }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) hist_add(cnt, d[j], blk * kRankTile + j * kHistThreads + tid < N);
   __syncthreads();
-  const RankCounts rc = rank_counts(counts, pass, segments, nblk);
-  rc.blk[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];
-  if (cnt[tid]) atomicAdd(&rc.chunk[((int64_t)w * rc.nchunk + blk / kChunk) * 256 + tid], cnt[tid]);
+  blk_cnt[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];
 }
 
-// One stable LSD pass over this block's kRankTile keys (kItems per thread;
-// key i = blk*kRankTile + j*kThreads + tid, so index order is (item j, wave,
-// lane)).  Every wave matches the digits of each of its items with ballots,
-// giving each key its rank among equal digits of its (item, wave) group and
-// each group's digit counts; one pass per digit then turns the counts into
-// exclusive offsets in index order, and every key goes to
-// offset[block][digit] + offset[group][digit] + rank.
-__global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
-                                                                uint32_t* keys_out, uint32_t* vals_out,
-                                                                int32_t* ranks, uint32_t* counts, int N,
-                                                                int nblk, int pass, const int32_t* flag) {
+// Exclusive prefix over the 256 digits: thread d (< 256) passes digit d's
+// count and gets the counts of digits below d (threads past 255 pass 0 and
+// get nothing useful).  Every thread of the workgroup calls it.
+__device__ inline uint32_t digit_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(x, off, 64);
+    if (lane >= off) x += t;
+  }
+  if (wave < 4 && lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t add = 0;
+  for (int q = 0; q < wave && q < 4; ++q) add += wsum[q];
+  return x - v + add;
+}
+
+__global__ __launch_bounds__(kRankThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
+                                                                    uint32_t* keys_out, uint32_t* vals_out,
+                                                                    const uint32_t* blk_cnt, RankOut out, int N,
+                                                                    int nblk, int pass, const int32_t* flag) {
   if (*flag) return;
-  constexpr int kWaves = kThreads / 64;
-  __shared__ uint32_t cnt[kItems][kWaves][256];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t cnt[kRankItems][kRankWaves][256];
+  __shared__ uint32_t part[2][4][256];
   const int w = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int segments = gridDim.y, shift = 8 * pass, last = pass == 3;
-  __shared__ int32_t scan[kThreads];
-  // where this block's keys of digit tid start in the segment: keys of smaller
-  // digits in the whole segment (the chunk sums added over chunks, scanned
-  // over digits), plus keys of digit tid in the chunks before this block's
-  // chunk and in the blocks before it within its chunk
-  uint32_t run;
-  {
-    const RankCounts rc = rank_counts(counts, pass, segments, nblk);
-    const int c = blk / kChunk;
-    const uint32_t* ct = rc.chunk + (int64_t)w * rc.nchunk * 256 + tid;
-    uint32_t tot = 0, before = 0;
-    for (int cc = 0; cc < rc.nchunk; ++cc) {
-      const uint32_t x = ct[(int64_t)cc * 256];
-      tot += x;
-      before += cc < c ? x : 0u;
-    }
-    const uint32_t* col = rc.blk + ((int64_t)w * nblk + (int64_t)c * kChunk) * 256 + tid;
-    for (int b = c * kChunk; b < blk; ++b) before += col[(int64_t)(b - c * kChunk) * 256];
-    run = (uint32_t)block_excl_scan<kThreads>((int32_t)tot, scan, nullptr) + before;
-  }
-#pragma unroll
-  for (int j = 0; j < kItems; ++j)
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) cnt[j][q][tid] = 0;
+  const int shift = 8 * pass, last = pass == 3;
   const int64_t seg = (int64_t)w * N;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  uint32_t key[kItems], val[kItems], rnk[kItems];
 #pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int i = blk * kRankTile + j * kThreads + tid;
+  for (int j = 0; j < kRankItems; ++j)
+    for (int q = tid >> 8; q < kRankWaves; q += kRankThreads / 256) cnt[j][q][tid & 255] = 0;
+  // digit d's counts over the segment and over the blocks before this one:
+  // four threads per digit, each adding every fourth block with all its loads
+  // in flight together, then combined through LDS
+  {
+    const int d = tid & 255, q = tid >> 8;
+    const uint32_t* col = blk_cnt + (int64_t)w * nblk * 256 + d;
+    constexpr int kBatch = 16;  // blocks per thread and batch: 64 blocks (131,072 keys) in one batch
+    uint32_t b = 0, t = 0;
+    for (int c0 = 0; c0 < nblk; c0 += 4 * kBatch) {
+      uint32_t x[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = c0 + 4 * j + q;
+        x[j] = c < nblk ? col[(int64_t)c * 256] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        t += x[j];
+        b += c0 + 4 * j + q < blk ? x[j] : 0u;
+      }
+    }
+    part[0][q][d] = b;
+    part[1][q][d] = t;
+  }
+  const int start = blk * kRankTile;
+  const uint32_t* ks = keys_in + seg;
+  uint32_t key[kRankItems], val[kRankItems], rnk[kRankItems];
+  const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kRankItems; ++j) {
+    const int i = start + j * kRankThreads + tid;
     const bool valid = i < N;
-    key[j] = valid ? keys_in[seg + i] : 0u;
+    key[j] = valid ? ks[i] : 0u;
     val[j] = valid ? (vals_in ? vals_in[seg + i] : (uint32_t)i) : 0u;
   }
   __syncthreads();  // counters zeroed
 #pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int i = blk * kRankTile + j * kThreads + tid;
-    const bool valid = i < N;
+  for (int j = 0; j < kRankItems; ++j) {
+    const bool valid = start + j * kRankThreads + tid < N;
     const uint32_t d = (key[j] >> shift) & 255u;
     unsigned long long m = __ballot(valid);
 #pragma unroll
@@ -219,25 +246,36 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* 
     rnk[j] = (uint32_t)__popcll(m & lt);
     if (valid && rnk[j] == 0) cnt[j][wave][d] = (uint32_t)__popcll(m);
   }
-  __syncthreads();
-  // thread tid owns digit tid: exclusive offsets over the groups in index order
+  // thread d < 256 owns digit d: exclusive offsets over the groups in index order
+  uint32_t before = 0, total = 0;
+  if (tid < 256) {
 #pragma unroll
-  for (int j = 0; j < kItems; ++j)
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) {
-      const uint32_t c = cnt[j][q][tid];
-      cnt[j][q][tid] = run;
-      run += c;
+    for (int q = 0; q < 4; ++q) {
+      before += part[0][q][tid];
+      total += part[1][q][tid];
     }
+  }
+  const uint32_t base = digit_excl_scan(tid < 256 ? total : 0u, wsum);  // its barrier also orders cnt
+  if (tid < 256) {
+    uint32_t run = base + before;
+#pragma unroll
+    for (int j = 0; j < kRankItems; ++j)
+#pragma unroll
+      for (int q = 0; q < kRankWaves; ++q) {
+        const uint32_t c = cnt[j][q][tid];
+        cnt[j][q][tid] = run;
+        run += c;
+      }
+  }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int i = blk * kRankTile + j * kThreads + tid;
+  for (int j = 0; j < kRankItems; ++j) {
+    const int i = start + j * kRankThreads + tid;
     if (i < N) {
       const uint32_t d = (key[j] >> shift) & 255u;
       const uint32_t off = cnt[j][wave][d] + rnk[j];
       if (last) {
-        ranks[seg + val[j]] = (int32_t)off;
+        out.seg[w][val[j]] = (int32_t)off;
       } else {
         keys_out[seg + off] = key[j];
         vals_out[seg + off] = val[j];
@@ -246,88 +284,108 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(const uint32_t* 
   }
 }
 
-// Also the first select pass: the histogram of the top byte of s_hat, and
+// Bits of select digit p of a 64-bit key: 11 bits from the top for passes
+// 0-4, the low 9 bits for pass 5.
+__device__ inline int sel_shift(int p) { return p < kSelPasses - 1 ? 64 - kSelBits * (p + 1) : 0; }
+
+// Adds an LDS histogram of kSelBins counters into the global one (zeros skipped).
+__device__ inline void flush_hist(const uint32_t* cnt, uint32_t* dst) {
+  for (int d = threadIdx.x; d < kSelBins; d += kThreads)
+    if (cnt[d]) atomicAdd(&dst[d], cnt[d]);
+}
+
+// Also the first select pass: the histogram of the top digit of s_hat, and
 // the state before it (nothing fixed, keep_count to find).
-__global__ __launch_bounds__(kThreads) void fuse_kernel(const int32_t* ranks, const float* scur,
-                                                        unsigned long long* shat, int N, int n_win, double lambda,
+__global__ __launch_bounds__(kThreads) void fuse_kernel(RankIn ranks, const float* scur, unsigned long long* shat,
+                                                        double* shat_out, int N, int n_win, double lambda,
                                                         double sqrt12, uint32_t* sel_hist, SelState* states,
                                                         long long keep, const int32_t* flag) {
 #pragma clang fp contract(off)
   if (*flag) return;
-  __shared__ uint32_t cnt[256];
-  cnt[threadIdx.x] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) states[0] = SelState{0ull, keep};
+  __shared__ uint32_t cnt[kSelBins];
+  for (int d = threadIdx.x; d < kSelBins; d += kThreads) cnt[d] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) states[0] = SelState{0ull, 0ull, keep, keep == 0, 0};
   __syncthreads();
   const int i = blockIdx.x * kThreads + threadIdx.x;
   const bool valid = i < N;
   unsigned long long bits = 0;
   if (valid) {
-  const double denom = (double)(N - 1);
-  double r[8];
-  double acc = 0.0;
+    const double denom = (double)(N - 1);
+    double r[kMaxWindow];
+    double acc = 0.0;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    if (w < n_win) {
-      r[w] = N > 1 ? (double)ranks[(int64_t)w * N + i] / denom : 0.0;
-      acc = acc + r[w];
+    for (int w = 0; w < kMaxWindow; ++w) {
+      if (w < n_win) {
+        r[w] = N > 1 ? (double)ranks.w[w][i] / denom : 0.0;
+        acc = acc + r[w];
+      }
     }
-  }
-  const double mu = acc / (double)n_win;
-  double acc2 = 0.0;
+    const double mu = acc / (double)n_win;
+    double acc2 = 0.0;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    if (w < n_win) {
-      const double d = r[w] - mu;
-      acc2 = acc2 + d * d;
+    for (int w = 0; w < kMaxWindow; ++w) {
+      if (w < n_win) {
+        const double d = r[w] - mu;
+        acc2 = acc2 + d * d;
+      }
     }
+    const double var = acc2 / (double)n_win;
+    const double sigma = sqrt(var);
+    const double c = 1.0 - sigma * sqrt12;
+    const double cons = c > 0.0 ? c : 0.0;
+    const double sh = (double)scur[i] * (1.0 + lambda * cons) + 0.0;
+    bits = (unsigned long long)__double_as_longlong(sh);
+    shat[i] = bits;
+    if (shat_out) shat_out[i] = sh;
   }
-  const double var = acc2 / (double)n_win;
-  const double sigma = sqrt(var);
-  const double c = 1.0 - sigma * sqrt12;
-  const double cons = c > 0.0 ? c : 0.0;
-  const double sh = (double)scur[i] * (1.0 + lambda * cons) + 0.0;
-  bits = (unsigned long long)__double_as_longlong(sh);
-  shat[i] = bits;
-  }
-  hist_add(cnt, (uint32_t)(bits >> 56), valid);
+  hist_add(cnt, (uint32_t)(bits >> sel_shift(0)), valid);
   __syncthreads();
-  if (cnt[threadIdx.x]) atomicAdd(&sel_hist[threadIdx.x], cnt[threadIdx.x]);
+  flush_hist(cnt, sel_hist);
 }
 
 // One select step: from the state before pass p and that pass's digit
 // histogram, fix digit p (the largest digit whose suffix count reaches k_rem)
-// and reduce k_rem by the count of larger digits.  Wave 0 runs a suffix scan
-// over its 64 lanes (4 digits each); the result is broadcast through LDS.
+// and reduce k_rem by the count of larger digits.  Thread t owns digits
+// 8t .. 8t+7; a suffix scan over the threads (within each wave, then across
+// the four waves) finds the owner, which walks its digits downward; the
+// result is broadcast through LDS.
 __device__ SelState select_advance(SelState st, const uint32_t* hist, int p) {
-  __shared__ uint32_t cnt[256];
+  constexpr int kPer = kSelBins / kThreads;  // 8
+  __shared__ uint32_t cnt[kSelBins];
+  __shared__ long long wtot[kThreads / 64];
   __shared__ SelState out;
-  cnt[threadIdx.x] = hist[threadIdx.x];
-  if (threadIdx.x == 0) out = st;
+  if (st.done) return st;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int d = tid; d < kSelBins; d += kThreads) cnt[d] = hist[d];
+  if (tid == 0) out = st;
   __syncthreads();
-  if (threadIdx.x < 64 && st.k_rem > 0) {
-    const int lane = threadIdx.x;
-    long long own = 0;
+  long long own = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) own += cnt[4 * lane + j];
-    long long suf = own;  // inclusive suffix sum over lanes >= lane
+  for (int j = 0; j < kPer; ++j) own += cnt[kPer * tid + j];
+  long long suf = own;  // inclusive suffix sum over the lanes >= lane of this wave
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long t = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += t;
-    }
-    long long above = __shfl_down(suf, 1, 64);  // lanes > lane
-    if (lane == 63) above = 0;
-    if (above < st.k_rem && suf >= st.k_rem) {
-      long long cum = above;
-      for (int j = 3; j >= 0; --j) {
-        const long long c = cnt[4 * lane + j];
-        if (cum + c >= st.k_rem) {
-          out.prefix = st.prefix | ((unsigned long long)(4 * lane + j) << (56 - 8 * p));
-          out.k_rem = st.k_rem - cum;
-          break;
-        }
-        cum += c;
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long t = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += t;
+  }
+  if (lane == 0) wtot[wave] = suf;
+  __syncthreads();
+  for (int q = wave + 1; q < kThreads / 64; ++q) suf += wtot[q];
+  const long long above = suf - own;
+  if (above < st.k_rem && suf >= st.k_rem) {
+    long long cum = above;
+    for (int j = kPer - 1; j >= 0; --j) {
+      const long long c = cnt[kPer * tid + j];
+      if (cum + c >= st.k_rem) {
+        const int shift = sel_shift(p);
+        const int width = (p > 0 ? sel_shift(p - 1) : 64) - shift;
+        out.prefix = st.prefix | ((unsigned long long)(kPer * tid + j) << shift);
+        out.mask = st.mask | (((1ull << width) - 1ull) << shift);
+        out.k_rem = st.k_rem - cum;
+        out.done = out.k_rem == c || p == kSelPasses - 1;
+        break;
       }
+      cum += c;
     }
   }
   __syncthreads();
@@ -336,28 +394,29 @@ __device__ SelState select_advance(SelState st, const uint32_t* hist, int p) {
   return r;
 }
 
-// Pass p histograms digit p of the keys that match the digits fixed so far.
-// The state before pass p is advanced once from the previous pass's state
-// (stored by its workgroup 0) and histogram; workgroup 0 stores it in turn.
+// Pass p (1..5) histograms digit p of the keys that match the digits fixed so
+// far.  The state before pass p is advanced once from the previous pass's
+// state (stored by its workgroup 0) and histogram; workgroup 0 stores it in turn.
 __global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned long long* keys, int N,
-                                                               uint32_t* sel_hist, SelState* states, long long keep,
-                                                               int p, const int32_t* flag) {
+                                                               uint32_t* sel_hist, SelState* states, int p,
+                                                               const int32_t* flag) {
   if (*flag) return;
-  __shared__ uint32_t cnt[256];
-  const SelState st = p == 0 ? SelState{0ull, keep} : select_advance(states[p - 1], sel_hist + (p - 1) * 256, p - 1);
+  __shared__ uint32_t cnt[kSelBins];
+  const SelState st = select_advance(states[p - 1], sel_hist + (p - 1) * kSelBins, p - 1);
   if (blockIdx.x == 0 && threadIdx.x == 0) states[p] = st;
-  cnt[threadIdx.x] = 0;
+  if (st.done) return;
+  for (int d = threadIdx.x; d < kSelBins; d += kThreads) cnt[d] = 0;
   __syncthreads();
-  const int shift = 56 - 8 * p;
-  const unsigned long long hi = p == 0 ? 0ull : (~0ull << (shift + 8));
+  const int shift = sel_shift(p);
+  const unsigned long long dmask = (1ull << (sel_shift(p - 1) - shift)) - 1ull;
   for (int j = 0; j < kItems; ++j) {
-    const int i = blockIdx.x * kRankTile + j * kThreads + threadIdx.x;
+    const int i = blockIdx.x * kSelTile + j * kThreads + threadIdx.x;
     const unsigned long long k = i < N ? keys[i] : 0ull;
-    const bool match = i < N && (k & hi) == st.prefix;
-    hist_add(cnt, (uint32_t)((k >> shift) & 255ull), match);
+    const bool match = i < N && (k & st.mask) == st.prefix;
+    hist_add(cnt, (uint32_t)((k >> shift) & dmask), match);
   }
   __syncthreads();
-  if (cnt[threadIdx.x]) atomicAdd(&sel_hist[p * 256 + threadIdx.x], cnt[threadIdx.x]);
+  flush_hist(cnt, sel_hist + p * kSelBins);
 }
 
 struct MarkArgs {
@@ -367,7 +426,7 @@ struct MarkArgs {
   long long keep;
   int32_t* n_gt;
   int32_t* n_eq;
-  SelState* states;  // [0..7] states before each pass, [8] the final threshold
+  SelState* states;  // [0..5] states before each pass, [6] the final threshold
   const int32_t* flag;
 };
 
@@ -375,15 +434,16 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
   if (*a.flag) return;
   __shared__ int32_t sg, se;
   // threshold = the keep_count-th largest key; keep 0 keeps nothing
-  SelState st = a.keep == 0 ? SelState{~0ull, 0} : select_advance(a.states[7], a.sel_hist + 7 * 256, 7);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.states[8] = st;
+  const SelState st =
+      select_advance(a.states[kSelPasses - 1], a.sel_hist + (kSelPasses - 1) * kSelBins, kSelPasses - 1);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.states[kSelPasses] = st;
   if (threadIdx.x == 0) { sg = 0; se = 0; }
   __syncthreads();
   const DevEntry en = a.entries[blockIdx.x];
   const int j = blockIdx.y * kThreads + threadIdx.x;
   int gt = 0, eq = 0;
   if (j < en.len) {
-    const unsigned long long k = a.shat[en.tok_start + j];
+    const unsigned long long k = a.shat[en.tok_start + j] & st.mask;
     gt = k > st.prefix;
     eq = k == st.prefix;
   }
@@ -452,12 +512,12 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   const int b = tid * per, end = min(b + per, len);
   const unsigned long long* sh = a.shat + en.tok_start;
   int32_t n_eq = 0;
-  for (int j = b; j < end; ++j) n_eq += sh[j] == st.prefix;
+  for (int j = b; j < end; ++j) n_eq += (sh[j] & st.mask) == st.prefix;
   const int32_t eq_start = eq_tot + block_excl_scan<kThreads>(n_eq, scan, nullptr);
   int32_t eq_rank = eq_start;
   int32_t n_keep = 0, n_hole = 0;
   for (int j = b; j < end; ++j) {
-    const unsigned long long k = sh[j];
+    const unsigned long long k = sh[j] & st.mask;
     bool keep = k > st.prefix;
     if (k == st.prefix) keep = eq_rank++ < st.k_rem;
     n_keep += keep;
@@ -476,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   uint16_t* dst = a.move_dst + (int64_t)e * a.g.ts;
   eq_rank = eq_start;
   for (int j = b; j < end; ++j) {
-    const unsigned long long k = sh[j];
+    const unsigned long long k = sh[j] & st.mask;
     bool keep = k > st.prefix;
     if (k == st.prefix) keep = eq_rank++ < st.k_rem;
     if (keep)
@@ -527,7 +587,6 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.n_max = n_max;
   z.p_max = p_max;
   z.w_max = w_max;
-  z.nblk_max = (int32_t)((n_max + kRankTile - 1) / kRankTile);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -539,12 +598,11 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.keys_b = take(wn * 4);
   z.vals_a = take(wn * 4);
   z.vals_b = take(wn * 4);
-  z.ranks = take(wn * 4);
+  z.blk_cnt = take((size_t)w_max * ((n_max + kRankTile - 1) / kRankTile) * 256 * 4);
   z.scur = take((size_t)n_max * 4);
   z.shat = take((size_t)n_max * 8);
-  z.hist = take((size_t)rank_counters((int)n_max, w_max) * 4);  // rank counts of the 4 passes
-  z.sel_hist = take(8 * 256 * 4);
-  z.sel_state = take(9 * sizeof(SelState));
+  z.sel_hist = take((size_t)kSelPasses * kSelBins * 4);
+  z.sel_state = take((kSelPasses + 1) * sizeof(SelState));
   z.entries = take((size_t)p_max * sizeof(DevEntry));
   z.counts = take((size_t)p_max * 2 * 4);
   z.move_src = take((size_t)p_max * ts_max * 2);
@@ -555,23 +613,18 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   return z;
 }
 
-int64_t rank_counters(int N, int segments) {
-  const int nblk = (N + kRankTile - 1) / kRankTile;
-  return rank_chunk_counters(segments, nblk) + 4 * (int64_t)segments * nblk * 256;
-}
-
-hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, int32_t* ranks,
-                                uint32_t* counts, int N, int segments, const int32_t* flag, hipStream_t s) {
+hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b,
+                                uint32_t* blk_cnt, const RankOut& out, int N, int segments, const int32_t* flag,
+                                hipStream_t s) {
   const int nblk = (N + kRankTile - 1) / kRankTile;
   uint32_t* kin = keys_a;
   uint32_t* kout = keys_b;
   uint32_t* vin = nullptr;
   uint32_t* vout = vals_b;
+  const dim3 grid((unsigned)nblk, (unsigned)segments);
   for (int pass = 0; pass < 4; ++pass) {
-    rank_hist_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(kin, counts, N, nblk, pass,
-                                                                                          flag);
-    rank_scatter_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kThreads), 0, s>>>(
-        kin, vin, kout, vout, ranks, counts, N, nblk, pass, flag);
+    rank_hist_kernel<<<grid, dim3(kHistThreads), 0, s>>>(kin, blk_cnt, N, nblk, pass, flag);
+    rank_scatter_kernel<<<grid, dim3(kRankThreads), 0, s>>>(kin, vin, kout, vout, blk_cnt, out, N, nblk, pass, flag);
     std::swap(kin, kout);
     vin = vout;
     vout = vout == vals_b ? vals_a : vals_b;
@@ -587,16 +640,15 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
   auto* keys_b = reinterpret_cast<uint32_t*>(ws + z.keys_b);
   auto* vals_a = reinterpret_cast<uint32_t*>(ws + z.vals_a);
   auto* vals_b = reinterpret_cast<uint32_t*>(ws + z.vals_b);
-  auto* ranks = a.ranks_out ? a.ranks_out : reinterpret_cast<int32_t*>(ws + z.ranks);
   auto* scur = reinterpret_cast<float*>(ws + z.scur);
   auto* shat = reinterpret_cast<unsigned long long*>(ws + z.shat);
-  auto* hist = reinterpret_cast<uint32_t*>(ws + z.hist);
   auto* sel_hist = reinterpret_cast<uint32_t*>(ws + z.sel_hist);
   auto* sel_state = reinterpret_cast<SelState*>(ws + z.sel_state);
   auto* counts = reinterpret_cast<int32_t*>(ws + z.counts);
   auto* flag = reinterpret_cast<int32_t*>(ws + z.flag);
   const int P = a.n_entries, N = a.n_tokens, W = a.n_window;
-  if (P > z.p_max || (int64_t)N > z.n_max || W > z.w_max || a.geom.ts > kMaxPageTokensScored)
+  if (P > z.p_max || (int64_t)N > z.n_max || W > z.w_max || W > kMaxWindow || a.n_rank > W ||
+      a.geom.ts > kMaxPageTokensScored)
     return hipErrorInvalidValue;
 
   {
@@ -604,29 +656,53 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
     c.first = 0;
     c.count = std::min(P, kUploadChunk);
     for (int i = 0; i < c.count; ++i) c.e[i] = a.entries_host[i];
-    const int64_t n_rank = rank_chunk_counters(W, (N + kRankTile - 1) / kRankTile);  // the chunk sums
-    const int64_t nz = std::max<int64_t>(std::max(8 * 256, 2 * P), n_rank);
-    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, hist, n_rank, sel_hist, counts,
-                                                                          2 * P, flag);
+    const int n_hist = kSelPasses * kSelBins;
+    const int64_t nz = std::max(n_hist, 2 * P);
+    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, sel_hist, n_hist, counts, 2 * P,
+                                                                          flag);
   }
   hipError_t e = P > kUploadChunk ? launch_table_upload(entries + kUploadChunk, a.entries_host + kUploadChunk,
                                                         P - kUploadChunk, s)
                                   : hipGetLastError();
   if (e != hipSuccess) return e;
 
-  GatherArgs g{entries, a.pool, a.geom.page_bytes, a.geom.id_off, a.score_table, a.score_rows, a.score_cols,
-               a.first_layer, W, N, keys_a, scur, flag};
+  // raw scores: the layers to rank (window slots with rank_out set), then the current layer
+  GatherArgs g{};
+  g.entries = entries;
+  g.pool = a.pool;
+  g.page_bytes = a.geom.page_bytes;
+  g.id_off = a.geom.id_off;
+  g.table = a.score_table;
+  g.rows = a.score_rows;
+  g.cols = a.score_cols;
+  g.col_cur = a.first_layer + W - 1;
+  g.N = N;
+  g.keys = keys_a;
+  g.scur = scur;
+  g.flag = flag;
+  RankOut ro{};
+  int nseg = 0;
+  for (int w = 0; w < W; ++w)
+    if (a.rank_new[w]) {
+      g.seg_col[nseg] = a.first_layer + w;
+      ro.seg[nseg] = a.rank_dst[w];
+      ++nseg;
+    }
+  g.n_seg = nseg;
   gather_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(g);
-
-  const int nblk = (N + kRankTile - 1) / kRankTile;
-  e = launch_rank_segments(keys_a, keys_b, vals_a, vals_b, ranks, hist, N, W, flag, s);
-  if (e != hipSuccess) return e;
+  if (nseg > 0) {
+    e = launch_rank_segments(keys_a, keys_b, vals_a, vals_b, reinterpret_cast<uint32_t*>(ws + z.blk_cnt), ro, N, nseg,
+                             flag, s);
+    if (e != hipSuccess) return e;
+  }
+  RankIn ri{};
+  for (int w = 0; w < W; ++w) ri.w[w] = a.rank_dst[w];
   fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
-      ranks, scur, shat, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
+      ri, scur, shat, a.s_hat_out, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
+  const int nblk = (N + kSelTile - 1) / kSelTile;
   if (a.keep > 0) {
-    for (int p = 1; p < 8; ++p)
-      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, a.keep, p,
-                                                                         flag);
+    for (int p = 1; p < kSelPasses; ++p)
+      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, p, flag);
   }
   MarkArgs m{entries, shat, sel_hist, a.keep, counts, counts + P, sel_state, flag};
   mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
@@ -634,7 +710,7 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
                  reinterpret_cast<uint16_t*>(ws + z.move_src),
                  reinterpret_cast<uint16_t*>(ws + z.move_dst),
                  reinterpret_cast<int32_t*>(ws + z.n_moves),
-                 shat, sel_state + 8, counts, counts + P, flag + 1, P, a.pool, a.geom, a.keep_ids_out, flag,
+                 shat, sel_state + kSelPasses, counts, counts + P, flag + 1, P, a.pool, a.geom, a.keep_ids_out, flag,
                  flag};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
@@ -654,18 +730,5 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
 }
 
 int32_t* clces_result(const ClcesArgs& a) { return reinterpret_cast<int32_t*>(a.ws + a.sizes.flag); }
-
-hipError_t run_clces(const ClcesArgs& a, int32_t* new_lens_host, int32_t* err_flag_host, hipStream_t s) {
-  hipError_t e = enqueue_clces(a, s);
-  if (e != hipSuccess) return e;
-  // one read-back: the error flag and, after it, the new page lengths
-  std::vector<int32_t> rb((size_t)a.n_entries + 1);
-  e = hipMemcpyAsync(rb.data(), clces_result(a), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return e;
-  *err_flag_host = rb[0];
-  std::copy(rb.begin() + 1, rb.end(), new_lens_host);
-  return hipSuccess;
-}
 
 }  // namespace kvs

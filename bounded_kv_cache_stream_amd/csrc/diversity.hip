@@ -74,7 +74,7 @@ struct DSel {
   int32_t done;
   int32_t pad;
 };
-constexpr int kSelPasses = 8;
+constexpr int kDivSelPasses = 8;
 
 struct DivK {
   const DivLayer* layers;  // [n]
@@ -428,7 +428,7 @@ __device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
           out.prefix = st.prefix | ((uint64_t)(4 * tid + j) << shift);
           out.mask = st.mask | (0xffull << shift);
           out.k_rem = st.k_rem - cum;
-          out.done = out.k_rem == c || p == kSelPasses - 1;
+          out.done = out.k_rem == c || p == kDivSelPasses - 1;
           break;
         }
         cum += c;
@@ -442,10 +442,10 @@ __device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
 }
 
 __device__ inline uint32_t* sel_hist(const DivK& a, int slot, int p, int h) {
-  return a.dhist + (((int64_t)slot * kSelPasses + p) * a.H + h) * 256;
+  return a.dhist + (((int64_t)slot * kDivSelPasses + p) * a.H + h) * 256;
 }
 __device__ inline DSel* sel_state(const DivK& a, int slot, int p, int h) {
-  return a.dstate + ((int64_t)slot * (kSelPasses + 1) + p) * a.H + h;
+  return a.dstate + ((int64_t)slot * (kDivSelPasses + 1) + p) * a.H + h;
 }
 
 // One workgroup per (head, slot): the state before pass p (p = 0: nothing
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void div_mark_kernel(DivK a) {
   const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
   const DivLayer L = a.layers[slot];
   if (p >= L.P) return;
-  const DSel st = *sel_state(a, slot, kSelPasses, h);
+  const DSel st = *sel_state(a, slot, kDivSelPasses, h);
   if (tid == 0) {
     s_lt = 0;
     s_eq = 0;
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
   const int wave = tid >> 6, lane = tid & 63;
   const DevEntry en = tab(a, slot, h, p);
   const int len = en.len;
-  const DSel st = *sel_state(a, slot, kSelPasses, h);
+  const DSel st = *sel_state(a, slot, kDivSelPasses, h);
   const int64_t cnt_at = ((int64_t)slot * a.H + h) * a.p_max;
   const int32_t eq = a.eq_cnt[cnt_at + p];
   // keys equal to t in the earlier pages: only a page holding such a key
@@ -690,8 +690,8 @@ DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers) 
   z.partial = take(L * H * P * kHeadDim * 8);
   z.mean = take(L * H * (kHeadDim + 1) * 8);
   z.spart = take(L * H * P * 8);
-  z.dhist = take(L * kSelPasses * H * 256 * 4);
-  z.dstate = take(L * (kSelPasses + 1) * H * sizeof(DSel));
+  z.dhist = take(L * kDivSelPasses * H * 256 * 4);
+  z.dstate = take(L * (kDivSelPasses + 1) * H * sizeof(DSel));
   z.lt_cnt = take(L * H * P * 4);
   z.eq_cnt = take(L * H * P * 4);
   // the outputs the host reads back, adjacent: a scoring reads totals and
@@ -716,7 +716,7 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   const int H = c.geom.heads;
   hipError_t e = hipMemcpyAsync(c.ws + z.params, c.staging, div_staging_bytes(z, c.n), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
-  const int n_hist = c.prune ? c.n * kSelPasses * H * 256 : 0;
+  const int n_hist = c.prune ? c.n * kDivSelPasses * H * 256 : 0;
   div_zero_kernel<<<dim3((unsigned)((std::max(n_hist, c.n + 1) + 255) / 256)), dim3(256), 0, s>>>(
       k.flags, c.n + 1, reinterpret_cast<int32_t*>(k.dhist), n_hist);
   div_tables_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k);
@@ -736,11 +736,11 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   if (c.prune) {
     const unsigned nblk = (unsigned)((c.max_N + kSelTile - 1) / kSelTile);
     const dim3 heads((unsigned)H, (unsigned)c.n);
-    for (int p = 0; p < kSelPasses; ++p) {
+    for (int p = 0; p < kDivSelPasses; ++p) {
       div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, p);
       div_select_kernel<<<dim3(nblk, (unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k, p);
     }
-    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, kSelPasses);
+    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, kDivSelPasses);
     div_mark_kernel<<<pages, dim3(kThreads), 0, s>>>(k);
     if (c.geom.esize == 2)
       div_compact_kernel<__bf16><<<pages, dim3(kThreads), 0, s>>>(k);

@@ -59,7 +59,7 @@ struct Layout {
   size_t pool_bytes;
   // workspace regions (byte offsets); the CLCES and diversity steps share one
   // region (each waits for its own work before it returns)
-  size_t tables, part_o, part_ml, hlens, dkeys, clces, div, ws_bytes;
+  size_t tables, part_o, part_ml, hlens, dkeys, rank_cache, clces, div, ws_bytes;
   int64_t part_rows;  // capacity in (split x query) rows
   kvs::ClcesSizes cl;
   kvs::DivSizes dv;
@@ -117,6 +117,9 @@ Layout make_layout(const kv_pool_config* c) {
   // head) against the 256 of its K and V rows
   L.dkeys = off;
   off = align_up(off + (size_t)c->num_layers * (size_t)H * (size_t)c->pages_per_layer * (size_t)c->page_tokens * 8);
+  // CLCES ranks kept for later steps: int32 [max_window][pages_per_layer * page_tokens]
+  L.rank_cache = off;
+  off = align_up(off + (size_t)c->max_window * (size_t)c->pages_per_layer * (size_t)c->page_tokens * 4);
   L.cl = kvs::clces_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, c->max_window,
                           (int32_t)ts);
   L.dv = kvs::div_sizes((int64_t)c->pages_per_layer * c->page_tokens, c->pages_per_layer, (int32_t)H,
@@ -153,6 +156,19 @@ struct kv_pool {
   };
   std::vector<Pending> pending;
   int32_t* pinned = nullptr;
+  // CLCES rank history: per slot of the rank-cache region, which score-table
+  // column it ranks and over which candidate sequence (score table, its rows,
+  // the candidate frames of a layer never compacted, merged or pruned)
+  struct RankSlot {
+    bool valid = false;
+    int32_t column = -1;
+    const float* table = nullptr;
+    int64_t rows = 0;
+    std::vector<int64_t> frames;
+    uint64_t used = 0;  // last step that named it
+  };
+  std::vector<RankSlot> rank_slots;
+  uint64_t rank_clock = 0;
 };
 
 namespace {
@@ -477,6 +493,7 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   p->layers.resize((size_t)cfg->num_layers);
   p->scored_gen.assign((size_t)cfg->num_layers, -1);
   p->pending.resize((size_t)cfg->num_layers);
+  p->rank_slots.resize((size_t)cfg->max_window);
   for (auto& l : p->layers)
     l.init(cfg->pages_per_layer, cfg->scale_frames, cfg->sliding_window, cfg->keyframe_interval, cfg->page_tokens,
            cfg->special_tokens);
@@ -500,6 +517,7 @@ kv_status kv_reset(kv_pool_t* pool) {
   if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
   discard_pending(pool);
   for (auto& l : pool->layers) l.reset();
+  for (auto& r : pool->rank_slots) r.valid = false;
   return ok();
 }
 
@@ -871,7 +889,8 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
     return fail(KV_ERR_ARG, "window %d out of 1..max_window (%d)", params->window, pool->cfg.max_window);
   if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
-  if (params->flags & ~KV_CLCES_DEFER) return fail(KV_ERR_ARG, "unknown CLCES flags 0x%x", params->flags);
+  if (params->flags & ~(KV_CLCES_DEFER | KV_CLCES_REUSE_RANKS))
+    return fail(KV_ERR_ARG, "unknown CLCES flags 0x%x", params->flags);
   auto& L = pool->layers[(size_t)layer];
   if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
   if (pool->cfg.special_tokens > 0)
@@ -917,7 +936,70 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   a.lambda = params->lambda;
   a.keep = params->keep_count;
   a.keep_ids_out = keep_ids_out_dev;
-  a.ranks_out = ranks_out_dev;
+  a.s_hat_out = params->s_hat_out;
+  // Rank history ([SCV] 2.1.4): with KV_CLCES_REUSE_RANKS, a window layer
+  // whose ranks an earlier synchronous step computed over the same candidate
+  // sequence (a layer never compacted, merged or pruned holds whole frames, so
+  // its candidate frames name the sequence) and the same score table is not
+  // ranked again.  Every other window layer is ranked into the least recently
+  // used slot not taken by this step.
+  const bool pristine = L.compactions == 0 && L.merges == 0 && L.prunes == 0;
+  const bool reuse = (params->flags & KV_CLCES_REUSE_RANKS) != 0 && pristine;
+  std::vector<int64_t> frames;
+  if (reuse)
+    for (size_t i = first; i < L.table.size(); ++i) frames.push_back(L.table[i].frame);
+  auto& slots = pool->rank_slots;
+  std::vector<char> taken(slots.size(), 0);
+  std::vector<int32_t> slot_of((size_t)n_win, -1);
+  const uint64_t now = ++pool->rank_clock;
+  for (int32_t w = 0; w < n_win && reuse; ++w)
+    for (size_t k = 0; k < slots.size(); ++k) {
+      const auto& r = slots[k];
+      if (r.valid && r.column == a.first_layer + w && r.table == score_table_dev && r.rows == score_rows &&
+          r.frames == frames) {
+        slot_of[(size_t)w] = (int32_t)k;
+        taken[k] = 1;
+        break;
+      }
+    }
+  a.n_rank = 0;
+  for (int32_t w = 0; w < n_win; ++w) {
+    if (slot_of[(size_t)w] < 0) {
+      size_t best = slots.size();
+      for (size_t k = 0; k < slots.size(); ++k)
+        if (!taken[k] && (best == slots.size() || !slots[k].valid ||
+                          (slots[best].valid && slots[k].used < slots[best].used)))
+          best = k;
+      slot_of[(size_t)w] = (int32_t)best;
+      taken[best] = 1;
+      slots[best].valid = false;  // overwritten by this step
+      a.rank_new[w] = 1;
+      ++a.n_rank;
+    }
+    slots[(size_t)slot_of[(size_t)w]].used = now;
+    a.rank_dst[w] = reinterpret_cast<int32_t*>(pool->ws + pool->lay.rank_cache) +
+                    (int64_t)slot_of[(size_t)w] * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
+  }
+  auto copy_ranks = [&](hipStream_t st) -> hipError_t {
+    for (int32_t w = 0; w < n_win && ranks_out_dev; ++w) {
+      hipError_t ce = hipMemcpyAsync(ranks_out_dev + (int64_t)w * N, a.rank_dst[w], sizeof(int32_t) * (size_t)N,
+                                     hipMemcpyDeviceToDevice, st);
+      if (ce != hipSuccess) return ce;
+    }
+    return hipSuccess;
+  };
+  auto record_ranks = [&]() {
+    if (!reuse) return;
+    for (int32_t w = 0; w < n_win; ++w)
+      if (a.rank_new[w]) {
+        auto& r = slots[(size_t)slot_of[(size_t)w]];
+        r.valid = true;
+        r.column = a.first_layer + w;
+        r.table = score_table_dev;
+        r.rows = score_rows;
+        r.frames = frames;
+      }
+  };
   if (params->flags & KV_CLCES_DEFER) {
     // enqueue the step and its read-back; the next call on this layer applies it
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -929,6 +1011,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
                         hipHostMallocDefault);
     if (e == hipSuccess && !ps.done) e = hipEventCreateWithFlags(&ps.done, hipEventDisableTiming);
     if (e == hipSuccess) e = kvs::enqueue_clces(a, st);
+    if (e == hipSuccess) e = copy_ranks(st);
     if (e == hipSuccess)
       e = hipMemcpyAsync(pool->pinned + (size_t)layer * ((size_t)pool->cfg.pages_per_layer + 1), kvs::clces_result(a),
                          sizeof(int32_t) * ((size_t)a.n_entries + 1), hipMemcpyDeviceToHost, st);
@@ -942,8 +1025,17 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   }
   std::vector<int32_t> new_lens((size_t)a.n_entries);
   int32_t err_flag = 0;
-  hipError_t e = kvs::run_clces(a, new_lens.data(), &err_flag, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kvs::enqueue_clces(a, st);
+  if (e == hipSuccess) e = copy_ranks(st);
+  // one read-back: the error flag and, after it, the new page lengths
+  std::vector<int32_t> rb((size_t)a.n_entries + 1);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(rb.data(), kvs::clces_result(a), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "CLCES step");
+  err_flag = rb[0];
+  std::copy(rb.begin() + 1, rb.end(), new_lens.begin());
   if (err_flag & kvs::kClcesErrNan) return fail(KV_ERR_NAN, "layer %d: a raw score is NaN or negative", layer);
   if (err_flag & kvs::kClcesErrRow) return fail(KV_ERR_ARG, "layer %d: a token id is >= score_rows", layer);
   if (err_flag) return fail(KV_ERR_HIP, "layer %d: CLCES consistency check failed (flag %d)", layer, err_flag);
@@ -952,6 +1044,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   if (kept != params->keep_count)
     return fail(KV_ERR_HIP, "layer %d: kept %lld tokens, expected %lld", layer, (long long)kept,
                 (long long)params->keep_count);
+  record_ranks();
   L.apply_compaction(new_lens, kept);
   if (n_kept) *n_kept = kept;
   return ok();

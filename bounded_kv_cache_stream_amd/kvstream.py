@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_ERR_ARG, KV_ERR_SHAPE, KV_ERR_NO_PAGES, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_NAN = 0, -1, -2, -3, -4, -5, -6
 KV_CLCES_DEFER = 1
+KV_CLCES_REUSE_RANKS = 2
 KV_BF16, KV_FP32 = 0, 1
 KV_TRANSIENT = 1
 
@@ -38,7 +39,7 @@ class kv_pool_config(ctypes.Structure):
 
 class kv_clces_params(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("flags", ctypes.c_uint32), ("lambda_", ctypes.c_double),
-                ("keep_count", ctypes.c_int64)]
+                ("keep_count", ctypes.c_int64), ("s_hat_out", ctypes.c_void_p)]
 
 
 class kv_cache_info(ctypes.Structure):
@@ -184,8 +185,9 @@ def kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_pt
 
 
 def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_count, keep_ids_ptr=None,
-                      ranks_ptr=None, stream=None, defer=False) -> int:
-    prm = kv_clces_params(window, KV_CLCES_DEFER if defer else 0, lam, keep_count)
+                      ranks_ptr=None, stream=None, defer=False, reuse_ranks=False, s_hat_ptr=None) -> int:
+    flags = (KV_CLCES_DEFER if defer else 0) | (KV_CLCES_REUSE_RANKS if reuse_ranks else 0)
+    prm = kv_clces_params(window, flags, lam, keep_count, s_hat_ptr)
     n = ctypes.c_int64()
     _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
                                    ctypes.byref(n), stream))
@@ -384,7 +386,7 @@ class KVCache:
         return out, n
 
     def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None,
-                          defer=False) -> int:
+                          defer=False, reuse_ranks=False, s_hat=None) -> int:
         torch = self.torch
         if score_table.dtype != torch.float32 or not score_table.is_contiguous() or score_table.dim() != 2 \
                 or score_table.shape[1] != self.cfg.num_layers:
@@ -392,21 +394,26 @@ class KVCache:
         for t in (keep_ids, ranks):
             if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError("keep_ids / ranks must be contiguous int32 tensors")
-        # the library writes up to keep_count ids and n_window x N ranks (N = the candidate tokens, pages of
-        # the scale frames excluded); it cannot see the buffers' sizes
+        if s_hat is not None and (s_hat.dtype != torch.float64 or not s_hat.is_contiguous()):
+            raise ValueError("s_hat must be a contiguous float64 tensor")
+        # the library writes up to keep_count ids, n_window x N ranks and N fused scores (N = the candidate
+        # tokens, pages of the scale frames excluded); it cannot see the buffers' sizes
         if keep_ids is not None and keep_ids.numel() < keep_count:
             raise ValueError(f"keep_ids holds {keep_ids.numel()} ids, the step may write {keep_count}")
-        if ranks is not None:
+        if ranks is not None or s_hat is not None:
             _, lens, frames = self.page_table(layer)
             n_cand = sum(n for n, f in zip(lens, frames) if f >= self.cfg.scale_frames)
-            if ranks.numel() < min(window, layer + 1) * n_cand:
+            if ranks is not None and ranks.numel() < min(window, layer + 1) * n_cand:
                 raise ValueError(f"ranks holds {ranks.numel()} entries, the step writes "
                                  f"{min(window, layer + 1) * n_cand}")
+            if s_hat is not None and s_hat.numel() < n_cand:
+                raise ValueError(f"s_hat holds {s_hat.numel()} entries, the step writes {n_cand}")
         return score_and_compact(self.handle, layer, ctypes.c_void_p(score_table.data_ptr()), score_table.shape[0],
                                  window, lam, keep_count,
                                  None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),
                                  None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream(),
-                                 defer)
+                                 defer, reuse_ranks,
+                                 None if s_hat is None else ctypes.c_void_p(s_hat.data_ptr()))
 
     def sync(self, layer=-1) -> None:
         """Complete deferred score_and_compact steps (layer -1: every layer); raises their error, if any."""

@@ -77,17 +77,22 @@ typedef struct {
                              /* "Special Token Persistence"), 0..page_tokens       */
 } kv_pool_config;
 
-/* score_and_compact flag: return once the step is enqueued (see there). */
+/* score_and_compact flags: return once the step is enqueued; reuse the ranks
+ * of window layers from earlier steps over the same candidates (see there). */
 #define KV_CLCES_DEFER 1u
+#define KV_CLCES_REUSE_RANKS 2u
 
 /* Parameters of one CLCES step ([SCV] 2.1.1-2.1.3): window W = 5 layers,
  * lambda = 0.5 on the pages; keep_count = tokens kept (the budget); flags =
- * 0 or KV_CLCES_DEFER. */
+ * a combination of KV_CLCES_DEFER and KV_CLCES_REUSE_RANKS; s_hat_out:
+ * optional device float64 [N], the fused score of every candidate in
+ * candidate order (NULL: not written). */
 typedef struct {
   int32_t window;
   uint32_t flags;
   double lambda;
   int64_t keep_count;
+  double* s_hat_out;
 } kv_clces_params;
 
 /* Cache statistics ([GCT] "Cache Monitoring", get_kv_cache_info()). */
@@ -252,6 +257,17 @@ kv_status kv_append_attend(kv_pool_t* pool, int32_t layer, int64_t frame_idx, co
  * keep_ids_out_dev: optional int32 [keep_count], kept global token ids in
  * candidate order (table order, then slot order before compaction).
  * ranks_out_dev: optional int32 [n_window][N], oldest window layer first.
+ * The rank of every window layer is kept in the pool after the step (one
+ * slot per layer of max_window slots, least recently used replaced).  With
+ * KV_CLCES_REUSE_RANKS ([SCV] 2.1.4: the rank history of a frame is reused
+ * across layers) a window layer ranked by an earlier synchronous step over
+ * the same candidate sequence is not ranked again: the layer must never have
+ * been compacted, merged or pruned since kv_reset (its pages then hold whole
+ * frames, so its candidate frames name the sequence), the score table pointer
+ * and score_rows must be the same, and the caller guarantees that the table's
+ * entries of those layers have not changed since (a new frame's scores go to
+ * new rows).  kv_reset forgets every kept rank; deferred steps do not add to
+ * the history.
  * n_kept: optional host int64.  KV_ERR_STATE on a layer that
  * kv_diversity_prune has pruned (its heads hold different tokens), and on a
  * pool with special_tokens > 0 (compaction would move the special tokens out

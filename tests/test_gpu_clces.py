@@ -186,7 +186,12 @@ def test_budget_stream_small_ragged_pages(merge):
         _page_bytes_equal(cache, l, pid, len(idv), krows, vrows, idv)
 
 
-def test_clces_24_layers_72288_tokens_keep_half():
+@pytest.mark.parametrize("reuse", [False, True])
+def test_clces_24_layers_72288_tokens_keep_half(reuse):
+    # every layer's step against the oracle: ranks of every window layer, the fused score s_hat of every
+    # candidate (float64, bit for bit), the kept ids, page tables and sampled page bytes.  With reuse, each
+    # step ranks only its own layer and takes the other window layers' ranks from the earlier steps (every
+    # layer holds the same 72 whole frames), with the same results
     torch = torch_cuda()
     w = synth.WORKLOADS[3]
     T, H, L, F, K = w["tokens"], w["heads"], w["layers"], w["cache_frames"], w["keep"]
@@ -198,16 +203,23 @@ def test_clces_24_layers_72288_tokens_keep_half():
         _fill(cache, l, F, T, H, 3, host.get(l))
     scores = synth.raw_scores(3, N, L)
     table = torch.from_numpy(scores).cuda()
+    gaps = []
     for l in range(L):
         n_win = min(w["clces_window"], l + 1)
         ranks = torch.empty((n_win, N), dtype=torch.int32, device="cuda")
         keep = torch.empty(K, dtype=torch.int32, device="cuda")
-        assert cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep, ranks=ranks) == K
+        s_hat = torch.empty(N, dtype=torch.float64, device="cuda")
+        assert cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep, ranks=ranks,
+                                       s_hat=s_hat, reuse_ranks=reuse) == K
         b = budget.BudgetCache(l, T, K, F, window=w["clces_window"], lam=w["lam"])
         for t in range(F):
             b.append(t)
         assert b.score_and_compact(scores)
         assert np.array_equal(ranks.cpu().numpy(), b.last["ranks"]), f"ranks layer {l}"
+        sh = s_hat.cpu().numpy()
+        assert np.array_equal(sh.view(np.uint64), b.last["s_hat"].view(np.uint64)), f"s_hat layer {l}"
+        srt = np.sort(b.last["s_hat"])[::-1]
+        gaps.append(float(srt[K - 1] - srt[K]))
         assert np.array_equal(keep.cpu().numpy(), b.last["keep_ids"]), f"keep set layer {l}"
         ids, lens, fr = cache.page_table(l)
         assert list(zip(ids, fr, lens)) == b.page_table(), f"page table layer {l}"
@@ -215,7 +227,63 @@ def test_clces_24_layers_72288_tokens_keep_half():
             for pid, f, idv in b.table:
                 sl = torch.from_numpy(idv - f * T)
                 _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
-        say(f"CLCES layer {l}: ranks, {K} kept ids and {len(ids)} page lengths bit-exact")
+    say(f"CLCES 24 layers (rank reuse {reuse}): ranks, s_hat, {K} kept ids and page lengths bit-exact; "
+        f"gap between the {K}th and {K + 1}th s_hat: min {min(gaps):.3e}, median {np.median(gaps):.3e}")
+
+
+def test_rank_history_is_reused_only_for_unchanged_candidates():
+    # with KV_CLCES_REUSE_RANKS the step at layer 1 takes layer 0's ranks from layer 0's step: after the
+    # table's layer-0 column is changed in place in between (which the flag's contract forbids), the result is
+    # still that of the original table, while the same calls without the flag rank the changed column.  A
+    # layer that has been compacted, and every layer after kv_reset, is ranked afresh.
+    torch = torch_cuda()
+    T, H, L, F, K = 64, 2, 3, 4, 150
+    scores = synth.raw_scores(86, F * T, L)
+    changed = scores.copy()
+    changed[:, 0] = scores[::-1, 0]
+    changed_dev = torch.from_numpy(changed).cuda()
+
+    def oracle(layer, sc):
+        b = budget.BudgetCache(layer, T, K, F + 1)
+        for t in range(F):
+            b.append(t)
+        b.score_and_compact(sc)
+        return b.last["keep_ids"].tolist()
+
+    assert oracle(1, scores) != oracle(1, changed)  # the change matters
+    keep = torch.empty(K, dtype=torch.int32, device="cuda")
+    for reuse in (True, False):
+        c = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+        for layer in range(L):
+            _fill(c, layer, F, T, H, 86)
+        table = torch.from_numpy(scores).cuda()
+        c.score_and_compact(0, table, 5, 0.5, K, reuse_ranks=reuse)
+        table.copy_(changed_dev)  # same buffer, layer-0 column changed
+        # the layer-0 step compacted layer 0 only; layer 1 still holds the 4 whole frames
+        c.score_and_compact(1, table, 5, 0.5, K, keep_ids=keep, reuse_ranks=reuse)
+        assert keep.cpu().numpy().tolist() == oracle(1, scores if reuse else changed), reuse
+        # layer 1 is compacted now: its next step (keep 100 of its 150) ranks every window layer again
+        keep2 = torch.empty(100, dtype=torch.int32, device="cuda")
+        c.score_and_compact(1, table, 5, 0.5, 100, keep_ids=keep2, reuse_ranks=True)
+        b = budget.BudgetCache(1, T, K, F + 1)
+        for t in range(F):
+            b.append(t)
+        b.score_and_compact(scores if reuse else changed)
+        b.score_and_compact(changed, keep_count=100)
+        assert keep2.cpu().numpy().tolist() == b.last["keep_ids"].tolist(), reuse
+    # kv_reset forgets the kept ranks
+    c = kv.KVCache(_cfg(L, T, F + 1, H=H), device="cuda")
+    for layer in range(L):
+        _fill(c, layer, F, T, H, 86)
+    table = torch.from_numpy(scores).cuda()
+    c.score_and_compact(1, table, 5, 0.5, K, reuse_ranks=True)
+    c.reset()
+    for layer in range(L):
+        _fill(c, layer, F, T, H, 86)
+    table.copy_(changed_dev)
+    c.score_and_compact(2, table, 5, 0.5, K, keep_ids=keep, reuse_ranks=True)
+    assert keep.cpu().numpy().tolist() == oracle(2, changed)
+    assert oracle(2, changed) != oracle(2, scores)
 
 
 def test_deferred_steps_match_synchronous_ones():
