@@ -37,7 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flo
 PEAK_HBM_GBS = 8000.0
 PEAK_SCLK_MHZ = 2400.0  # the clock the bf16 peak assumes
 ATTEND_SOURCE = os.path.join(ROOT, "bounded_kv_cache_stream_amd", "csrc", "attend.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_traffic.json")
+KERNELS_FILE = os.path.join(ROOT, "profiles", "kernels_stream.json")  # written by profile_bench.py
 
 
 def parse():
@@ -82,6 +82,17 @@ def parse():
     return ap.parse_args()
 
 
+def calib_copy(mib, dev):
+    """One device-to-device copy of `mib` MiB: a kernel of known traffic, for the counter calibration."""
+    import torch
+    if not mib:
+        return
+    src = torch.empty(mib * (1 << 20), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -124,19 +135,22 @@ class ClockSampler:
                 "source": "rocm-smi current sclk level, read during the timed steps"}
 
 
-def recorded_traffic(heads, splits):
-    """HBM bytes per attention call from the committed counter summary, if it was taken with this kernel
-    source, this head count and this split count (0 = the library's choice)."""
+def recorded_counters(heads, splits):
+    """The attention kernel's HBM bytes and MFMA utilisation per call from the committed rocprofv3 summary
+    (profile_bench.py), if it was taken with this attention source at this shape (16 heads, the library's
+    split count); else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(KERNELS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(ATTEND_SOURCE) or rec.get("heads") != heads:
+    if rec.get("source_sha256_16", {}).get("attend.hip") != source_hash(ATTEND_SOURCE) or heads != 16 or splits:
         return None
-    if splits not in (0, rec.get("splits")):
+    k = rec.get("kernels", {}).get("attend_bf16_kernel")
+    if not k or "fetch_bytes" not in k or "write_bytes" not in k:
         return None
-    return rec.get("bytes_per_call")
+    return {"traffic": k["fetch_bytes"] + k["write_bytes"], "mfma_util_pct": k.get("mfma_util_pct"),
+            "rocprof_kernel_avg_us": k["avg_us"], "summary": os.path.relpath(KERNELS_FILE, ROOT)}
 
 
 def cpu_baseline(frames_kv, q_frame, attended, min_seconds=10.0, max_frames=6):
@@ -228,6 +242,7 @@ def run_clces(args):
             times.append(time.perf_counter() - t0)  # the call synchronises once (new page lengths)
             kept = set(keep.cpu().numpy().tolist())
             moved += moved_tokens([[(t * T + j) in kept for j in range(T)] for t in range(F)])
+    calib_copy(args.calib_copy_mib, dev)
     times.sort()
     med = times[len(times) // 2]
     bytes_per_layer = moved / L * 2 * H * 64 * 2 * 2  # read + write of K and V rows, bf16
@@ -299,6 +314,7 @@ def run_append(args):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     med = ms[len(ms) // 2]
+    calib_copy(args.calib_copy_mib, dev)
     nbytes = 2 * 2 * L * T * H * D * 2  # K and V, read and written, bf16
     t0 = time.perf_counter()
     for l in range(L):
@@ -687,6 +703,8 @@ def main():
     for i in range(args.warmup):
         step(fill + i)
     torch.cuda.synchronize()
+    # the library records an event pair around the attention kernel of each timed call
+    kv.kv_attend_timing(cache.handle, args.steps)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     sampler = ClockSampler() if args.sclk else None
@@ -711,14 +729,14 @@ def main():
     # per step: the mean over the timed steps is the last count less sp * (steps - 1) / 2
     n_keys = (S + Wf) * T + info["special_tokens"] - sp * (args.steps - 1) / 2.0
     flops = 4.0 * H * D * T * n_keys
-    achieved = flops / attend_avg_s / 1e12
+    kern_ms, kern_n = kv.kv_attend_timing_read(cache.handle)
+    kv.kv_attend_timing(cache.handle, 0)
+    assert kern_n == args.steps
+    kernel_avg_s = kern_ms / kern_n / 1e3
+    achieved = flops / kernel_avg_s / 1e12
+    achieved_call = flops / attend_avg_s / 1e12
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    calib_copy(args.calib_copy_mib, dev)
 
     result = {
         "metric": "frames/sec per layer at 1004 tok/frame, 72-frame cache; % bf16 MFMA peak",
@@ -733,7 +751,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded AR(1) frame-correlated Q/K/V, bf16)",
-        "config": {"workload": w["name"].replace("_h16_", f"_h{H}_") + (f"_sp{sp}" if sp else ""),
+        "config": {"workload": re.sub(r"_f\d+$", f"_f{total}", w["name"].replace("_h16_", f"_h{H}_"))
+                               + (f"_sp{sp}" if sp else ""),
                    "tokens_per_frame": T, "heads": H, "head_dim": D, "special_tokens": sp,
                    "cache_frames": S + Wf, "cached_tokens": n_keys, "scale_frames": S, "sliding_window": Wf,
                    "keyframe_interval": 1,
@@ -742,14 +761,25 @@ def main():
                    "stream_frames": total},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None if sp else recorded_traffic(H, args.splits),
-                     "kernel": "kv_append_attend (page write with the table upload, attend_bf16_kernel, split-KV "
-                               "combine)" if args.fused else "stream_attend (attend_bf16_kernel + split-KV combine)",
+                     "traffic": None,
+                     "kernel": "attend_bf16_kernel (HIP events around the kernel alone, recorded by the library on "
+                               "the call's stream)",
+                     "kernel_avg_us": kernel_avg_s * 1e6,
+                     "call": "kv_append_attend (page write with the table upload, attend_bf16_kernel, split-KV "
+                             "combine)" if args.fused else "stream_attend (table upload, attend_bf16_kernel, "
+                                                           "split-KV combine)",
+                     "achieved_call": achieved_call, "frac_call": achieved_call / PEAK_BF16_TFLOPS,
                      "avg_call_us": attend_avg_s * 1e6, "flop_per_call": flops,
                      "median_call_us": attend_sorted[len(attend_sorted) // 2] * 1e3,
                      "p90_call_us": attend_sorted[int(0.9 * (len(attend_sorted) - 1))] * 1e3},
         "wall_s_timed": wall,
     }
+    rc = None if sp else recorded_counters(H, args.splits)
+    if rc is not None:
+        result["roofline"]["traffic"] = rc["traffic"]
+        result["roofline"]["mfma_util_pct_counters"] = rc["mfma_util_pct"]
+        result["roofline"]["rocprof_kernel_avg_us"] = rc["rocprof_kernel_avg_us"]
+        result["roofline"]["counters"] = rc["summary"]
     if sclk is not None:
         result["sclk_mhz"] = sclk
         if sclk["median"]:

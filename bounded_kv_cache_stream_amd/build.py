@@ -3,6 +3,15 @@
 Usage: ``python -m bounded_kv_cache_stream_amd.build`` (or ``build()``).
 Every HIP source is compiled with packed fp32 instructions disabled; the
 host-only runtime is compiled with g++ against the HIP runtime headers.
+
+``python -m bounded_kv_cache_stream_amd.build --host-sanitize`` also builds
+``_build/libkvstream_hostsan.so``: the host runtime (kvstream.cpp with the
+page policy) compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer,
+linked with the unchanged kernel objects.  It is for CPU runs of the host
+tests only; load it with gcc's ASan runtime first:
+
+    KVSTREAM_LIB=_build/libkvstream_hostsan.so LD_PRELOAD=$(g++ -print-file-name=libasan.so) \
+        ASAN_OPTIONS=detect_leaks=0 python -m pytest tests/test_lib_host.py
 """
 
 from __future__ import annotations
@@ -70,5 +79,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libkvstream_hostsan.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized() -> str:
+    """The host runtime with ASan + UBSan (g++ only; the kernel objects of build() are linked as they are)."""
+    build()
+    obj = os.path.join(BUILD, "kvstream.cpp.san.o")
+    flags = [f if f != "-O2" else "-O1" for f in GXX_FLAGS] + ["-g", *SAN_FLAGS]
+    _run(["g++", *flags, "-c", os.path.join(CSRC, "kvstream.cpp"), "-o", obj])
+    objs = [obj] + [os.path.join(BUILD, src + ".o") for src in HIP_SOURCES]
+    _run(["g++", "-shared", *SAN_FLAGS, "-o", SAN_LIB, *objs, f"-L{ROCM}/lib", "-lamdhip64",
+          f"-Wl,-rpath,{ROCM}/lib"])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitize" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -471,16 +471,21 @@ hipError_t attend_scratch_address(char** out) {
   return hipSuccess;
 }
 
-hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s) {
+hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
+  hipError_t err = ev_start ? hipEventRecord(ev_start, s) : hipSuccess;
+  if (err != hipSuccess) return err;
   if (!bf16) {
     const int64_t rows = (int64_t)p.n_q * g.heads;
     attend_f32_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(g, p);
-    return hipGetLastError();
+    err = hipGetLastError();
+    return err == hipSuccess && ev_stop ? hipEventRecord(ev_stop, s) : err;
   }
   const int qtiles = (p.n_q + BM - 1) / BM;
   const int64_t nwg = (int64_t)qtiles * g.heads * p.splits;
   attend_bf16_kernel<<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
+  if (err == hipSuccess && ev_stop) err = hipEventRecord(ev_stop, s);
   if (err != hipSuccess || p.splits == 1) return err;
   const int64_t rows = (int64_t)p.n_q * g.heads;
   if (p.splits <= 16)

@@ -14,10 +14,12 @@ constexpr int32_t kDivErrNan = 1;  // a key is not finite (its score is NaN)
 // One layer of a call (device copy, one per slot).
 struct DivLayer {
   int64_t keys_off;  // the layer's keys start at key store + keys_off: [H][N]
-  int64_t N;         // key stride per head: the layer's largest candidate count
+  int64_t N;         // key stride per head: at least the layer's largest candidate count
   int64_t keep;      // candidates kept per head (prune)
   int32_t P;         // candidate pages
   int32_t rescore;   // 1: score the layer in this call
+  int32_t layer;     // the pool layer (indexes the per-layer first-digit histograms)
+  int32_t pad;
 };
 
 // Byte offsets of the diversity buffers inside its workspace region, sized
@@ -26,7 +28,8 @@ struct DivLayer {
 struct DivSizes {
   int64_t n_max;  // candidates per head
   int32_t p_max, h_max, layers;
-  size_t params, bases, tabs, partial, mean, spart, totals, flags, dhist, dstate, lt_cnt, eq_cnt, new_len, total;
+  size_t params, bases, tabs, partial, mean, spart, totals, flags, dstate, lt_cnt, eq_cnt, hist0, hcount, kept,
+      new_len, total;
 };
 
 DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers);

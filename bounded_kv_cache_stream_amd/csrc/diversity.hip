@@ -12,10 +12,11 @@
 //
 // One call covers several layers at once: every kernel runs over all of them
 // (the last grid dimension is the layer's slot), so a 24-layer step is about
-// a dozen launches.  Page-level kernels run one workgroup per (page, head,
-// slot); 8 threads share a key row (8 of its 64 dims each) and the row sums
-// are completed with butterfly shuffles, so every lane of a row holds the
-// same bits.  Every sum has a fixed order, so results are bit-reproducible
+// a dozen launches.  The sum and score kernels run one workgroup per (page,
+// head, slot); 8 threads share a key row (8 of its 64 dims each) and the row
+// sums are completed with butterfly shuffles, so every lane of a row holds the
+// same bits.  The mark and compact kernels run one workgroup per (page,
+// slot), one wave per head at a time.  Every sum has a fixed order, so results are bit-reproducible
 // from run to run.
 //   tables  per (head, slot): candidate pages, the head's rows in each and
 //           the prefixes, from the layer's shared table and the per-page
@@ -27,14 +28,14 @@
 //           stored as a 64-bit key that orders the scores descending, split
 //           in a high and a low 32-bit plane; float64 score sums per block;
 //   total   per slot, the block sums added in a fixed order;
-//   select  per (head, slot), up to 8 radix passes of 8 bits (most
-//           significant first; the first four read only the high plane)
-//           find the K-th smallest key t and how many keys equal to t are
-//           kept: the first ones in candidate order, as a stable sort would
-//           keep them (a histogram pass over the keys, then one workgroup per
-//           (head, slot) fixes the digit).  Once every key matching the
-//           digits fixed so far is kept, the remaining passes are skipped and
-//           t compares under the mask of the fixed bits;
+//   select  one workgroup per (head, slot), up to 8 radix passes of 8 bits
+//           in one launch (most significant first; the first four read only
+//           the high plane) find the K-th smallest key t and how many keys
+//           equal to t are kept: the first ones in candidate order, as a
+//           stable sort would keep them.  Once every key matching the digits
+//           fixed so far is kept, the remaining passes are skipped and t
+//           compares under the mask of the fixed bits; once few keys match,
+//           they are copied to LDS and the later passes read only those;
 //   mark    per (page, head, slot): keys below t and equal to t;
 //   compact per (page, head, slot): the page's new length n follows from the
 //           counts; kept = key < t, or key == t within the tie quota; the
@@ -59,7 +60,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTPR = 8;                        // threads per key row
 constexpr int kRowsPerPass = kThreads / kTPR;  // 32
-constexpr int kMaxMoves = kMaxPageTokensScored / 2;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -91,11 +91,14 @@ struct DivK {
   uint32_t* keys;   // the key store: per layer and head a high plane [N], then a low plane [N]
   double* scores;   // optional [H][score_stride] of slot 0
   int64_t score_stride;
-  uint32_t* dhist;  // [n][8][H][256] select histograms
-  DSel* dstate;     // [n][9][H] states before each pass, [8] final
+  DSel* dstate;     // [n][H] final select states
+  uint32_t* hist0;  // [layer][H][256] counts of each key's top byte (the first select digit), per pool layer
   int32_t* lt_cnt;  // [n][H][p_max] keys below the threshold per page
   int32_t* eq_cnt;  // [n][H][p_max] keys equal to the threshold per page
-  int32_t* new_len; // [n][p_max][H]
+  int32_t* new_len; // [n][items_p][H]
+  int32_t items_p;  // pages per slot in the launch grids (the call's largest P)
+  int32_t* hcount;    // [n][H] candidates per head (the tables kernel's totals)
+  int32_t* kept;      // [n][H] kept candidates per head (the compaction's new lengths added up)
   int32_t* hlen;    // [phys][H]
   int32_t* flags;   // [n] per slot, [n] the call's
 };
@@ -132,13 +135,17 @@ __global__ __launch_bounds__(kThreads) void div_tables_kernel(DivK a) {
     t[i] = DevEntry{be.phys, len, 0, k0};
     k0 += len;
   }
-  if (tid == 0) t[n] = DevEntry{0, 0, 0, total};
+  if (tid == 0) {
+    t[n] = DevEntry{0, 0, 0, total};
+    a.hcount[(int64_t)slot * a.H + h] = total;
+  }
+  // the score kernel of this call counts the first select digit afresh
+  if (a.layers[slot].rescore) a.hist0[((int64_t)a.layers[slot].layer * a.H + h) * 256 + tid] = 0u;
 }
 
-__global__ void div_zero_kernel(int32_t* p0, int n0, int32_t* p1, int n1) {
+__global__ void div_zero_kernel(int32_t* p0, int n0) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n0) p0[i] = 0;
-  if (i < n1) p1[i] = 0;
 }
 
 // The 8 elements c*8 .. c*8+7 of one row as loaded (one 16-byte vector for
@@ -289,6 +296,26 @@ __global__ __launch_bounds__(kMeanThreads) void div_mean_kernel(DivK a) {
   }
 }
 
+// Add one to bin d of the LDS histogram for every lane with valid set.  The
+// wave's lanes are grouped by digit for up to two distinct digits (one LDS
+// atomic per group); lanes with further digits add one each.  The first
+// select digits take only a few values (sign and exponent bits), and
+// same-address atomics from many lanes, which the LDS serialises, are avoided.
+__device__ inline void hist_add2(uint32_t* cnt, uint32_t d, bool valid) {
+  unsigned long long left = __ballot(valid);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (!left) return;
+    const int first = __ffsll((long long)left) - 1;
+    const uint32_t lead = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
+    const unsigned long long same = __ballot(valid && d == lead) & left;
+    if (lane == first) atomicAdd(&cnt[lead], (uint32_t)__popcll(same));
+    left &= ~same;
+  }
+  if ((left >> lane) & 1ull) atomicAdd(&cnt[d], 1u);
+}
+
 // Rank key of a float64 score: ascending keys = descending scores (-0 as +0).
 __device__ inline uint64_t desc_key(double f) {
   if (f == 0.0) f = 0.0;
@@ -301,10 +328,13 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
 #pragma clang fp contract(off)
   __shared__ double red[kThreads];
+  __shared__ uint32_t h0[256];
   const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
   const DivLayer L = a.layers[slot];
   if (!L.rescore || p >= L.P) return;
   const int r = tid / kTPR, c = tid % kTPR;
+  h0[tid] = 0u;
+  __syncthreads();
   const DevEntry en = tab(a, slot, h, p);
   const char* rows = key_rows<T>(a, en, h);
   const double* m = a.mean + ((int64_t)slot * a.H + h) * (kHeadDim + 1);
@@ -336,6 +366,8 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
     }
     // lane u of each row group finishes unrolled row u: the square root and
     // the division run once for kUnroll rows
+    uint32_t digit0 = 0u;
+    bool counted = false;
     if (c < kUnroll) {
       double s2 = s2u[0], dot = dotu[0];
 #pragma unroll
@@ -352,10 +384,13 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
         const uint64_t key = desc_key(sc);
         kk[idx] = (uint32_t)(key >> 32);
         kk[L.N + idx] = (uint32_t)key;
+        digit0 = (uint32_t)(key >> 56);
+        counted = true;
         if (a.scores && slot == 0) a.scores[(int64_t)h * a.score_stride + idx] = sc;
         ssum = ssum + sc;
       }
     }
+    hist_add2(h0, digit0, counted);
   }
   if (__ballot(bad) != 0ull && (tid & 63) == 0) {
     atomicOr(&a.flags[slot], kDivErrNan);
@@ -368,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void div_score_kernel(DivK a) {
     __syncthreads();
   }
   if (tid == 0) a.spart[((int64_t)slot * a.H + h) * a.p_max + p] = red[0];
+  if (h0[tid]) atomicAdd(&a.hist0[((int64_t)L.layer * a.H + h) * 256 + tid], h0[tid]);
 }
 
 // One workgroup per slot: the block sums of every head and page, in a fixed order.
@@ -391,251 +427,295 @@ __global__ __launch_bounds__(kThreads) void div_total_kernel(DivK a) {
   if (tid == 0) a.totals[slot] = red[0];
 }
 
-constexpr int kSelItems = 8;
-constexpr int kSelTile = kThreads * kSelItems;
+// The select runs one workgroup of kSelThreads per (head, slot) through all
+// its passes in one launch: the histogram of each pass and the choice of its
+// digit stay in LDS.  Pass p histograms digit p (bits 56 - 8p .. 63 - 8p) of
+// the keys that match the digits fixed so far, then fixes it: the smallest
+// digit whose prefix count (over digits in ascending order) reaches k_rem;
+// k_rem drops by the count of the smaller digits.  When every key matching
+// the new prefix is to be kept, no later pass can change the outcome (done).
+// Once at most kSelListCap keys match the prefix, the pass that reads them
+// also copies them (64-bit) into LDS, and the later passes read that list.
+constexpr int kSelThreads = 512;
+constexpr int kSelBatch = 16;      // keys per thread in flight
+constexpr int kSelListCap = 7168;  // keys listed in LDS (56 KB)
 
-// Fix digit p (bits 56 - 8p .. 63 - 8p of the key): the smallest digit whose
-// prefix count (over digits in ascending order) reaches k_rem; k_rem drops by
-// the count of smaller digits.  When every key matching the new prefix is to
-// be kept, no later pass can change the outcome (done).  Wave 0 scans its 64
-// lanes (4 digits each); the result goes through LDS.  Every thread of the
-// (256-thread) workgroup calls it.
-__device__ DSel select_advance(DSel st, const uint32_t* hist, int p) {
+__global__ __launch_bounds__(kSelThreads) void div_select_kernel(DivK a) {
+  extern __shared__ uint64_t sel_list[];  // [kSelListCap]
   __shared__ uint32_t cnt[256];
-  __shared__ DSel out;
-  if (st.done) return st;
-  const int tid = threadIdx.x;
-  cnt[tid] = hist[tid];
-  if (tid == 0) out = st;
-  __syncthreads();
-  if (tid < 64) {
-    long long own = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) own += cnt[4 * tid + j];
-    long long pre = own;  // inclusive prefix over lanes <= tid
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long t = __shfl_up(pre, off, 64);
-      if (tid >= off) pre += t;
-    }
-    const long long below = pre - own;
-    if (below < st.k_rem && pre >= st.k_rem) {
-      long long cum = below;
-      for (int j = 0; j < 4; ++j) {
-        const long long c = cnt[4 * tid + j];
-        if (cum + c >= st.k_rem) {
-          const int shift = 56 - 8 * p;
-          out.prefix = st.prefix | ((uint64_t)(4 * tid + j) << shift);
-          out.mask = st.mask | (0xffull << shift);
-          out.k_rem = st.k_rem - cum;
-          out.done = out.k_rem == c || p == kDivSelPasses - 1;
-          break;
-        }
-        cum += c;
-      }
-    }
-  }
-  __syncthreads();
-  const DSel r = out;
-  __syncthreads();
-  return r;
-}
-
-__device__ inline uint32_t* sel_hist(const DivK& a, int slot, int p, int h) {
-  return a.dhist + (((int64_t)slot * kDivSelPasses + p) * a.H + h) * 256;
-}
-__device__ inline DSel* sel_state(const DivK& a, int slot, int p, int h) {
-  return a.dstate + ((int64_t)slot * (kDivSelPasses + 1) + p) * a.H + h;
-}
-
-// One workgroup per (head, slot): the state before pass p (p = 0: nothing
-// fixed, min(keep, candidates) to keep; p = 1..8: pass p-1's state advanced
-// by its histogram; state 8 is the final one).
-__global__ __launch_bounds__(kThreads) void div_advance_kernel(DivK a, int p) {
+  __shared__ DSel s_st;
+  __shared__ long long s_c;
+  __shared__ int32_t s_n;
+  const int h = blockIdx.x, slot = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   if (a.flags[a.n]) return;
-  const int h = blockIdx.x, slot = blockIdx.y;
-  DSel st;
-  if (p == 0) {
-    const int64_t nh = head_count(a, slot, h);
-    const long long k0 = (long long)min<int64_t>(a.layers[slot].keep, nh);
-    st = DSel{0ull, 0ull, k0, k0 == 0 || k0 == nh, 0};
-  } else {
-    st = select_advance(*sel_state(a, slot, p - 1, h), sel_hist(a, slot, p - 1, h), p - 1);
-  }
-  if (threadIdx.x == 0) *sel_state(a, slot, p, h) = st;
-}
-
-// Pass p: histogram of digit p over head h's keys that match the digits
-// fixed so far.  Passes 0-3 take their digit from the high plane; passes 4-7
-// read a key's low word only when its high word matches.
-__global__ __launch_bounds__(kThreads) void div_select_kernel(DivK a, int p) {
-  if (a.flags[a.n]) return;
-  __shared__ uint32_t cnt[256];
-  const int h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
-  const int64_t nh = head_count(a, slot, h);
-  if ((int64_t)blockIdx.x * kSelTile >= nh) return;  // past the head's keys
-  const DSel st = *sel_state(a, slot, p, h);
-  if (st.done) return;
-  cnt[tid] = 0;
-  __syncthreads();
   const DivLayer L = a.layers[slot];
+  const int64_t nh = a.hcount[(int64_t)slot * a.H + h];
+  const long long k0 = (long long)min<int64_t>(L.keep, nh);
+  DSel st{0ull, 0ull, k0, k0 == 0 || k0 == nh, 0};
   const uint32_t* kh = head_keys(a, L, h);
   const uint32_t* kl = kh + L.N;
-  const uint32_t pre_hi = (uint32_t)(st.prefix >> 32), mask_hi = (uint32_t)(st.mask >> 32);
-  const uint32_t pre_lo = (uint32_t)st.prefix, mask_lo = (uint32_t)st.mask;
-  const int shift = 24 - 8 * (p & 3);
+  bool listed = false;      // the keys matching the prefix are in sel_list (s_n of them)
+  long long c_match = nh;   // keys matching the prefix
+  for (int p = 0; p < kDivSelPasses && !st.done; ++p) {
+    const bool listing = p > 0 && !listed && c_match <= kSelListCap;
+    const bool need_lo = p >= 4 || listing;
+    const int shift = 56 - 8 * p;
+    const uint32_t pre_hi = (uint32_t)(st.prefix >> 32), mask_hi = (uint32_t)(st.mask >> 32);
+    // pass 0 takes the counts the score kernel made of the same keys
+    if (tid < 256) cnt[tid] = p == 0 ? a.hist0[((int64_t)L.layer * a.H + h) * 256 + tid] : 0u;
+    if (tid == 0 && listing) s_n = 0;
+    __syncthreads();
+    if (p == 0) {
+    } else if (listed) {
+      const int n_list = min(s_n, kSelListCap);
+      for (int i = tid; i < n_list; i += kSelThreads) {
+        const uint64_t key = sel_list[i];
+        if ((key & st.mask) == st.prefix) atomicAdd(&cnt[(uint32_t)(key >> shift) & 255u], 1u);
+      }
+    } else {
+      for (int64_t b = 0; b < nh; b += (int64_t)kSelThreads * kSelBatch) {
+        const int64_t i0 = b + tid;
+        uint32_t hi[kSelBatch], lo[kSelBatch];
+        bool match[kSelBatch];
+        // every load of the batch is issued before any key is counted
 #pragma unroll
-  for (int j = 0; j < kSelItems; ++j) {
-    const int64_t i = (int64_t)blockIdx.x * kSelTile + j * kThreads + tid;
-    const bool valid = i < nh;
-    const uint32_t hi = valid ? kh[i] : 0u;
-    bool match = valid && (hi & mask_hi) == pre_hi;
-    uint32_t word = hi;
-    if (p >= 4) {
-      word = match ? kl[i] : 0u;
-      match = match && (word & mask_lo) == pre_lo;
+        for (int j = 0; j < kSelBatch; ++j) hi[j] = i0 + j * kSelThreads < nh ? kh[i0 + j * kSelThreads] : 0u;
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          match[j] = i0 + j * kSelThreads < nh && (hi[j] & mask_hi) == pre_hi;
+          lo[j] = 0u;
+        }
+        // low words of the matching keys; the other lanes all read the
+        // plane's first word (one shared line), so the loads need no branch
+        if (need_lo) {
+#pragma unroll
+          for (int j = 0; j < kSelBatch; ++j) lo[j] = kl[match[j] ? i0 + j * kSelThreads : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const uint64_t key = ((uint64_t)hi[j] << 32) | lo[j];
+          const bool m = match[j] && (key & st.mask) == st.prefix;
+          // the first digit (sign and exponent bits) takes few values: group
+          // the lanes; later digits are spread: one atomic per lane
+          if (p == 0)
+            hist_add2(cnt, (uint32_t)(key >> shift) & 255u, m);
+          else if (m)
+            atomicAdd(&cnt[(uint32_t)(key >> shift) & 255u], 1u);
+          if (listing) {
+            const unsigned long long bm = __ballot(m);
+            if (bm) {
+              int32_t base = 0;
+              if (lane == 0) base = atomicAdd(&s_n, (int32_t)__popcll(bm));
+              base = __builtin_amdgcn_readfirstlane(base);
+              const int32_t at = base + (int32_t)__popcll(bm & ((1ull << lane) - 1ull));
+              if (m && at < kSelListCap) sel_list[at] = key;
+            }
+          }
+        }
+      }
     }
-    hist_add(cnt, (word >> shift) & 255u, match);
+    __syncthreads();
+    // fix digit p (wave 0: 4 digits per lane, inclusive prefix over lanes)
+    if (tid < 64) {
+      if (tid == 0) {
+        s_st = st;
+        s_st.done = 1;  // kept if no digit reaches k_rem (inconsistent counts)
+        s_c = 0;
+      }
+      uint32_t c4[4];
+      long long own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c4[j] = cnt[4 * tid + j];
+        own += c4[j];
+      }
+      long long pre = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const long long t = __shfl_up(pre, off, 64);
+        if (tid >= off) pre += t;
+      }
+      const long long below = pre - own;
+      if (below < st.k_rem && pre >= st.k_rem) {
+        long long cum = below;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c4[j] >= st.k_rem) {
+            DSel out = st;
+            out.prefix = st.prefix | ((uint64_t)(4 * tid + j) << shift);
+            out.mask = st.mask | (0xffull << shift);
+            out.k_rem = st.k_rem - cum;
+            out.done = out.k_rem == (long long)c4[j] || p == kDivSelPasses - 1;
+            s_st = out;
+            s_c = c4[j];
+            break;
+          }
+          cum += c4[j];
+        }
+      }
+    }
+    __syncthreads();
+    st = s_st;
+    c_match = s_c;
+    listed = listed || listing;
+    __syncthreads();  // s_st and s_c are rewritten by the next pass
   }
-  __syncthreads();
-  if (cnt[tid]) atomicAdd(&sel_hist(a, slot, p, h)[tid], cnt[tid]);
+  if (tid == 0) a.dstate[(int64_t)slot * a.H + h] = st;
 }
 
-// The key of candidate i under the final state's mask (the low plane is read
-// only when the mask reaches it).
-__device__ inline uint64_t masked_key(const uint32_t* kh, const uint32_t* kl, int64_t i, const DSel& st) {
-  const uint64_t hi = (uint64_t)kh[i] << 32;
-  return ((uint32_t)st.mask ? (hi | kl[i]) : hi) & st.mask;
+// Candidate i's key under the final state's mask against the threshold
+// prefix: -1 below, 0 equal, 1 above.  hi is the key's high word; the low
+// word is read only when the high words match under the mask.
+__device__ inline int key_cmp(uint32_t hi, const uint32_t* kl, int64_t i, const DSel& st) {
+  const uint32_t h = hi & (uint32_t)(st.mask >> 32), ph = (uint32_t)(st.prefix >> 32);
+  if (h != ph) return h < ph ? -1 : 1;
+  const uint32_t ml = (uint32_t)st.mask;
+  if (!ml) return 0;
+  const uint32_t l = kl[i] & ml, pl = (uint32_t)st.prefix;
+  return l == pl ? 0 : (l < pl ? -1 : 1);
 }
+
+// The mark and compact kernels run one workgroup per (page, slot) of up to
+// 4 waves (more waves per workgroup measured slower: fewer workgroups in
+// flight per CU); wave w takes heads w, w + waves, ..., and loads 512 of a
+// head's keys (8 per lane) before it compares them.
+constexpr int kMaxItemWaves = 4;
+constexpr int kBatch = 8;
 
 // Per (page, head, slot): the keys below the threshold t and equal to it.
-__global__ __launch_bounds__(kThreads) void div_mark_kernel(DivK a) {
+__global__ __launch_bounds__(64 * kMaxItemWaves) void div_mark_kernel(DivK a) {
   if (a.flags[a.n]) return;
-  __shared__ int32_t s_lt, s_eq;
-  const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
+  const int p = blockIdx.x, slot = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6;
   const DivLayer L = a.layers[slot];
   if (p >= L.P) return;
-  const DSel st = *sel_state(a, slot, kDivSelPasses, h);
-  if (tid == 0) {
-    s_lt = 0;
-    s_eq = 0;
-  }
-  __syncthreads();
-  const DevEntry en = tab(a, slot, h, p);
-  const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
-  const uint32_t* kl = kh + L.N;
-  int32_t lt = 0, eq = 0;
-  for (int j = tid; j < en.len; j += kThreads) {
-    const uint64_t key = masked_key(kh, kl, j, st);
-    lt += key < st.prefix;
-    eq += key == st.prefix;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    lt += __shfl_xor(lt, off, 64);
-    eq += __shfl_xor(eq, off, 64);
-  }
-  if ((tid & 63) == 0) {
-    if (lt) atomicAdd(&s_lt, lt);
-    if (eq) atomicAdd(&s_eq, eq);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int64_t at = ((int64_t)slot * a.H + h) * a.p_max + p;
-    a.lt_cnt[at] = s_lt;
-    a.eq_cnt[at] = s_eq;
+  for (int h = wave; h < a.H; h += waves) {
+    const DSel st = a.dstate[(int64_t)slot * a.H + h];
+    const DevEntry en = tab(a, slot, h, p);
+    const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
+    const uint32_t* kl = kh + L.N;
+    int32_t lt = 0, eq = 0;
+    for (int j0 = 0; j0 < en.len; j0 += 64 * kBatch) {
+      uint32_t hi[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + 64 * u + lane;
+        hi[u] = j < en.len ? kh[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + 64 * u + lane;
+        const int c = j < en.len ? key_cmp(hi[u], kl, j, st) : 1;
+        lt += __popcll(__ballot(c < 0));
+        eq += __popcll(__ballot(c == 0));
+      }
+    }
+    if (lane == 0) {
+      const int64_t at = ((int64_t)slot * a.H + h) * a.p_max + p;
+      a.lt_cnt[at] = lt;
+      a.eq_cnt[at] = eq;
+    }
   }
 }
 
-// Per (page, head, slot): the new length n (keys below t, plus the page's
-// share of the tie quota), then, walking the page in chunks of 256 slots with
-// wave ballots, the dropped slots below n and the kept slots at or past n in
-// ascending order, and the row moves between them.
+// Per (page, head, slot), one wave: the new length n (keys below t, plus the
+// page's share of the tie quota), then, walking the page in 64-slot chunks
+// with ballots, the dropped slots below n and the kept slots at or past n in
+// ascending order (lists in the wave's part of LDS, max_moves entries each),
+// and the row moves between them.  The lists are written and read by the
+// same wave, whose LDS accesses complete in order.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void div_compact_kernel(DivK a) {
+__global__ __launch_bounds__(64 * kMaxItemWaves) void div_compact_kernel(DivK a, int max_moves) {
   if (a.flags[a.n]) return;
-  constexpr int kWaves = kThreads / 64;
-  __shared__ int32_t s_eqb;
-  __shared__ int32_t wsum[3][kWaves];
-  __shared__ uint16_t holes[kMaxMoves], fills[kMaxMoves];
-  const int p = blockIdx.x, h = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
+  extern __shared__ uint16_t move_lists[];  // [wave][2][max_moves]: holes, then fills
+  const int p = blockIdx.x, slot = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6;
   const DivLayer L = a.layers[slot];
   if (p >= L.P) return;
-  const int wave = tid >> 6, lane = tid & 63;
-  const DevEntry en = tab(a, slot, h, p);
-  const int len = en.len;
-  const DSel st = *sel_state(a, slot, kDivSelPasses, h);
-  const int64_t cnt_at = ((int64_t)slot * a.H + h) * a.p_max;
-  const int32_t eq = a.eq_cnt[cnt_at + p];
-  // keys equal to t in the earlier pages: only a page holding such a key
-  // needs them (its share of the tie quota), and such pages are rare
-  if (tid == 0) s_eqb = 0;
-  __syncthreads();
-  if (eq > 0) {
-    int32_t e = 0;
-    for (int i = tid; i < p; i += kThreads) e += a.eq_cnt[cnt_at + i];
-    if (e) atomicAdd(&s_eqb, e);
-    __syncthreads();
-  }
-  const long long eq_before = s_eqb;
-  const long long quota = st.k_rem - eq_before;
-  const int32_t n = a.lt_cnt[cnt_at + p] + (int32_t)(quota < 0 ? 0 : (quota > eq ? eq : quota));
-  if (tid == 0) {
-    a.new_len[((int64_t)slot * a.p_max + p) * a.H + h] = n;
-    a.hlen[(int64_t)en.phys * a.H + h] = n;
-  }
-  if (n == len) return;  // nothing dropped in this page and head
-  const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
-  const uint32_t* kl = kh + L.N;
+  uint16_t* holes = move_lists + (size_t)wave * 2 * max_moves;
+  uint16_t* fills = holes + max_moves;
   const unsigned long long below = (1ull << lane) - 1ull;
-  long long eq_run = eq_before;
-  int32_t h_run = 0, f_run = 0;
-  for (int c0 = 0; c0 < len; c0 += kThreads) {
-    const int j = c0 + tid;
-    const bool valid = j < len;
-    const uint64_t key = valid ? masked_key(kh, kl, j, st) : ~0ull;
-    const bool is_eq = valid && key == st.prefix;
-    const unsigned long long be = __ballot(is_eq);
-    if (lane == 0) wsum[0][wave] = __popcll(be);
-    __syncthreads();
-    long long eq_rank = eq_run + __popcll(be & below);
-    int32_t chunk_eq = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      eq_rank += w < wave ? wsum[0][w] : 0;
-      chunk_eq += wsum[0][w];
+  for (int h = wave; h < a.H; h += waves) {
+    const DevEntry en = tab(a, slot, h, p);
+    const int len = en.len;
+    const DSel st = a.dstate[(int64_t)slot * a.H + h];
+    const int64_t cnt_at = ((int64_t)slot * a.H + h) * a.p_max;
+    const int32_t eq = a.eq_cnt[cnt_at + p];
+    // keys equal to t in the earlier pages: only a page holding such a key
+    // needs them (its share of the tie quota)
+    long long eq_before = 0;
+    if (eq > 0) {
+      int32_t e = 0;
+      for (int q = lane; q < p; q += 64) e += a.eq_cnt[cnt_at + q];
+      for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
+      eq_before = e;
     }
-    const bool keep = valid && (key < st.prefix || (is_eq && eq_rank < st.k_rem));
-    const bool hole = valid && !keep && j < n;
-    const bool fill = keep && j >= n;
-    const unsigned long long bh = __ballot(hole), bf = __ballot(fill);
+    const long long quota = st.k_rem - eq_before;
+    const int32_t n = a.lt_cnt[cnt_at + p] + (int32_t)(quota < 0 ? 0 : (quota > eq ? eq : quota));
     if (lane == 0) {
-      wsum[1][wave] = __popcll(bh);
-      wsum[2][wave] = __popcll(bf);
+      a.new_len[((int64_t)slot * a.items_p + p) * a.H + h] = n;
+      a.hlen[(int64_t)en.phys * a.H + h] = n;
     }
+    if (n == len) continue;  // nothing dropped in this page and head
+    const uint32_t* kh = head_keys(a, L, h) + en.tok_start;
+    const uint32_t* kl = kh + L.N;
+    long long eq_run = eq_before;
+    int32_t h_run = 0, f_run = 0;
+    for (int j0 = 0; j0 < len; j0 += 64 * kBatch) {
+      uint32_t hi[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + 64 * u + lane;
+        hi[u] = j < len ? kh[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + 64 * u + lane;
+        const bool valid = j < len;
+        const int c = valid ? key_cmp(hi[u], kl, j, st) : 1;
+        const unsigned long long be = __ballot(c == 0);
+        const bool keep = c < 0 || (c == 0 && eq_run + __popcll(be & below) < st.k_rem);
+        const bool hole = valid && !keep && j < n;
+        const bool fill = keep && j >= n;
+        const unsigned long long bh = __ballot(hole), bf = __ballot(fill);
+        const int32_t hp = h_run + __popcll(bh & below), fp = f_run + __popcll(bf & below);
+        // a consistent plan has at most len / 2 moves; the counts are checked below
+        if (hole && hp < max_moves) holes[hp] = (uint16_t)j;
+        if (fill && fp < max_moves) fills[fp] = (uint16_t)j;
+        eq_run += __popcll(be);
+        h_run += __popcll(bh);
+        f_run += __popcll(bf);
+      }
+    }
+    // cannot happen when the counts and the walk agree; never move on a mismatch
+    if (h_run != f_run || h_run > max_moves) {
+      if (lane == 0) atomicOr(&a.flags[slot], kClcesErrCount);
+      continue;
+    }
+    __builtin_amdgcn_wave_barrier();
+    constexpr int VPR = kHeadDim * sizeof(T) / 16;
+    char* page = a.pool + (int64_t)en.phys * a.page_bytes;
+    move_rows<T, 64>(reinterpret_cast<V16*>(page + a.k_off) + (int64_t)h * a.ts * VPR, fills, holes, h_run, lane);
+    move_rows<T, 64>(reinterpret_cast<V16*>(page + a.v_off) + (int64_t)h * a.ts * VPR, fills, holes, h_run, lane);
+    __builtin_amdgcn_wave_barrier();  // the next head's lists are written after these reads
+  }
+}
+
+// One workgroup per (head, slot): the head's kept total, its new lengths
+// added over the pages (checked against min(keep, candidates) on the host).
+__global__ __launch_bounds__(kThreads) void div_kept_kernel(DivK a) {
+  __shared__ int32_t red[kThreads];
+  const int h = blockIdx.x, slot = blockIdx.y, tid = threadIdx.x;
+  const int P = a.layers[slot].P;
+  int32_t k = 0;
+  for (int p = tid; p < P; p += kThreads) k += a.new_len[((int64_t)slot * a.items_p + p) * a.H + h];
+  red[tid] = k;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
     __syncthreads();
-    int32_t hp = h_run + __popcll(bh & below), fp = f_run + __popcll(bf & below);
-    int32_t chunk_h = 0, chunk_f = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      hp += w < wave ? wsum[1][w] : 0;
-      fp += w < wave ? wsum[2][w] : 0;
-      chunk_h += wsum[1][w];
-      chunk_f += wsum[2][w];
-    }
-    // a consistent plan has at most len / 2 moves; the counts are checked below
-    if (hole && hp < kMaxMoves) holes[hp] = (uint16_t)j;
-    if (fill && fp < kMaxMoves) fills[fp] = (uint16_t)j;
-    eq_run += chunk_eq;
-    h_run += chunk_h;
-    f_run += chunk_f;
-    __syncthreads();  // wsum is rewritten by the next chunk; the lists are read below
   }
-  if (h_run != f_run || h_run > kMaxMoves) {  // cannot happen when the counts and the walk agree; never move on a mismatch
-    if (tid == 0) atomicOr(&a.flags[slot], kClcesErrCount);
-    return;
-  }
-  constexpr int VPR = kHeadDim * sizeof(T) / 16;
-  char* page = a.pool + (int64_t)en.phys * a.page_bytes;
-  move_rows<T, kThreads>(reinterpret_cast<V16*>(page + a.k_off) + (int64_t)h * a.ts * VPR, fills, holes, h_run, tid);
-  move_rows<T, kThreads>(reinterpret_cast<V16*>(page + a.v_off) + (int64_t)h * a.ts * VPR, fills, holes, h_run, tid);
+  if (tid == 0) a.kept[(int64_t)slot * a.H + h] = red[0];
 }
 
 DivK make_k(const DivCall& c) {
@@ -646,6 +726,7 @@ DivK make_k(const DivCall& c) {
   k.tabs = reinterpret_cast<DevEntry*>(c.ws + z.tabs);
   k.n = c.n;
   k.p_max = z.p_max;
+  k.items_p = c.max_P;
   k.H = c.geom.heads;
   k.pool = c.pool;
   k.page_bytes = c.geom.page_bytes;
@@ -659,11 +740,13 @@ DivK make_k(const DivCall& c) {
   k.keys = c.keys_dev;
   k.scores = c.scores_out;
   k.score_stride = c.score_stride;
-  k.dhist = reinterpret_cast<uint32_t*>(c.ws + z.dhist);
   k.dstate = reinterpret_cast<DSel*>(c.ws + z.dstate);
+  k.hist0 = reinterpret_cast<uint32_t*>(c.ws + z.hist0);
   k.lt_cnt = reinterpret_cast<int32_t*>(c.ws + z.lt_cnt);
   k.eq_cnt = reinterpret_cast<int32_t*>(c.ws + z.eq_cnt);
   k.new_len = reinterpret_cast<int32_t*>(c.ws + z.new_len);
+  k.hcount = reinterpret_cast<int32_t*>(c.ws + z.hcount);
+  k.kept = reinterpret_cast<int32_t*>(c.ws + z.kept);
   k.hlen = c.hlen_dev;
   k.flags = reinterpret_cast<int32_t*>(c.ws + z.flags);
   return k;
@@ -690,15 +773,19 @@ DivSizes div_sizes(int64_t n_max, int32_t p_max, int32_t heads, int32_t layers) 
   z.partial = take(L * H * P * kHeadDim * 8);
   z.mean = take(L * H * (kHeadDim + 1) * 8);
   z.spart = take(L * H * P * 8);
-  z.dhist = take(L * kDivSelPasses * H * 256 * 4);
-  z.dstate = take(L * (kDivSelPasses + 1) * H * sizeof(DSel));
+  z.dstate = take(L * H * sizeof(DSel));
+  z.hist0 = take(L * H * 256 * 4);
   z.lt_cnt = take(L * H * P * 4);
   z.eq_cnt = take(L * H * P * 4);
-  // the outputs the host reads back, adjacent: a scoring reads totals and
-  // flags in one copy, a prune flags and new lengths in one copy
+  // the outputs the host reads back, adjacent (no alignment padding between
+  // them): a scoring reads totals, flags and head counts in one copy; a prune
+  // flags, head counts, kept totals and new lengths in one copy
   z.totals = take(L * 8);
-  z.flags = take((L + 1) * 4);
-  z.new_len = take(L * P * H * 4);
+  z.flags = z.totals + L * 8;
+  z.hcount = z.flags + (L + 1) * 4;
+  z.kept = z.hcount + L * H * 4;
+  z.new_len = z.kept + L * H * 4;
+  off = align256(z.new_len + L * P * H * 4);
   z.total = off;
   return z;
 }
@@ -716,9 +803,7 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
   const int H = c.geom.heads;
   hipError_t e = hipMemcpyAsync(c.ws + z.params, c.staging, div_staging_bytes(z, c.n), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
-  const int n_hist = c.prune ? c.n * kDivSelPasses * H * 256 : 0;
-  div_zero_kernel<<<dim3((unsigned)((std::max(n_hist, c.n + 1) + 255) / 256)), dim3(256), 0, s>>>(
-      k.flags, c.n + 1, reinterpret_cast<int32_t*>(k.dhist), n_hist);
+  div_zero_kernel<<<dim3((unsigned)((c.n + 1 + 255) / 256)), dim3(256), 0, s>>>(k.flags, c.n + 1);
   div_tables_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k);
   const dim3 pages((unsigned)c.max_P, (unsigned)H, (unsigned)c.n);
   if (c.any_rescore) {
@@ -734,18 +819,18 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
     div_total_kernel<<<dim3((unsigned)c.n), dim3(kThreads), 0, s>>>(k);
   }
   if (c.prune) {
-    const unsigned nblk = (unsigned)((c.max_N + kSelTile - 1) / kSelTile);
-    const dim3 heads((unsigned)H, (unsigned)c.n);
-    for (int p = 0; p < kDivSelPasses; ++p) {
-      div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, p);
-      div_select_kernel<<<dim3(nblk, (unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k, p);
-    }
-    div_advance_kernel<<<heads, dim3(kThreads), 0, s>>>(k, kDivSelPasses);
-    div_mark_kernel<<<pages, dim3(kThreads), 0, s>>>(k);
+    div_select_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kSelThreads), kSelListCap * sizeof(uint64_t), s>>>(k);
+    const dim3 page_grid((unsigned)c.max_P, (unsigned)c.n);
+    div_mark_kernel<<<page_grid, dim3(64 * std::min(H, kMaxItemWaves)), 0, s>>>(k);
+    // one wave per head (up to 4), as many as 64 KB of move lists allow
+    const int max_moves = std::max(1, c.geom.ts / 2);
+    const size_t per_wave = 2 * (size_t)max_moves * sizeof(uint16_t);
+    const int waves = std::max(1, std::min({H, kMaxItemWaves, (int)((64 << 10) / per_wave)}));
     if (c.geom.esize == 2)
-      div_compact_kernel<__bf16><<<pages, dim3(kThreads), 0, s>>>(k);
+      div_compact_kernel<__bf16><<<page_grid, dim3(64 * waves), waves * per_wave, s>>>(k, max_moves);
     else
-      div_compact_kernel<float><<<pages, dim3(kThreads), 0, s>>>(k);
+      div_compact_kernel<float><<<page_grid, dim3(64 * waves), waves * per_wave, s>>>(k, max_moves);
+    div_kept_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k);
   }
   return hipGetLastError();
 }

@@ -113,7 +113,10 @@ struct AttendParams {
   float scale_log2;  // sm_scale * log2(e)
 };
 
-hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s);
+// ev_start / ev_stop (optional): recorded on s right before and right after
+// the attention kernel (before the split-KV combine).
+hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Device scratch of the allocation-free attention entry point: a file-scope
 // array in attend.hip, one copy per GPU, holding the split-KV partials.

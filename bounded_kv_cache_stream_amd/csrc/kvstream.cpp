@@ -143,7 +143,13 @@ struct kv_pool {
   std::vector<kvs::LayerPolicy> layers;
   std::vector<int64_t> scored_gen;  // per layer: the table generation its diversity keys belong to (-1: none)
   std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
-  std::vector<char> div_staging;       // host staging of the diversity calls (reused, never shrunk)
+  // pinned host memory of the diversity calls (allocated at the first one):
+  // the staging block copied to the device, then the read-back area; staged
+  // is recorded after each call's kernels, and the staging block is rewritten
+  // only once it has completed
+  char* div_pinned = nullptr;
+  size_t div_stage_bytes = 0;
+  hipEvent_t div_staged = nullptr;
   // deferred score_and_compact steps (KV_CLCES_DEFER): per layer, whether one
   // is pending, the event after its read-back, its page count and keep count;
   // the read-backs land in pinned host memory, (pages_per_layer + 1) ints per
@@ -169,6 +175,10 @@ struct kv_pool {
   };
   std::vector<RankSlot> rank_slots;
   uint64_t rank_clock = 0;
+  // kv_attend_timing: event pairs recorded around the attention kernel of the
+  // next calls (used pairs first)
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> timing;
+  size_t timing_used = 0;
 };
 
 namespace {
@@ -232,39 +242,39 @@ int32_t* hlens_dev(const kv_pool_t* p) { return reinterpret_cast<int32_t*>(p->ws
 
 // The candidate pages of a layer for the diversity steps (every page past the
 // scale frames, in table order; tile_start flags pages whose per-head lengths
-// are in the device array), each head's candidate count, and their largest
-// value and sum.
+// are in the device array) and n_ub, the sum of their lengths: at least any
+// head's candidate count (a page's length is the largest of its heads').  The
+// exact per-head counts come from the device (the tables kernel) with each
+// call's read-back; head_counts() computes them on the host where a call
+// needs them without a launch.
 struct DivPlan {
   std::vector<kvs::DevEntry> base;
-  std::vector<int64_t> n_head;
-  int64_t n_max = 0, n_total = 0;
+  int64_t n_ub = 0;
 };
 
 DivPlan div_plan(const kv_pool_t* pool, int32_t layer) {
   const auto& L = pool->layers[(size_t)layer];
-  const int32_t H = pool->cfg.num_heads;
   DivPlan d;
-  d.n_head.assign((size_t)H, 0);
   const size_t first = L.first_candidate();
   d.base.reserve(L.table.size() - std::min(first, L.table.size()));
-  int64_t uniform = 0;  // rows of pages whose heads all hold len rows
-  int64_t* nh = d.n_head.data();
   for (size_t i = first; i < L.table.size(); ++i) {
     const auto& e = L.table[i];
     d.base.push_back(kvs::DevEntry{(int32_t)phys_page(pool, layer, e.page), e.len, e.hlen.empty() ? 0 : 1, 0});
-    if (e.hlen.empty()) {
-      uniform += e.len;
-    } else {
-      const int32_t* hl = e.hlen.data();
-      for (int32_t h = 0; h < H; ++h) nh[h] += hl[h];
-    }
-  }
-  for (int32_t h = 0; h < H; ++h) nh[h] += uniform;
-  for (int64_t n : d.n_head) {
-    d.n_max = std::max(d.n_max, n);
-    d.n_total += n;
+    d.n_ub += e.len;
   }
   return d;
+}
+
+// Each head's candidate count of a layer, on the host.
+std::vector<int64_t> head_counts(const kv_pool_t* pool, int32_t layer) {
+  const auto& L = pool->layers[(size_t)layer];
+  const int32_t H = pool->cfg.num_heads;
+  std::vector<int64_t> n((size_t)H, 0);
+  for (size_t i = L.first_candidate(); i < L.table.size(); ++i) {
+    const auto& e = L.table[i];
+    for (int32_t h = 0; h < H; ++h) n[(size_t)h] += e.hlen.empty() ? e.len : e.hlen[(size_t)h];
+  }
+  return n;
 }
 
 kv_status check_layers(const kv_pool_t* p, int32_t first, int32_t n) {
@@ -285,6 +295,35 @@ struct DivBatch {
   kvs::DivCall call{};
 };
 
+// The pinned block of the diversity calls: staging for every layer, then the
+// larger of the two read-backs (scoring: totals, flags and head counts; prune:
+// flags, head counts, kept totals and every layer's new lengths).
+hipError_t div_pinned(kv_pool_t* pool) {
+  if (pool->div_pinned) return pool->div_staged ? hipEventSynchronize(pool->div_staged) : hipSuccess;
+  const kvs::DivSizes& z = pool->lay.dv;
+  const size_t stage = (kvs::div_staging_bytes(z, z.layers) + 255) / 256 * 256;
+  const size_t rb_score = (z.hcount - z.totals) + sizeof(int32_t) * (size_t)z.layers * z.h_max;
+  const size_t rb_prune = (z.new_len - z.flags) + sizeof(int32_t) * (size_t)z.layers * z.p_max * z.h_max;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&pool->div_pinned), stage + std::max(rb_score, rb_prune),
+                               hipHostMallocDefault);
+  if (e != hipSuccess) {
+    pool->div_pinned = nullptr;
+    return e;
+  }
+  e = hipEventCreateWithFlags(&pool->div_staged, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipHostFree(pool->div_pinned);
+    pool->div_pinned = nullptr;
+    pool->div_staged = nullptr;
+    return e;
+  }
+  pool->div_stage_bytes = stage;
+  return hipSuccess;
+}
+
+char* div_readback(kv_pool_t* pool) { return pool->div_pinned + pool->div_stage_bytes; }
+
+// Call after div_pinned() succeeded.
 DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
                    const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, double* scores,
                    int64_t stride) {
@@ -293,8 +332,7 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
   const int n = (int)layers.size();
   b.layer = layers;
   // only the parameters and each slot's first P entries are read on the device
-  if (pool->div_staging.size() < kvs::div_staging_bytes(z, n)) pool->div_staging.resize(kvs::div_staging_bytes(z, n));
-  char* staging = pool->div_staging.data();
+  char* staging = pool->div_pinned;
   kvs::DivCall& c = b.call;
   c.ws = pool->ws + pool->lay.div;
   c.sizes = z;
@@ -312,10 +350,11 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
     const DivPlan& d = *plans[(size_t)i];
     kvs::DivLayer& L = kvs::div_staging_layers(staging)[i];
     L.keys_off = (int64_t)layers[(size_t)i] * per_layer;
-    L.N = d.n_max;
+    L.N = d.n_ub;
     L.keep = keep[(size_t)i];
     L.P = (int32_t)d.base.size();
     L.rescore = rescore[(size_t)i];
+    L.layer = layers[(size_t)i];
     std::copy(d.base.begin(), d.base.end(), kvs::div_staging_bases(z, staging, i));
     c.max_P = std::max(c.max_P, L.P);
     c.max_N = std::max(c.max_N, L.N);
@@ -333,38 +372,50 @@ kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, doubl
   for (int32_t i = 0; i < n; ++i) {
     plans[(size_t)i] = div_plan(pool, first + i);
     means[i] = 0.0;
-    if (plans[(size_t)i].n_total > 0) {
+    if (plans[(size_t)i].n_ub > 0) {
       layers.push_back(first + i);
       pl.push_back(&plans[(size_t)i]);
     }
   }
   if (layers.empty()) return ok();
   if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
-  if (scores_dev && stride < plans[0].n_max)
-    return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)stride,
-                (long long)plans[0].n_max);
+  if (scores_dev) {
+    const std::vector<int64_t> nh = head_counts(pool, first);
+    const int64_t n_max = *std::max_element(nh.begin(), nh.end());
+    if (stride < n_max)
+      return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)stride,
+                  (long long)n_max);
+  }
   const size_t m = layers.size();
+  hipError_t e = div_pinned(pool);
+  if (e != hipSuccess) return hip_fail(e, "diversity staging");
   DivBatch b = div_batch(pool, layers, pl, std::vector<int64_t>(m, 0), std::vector<char>(m, 1), false, scores_dev,
                          stride);
   for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
-  hipError_t e = kvs::enqueue_diversity(b.call, st);
+  e = kvs::enqueue_diversity(b.call, st);
+  const hipError_t staged = hipEventRecord(pool->div_staged, st);  // also after a failed launch: the copy may be queued
+  if (e == hipSuccess) e = staged;
   if (e != hipSuccess) return hip_fail(e, "diversity scoring launch");
-  // one read-back: the float64 score sums, then (adjacent) the error flags
+  // one read-back: the float64 score sums, then (adjacent) the error flags and
+  // each head's candidate count
   const kvs::DivSizes& z = pool->lay.dv;
-  const size_t flags_at = z.flags - z.totals;
-  std::vector<char> rb(flags_at + sizeof(int32_t) * (m + 1));
-  e = hipMemcpyAsync(rb.data(), kvs::div_totals(b.call), rb.size(), hipMemcpyDeviceToHost, st);
+  const size_t flags_at = z.flags - z.totals, counts_at = z.hcount - z.totals;
+  const int32_t H = pool->cfg.num_heads;
+  char* rb = div_readback(pool);
+  e = hipMemcpyAsync(rb, kvs::div_totals(b.call), counts_at + sizeof(int32_t) * m * (size_t)H,
+                     hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "diversity scoring");
-  std::vector<double> sums(m);
-  std::vector<int32_t> flags(m + 1);
-  std::memcpy(sums.data(), rb.data(), sizeof(double) * m);
-  std::memcpy(flags.data(), rb.data() + flags_at, sizeof(int32_t) * (m + 1));
+  const double* sums = reinterpret_cast<const double*>(rb);
+  const int32_t* flags = reinterpret_cast<const int32_t*>(rb + flags_at);
+  const int32_t* counts = reinterpret_cast<const int32_t*>(rb + counts_at);
   for (size_t i = 0; i < m; ++i)
     if (flags[i] & kvs::kDivErrNan) return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite", layers[i]);
   for (size_t i = 0; i < m; ++i) {
     const int32_t l = layers[i];
-    means[l - first] = sums[i] / (double)pl[i]->n_total;
+    int64_t n_total = 0;
+    for (int32_t h = 0; h < H; ++h) n_total += counts[i * (size_t)H + (size_t)h];
+    means[l - first] = n_total > 0 ? sums[i] / (double)n_total : 0.0;
     pool->scored_gen[(size_t)l] = pool->layers[(size_t)l].gen;
   }
   return ok();
@@ -382,6 +433,9 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   if (pool->cfg.special_tokens > 0)
     return fail(KV_ERR_STATE, "a prune would move the special tokens out of a frame's first slots "
                               "(special_tokens > 0)");
+  // a layer whose sum of page lengths exceeds its keep goes to the device; one
+  // whose heads all turn out to hold at most keep candidates comes back
+  // unchanged and is not counted as pruned
   std::vector<DivPlan> plans((size_t)n);
   std::vector<int32_t> layers;
   std::vector<const DivPlan*> pl;
@@ -389,54 +443,79 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   std::vector<char> rescore;
   for (int32_t i = 0; i < n; ++i) {
     plans[(size_t)i] = div_plan(pool, first + i);
-    if (plans[(size_t)i].n_max > keep[i]) {
+    if (plans[(size_t)i].n_ub > keep[i]) {
       const int32_t l = first + i;
       layers.push_back(l);
       pl.push_back(&plans[(size_t)i]);
       kp.push_back(keep[i]);
       rescore.push_back(scores_dev || pool->scored_gen[(size_t)l] != pool->layers[(size_t)l].gen);
+    } else if (kept) {
+      const std::vector<int64_t> nh = head_counts(pool, first + i);
+      for (int32_t h = 0; h < H; ++h) kept[(int64_t)i * H + h] = std::min(keep[i], nh[(size_t)h]);
     }
   }
-  if (!layers.empty()) {
-    if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
-    if (scores_dev && stride < plans[0].n_max)
+  if (layers.empty()) return ok();
+  if (pool->meta_only) return fail(KV_ERR_STATE, "metadata-only pool has no device memory");
+  if (scores_dev) {
+    const std::vector<int64_t> nh = head_counts(pool, first);
+    const int64_t n_max = *std::max_element(nh.begin(), nh.end());
+    if (stride < n_max)
       return fail(KV_ERR_SHAPE, "score_stride %lld < %lld candidates of one head", (long long)stride,
-                  (long long)plans[0].n_max);
-    const size_t m = layers.size();
-    DivBatch b = div_batch(pool, layers, pl, kp, rescore, true, scores_dev, stride);
-    for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
-    hipError_t e = kvs::enqueue_diversity(b.call, st);
-    if (e != hipSuccess) return hip_fail(e, "diversity prune launch");
-    // one read-back: the error flags, then (adjacent) every slot's new lengths [slot][p_max][H]
-    const kvs::DivSizes& z = pool->lay.dv;
-    const size_t len_at = (z.new_len - z.flags) / sizeof(int32_t);
-    std::vector<int32_t> rb(len_at + m * (size_t)z.p_max * (size_t)H);
-    e = hipMemcpyAsync(rb.data(), kvs::div_flags(b.call), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "diversity prune");
-    const int32_t* flags = rb.data();
-    auto nl = [&](size_t i) { return rb.data() + len_at + i * (size_t)z.p_max * (size_t)H; };
-    for (size_t i = 0; i < m; ++i)
-      if (flags[i] & kvs::kDivErrNan)
-        return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite (no layer changed)", layers[i]);
-    for (size_t i = 0; i < m; ++i) {
-      if (flags[i]) return fail(KV_ERR_HIP, "layer %d: diversity prune consistency check failed (flag %d, pool "
-                                            "state undefined)", layers[i], flags[i]);
-      const int32_t* li = nl(i);
-      for (int32_t h = 0; h < H; ++h) {
-        int64_t k = 0;
-        for (size_t j = 0; j < pl[i]->base.size(); ++j) k += li[j * (size_t)H + (size_t)h];
-        if (k != std::min(kp[i], pl[i]->n_head[(size_t)h]))
-          return fail(KV_ERR_HIP, "layer %d head %d: kept %lld candidates, expected %lld (pool state undefined)",
-                      layers[i], h, (long long)k, (long long)std::min(kp[i], pl[i]->n_head[(size_t)h]));
-      }
-    }
-    for (size_t i = 0; i < m; ++i) pool->layers[(size_t)layers[i]].apply_head_compaction(nl(i), H);
+                  (long long)n_max);
   }
-  if (kept)
-    for (int32_t i = 0; i < n; ++i)
-      for (int32_t h = 0; h < H; ++h)
-        kept[(int64_t)i * H + h] = std::min(keep[i], plans[(size_t)i].n_head[(size_t)h]);
+  const size_t m = layers.size();
+  hipError_t e = div_pinned(pool);
+  if (e != hipSuccess) return hip_fail(e, "diversity staging");
+  DivBatch b = div_batch(pool, layers, pl, kp, rescore, true, scores_dev, stride);
+  std::vector<int64_t> gen_before(m);
+  for (size_t i = 0; i < m; ++i) {
+    gen_before[i] = pool->scored_gen[(size_t)layers[i]];
+    pool->scored_gen[(size_t)layers[i]] = -1;
+  }
+  e = kvs::enqueue_diversity(b.call, st);
+  const hipError_t staged = hipEventRecord(pool->div_staged, st);  // also after a failed launch: the copy may be queued
+  if (e == hipSuccess) e = staged;
+  if (e != hipSuccess) return hip_fail(e, "diversity prune launch");
+  // one read-back: the error flags, then (adjacent) each head's candidate
+  // count, each head's kept total and every slot's new lengths [slot][max_P][H]
+  const kvs::DivSizes& z = pool->lay.dv;
+  const size_t counts_at = (z.hcount - z.flags) / sizeof(int32_t), kept_at = (z.kept - z.flags) / sizeof(int32_t);
+  const size_t len_at = (z.new_len - z.flags) / sizeof(int32_t);
+  const size_t per_slot = (size_t)b.call.max_P * (size_t)H;
+  int32_t* rb = reinterpret_cast<int32_t*>(div_readback(pool));
+  e = hipMemcpyAsync(rb, kvs::div_flags(b.call), sizeof(int32_t) * (len_at + m * per_slot), hipMemcpyDeviceToHost,
+                     st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "diversity prune");
+  const int32_t* flags = rb;
+  auto counts = [&](size_t i) { return rb + counts_at + i * (size_t)H; };
+  auto kept_dev = [&](size_t i) { return rb + kept_at + i * (size_t)H; };
+  auto nl = [&](size_t i) { return rb + len_at + i * per_slot; };
+  for (size_t i = 0; i < m; ++i)
+    if (flags[i] & kvs::kDivErrNan)
+      return fail(KV_ERR_NAN, "layer %d: a candidate key is not finite (no layer changed)", layers[i]);
+  for (size_t i = 0; i < m; ++i) {
+    if (flags[i]) return fail(KV_ERR_HIP, "layer %d: diversity prune consistency check failed (flag %d, pool "
+                                          "state undefined)", layers[i], flags[i]);
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t want = std::min<int64_t>(kp[i], counts(i)[h]);
+      if (kept_dev(i)[h] != want)
+        return fail(KV_ERR_HIP, "layer %d head %d: kept %d candidates, expected %lld (pool state undefined)",
+                    layers[i], h, kept_dev(i)[h], (long long)want);
+    }
+  }
+  for (size_t i = 0; i < m; ++i) {
+    const int32_t l = layers[i];
+    const int32_t* c = counts(i);
+    if (*std::max_element(c, c + H) > kp[i]) {
+      pool->layers[(size_t)l].apply_head_compaction(nl(i), H);
+    } else {
+      pool->scored_gen[(size_t)l] = gen_before[i];  // nothing moved: the keys still describe the layer
+      if (rescore[i]) pool->scored_gen[(size_t)l] = pool->layers[(size_t)l].gen;
+    }
+    if (kept)
+      for (int32_t h = 0; h < H; ++h) kept[(int64_t)(l - first) * H + h] = std::min<int64_t>(kp[i], c[h]);
+  }
   return ok();
 }
 
@@ -503,12 +582,59 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* pool_dev, size_t pool_
   return ok();
 }
 
+namespace {
+void free_timing(kv_pool_t* pool) {
+  for (auto& pr : pool->timing) {
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  pool->timing.clear();
+  pool->timing_used = 0;
+}
+}  // namespace
+
+kv_status kv_attend_timing(kv_pool_t* pool, int32_t max_calls) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  if (max_calls < 0 || max_calls > (1 << 20)) return fail(KV_ERR_ARG, "max_calls %d out of 0..2^20", max_calls);
+  free_timing(pool);
+  for (int32_t i = 0; i < max_calls; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      free_timing(pool);
+      return hip_fail(e, "timing events");
+    }
+    pool->timing.emplace_back(a, b);
+  }
+  return ok();
+}
+
+kv_status kv_attend_timing_read(kv_pool_t* pool, double* total_ms, int32_t* n_calls) {
+  if (!pool || !total_ms || !n_calls) return fail(KV_ERR_ARG, "pool, total_ms and n_calls are required");
+  double sum = 0.0;
+  for (size_t i = 0; i < pool->timing_used; ++i) {
+    hipError_t e = hipEventSynchronize(pool->timing[i].second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pool->timing[i].first, pool->timing[i].second);
+    if (e != hipSuccess) return hip_fail(e, "timing events");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *n_calls = (int32_t)pool->timing_used;
+  return ok();
+}
+
 kv_status kv_pool_destroy(kv_pool_t* pool) {
   if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  free_timing(pool);
   discard_pending(pool);
   for (auto& ps : pool->pending)
     if (ps.done) (void)hipEventDestroy(ps.done);
   if (pool->pinned) (void)hipHostFree(pool->pinned);
+  if (pool->div_staged) (void)hipEventDestroy(pool->div_staged);
+  if (pool->div_pinned) (void)hipHostFree(pool->div_pinned);
   delete pool;
   return ok();
 }
@@ -799,7 +925,13 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
   ap.splits = splits;
   ap.n_q = n_q;
   ap.scale_log2 = sm_scale * 1.4426950408889634f;
-  e = kvs::launch_attend(pool->lay.geom, ap, bf16, st);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (pool->timing_used < pool->timing.size()) {
+    ev0 = pool->timing[pool->timing_used].first;
+    ev1 = pool->timing[pool->timing_used].second;
+    ++pool->timing_used;
+  }
+  e = kvs::launch_attend(pool->lay.geom, ap, bf16, st, ev0, ev1);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return KV_OK;
 }

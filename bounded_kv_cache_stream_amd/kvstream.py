@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvstream.so")
+# KVSTREAM_LIB: another build of the same library (the host-sanitized one of build.py)
+LIB_PATH = os.environ.get("KVSTREAM_LIB") or os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_ERR_ARG, KV_ERR_SHAPE, KV_ERR_NO_PAGES, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_NAN = 0, -1, -2, -3, -4, -5, -6
 KV_CLCES_DEFER = 1
@@ -27,7 +28,7 @@ EXPORTED = (
     "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_merge_pages_layers",
     "kv_diversity_score",
     "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
-    "kv_get_head_lengths", "kv_sync", "kv_last_error",
+    "kv_get_head_lengths", "kv_sync", "kv_attend_timing", "kv_attend_timing_read", "kv_last_error",
 )
 
 
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
             "kv_diversity_prune_layers": [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), P],
             "kv_get_head_lengths": [P, I32, P, I32, ctypes.POINTER(I32)],
             "kv_sync": [P, I32],
+            "kv_attend_timing": [P, I32],
+            "kv_attend_timing_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -192,6 +195,18 @@ def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_coun
     _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
                                    ctypes.byref(n), stream))
     return n.value
+
+
+def kv_attend_timing(pool, max_calls) -> None:
+    _check(lib().kv_attend_timing(pool, max_calls))
+
+
+def kv_attend_timing_read(pool) -> tuple:
+    """(sum of the timed attention kernels in ms, number of calls timed)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    _check(lib().kv_attend_timing_read(pool, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def kv_sync(pool, layer=-1) -> None:

@@ -224,6 +224,17 @@ kv_status stream_attend(kv_pool_t* pool, int32_t layer, const void* q_dev, int32
 kv_status stream_attend_scratch(kv_pool_t* pool, int32_t layer, const void* q_dev, int32_t n_q,
                                 float sm_scale, void* out_dev, float* lse_dev, void* stream);
 
+/* Measurement support: the next max_calls stream_attend / stream_attend_scratch
+ * / kv_append_attend calls record a HIP event pair on their stream right
+ * before and right after their attention kernel (before the split-KV
+ * combine), so the kernel's own duration can be read without a profiler.
+ * Creates the 2 * max_calls events here (max_calls = 0: frees them, timing
+ * off); calls beyond max_calls record nothing.  kv_attend_timing_read waits for
+ * the recorded events and returns the sum of the kernel times (ms) and the
+ * number of calls timed.  kv_pool_destroy frees the events. */
+kv_status kv_attend_timing(kv_pool_t* pool, int32_t max_calls);
+kv_status kv_attend_timing_read(kv_pool_t* pool, double* total_ms, int32_t* n_calls);
+
 /* One frame's cache step in one call: kv_append_frame(layer, frame_idx, k_dev,
  * v_dev, n_tokens, flags), then kv_evict(layer), then stream_attend(layer,
  * q_dev, n_q, sm_scale, out_dev, lse_dev), with the same arguments, checks,

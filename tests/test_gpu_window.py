@@ -159,6 +159,25 @@ def test_split_count_does_not_change_results():
         assert max_abs(o, outs[0]) <= 8e-3
 
 
+def test_attention_kernel_timing_events():
+    # kv_attend_timing records the kernel's own duration on the call's stream for the next max_calls calls
+    # and leaves the results unchanged; calls beyond max_calls are not timed
+    s = _Stream(1)
+    torch = s.torch
+    for t in range(12):
+        q, att = s.step(t)
+    plain = s.cache.attend(0, q, 1.0).clone()
+    kv.kv_attend_timing(s.cache.handle, 3)
+    outs = [s.cache.attend(0, q, 1.0).clone() for _ in range(5)]
+    ms, n = kv.kv_attend_timing_read(s.cache.handle)
+    assert n == 3 and 0.0 < ms < 1000.0
+    for o in outs:
+        assert torch.equal(o, plain)
+    kv.kv_attend_timing(s.cache.handle, 0)
+    s.cache.attend(0, q, 1.0)
+    assert kv.kv_attend_timing_read(s.cache.handle) == (0.0, 0)
+
+
 def test_long_stream_keyframe4_10000_frames():
     w = synth.WORKLOADS[2]
     S, W, k = w["scale_frames"], w["window"], w["keyframe_interval"]

@@ -378,3 +378,16 @@ def test_clces_flags_and_sync_on_a_metadata_pool():
     with pytest.raises(kv.KVError):
         kv.kv_sync(c.handle, 1)
     assert c.page_table(0)[1] == [16] * 3
+
+
+def test_attend_timing_arguments_on_a_metadata_pool():
+    # timing off (0 calls) needs no device; bad counts and NULL pools are refused
+    c = _meta_pool(0, 0, 1, 5)
+    kv.kv_attend_timing(c.handle, 0)
+    assert kv.kv_attend_timing_read(c.handle) == (0.0, 0)
+    for bad in (-1, (1 << 20) + 1):
+        with pytest.raises(kv.KVError) as e:
+            kv.kv_attend_timing(c.handle, bad)
+        assert e.value.status == kv.KV_ERR_ARG
+    assert kv.lib().kv_attend_timing(None, 1) == kv.KV_ERR_ARG
+    assert kv.lib().kv_attend_timing_read(c.handle, None, None) == kv.KV_ERR_ARG
