@@ -531,7 +531,7 @@ def run_diversity(args):
         means = cache.diversity_score_layers(0, L)
         marks[2].record(stream)
         budgets = kv.kv_layer_budgets(means, tau, total, H)
-        kept[:] = cache.diversity_prune_layers(0, budgets)
+        cache.diversity_prune_layers(0, budgets, out=kept)
         marks[3].record(stream)
         if args.merge:
             cache.merge_pages_layers(0, L)

@@ -51,7 +51,7 @@ struct DivCall {
   PageGeom geom;
   int32_t* hlen_dev;      // [physical page][heads] per-head lengths; a prune writes its pages' new lengths
   uint32_t* keys_dev;     // the key store (each layer's keys at its keys_off: per head a high plane, then a low plane)
-  const char* staging;    // host block of div_staging_bytes(sizes, n) bytes
+  const char* staging;    // device address of the pinned host block of div_staging_bytes(sizes, n) bytes
   int32_t n;              // slots
   int32_t max_P;          // the largest P over the slots
   int64_t max_N;          // the largest N over the slots

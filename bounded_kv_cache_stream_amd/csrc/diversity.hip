@@ -143,9 +143,14 @@ __global__ __launch_bounds__(kThreads) void div_tables_kernel(DivK a) {
   if (a.layers[slot].rescore) a.hist0[((int64_t)a.layers[slot].layer * a.H + h) * 256 + tid] = 0u;
 }
 
-__global__ void div_zero_kernel(int32_t* p0, int n0) {
+// The call's staging block (parameters and candidate pages, written by the
+// host into pinned memory) copied into the workspace, 16 bytes per thread,
+// and the error flags cleared.  A kernel reads the pinned block directly:
+// no separate copy operation has to start before the first kernel.
+__global__ void div_stage_kernel(const int4* src, int4* dst, int n16, int32_t* flags, int n_flags) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n0) p0[i] = 0;
+  if (i < n16) dst[i] = src[i];
+  if (i < n_flags) flags[i] = 0;
 }
 
 // The 8 elements c*8 .. c*8+7 of one row as loaded (one 16-byte vector for
@@ -801,9 +806,9 @@ hipError_t enqueue_diversity(const DivCall& c, hipStream_t s) {
     return hipErrorInvalidValue;
   const DivK k = make_k(c);
   const int H = c.geom.heads;
-  hipError_t e = hipMemcpyAsync(c.ws + z.params, c.staging, div_staging_bytes(z, c.n), hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return e;
-  div_zero_kernel<<<dim3((unsigned)((c.n + 1 + 255) / 256)), dim3(256), 0, s>>>(k.flags, c.n + 1);
+  const int n16 = (int)((div_staging_bytes(z, c.n) + 15) / 16);
+  div_stage_kernel<<<dim3((unsigned)((std::max(n16, c.n + 1) + 255) / 256)), dim3(256), 0, s>>>(
+      reinterpret_cast<const int4*>(c.staging), reinterpret_cast<int4*>(c.ws + z.params), n16, k.flags, c.n + 1);
   div_tables_kernel<<<dim3((unsigned)H, (unsigned)c.n), dim3(kThreads), 0, s>>>(k);
   const dim3 pages((unsigned)c.max_P, (unsigned)H, (unsigned)c.n);
   if (c.any_rescore) {

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -147,7 +148,9 @@ struct kv_pool {
   // the staging block copied to the device, then the read-back area; staged
   // is recorded after each call's kernels, and the staging block is rewritten
   // only once it has completed
+  hipEvent_t wait_ev = nullptr;  // wait_stream's marker
   char* div_pinned = nullptr;
+  char* div_pinned_dev = nullptr;  // the same block as the device addresses it (mapped, coherent)
   size_t div_stage_bytes = 0;
   hipEvent_t div_staged = nullptr;
   // deferred score_and_compact steps (KV_CLCES_DEFER): per layer, whether one
@@ -182,6 +185,32 @@ struct kv_pool {
 };
 
 namespace {
+
+// Waits until the stream has run everything enqueued on it so far, for a
+// call that reads results back.  It polls an event: a blocking wait can
+// return tens of microseconds after the GPU is done.  After kPollUs of
+// polling it blocks instead.
+constexpr double kPollUs = 20000.0;
+
+hipError_t wait_stream(kv_pool_t* p, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (!p->wait_ev) e = hipEventCreateWithFlags(&p->wait_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(p->wait_ev, st);
+  if (e != hipSuccess) return e;
+  const auto t0 = std::chrono::steady_clock::now();
+  while ((e = hipEventQuery(p->wait_ev)) == hipErrorNotReady)
+    if (std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count() > kPollUs)
+      return hipEventSynchronize(p->wait_ev);
+  return e;
+}
+
+// Pinned read-back slots of score_and_compact, (pages_per_layer + 1) ints per
+// layer: the error flag, then the new page lengths.
+hipError_t clces_pinned(kv_pool_t* p) {
+  return hipHostMalloc(reinterpret_cast<void**>(&p->pinned),
+                       sizeof(int32_t) * (size_t)p->cfg.num_layers * ((size_t)p->cfg.pages_per_layer + 1),
+                       hipHostMallocDefault);
+}
 
 // Completes the layer's deferred score_and_compact, if one is pending: waits
 // for its read-back and applies the new page lengths to the host table, or
@@ -240,29 +269,16 @@ kvs::DevEntry* dev_table(const kv_pool_t* p, int32_t layer) {
 
 int32_t* hlens_dev(const kv_pool_t* p) { return reinterpret_cast<int32_t*>(p->ws + p->lay.hlens); }
 
-// The candidate pages of a layer for the diversity steps (every page past the
-// scale frames, in table order; tile_start flags pages whose per-head lengths
-// are in the device array) and n_ub, the sum of their lengths: at least any
-// head's candidate count (a page's length is the largest of its heads').  The
-// exact per-head counts come from the device (the tables kernel) with each
-// call's read-back; head_counts() computes them on the host where a call
-// needs them without a launch.
-struct DivPlan {
-  std::vector<kvs::DevEntry> base;
-  int64_t n_ub = 0;
-};
-
-DivPlan div_plan(const kv_pool_t* pool, int32_t layer) {
+// The sum of the lengths of a layer's candidate pages (every page past the
+// scale frames): at least any head's candidate count, since a page's length
+// is the largest of its heads'.  The exact per-head counts come from the
+// device (the tables kernel) with each call's read-back; head_counts()
+// computes them on the host where a call needs them without a launch.
+int64_t candidate_bound(const kv_pool_t* pool, int32_t layer) {
   const auto& L = pool->layers[(size_t)layer];
-  DivPlan d;
-  const size_t first = L.first_candidate();
-  d.base.reserve(L.table.size() - std::min(first, L.table.size()));
-  for (size_t i = first; i < L.table.size(); ++i) {
-    const auto& e = L.table[i];
-    d.base.push_back(kvs::DevEntry{(int32_t)phys_page(pool, layer, e.page), e.len, e.hlen.empty() ? 0 : 1, 0});
-    d.n_ub += e.len;
-  }
-  return d;
+  int64_t n = 0;
+  for (size_t i = L.first_candidate(); i < L.table.size(); ++i) n += L.table[i].len;
+  return n;
 }
 
 // Each head's candidate count of a layer, on the host.
@@ -288,14 +304,16 @@ kv_status check_layers(const kv_pool_t* p, int32_t first, int32_t n) {
   return KV_OK;
 }
 
-// One diversity call over a set of layers (slots in order): the host staging
-// block (per-layer parameters and candidate tables) and the launch arguments.
+// One diversity call over a set of layers (slots in order) and its launch
+// arguments; the parameters and candidate pages of each slot are written
+// straight into the pinned staging block.
 struct DivBatch {
   std::vector<int32_t> layer;  // slot -> layer
   kvs::DivCall call{};
 };
 
-// The pinned block of the diversity calls: staging for every layer, then the
+// The pinned block of the diversity calls (mapped into the device's address
+// space): staging for every layer, then the
 // larger of the two read-backs (scoring: totals, flags and head counts; prune:
 // flags, head counts, kept totals and every layer's new lengths).
 hipError_t div_pinned(kv_pool_t* pool) {
@@ -304,13 +322,16 @@ hipError_t div_pinned(kv_pool_t* pool) {
   const size_t stage = (kvs::div_staging_bytes(z, z.layers) + 255) / 256 * 256;
   const size_t rb_score = (z.hcount - z.totals) + sizeof(int32_t) * (size_t)z.layers * z.h_max;
   const size_t rb_prune = (z.new_len - z.flags) + sizeof(int32_t) * (size_t)z.layers * z.p_max * z.h_max;
+  // mapped: the first kernel of a call reads the staging block itself;
+  // coherent: it sees the host's writes made before the launch
   hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&pool->div_pinned), stage + std::max(rb_score, rb_prune),
-                               hipHostMallocDefault);
+                               hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) {
     pool->div_pinned = nullptr;
     return e;
   }
-  e = hipEventCreateWithFlags(&pool->div_staged, hipEventDisableTiming);
+  e = hipHostGetDevicePointer(reinterpret_cast<void**>(&pool->div_pinned_dev), pool->div_pinned, 0);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&pool->div_staged, hipEventDisableTiming);
   if (e != hipSuccess) {
     (void)hipHostFree(pool->div_pinned);
     pool->div_pinned = nullptr;
@@ -323,15 +344,16 @@ hipError_t div_pinned(kv_pool_t* pool) {
 
 char* div_readback(kv_pool_t* pool) { return pool->div_pinned + pool->div_stage_bytes; }
 
-// Call after div_pinned() succeeded.
-DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<const DivPlan*>& plans,
+// Call after div_pinned() succeeded: stages every slot (its parameters, then
+// its candidate pages: phys, len, tile_start = per-head lengths in the
+// device array) in the pinned block and fills the launch arguments.
+DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const std::vector<int64_t>& n_ub,
                    const std::vector<int64_t>& keep, const std::vector<char>& rescore, bool prune, double* scores,
                    int64_t stride) {
   DivBatch b;
   const kvs::DivSizes& z = pool->lay.dv;
   const int n = (int)layers.size();
   b.layer = layers;
-  // only the parameters and each slot's first P entries are read on the device
   char* staging = pool->div_pinned;
   kvs::DivCall& c = b.call;
   c.ws = pool->ws + pool->lay.div;
@@ -340,22 +362,29 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
   c.geom = pool->lay.geom;
   c.hlen_dev = hlens_dev(pool);
   c.keys_dev = reinterpret_cast<uint32_t*>(pool->ws + pool->lay.dkeys);
-  c.staging = staging;
+  c.staging = pool->div_pinned_dev;
   c.n = n;
   c.prune = prune;
   c.scores_out = scores;
   c.score_stride = stride;
   const int64_t per_layer = 2 * (int64_t)pool->cfg.num_heads * pool->cfg.pages_per_layer * pool->cfg.page_tokens;
   for (int i = 0; i < n; ++i) {
-    const DivPlan& d = *plans[(size_t)i];
+    const int32_t layer = layers[(size_t)i];
+    const auto& T = pool->layers[(size_t)layer];
+    kvs::DevEntry* out = kvs::div_staging_bases(z, staging, i);
+    int32_t P = 0;
+    for (size_t j = T.first_candidate(); j < T.table.size(); ++j) {
+      const auto& e = T.table[j];
+      out[P++] = kvs::DevEntry{(int32_t)phys_page(pool, layer, e.page), e.len, e.hlen.empty() ? 0 : 1, 0};
+    }
     kvs::DivLayer& L = kvs::div_staging_layers(staging)[i];
-    L.keys_off = (int64_t)layers[(size_t)i] * per_layer;
-    L.N = d.n_ub;
+    L.keys_off = (int64_t)layer * per_layer;
+    L.N = n_ub[(size_t)i];
     L.keep = keep[(size_t)i];
-    L.P = (int32_t)d.base.size();
+    L.P = P;
     L.rescore = rescore[(size_t)i];
-    L.layer = layers[(size_t)i];
-    std::copy(d.base.begin(), d.base.end(), kvs::div_staging_bases(z, staging, i));
+    L.layer = layer;
+    L.pad = 0;
     c.max_P = std::max(c.max_P, L.P);
     c.max_N = std::max(c.max_N, L.N);
     c.any_rescore = c.any_rescore || L.rescore;
@@ -366,15 +395,14 @@ DivBatch div_batch(kv_pool_t* pool, const std::vector<int32_t>& layers, const st
 // Scores layers first .. first+n-1, one wait for all of them.
 kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, double* scores_dev, int64_t stride,
                                 double* means, hipStream_t st) {
-  std::vector<DivPlan> plans((size_t)n);
   std::vector<int32_t> layers;
-  std::vector<const DivPlan*> pl;
+  std::vector<int64_t> n_ub;
   for (int32_t i = 0; i < n; ++i) {
-    plans[(size_t)i] = div_plan(pool, first + i);
+    const int64_t nu = candidate_bound(pool, first + i);
     means[i] = 0.0;
-    if (plans[(size_t)i].n_ub > 0) {
+    if (nu > 0) {
       layers.push_back(first + i);
-      pl.push_back(&plans[(size_t)i]);
+      n_ub.push_back(nu);
     }
   }
   if (layers.empty()) return ok();
@@ -389,7 +417,7 @@ kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, doubl
   const size_t m = layers.size();
   hipError_t e = div_pinned(pool);
   if (e != hipSuccess) return hip_fail(e, "diversity staging");
-  DivBatch b = div_batch(pool, layers, pl, std::vector<int64_t>(m, 0), std::vector<char>(m, 1), false, scores_dev,
+  DivBatch b = div_batch(pool, layers, n_ub, std::vector<int64_t>(m, 0), std::vector<char>(m, 1), false, scores_dev,
                          stride);
   for (int32_t l : layers) pool->scored_gen[(size_t)l] = -1;
   e = kvs::enqueue_diversity(b.call, st);
@@ -404,7 +432,7 @@ kv_status diversity_score_range(kv_pool_t* pool, int32_t first, int32_t n, doubl
   char* rb = div_readback(pool);
   e = hipMemcpyAsync(rb, kvs::div_totals(b.call), counts_at + sizeof(int32_t) * m * (size_t)H,
                      hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = wait_stream(pool, st);
   if (e != hipSuccess) return hip_fail(e, "diversity scoring");
   const double* sums = reinterpret_cast<const double*>(rb);
   const int32_t* flags = reinterpret_cast<const int32_t*>(rb + flags_at);
@@ -436,17 +464,16 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   // a layer whose sum of page lengths exceeds its keep goes to the device; one
   // whose heads all turn out to hold at most keep candidates comes back
   // unchanged and is not counted as pruned
-  std::vector<DivPlan> plans((size_t)n);
   std::vector<int32_t> layers;
-  std::vector<const DivPlan*> pl;
+  std::vector<int64_t> n_ub;
   std::vector<int64_t> kp;
   std::vector<char> rescore;
   for (int32_t i = 0; i < n; ++i) {
-    plans[(size_t)i] = div_plan(pool, first + i);
-    if (plans[(size_t)i].n_ub > keep[i]) {
+    const int64_t nu = candidate_bound(pool, first + i);
+    if (nu > keep[i]) {
       const int32_t l = first + i;
       layers.push_back(l);
-      pl.push_back(&plans[(size_t)i]);
+      n_ub.push_back(nu);
       kp.push_back(keep[i]);
       rescore.push_back(scores_dev || pool->scored_gen[(size_t)l] != pool->layers[(size_t)l].gen);
     } else if (kept) {
@@ -466,7 +493,7 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   const size_t m = layers.size();
   hipError_t e = div_pinned(pool);
   if (e != hipSuccess) return hip_fail(e, "diversity staging");
-  DivBatch b = div_batch(pool, layers, pl, kp, rescore, true, scores_dev, stride);
+  DivBatch b = div_batch(pool, layers, n_ub, kp, rescore, true, scores_dev, stride);
   std::vector<int64_t> gen_before(m);
   for (size_t i = 0; i < m; ++i) {
     gen_before[i] = pool->scored_gen[(size_t)layers[i]];
@@ -485,7 +512,7 @@ kv_status diversity_prune_range(kv_pool_t* pool, int32_t first, int32_t n, const
   int32_t* rb = reinterpret_cast<int32_t*>(div_readback(pool));
   e = hipMemcpyAsync(rb, kvs::div_flags(b.call), sizeof(int32_t) * (len_at + m * per_slot), hipMemcpyDeviceToHost,
                      st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = wait_stream(pool, st);
   if (e != hipSuccess) return hip_fail(e, "diversity prune");
   const int32_t* flags = rb;
   auto counts = [&](size_t i) { return rb + counts_at + i * (size_t)H; };
@@ -634,6 +661,7 @@ kv_status kv_pool_destroy(kv_pool_t* pool) {
     if (ps.done) (void)hipEventDestroy(ps.done);
   if (pool->pinned) (void)hipHostFree(pool->pinned);
   if (pool->div_staged) (void)hipEventDestroy(pool->div_staged);
+  if (pool->wait_ev) (void)hipEventDestroy(pool->wait_ev);
   if (pool->div_pinned) (void)hipHostFree(pool->div_pinned);
   delete pool;
   return ok();
@@ -1137,10 +1165,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto& ps = pool->pending[(size_t)layer];
     hipError_t e = hipSuccess;
-    if (!pool->pinned)
-      e = hipHostMalloc(reinterpret_cast<void**>(&pool->pinned),
-                        sizeof(int32_t) * (size_t)pool->cfg.num_layers * ((size_t)pool->cfg.pages_per_layer + 1),
-                        hipHostMallocDefault);
+    if (!pool->pinned) e = clces_pinned(pool);
     if (e == hipSuccess && !ps.done) e = hipEventCreateWithFlags(&ps.done, hipEventDisableTiming);
     if (e == hipSuccess) e = kvs::enqueue_clces(a, st);
     if (e == hipSuccess) e = copy_ranks(st);
@@ -1158,16 +1183,19 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   std::vector<int32_t> new_lens((size_t)a.n_entries);
   int32_t err_flag = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kvs::enqueue_clces(a, st);
+  hipError_t e = pool->pinned ? hipSuccess : clces_pinned(pool);
+  if (e == hipSuccess) e = kvs::enqueue_clces(a, st);
   if (e == hipSuccess) e = copy_ranks(st);
-  // one read-back: the error flag and, after it, the new page lengths
-  std::vector<int32_t> rb((size_t)a.n_entries + 1);
+  // one read-back into the layer's pinned slot: the error flag and, after
+  // it, the new page lengths
+  const int32_t* rb = pool->pinned + (size_t)layer * ((size_t)pool->cfg.pages_per_layer + 1);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(rb.data(), kvs::clces_result(a), sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+    e = hipMemcpyAsync(const_cast<int32_t*>(rb), kvs::clces_result(a), sizeof(int32_t) * ((size_t)a.n_entries + 1),
+                       hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = wait_stream(pool, st);
   if (e != hipSuccess) return hip_fail(e, "CLCES step");
   err_flag = rb[0];
-  std::copy(rb.begin() + 1, rb.end(), new_lens.begin());
+  std::copy(rb + 1, rb + 1 + a.n_entries, new_lens.begin());
   if (err_flag & kvs::kClcesErrNan) return fail(KV_ERR_NAN, "layer %d: a raw score is NaN or negative", layer);
   if (err_flag & kvs::kClcesErrRow) return fail(KV_ERR_ARG, "layer %d: a token id is >= score_rows", layer);
   if (err_flag) return fail(KV_ERR_HIP, "layer %d: CLCES consistency check failed (flag %d)", layer, err_flag);

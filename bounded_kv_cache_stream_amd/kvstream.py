@@ -251,9 +251,17 @@ def kv_diversity_score_layers(pool, first_layer, n_layers, stream=None) -> list:
     return list(out)
 
 
-def kv_diversity_prune_layers(pool, first_layer, keep_per_head, heads, stream=None) -> list:
+def kv_diversity_prune_layers(pool, first_layer, keep_per_head, heads, stream=None, out=None):
+    """Kept candidates per layer and head: a list of lists, or written into `out` (a C-contiguous int64 numpy
+    array of n x heads, returned) without building Python lists."""
     n = len(keep_per_head)
     keep = (ctypes.c_int64 * max(n, 1))(*[int(k) for k in keep_per_head])
+    if out is not None:
+        if out.dtype.name != "int64" or out.size != n * heads or not out.flags["C_CONTIGUOUS"]:
+            raise ValueError("out must be a C-contiguous int64 array of len(keep_per_head) x heads")
+        _check(lib().kv_diversity_prune_layers(pool, first_layer, n, keep,
+                                               out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), stream))
+        return out
     kept = (ctypes.c_int64 * max(n * heads, 1))()
     _check(lib().kv_diversity_prune_layers(pool, first_layer, n, keep, kept, stream))
     return [list(kept[i * heads:(i + 1) * heads]) for i in range(n)]
@@ -464,10 +472,11 @@ class KVCache:
         """Mean diversity of each of n_layers layers, one wait."""
         return kv_diversity_score_layers(self.handle, first_layer, n_layers, self._stream())
 
-    def diversity_prune_layers(self, first_layer, keep_per_head) -> list:
-        """Per-head top-K prune of len(keep_per_head) layers, one wait; kept per layer and head."""
+    def diversity_prune_layers(self, first_layer, keep_per_head, out=None):
+        """Per-head top-K prune of len(keep_per_head) layers, one wait; kept per layer and head (into `out`,
+        an int64 numpy array, when given)."""
         return kv_diversity_prune_layers(self.handle, first_layer, keep_per_head, self.cfg.num_heads,
-                                         self._stream())
+                                         self._stream(), out=out)
 
     def head_lengths(self, layer) -> list:
         return kv_get_head_lengths(self.handle, layer, self.cfg.num_heads)

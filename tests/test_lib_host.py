@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from bounded_kv_cache_stream_amd import kvstream as kv
@@ -279,6 +280,10 @@ def test_diversity_host_rules():
     m.append(1, 0, None, None)
     m.append(1, 1, None, None)
     assert m.diversity_prune_layers(0, [5, 16, 0]) == [[0, 0], [16, 16], [0, 0]]
+    out = np.full((3, 2), -1, dtype=np.int64)
+    assert m.diversity_prune_layers(0, [5, 16, 0], out=out) is out and out.tolist() == [[0, 0], [16, 16], [0, 0]]
+    with pytest.raises(ValueError):
+        m.diversity_prune_layers(0, [5, 16, 0], out=np.zeros((3, 2), dtype=np.int32))
     for call in (lambda: m.diversity_prune_layers(1, [5, 5]), lambda: m.diversity_score_layers(0, 3)):
         with pytest.raises(kv.KVError) as e:
             call()
