@@ -31,8 +31,8 @@ struct RankOut {
 struct ClcesSizes {
   int64_t n_max;
   int32_t p_max, w_max;
-  size_t keys_a, keys_b, vals_a, vals_b, blk_cnt, scur, shat, sel_hist, sel_state, entries, counts, move_src,
-      move_dst, n_moves, flag, total;
+  size_t keys_a, keys_b, vals_a, vals_b, blk_cnt, scur, shat, sel_hist, sel_state, list, list_cnt, entries, counts,
+      move_src, move_dst, n_moves, flag, total;
 };
 
 ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_max);

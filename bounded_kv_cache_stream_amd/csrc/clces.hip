@@ -21,10 +21,12 @@
 //   fuse     float64 mean, population variance, Cons and s_hat with a fixed
 //            operation order and no contraction (bit-exact reproducible),
 //            plus the histogram of the first select digit;
-//   select   radix select of the keep_count-th largest s_hat (6 passes of
-//            11, 11, 11, 11, 11 and 9 bits over the 64-bit pattern, which
-//            orders non-negative doubles; the first histogram comes from fuse,
-//            the last step from mark);
+//   select   radix select of the keep_count-th largest s_hat (up to 6
+//            passes of 11, 11, 11, 11, 11 and 9 bits over the 64-bit
+//            pattern, which orders non-negative doubles): the first histogram
+//            comes from fuse, the second from a pass over every key, and one
+//            workgroup finishes from there (the first 22 bits almost always
+//            decide; otherwise it copies the still-matching keys to LDS);
 //   mark     per page: count of s_hat above / equal to the threshold;
 //   index    per page: its kept count and offsets (from all pages' counts),
 //            the kept token ids in slot order, and the moves: with
@@ -62,7 +64,7 @@ struct SelState {
   unsigned long long mask;
   long long k_rem;
   int32_t done;
-  int32_t pad;
+  int32_t match;  // keys matching the prefix (set by each advance; 0 before pass 0)
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -76,12 +78,15 @@ __device__ inline uint32_t order_key(float s) {
 // later kernels accumulate into set to zero (select histograms, per-page
 // counts, the error flag).
 __global__ void prep_kernel(DevEntry* entries, TableChunk chunk, uint32_t* sel_hist, int n_hist, int32_t* counts,
-                            int n_counts, int32_t* flag) {
+                            int n_counts, int32_t* list_cnt, int32_t* flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < chunk.count) entries[chunk.first + i] = chunk.e[i];
   if (i < n_hist) sel_hist[i] = 0;
   if (i < n_counts) counts[i] = 0;
-  if (i == 0) *flag = 0;
+  if (i == 0) {
+    *flag = 0;
+    *list_cnt = 0;
+  }
 }
 
 struct GatherArgs {
@@ -383,6 +388,7 @@ __device__ SelState select_advance(SelState st, const uint32_t* hist, int p) {
         out.mask = st.mask | (((1ull << width) - 1ull) << shift);
         out.k_rem = st.k_rem - cum;
         out.done = out.k_rem == c || p == kSelPasses - 1;
+        out.match = (int32_t)c;
         break;
       }
       cum += c;
@@ -394,17 +400,24 @@ __device__ SelState select_advance(SelState st, const uint32_t* hist, int p) {
   return r;
 }
 
-// Pass p (1..5) histograms digit p of the keys that match the digits fixed so
-// far.  The state before pass p is advanced once from the previous pass's
-// state (stored by its workgroup 0) and histogram; workgroup 0 stores it in turn.
+constexpr int kFinishCap = 4096;  // keys the finishing workgroup holds in LDS
+
+// Pass p histograms digit p of the keys that match the digits fixed so far
+// (launched for p = 1 and 2).  The state before pass p is advanced once from
+// the previous pass's state (stored by its workgroup 0) and histogram;
+// workgroup 0 stores it in turn.  Pass 2 also appends the matching keys to
+// `list` when at most kFinishCap of them match (the count of the digit pass 1
+// fixed), for the finishing workgroup.
 __global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned long long* keys, int N,
                                                                uint32_t* sel_hist, SelState* states, int p,
+                                                               unsigned long long* list, int32_t* list_cnt,
                                                                const int32_t* flag) {
   if (*flag) return;
   __shared__ uint32_t cnt[kSelBins];
   const SelState st = select_advance(states[p - 1], sel_hist + (p - 1) * kSelBins, p - 1);
   if (blockIdx.x == 0 && threadIdx.x == 0) states[p] = st;
   if (st.done) return;
+  const bool listing = p == 2 && st.match <= kFinishCap;
   for (int d = threadIdx.x; d < kSelBins; d += kThreads) cnt[d] = 0;
   __syncthreads();
   const int shift = sel_shift(p);
@@ -414,9 +427,58 @@ __global__ __launch_bounds__(kThreads) void select_pass_kernel(const unsigned lo
     const unsigned long long k = i < N ? keys[i] : 0ull;
     const bool match = i < N && (k & st.mask) == st.prefix;
     hist_add(cnt, (uint32_t)((k >> shift) & dmask), match);
+    if (listing) {
+      const unsigned long long bm = __ballot(match);
+      if (bm) {
+        int32_t base = 0;
+        if ((threadIdx.x & 63) == 0) base = atomicAdd(list_cnt, (int32_t)__popcll(bm));
+        base = __shfl(base, 0, 64);
+        const int32_t at = base + (int32_t)__popcll(bm & ((1ull << (threadIdx.x & 63)) - 1ull));
+        if (match && at < kFinishCap) list[at] = k;
+      }
+    }
   }
   __syncthreads();
   flush_hist(cnt, sel_hist + p * kSelBins);
+}
+
+// The passes after pass 2, in one workgroup: from pass 2's state and
+// histogram, the final state.  When pass 2 listed the keys still matching
+// (few: the first 22 bits of s_hat fix most of the order), the remaining
+// passes read that list from LDS; otherwise every remaining pass scans all
+// the keys.  keep == 0: the state before pass 0 is final (nothing is kept).
+__global__ __launch_bounds__(kThreads) void select_finish_kernel(const unsigned long long* keys, int N,
+                                                                 const uint32_t* sel_hist, SelState* states,
+                                                                 const unsigned long long* glist,
+                                                                 const int32_t* list_cnt, long long keep,
+                                                                 const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ unsigned long long list[kFinishCap];
+  const int tid = threadIdx.x;
+  if (keep == 0) {
+    if (tid == 0) states[kSelPasses] = states[0];
+    return;
+  }
+  const SelState s2 = states[2];
+  const bool listed = !s2.done && s2.match <= kFinishCap;
+  const int32_t n_list = listed ? min(*list_cnt, kFinishCap) : 0;
+  for (int i = tid; i < n_list; i += kThreads) list[i] = glist[i];
+  SelState st = select_advance(s2, sel_hist + 2 * kSelBins, 2);
+  for (int p = 3; p < kSelPasses && !st.done; ++p) {
+    for (int d = tid; d < kSelBins; d += kThreads) hist[d] = 0;
+    __syncthreads();
+    const int shift = sel_shift(p);
+    const unsigned long long dmask = (1ull << (sel_shift(p - 1) - shift)) - 1ull;
+    const int n = listed ? n_list : N;
+    for (int i = tid; i < n; i += kThreads) {
+      const unsigned long long k = listed ? list[i] : keys[i];
+      if ((k & st.mask) == st.prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    st = select_advance(st, hist, p);
+  }
+  if (tid == 0) states[kSelPasses] = st;
 }
 
 struct MarkArgs {
@@ -434,9 +496,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(MarkArgs a) {
   if (*a.flag) return;
   __shared__ int32_t sg, se;
   // threshold = the keep_count-th largest key; keep 0 keeps nothing
-  const SelState st =
-      select_advance(a.states[kSelPasses - 1], a.sel_hist + (kSelPasses - 1) * kSelBins, kSelPasses - 1);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.states[kSelPasses] = st;
+  const SelState st = a.states[kSelPasses];
   if (threadIdx.x == 0) { sg = 0; se = 0; }
   __syncthreads();
   const DevEntry en = a.entries[blockIdx.x];
@@ -603,6 +663,8 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   z.shat = take((size_t)n_max * 8);
   z.sel_hist = take((size_t)kSelPasses * kSelBins * 4);
   z.sel_state = take((kSelPasses + 1) * sizeof(SelState));
+  z.list = take(kFinishCap * sizeof(unsigned long long));
+  z.list_cnt = take(4);
   z.entries = take((size_t)p_max * sizeof(DevEntry));
   z.counts = take((size_t)p_max * 2 * 4);
   z.move_src = take((size_t)p_max * ts_max * 2);
@@ -658,8 +720,8 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
     for (int i = 0; i < c.count; ++i) c.e[i] = a.entries_host[i];
     const int n_hist = kSelPasses * kSelBins;
     const int64_t nz = std::max(n_hist, 2 * P);
-    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(entries, c, sel_hist, n_hist, counts, 2 * P,
-                                                                          flag);
+    prep_kernel<<<dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s>>>(
+        entries, c, sel_hist, n_hist, counts, 2 * P, reinterpret_cast<int32_t*>(ws + z.list_cnt), flag);
   }
   hipError_t e = P > kUploadChunk ? launch_table_upload(entries + kUploadChunk, a.entries_host + kUploadChunk,
                                                         P - kUploadChunk, s)
@@ -700,10 +762,14 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
   fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
       ri, scur, shat, a.s_hat_out, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
   const int nblk = (N + kSelTile - 1) / kSelTile;
-  if (a.keep > 0) {
-    for (int p = 1; p < kSelPasses; ++p)
-      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, p, flag);
-  }
+  unsigned long long* list = reinterpret_cast<unsigned long long*>(ws + z.list);
+  int32_t* list_cnt = reinterpret_cast<int32_t*>(ws + z.list_cnt);
+  if (a.keep > 0)
+    for (int p = 1; p <= 2; ++p)
+      select_pass_kernel<<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, p, list,
+                                                                        list_cnt, flag);
+  select_finish_kernel<<<dim3(1), dim3(kThreads), 0, s>>>(shat, N, sel_hist, sel_state, list, list_cnt, a.keep,
+                                                          flag);
   MarkArgs m{entries, shat, sel_hist, a.keep, counts, counts + P, sel_state, flag};
   mark_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(m);
   CompactArgs ca{entries,
