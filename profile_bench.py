@@ -22,9 +22,11 @@ recorded).
 
 The CLCES workload gets the trace pass only: its FETCH_SIZE pass went silent
 for minutes where every other pass ends in seconds, with no cause found, so no
-counter pass is run on it.
+counter pass is run on it.  The diversity and token-budget stacks also get the
+trace pass only (the last 10 frames: per kernel the last 10 dispatches, which
+for the per-layer kernels is the last layers of the last frame).
 
-    python profile_bench.py [--workloads stream,append,clces] [--out gpurun_out/prof]
+    python profile_bench.py [--workloads stream,append,clces,diversity,budget] [--out gpurun_out/prof]
     python profile_bench.py --parse-only ...    # rebuild the summaries from existing output
 """
 
@@ -54,6 +56,12 @@ WORKLOADS = {
                "pmc": True, "mfma": False},
     "clces": {"args": ["--workload", "clces", "--no-cpu-baseline"], "trace_steps": None, "pmc_steps": None,
               "pmc": False, "mfma": False},
+    # the stacks: every dispatch from the start of the last trace_steps frames (found from a kernel that runs
+    # `per_step` times a frame) counts
+    "diversity": {"args": ["--workload", "diversity", "--no-cpu-baseline"], "trace_steps": 10, "pmc_steps": None,
+                  "pmc": False, "mfma": False, "marker": "append_layers_kernel", "per_step": 1},
+    "budget": {"args": ["--workload", "budget", "--no-cpu-baseline"], "trace_steps": 10, "pmc_steps": None,
+               "pmc": False, "mfma": False, "marker": "append_kernel", "per_step": 24},
 }
 
 
@@ -97,15 +105,23 @@ def last(values: list, n) -> list:
     return values if n is None else values[-n:]
 
 
-def kernel_times(d: str, n) -> dict:
-    """Per kernel name: mean and min/max duration (us) over its last n dispatches, from the kernel trace."""
+def kernel_times(d: str, n, marker=None, per_step=1) -> dict:
+    """Per kernel name: mean and min/max duration (us) over its last n dispatches, from the kernel trace; with a
+    marker kernel, over every dispatch that starts at or after the marker's (n * per_step)-th last dispatch."""
     by = {}
     for r in read_csv(d, "kernel_trace.csv"):
         by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    t_from = None
+    if marker:
+        starts = sorted(s for k, v in by.items() if marker in k for s, _ in v)
+        t_from = starts[-n * per_step] if len(starts) >= n * per_step else starts[0]
     out = {}
     for k, v in by.items():
         v.sort()
-        dur = [(e - s) / 1e3 for s, e in last(v, n)]
+        sel = [x for x in v if x[0] >= t_from] if t_from is not None else last(v, n)
+        if not sel:
+            continue
+        dur = [(e - s) / 1e3 for s, e in sel]
         out[k] = {"dispatches": len(v), "used": len(dur), "avg_us": sum(dur) / len(dur), "min_us": min(dur),
                   "max_us": max(dur)}
     return out
@@ -133,7 +149,7 @@ def profile(workload: str, out_dir: str, parse_only: bool = False) -> dict:
     targs = base + steps(w["trace_steps"])
     t = run_pass(f"{workload}_trace", out_dir, ["--kernel-trace", "--stats"], targs, 600, parse_only)
     commands.append("rocprofv3 --kernel-trace --stats -- python3 bench.py " + " ".join(targs))
-    times = kernel_times(t, w["trace_steps"])
+    times = kernel_times(t, w["trace_steps"], w.get("marker"), w.get("per_step", 1))
     f, wr, m, calib = {}, {}, {}, None
     n = w["pmc_steps"]
     if w["pmc"]:
@@ -170,7 +186,8 @@ def profile(workload: str, out_dir: str, parse_only: bool = False) -> dict:
             e["mfma_flops_bf16"] = None if mops is None else mops * 512
         kernels[k] = e
     return {"workload": workload, "source_sha256_16": source_hashes(), "commands": commands,
-            "dispatches_used": "last %s per kernel" % (w["trace_steps"] or "all") if not w["pmc"] else
+            "dispatches_used": ("every dispatch of the last %d frames" % w["trace_steps"]) if w.get("marker") else
+            "last %s per kernel" % (w["trace_steps"] or "all") if not w["pmc"] else
             "last %s per kernel (trace), last %s (counters)" % (w["trace_steps"], n),
             "calibration": calib, "counters": "not collected" if not w["pmc"] else "FETCH_SIZE, WRITE_SIZE"
             + (", MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16" if w["mfma"] else ""), "kernels": kernels}
