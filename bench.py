@@ -258,8 +258,49 @@ def run_clces(args):
         "data": "synthetic (seeded chi-square raw scores, iid N(0,1) K/V)",
         "config": {"workload": w["name"], "layers": L, "tokens": N, "keep": K, "window": w["clces_window"]},
         "p90_us": times[int(0.9 * (L - 1))] * 1e6, "moved_tokens_per_layer": moved / L,
-        "compaction_bytes_per_layer": bytes_per_layer, "cpu_baseline": cpu,
+        "compaction_bytes_per_layer": bytes_per_layer,
+        "rooflines_recorded": clces_rooflines(N, w["clces_window"], bytes_per_layer), "cpu_baseline": cpu,
     }), flush=True)
+
+
+CLCES_SOURCE = os.path.join(ROOT, "bounded_kv_cache_stream_amd", "csrc", "clces.hip")
+CLCES_KERNELS = os.path.join(ROOT, "profiles", "kernels_clces.json")  # written by profile_bench.py
+
+
+def clces_rooflines(N, W, compaction_bytes):
+    """HBM position of the scoring kernels and of the compaction, from the committed rocprofv3 record of this
+    workload (per call: every kernel's mean time x its launches per call), if clces.hip still hashes as
+    recorded; else None.  Algorithmic bytes of the scoring per call (all window layers ranked):
+    gather 12 B per key and layer + 4 B per token (raw score, id, order key; the current score), four radix
+    passes of 20 B per key and layer (counts read, key and value read and written), fuse 4 B per rank + 12 B
+    per token, two select passes and mark and index 8 B per token each: N x (96 W + 48) bytes."""
+    try:
+        with open(CLCES_KERNELS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16", {}).get("clces.hip") != source_hash(CLCES_SOURCE):
+        return None
+    ks = rec.get("kernels", {})
+    calls = next((e["used"] for k, e in ks.items() if k.startswith("prep_kernel")), None)
+    if not calls:
+        return None
+    score_us, compact_us = 0.0, 0.0
+    for k, e in ks.items():
+        per_call = e["avg_us"] * e["used"] / calls
+        if "compact_kernel" in k:
+            compact_us += per_call
+        elif any(k.startswith(n) for n in ("prep_kernel", "gather_kernel", "rank_hist_kernel", "rank_scatter_kernel",
+                                             "fuse_kernel", "select_pass_kernel", "select_finish_kernel",
+                                             "mark_kernel", "index_kernel")):
+            score_us += per_call
+    score_bytes = N * (96 * W + 48)
+    out = {"source": os.path.relpath(CLCES_KERNELS, ROOT)}
+    for name, by, us in (("scoring", score_bytes, score_us), ("compaction", compaction_bytes, compact_us)):
+        gbs = by / (us * 1e-6) / 1e9 if us else None
+        out[name] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS if gbs else None, "bytes_per_call": by, "kernels_us_per_call": us}
+    return out
 
 
 def clces_cpu_baseline(scores, T, F, K, w):
