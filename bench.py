@@ -9,9 +9,12 @@ frame by frame); every later frame is a steady-state step:
     append(frame) -> evict(oldest) -> attend(1004 queries over 72,288 cached tokens)
 
 Untimed: the fill and ``--warmup`` steps.  Timed: exactly ``--steps`` steps,
-bracketed by device synchronisation; the inputs of every timed frame are
-generated into HBM before the clock starts.  With the defaults the stream is
-200 frames long (72 + 8 + 120).
+bracketed by device synchronisation, with nothing recorded between the calls;
+the inputs of every timed frame are generated into HBM before the clock
+starts.  Then ``--steps`` more steps with HIP events around every call and
+its attention kernel give the per-call split (an event record costs the GPU a
+few microseconds, so those steps are not the timed ones).  With the defaults
+the stream is 322 frames long (72 + 10 + 2 x 120).
 
 Printed: one JSON line (metric frames/s per layer) with the attention kernel's
 roofline position (MFMA-bound; algorithmic FLOP = 4*H*D*n_q*N per call) and
@@ -440,7 +443,8 @@ def run_budget(args):
     """The 24-layer token-budget stack: per frame and layer append -> attend -> score_and_compact.
 
     Frames 0..warmup-1 fill the cache (the budget of 128,512 tokens is reached at frame 128); the next
-    `steps` frames are timed, with HIP events around each call for the per-kernel split.  K/V/Q come
+    `steps` frames are timed with nothing recorded between the calls, and `steps` more carry HIP events
+    around each call for the per-call split.  K/V/Q come
     from a ring of 8 AR(1) frames per layer in HBM; the raw-score table covers every token id."""
     import numpy as np
     import torch
@@ -453,7 +457,7 @@ def run_budget(args):
     w = synth.WORKLOADS[4]
     T, H, D, L, B = w["tokens"], w["heads"], w["head_dim"], w["layers"], w["budget"]
     warm = max(args.warmup, 140)
-    F = warm + args.steps
+    F = warm + 2 * args.steps  # the timed frames, then as many with events for the per-call split
     cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=0,
                          keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16,
                          max_window=w["clces_window"])
@@ -497,10 +501,13 @@ def run_budget(args):
     torch.cuda.synchronize()
     n_tok = cache.info(0)["tokens"]
     wall0 = time.perf_counter()
-    for t in range(warm, F):
-        frame(t, True)
+    for t in range(warm, warm + args.steps):
+        frame(t, False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    for t in range(warm + args.steps, F):
+        frame(t, True)
+    torch.cuda.synchronize()
     split = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3 for name, pairs in ev.items()}
     attended = n_tok + T
     flops = 4.0 * H * D * T * attended
@@ -529,7 +536,8 @@ def run_diversity(args):
 
     Frame 0 is the anchor (scale_frames = 1).  The total budget is layers x heads x per_head tokens; the
     untimed frames run until every layer has pruned at least 8 times.  K/V/Q come from a ring of 8 AR(1)
-    frames per layer in HBM.  HIP events bracket each phase; the batched scoring and prune each wait once
+    frames per layer in HBM.  The `steps` timed frames record nothing between the phases; `steps` more
+    frames carry HIP events around each phase for the split.  The batched scoring and prune each wait once
     for all layers (they read back the means, the new lengths and the error flags); the prune reuses the
     keys of the scoring."""
     import numpy as np
@@ -544,7 +552,7 @@ def run_diversity(args):
     T, H, D = synth.TOKENS_PER_FRAME, 16, 64
     total = L * H * per_head
     warm = max(args.warmup, 2 * ((per_head + T - 1) // T) + 9)
-    F = warm + args.steps
+    F = warm + 2 * args.steps  # the timed frames, then as many with events for the phase split
     cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=1, sliding_window=0,
                          keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16)
     cache = kv.KVCache(cfg, device=dev)
@@ -564,22 +572,24 @@ def run_diversity(args):
            "budgets": []}
 
     def frame(t, timed):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        marks[0].record(stream)
+        # timed: HIP events between the phases, for the split
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if timed else None
+        rec = (lambda i: marks[i].record(stream)) if timed else (lambda i: None)  # noqa: E731
+        rec(0)
         cache.append_layers(0, t, rings_k[t % 8], rings_v[t % 8])
-        marks[1].record(stream)
+        rec(1)
         cand[:] = kept + (T if t > 0 else 0)
         means = cache.diversity_score_layers(0, L)
-        marks[2].record(stream)
+        rec(2)
         budgets = kv.kv_layer_budgets(means, tau, total, H)
         cache.diversity_prune_layers(0, budgets, out=kept)
-        marks[3].record(stream)
+        rec(3)
         if args.merge:
             cache.merge_pages_layers(0, L)
-        marks[4].record(stream)
+        rec(4)
         for l in range(L):
             cache.attend(l, rings_q[t % 8][l], 1.0, out=out)
-        marks[5].record(stream)
+        rec(5)
         if timed:
             log["append"].append((marks[0], marks[1]))
             log["score"].append((marks[1], marks[2]))
@@ -595,10 +605,13 @@ def run_diversity(args):
     torch.cuda.synchronize()
     assert min(cache.info(l)["prunes"] for l in range(L)) >= 8, "the untimed frames must reach every budget"
     wall0 = time.perf_counter()
-    for t in range(warm, F):
-        frame(t, True)
+    for t in range(warm, warm + args.steps):
+        frame(t, False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    for t in range(warm + args.steps, F):
+        frame(t, True)
+    torch.cuda.synchronize()
     split = {k: float(np.mean([a.elapsed_time(b) for a, b in log[k]])) * 1e3
              for k in ("append", "score", "prune", "merge", "attend")}
     cand_rows = float(np.mean([c.sum() for c in log["cand"]]))  # candidate rows (head x token) per frame
@@ -700,7 +713,9 @@ def main():
         cache.set_splits(args.splits)
     ar = synth.AR1Stream(1, 0, (T, H, D), device=dev)
     fill = S + Wf  # frames 0..71 fill the cache; from frame 71 on the cache holds 72 frames
-    total = fill + args.warmup + args.steps
+    # warmup, then the timed steps (no per-step events), then as many steps again with events for the
+    # per-call and kernel-only split
+    total = fill + args.warmup + 2 * args.steps
 
     # generate every frame's inputs into HBM first
     frames = [ar.next() for _ in range(total)]
@@ -744,8 +759,7 @@ def main():
     for i in range(args.warmup):
         step(fill + i)
     torch.cuda.synchronize()
-    # the library records an event pair around the attention kernel of each timed call
-    kv.kv_attend_timing(cache.handle, args.steps)
+    # timed steps: nothing recorded between the calls (an event record costs the GPU a few microseconds)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     sampler = ClockSampler() if args.sclk else None
@@ -754,12 +768,23 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(fill + args.warmup + i, ev[i])
+        step(fill + args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     sclk = sampler.stop(wall0, wall0 + wall) if sampler else None
     ms_total = t_start.elapsed_time(t_end)
+    # the split: the same number of steps again, with events around each call and (recorded by the
+    # library on the call's stream) around its attention kernel
+    kv.kv_attend_timing(cache.handle, args.steps)
+    s_start = torch.cuda.Event(enable_timing=True)
+    s_end = torch.cuda.Event(enable_timing=True)
+    s_start.record(stream)
+    for i in range(args.steps):
+        step(fill + args.warmup + args.steps + i, ev[i])
+    s_end.record(stream)
+    torch.cuda.synchronize()
+    ms_instrumented = s_start.elapsed_time(s_end)
     info = cache.info(0)
     assert info["persisted_frames"] == S + Wf and info["tokens"] == (S + Wf) * T + info["special_tokens"]
 
@@ -814,6 +839,7 @@ def main():
                      "median_call_us": attend_sorted[len(attend_sorted) // 2] * 1e3,
                      "p90_call_us": attend_sorted[int(0.9 * (len(attend_sorted) - 1))] * 1e3},
         "wall_s_timed": wall,
+        "ms_per_step_instrumented": ms_instrumented / args.steps,
     }
     rc = None if sp else recorded_counters(H, args.splits)
     if rc is not None:
@@ -829,7 +855,7 @@ def main():
             result["roofline"]["peak_at_measured_sclk"] = clk_peak
             result["roofline"]["frac_at_measured_sclk"] = achieved / clk_peak
     if not args.no_cpu_baseline:
-        last = fill + args.warmup + args.steps - 1
+        last = fill + args.warmup + 2 * args.steps - 1
         attended = list(range(S)) + list(range(last - Wf + 1, last + 1))
         frames_kv = {f: (frames[f][1].float().cpu().numpy(), frames[f][2].float().cpu().numpy()) for f in attended}
         result["cpu_baseline"] = cpu_baseline(frames_kv, frames[last][0].float().cpu().numpy(), attended)
