@@ -92,6 +92,39 @@ def test_clces_small_edge_cases():
     assert list(zip(ids, fr, lens)) == b.page_table()
 
 
+@pytest.mark.parametrize("pattern", ["equal", "two_values"])
+def test_clces_ties_beyond_the_select_list(pattern):
+    # more keys tie at the threshold than the select's final workgroup lists (4096), so its remaining
+    # passes scan every key.  equal: every raw score 1.0, every s_hat equal, the first K in candidate order
+    # stay (no row moves).  two_values: odd slots 2.0, even slots 1.0: every odd slot stays and the first
+    # even slots in candidate order fill the rest, so kept odd rows move into the dropped even slots
+    torch = torch_cuda()
+    T, H, F = 1004, 2, 10
+    cache = kv.KVCache(_cfg(1, T, F + 1, H=H), device="cuda")
+    host = {}
+    _fill(cache, 0, F, T, H, 96, host)
+    N = F * T
+    if pattern == "equal":
+        scores = np.ones((N, 1), dtype=np.float32)
+        K = 3001
+    else:
+        scores = np.where(np.arange(N) % 2 == 1, 2.0, 1.0).astype(np.float32)[:, None]
+        K = N // 2 + 1500
+    table = torch.from_numpy(scores).cuda()
+    keep = torch.empty(K, dtype=torch.int32, device="cuda")
+    assert cache.score_and_compact(0, table, 5, 0.5, K, keep_ids=keep) == K
+    b = budget.BudgetCache(0, T, K, F + 1)
+    for t in range(F):
+        b.append(t)
+    b.score_and_compact(scores)
+    assert keep.cpu().numpy().tolist() == b.last["keep_ids"].tolist()
+    ids, lens, fr = cache.page_table(0)
+    assert list(zip(ids, fr, lens)) == b.page_table()
+    for pid, f, idv in b.table:
+        sl = torch.from_numpy(idv - f * T)
+        _page_bytes_equal(cache, 0, pid, len(idv), host[f][0][sl], host[f][1][sl], idv)
+
+
 def test_clces_output_buffers_too_small_are_refused():
     # the step writes keep_count ids and n_window x N ranks into caller buffers whose sizes the C ABI
     # cannot see: the binding refuses smaller ones before any device work, and nothing changes

@@ -257,6 +257,24 @@ def test_diversity_edge_cases():
     assert e.value.status == kv.KV_ERR_SHAPE
 
 
+def test_diversity_select_with_more_ties_than_the_lds_list():
+    # head 0: every key zero, so every score ties (0) at all 64 bits and more keys match each fixed prefix
+    # (8192) than the select's LDS list holds: every pass scans the key planes.  Head 1: iid keys (the list
+    # path).  The first K candidates of head 0 stay, in candidate order
+    torch = torch_cuda()
+    T, H, F = 1024, 2, 9
+    cache = kv.KVCache(_cfg(T, F + 1, H, kv.KV_BF16), device="cuda")
+    s = Stream(cache, T, H, F + 1, wid=95)
+    for t in range(F):
+        _, k, v = synth.iid_frame(95, 0, t, (T, H, 64), device="cuda", dtype=torch.float32)
+        k[:, 0, :] = 0.0
+        s.append(t, k.to(torch.bfloat16).contiguous(), v.to(torch.bfloat16).contiguous())
+    assert cache.diversity_prune(0, 5000) == [5000, 5000]
+    s.prune(5000)
+    s.check_pages("ties beyond the LDS list")
+    assert [n[0] for n in cache.head_lengths(0)] == [T, T, T, T, T, 5000 - 4 * T, 0, 0, 0]
+
+
 @pytest.mark.parametrize("dname", ["bf16", "fp32"])
 def test_diversity_stream_every_frame(dname):
     # per frame: append -> attend over the per-head pages -> prune to a fixed
