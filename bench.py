@@ -273,10 +273,14 @@ CLCES_KERNELS = os.path.join(ROOT, "profiles", "kernels_clces.json")  # written 
 def clces_rooflines(N, W, compaction_bytes):
     """HBM position of the scoring kernels and of the compaction, from the committed rocprofv3 record of this
     workload (per call: every kernel's mean time x its launches per call), if clces.hip still hashes as
-    recorded; else None.  Algorithmic bytes of the scoring per call (all window layers ranked):
-    gather 12 B per key and layer + 4 B per token (raw score, id, order key; the current score), four radix
-    passes of 20 B per key and layer (counts read, key and value read and written), fuse 4 B per rank + 12 B
-    per token, two select passes and mark and index 8 B per token each: N x (96 W + 48) bytes."""
+    recorded; else None.  Algorithmic bytes of the scoring per call (all window layers ranked): gather 12 B
+    per key and layer + 4 B per token (raw score, id, order key; the current score), fuse 12 B per token, two
+    select passes and mark and index 8 B per token each (48 B per token in all), and per key and layer the
+    rank method the record shows: block sort + counts (sort: key read, sorted key, index and block rank
+    written, 16 B; counts: sorted key and index read once, G = min(8, blocks) count slices written, 8 + 4 G B;
+    fuse: 1 + G slices read and the rank written, 4 G + 8 B), N x ((44 + 8 G) W + 48) bytes; or four radix
+    passes of 20 B (counts read, key and value read and written) and the rank read by fuse, 4 B,
+    N x (96 W + 48) bytes."""
     try:
         with open(CLCES_KERNELS) as f:
             rec = json.load(f)
@@ -294,10 +298,15 @@ def clces_rooflines(N, W, compaction_bytes):
         if "compact_kernel" in k:
             compact_us += per_call
         elif any(k.startswith(n) for n in ("prep_kernel", "gather_kernel", "rank_hist_kernel", "rank_scatter_kernel",
-                                             "fuse_kernel", "select_pass_kernel", "select_finish_kernel",
-                                             "mark_kernel", "index_kernel")):
+                                             "rank_sort_kernel", "rank_count_kernel", "fuse_kernel",
+                                             "select_pass_kernel", "select_finish_kernel", "mark_kernel",
+                                             "index_kernel")):
             score_us += per_call
-    score_bytes = N * (96 * W + 48)
+    if any(k.startswith("rank_count_kernel") for k in ks):
+        G = min(8, (N + 2047) // 2048)
+        score_bytes = N * ((44 + 8 * G) * W + 48)
+    else:
+        score_bytes = N * (96 * W + 48)
     out = {"source": os.path.relpath(CLCES_KERNELS, ROOT)}
     for name, by, us in (("scoring", score_bytes, score_us), ("compaction", compaction_bytes, compact_us)):
         gbs = by / (us * 1e-6) / 1e9 if us else None

@@ -12,26 +12,34 @@ namespace kvs {
 constexpr int32_t kClcesErrNan = 1;    // a raw score is NaN or negative
 constexpr int32_t kClcesErrRow = 2;    // a token id is outside the score table
 constexpr int32_t kClcesErrCount = 4;  // a page's kept count disagrees with its planned length
-constexpr int32_t kRankTile = 2048;    // keys per radix-rank workgroup
+constexpr int32_t kRankTile = 2048;    // keys per rank block (sorted by one workgroup)
+constexpr int32_t kRankGroups = 8;     // most groups of blocks a key is counted against
+constexpr int32_t kRankParts = 1 + kRankGroups;  // count slices per ranked segment
+// Largest segments x blocks^2 ranked by block sort + counts (their search work
+// grows as N x blocks); beyond it the radix passes, whose cost is nearly flat
+// in N, are faster.
+constexpr int64_t kSortCountMax = 12000;
 constexpr int32_t kMaxPageTokensScored = 8192;
 constexpr int kMaxWindow = 8;          // largest CLCES layer window
 constexpr int kSelBits = 11;           // bits of the select digits (the last pass takes the 9 left)
 constexpr int kSelPasses = 6;
 
-// Rank arrays of one step: per window slot (rank in) or per ranked segment
-// (rank out), int32 [N] each.
+// Ranks of one step's window slots, int32 [N] each: a slot ranked in an
+// earlier step reads w[slot]; a slot ranked in this step has n_part count
+// slices of N at part[slot] (stride N) whose sum is its rank, stored at
+// dst[slot] for later steps.
 struct RankIn {
   const int32_t* w[kMaxWindow];
-};
-struct RankOut {
-  int32_t* seg[kMaxWindow];
+  const int32_t* part[kMaxWindow];
+  int32_t* dst[kMaxWindow];
+  int32_t n_part;
 };
 
 // Byte offsets of the CLCES buffers inside its workspace region.
 struct ClcesSizes {
   int64_t n_max;
   int32_t p_max, w_max;
-  size_t keys_a, keys_b, vals_a, vals_b, blk_cnt, scur, shat, sel_hist, sel_state, list, list_cnt, entries, counts,
+  size_t keys, keys_b, vals_a, vals_b, blk_cnt, sorted, sorted_idx, part, scur, shat, sel_hist, sel_state, list, list_cnt, entries, counts,
       move_src, move_dst, n_moves, flag, total;
 };
 
@@ -58,16 +66,23 @@ struct ClcesArgs {
   int32_t* rank_dst[kMaxWindow];
   uint8_t rank_new[kMaxWindow];
   int32_t n_rank;      // slots with rank_new set
+  bool rank_radix;     // rank by the radix passes whatever the size
   double* s_hat_out;   // optional float64 [N]
 };
 
 // Stable ascending rank of every key within each of `segments` segments of N
-// keys (keys_a: [segments][N], overwritten): 4 LSD passes of 8 bits, two
-// launches each (block digit counts into blk_cnt, then the scatter);
-// segment w's ranks go to out.seg[w] ([N]).
-hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b,
-                                uint32_t* blk_cnt, const RankOut& out, int N, int segments, const int32_t* flag,
-                                hipStream_t s);
+// keys (keys: [segments][N]) as count slices whose sum is the rank: the blocks
+// of kRankTile keys are sorted (sorted, sorted_idx: [segments][whole blocks]),
+// each key's rank within its block goes to slice 0 of part
+// ([segments][kRankParts][N]) and its counts against the other blocks to the
+// next slices.  Returns the number of slices written per segment through
+// *n_part.
+hipError_t launch_rank_sort_count(const uint32_t* keys, uint32_t* sorted, uint32_t* sorted_idx, int32_t* part, int N,
+                                  int segments, const int32_t* flag, int* n_part, hipStream_t s);
+// The same ranks by 4 LSD radix passes of 8 bits (two launches each; keys_a
+// is overwritten), written to dst[w] ([N] each).
+hipError_t launch_rank_radix(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, uint32_t* blk_cnt,
+                             int32_t* const* dst, int N, int segments, const int32_t* flag, hipStream_t s);
 
 // Enqueues the whole step (kernels only, no wait).  Its result (the
 // error flag, then the new length of each of the n_entries pages) is at

@@ -13,12 +13,13 @@
 //   gather   raw scores of every candidate at every window layer whose ranks
 //            are not reused from an earlier step (by global token id),
 //            validate them, write 32-bit order keys;
-//   rank     stable LSD radix sort of those layers' keys, 4 passes of 8 bits
-//            over blocks of 2048 keys: the digit counts of every block, then
-//            a scatter whose workgroups add the counts of the blocks before
-//            them (all loads in flight together) and rank their own keys with
-//            wave ballots; the last pass writes rank[token] directly;
-//   fuse     float64 mean, population variance, Cons and s_hat with a fixed
+//   rank     stable ranks of those layers' keys: every block of 2048 keys
+//            sorted in LDS (each key's rank within its block), then each
+//            key's count of smaller keys in the other blocks by binary search,
+//            per group of blocks (two launches); or, where segments x blocks^2
+//            is large, 4 LSD radix passes of 8 bits over the blocks (eight);
+//   fuse     the ranks as the sums of those counts (stored for later steps),
+//            float64 mean, population variance, Cons and s_hat with a fixed
 //            operation order and no contraction (bit-exact reproducible),
 //            plus the histogram of the first select digit;
 //   select   radix select of the keep_count-th largest s_hat (up to 6
@@ -126,25 +127,159 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs g) {
   g.scur[idx] = __uint_as_float(order_key(s));
 }
 
-// One stable LSD pass of 8 bits over every segment to rank (grid: blocks x
-// segments) in two launches.  Block blk of a segment holds keys
-// blk*kRankTile + j*kRankThreads + tid (item-major, so index order is (item
-// j, wave, lane)).
+// Stable rank of every key of a segment: the number of keys that are smaller,
+// or equal at a smaller index.  Split by blocks of kRankTile consecutive
+// indices, that is, for a key in block a, its rank within a plus, per other
+// block b, the count of b's keys below it (b after a) or at most it (b before
+// a).  Two launches:
+//   rank_sort_kernel   one workgroup per block: a stable LSD radix sort of the
+//                      block in LDS (4 passes of 8 bits; within each wave the
+//                      keys of equal digit are matched with ballots, giving
+//                      each key its rank among equal digits of its (item,
+//                      wave) group and each group's digit counts; a pass over
+//                      the groups in index order turns those into offsets).
+//                      It writes the block's sorted keys, the index of each,
+//                      and each key's rank within the block (count slice 0);
+//   rank_count_kernel  one workgroup per (block a, group g of blocks): the
+//                      sorted keys of group g's blocks in LDS, and the count
+//                      of each of a's keys in every block of g but a (count
+//                      slice 1 + g) by binary search.
+// The rank is the sum of the slices, taken where it is used (fuse_kernel).
+constexpr int kRankThreads = 1024;
+constexpr int kRankItems = kRankTile / kRankThreads;  // 2
+constexpr int kRankWaves = kRankThreads / 64;
+constexpr int kRankGroupsIdx = kRankItems * kRankWaves;  // (item, wave) groups of a block
+constexpr int kCountThreads = 256;
+constexpr int kCountItems = kRankTile / kCountThreads;  // 8
+constexpr int kCountChunk = 8;                           // blocks in LDS at once (64 KB)
+constexpr uint32_t kPadKey = 0xFFFFFFFFu;  // above every valid key (those have the sign bit clear)
+
+// Exclusive prefix over the 256 digits: thread d (< 256) passes digit d's
+// count and gets the counts of digits below d (threads past 255 pass 0 and
+// get nothing useful).  Every thread of the workgroup calls it.
+__device__ inline uint32_t digit_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(x, off, 64);
+    if (lane >= off) x += t;
+  }
+  if (wave < 4 && lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t add = 0;
+  for (int q = 0; q < wave && q < 4; ++q) add += wsum[q];
+  return x - v + add;
+}
+
+// sorted, sorted_idx: [segments][Ns], Ns = whole blocks (kRankTile-aligned)
+__global__ __launch_bounds__(kRankThreads) void rank_sort_kernel(const uint32_t* keys, uint32_t* sorted,
+                                                                 uint32_t* sorted_idx, int32_t* part, int N,
+                                                                 int64_t Ns, const int32_t* flag) {
+  if (*flag) return;
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t cnt[kRankGroupsIdx][256];
+  __shared__ uint32_t kbuf[kRankTile];
+  __shared__ uint16_t ibuf[kRankTile];
+  const int blk = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int start = blk * kRankTile;
+  const int n = min(kRankTile, N - start);
+  const int64_t seg = (int64_t)w * N;
+  const int64_t sseg = (int64_t)w * Ns;
+  // item j of thread tid is the key at block position j*kRankThreads + tid
+  // (index order: item, wave, lane); positions past n hold the pad key, which
+  // sorts after every valid key
+  uint32_t key[kRankItems], idx[kRankItems];
+#pragma unroll
+  for (int j = 0; j < kRankItems; ++j) {
+    const int p = j * kRankThreads + tid;
+    key[j] = p < n ? keys[seg + start + p] : kPadKey;
+    idx[j] = (uint32_t)p;
+  }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    for (int x = tid; x < kRankGroupsIdx * 256; x += kRankThreads) (&cnt[0][0])[x] = 0;
+    __syncthreads();  // counters zeroed; the previous pass's reads of kbuf and ibuf are done
+    uint32_t d[kRankItems], rnk[kRankItems];
+#pragma unroll
+    for (int j = 0; j < kRankItems; ++j) {
+      d[j] = (key[j] >> shift) & 255u;
+      unsigned long long m = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (d[j] >> bit) & 1u;
+        const unsigned long long bb = __ballot(on);
+        m &= on ? bb : ~bb;
+      }
+      rnk[j] = (uint32_t)__popcll(m & lt);
+      if (rnk[j] == 0) cnt[j * kRankWaves + wave][d[j]] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    // thread t < 256 owns digit t: its offset is the count of smaller digits,
+    // then the counts of the groups before it in index order
+    uint32_t c[kRankGroupsIdx];
+    uint32_t total = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int q = 0; q < kRankGroupsIdx; ++q) {
+        c[q] = cnt[q][tid];
+        total += c[q];
+      }
+    }
+    const uint32_t base = digit_excl_scan(tid < 256 ? total : 0u, wsum);
+    if (tid < 256) {
+      uint32_t run = base;
+#pragma unroll
+      for (int q = 0; q < kRankGroupsIdx; ++q) {
+        cnt[q][tid] = run;
+        run += c[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRankItems; ++j) {
+      const uint32_t np = cnt[j * kRankWaves + wave][d[j]] + rnk[j];
+      kbuf[np] = key[j];
+      ibuf[np] = (uint16_t)idx[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRankItems; ++j) {
+      const int p = j * kRankThreads + tid;
+      key[j] = kbuf[p];
+      idx[j] = ibuf[p];
+    }
+  }
+  // sorted position r: the pad keys are last, so r < n holds every valid key;
+  // the whole block is written, pads included
+#pragma unroll
+  for (int j = 0; j < kRankItems; ++j) {
+    const int r = j * kRankThreads + tid;
+    sorted[sseg + start + r] = key[j];
+    if (r < n) {
+      sorted_idx[sseg + start + r] = idx[j];
+      part[(int64_t)w * kRankParts * N + start + idx[j]] = r;
+    }
+  }
+}
+
+// The multi-pass alternative (taken where segments x blocks^2 grows large,
+// since the counts above cost N x blocks searches): a stable LSD radix sort of
+// the keys, 4 passes of 8 bits over the same blocks, two launches each:
 //   rank_hist_kernel     the digit counts of each block, stored as they are;
 //   rank_scatter_kernel  thread d < 256 adds digit d's counts over every block
 //                        of the segment (total) and over the blocks before
 //                        its own (before), all loads in flight together; the
 //                        keys of digit d go to (keys of smaller digits) +
 //                        (keys of digit d in earlier blocks) + (their rank in
-//                        this block).  Within the block every wave matches
-//                        the digits of each of its items with ballots, giving
-//                        each key its rank among equal digits of its (item,
-//                        wave) group and each group's digit counts; a pass over
-//                        the groups in index order turns those into offsets.
-constexpr int kRankThreads = 1024;
-constexpr int kRankItems = kRankTile / kRankThreads;  // 2
-constexpr int kRankWaves = kRankThreads / 64;
+//                        this block), ranked within the block by the same
+//                        ballot matching; the last pass writes each key's rank.
 constexpr int kHistThreads = 256;
+struct RankOut {
+  int32_t* seg[kMaxWindow];
+};
 
 __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(const uint32_t* keys, uint32_t* blk_cnt, int N,
                                                                  int nblk, int pass, const int32_t* flag) {
@@ -166,24 +301,6 @@ __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(const uint32_t*
   for (int j = 0; j < kPer; ++j) hist_add(cnt, d[j], blk * kRankTile + j * kHistThreads + tid < N);
   __syncthreads();
   blk_cnt[((int64_t)w * nblk + blk) * 256 + tid] = cnt[tid];
-}
-
-// Exclusive prefix over the 256 digits: thread d (< 256) passes digit d's
-// count and gets the counts of digits below d (threads past 255 pass 0 and
-// get nothing useful).  Every thread of the workgroup calls it.
-__device__ inline uint32_t digit_excl_scan(uint32_t v, uint32_t* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(x, off, 64);
-    if (lane >= off) x += t;
-  }
-  if (wave < 4 && lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t add = 0;
-  for (int q = 0; q < wave && q < 4; ++q) add += wsum[q];
-  return x - v + add;
 }
 
 __global__ __launch_bounds__(kRankThreads) void rank_scatter_kernel(const uint32_t* keys_in, const uint32_t* vals_in,
@@ -289,6 +406,83 @@ __global__ __launch_bounds__(kRankThreads) void rank_scatter_kernel(const uint32
   }
 }
 
+// tab: dynamic LDS of min(largest group, kCountChunk) blocks.  Lanes take
+// consecutive sorted keys of block a (key r = j*kCountThreads + thread), so
+// the lanes of a wave follow nearly the same path down each search (broadcast
+// reads first, then neighbouring words).  Each key's count in a block is a
+// binary search over byte offsets (the step goes into the read's offset),
+// eight keys per thread in flight together.
+__global__ __launch_bounds__(kCountThreads) void rank_count_kernel(const uint32_t* sorted, const uint32_t* sorted_idx,
+                                                                   int32_t* part, int N, int64_t Ns, int nblk,
+                                                                   int groups, int chunk, const int32_t* flag) {
+  if (*flag) return;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kVec = kRankTile / 4 / kCountThreads;  // 16-byte loads per thread and block
+  extern __shared__ __attribute__((aligned(16))) uint32_t tab[];
+  const int a = blockIdx.x, g = blockIdx.y, w = blockIdx.z, tid = threadIdx.x;
+  const int b0 = (int)((int64_t)g * nblk / groups), b1 = (int)((int64_t)(g + 1) * nblk / groups);
+  const uint32_t* sseg = sorted + (int64_t)w * Ns;
+  const int start = a * kRankTile;
+  const int n = min(kRankTile, N - start);
+  uint32_t q[kCountItems];
+  int32_t c[kCountItems];
+#pragma unroll
+  for (int j = 0; j < kCountItems; ++j) {
+    q[j] = sseg[start + j * kCountThreads + tid];  // pad keys past n (their counts are not stored)
+    c[j] = 0;
+  }
+  for (int c0 = b0; c0 < b1; c0 += chunk) {
+    const int nb = min(chunk, b1 - c0);
+    if (c0 != b0) __syncthreads();  // the previous chunk's searches are done
+    // the chunk's blocks (whole, pads included): every load in flight before the first LDS write
+    const u32x4* src = reinterpret_cast<const u32x4*>(sseg + (int64_t)c0 * kRankTile);
+    u32x4* dst = reinterpret_cast<u32x4*>(tab);
+    u32x4 v[kCountChunk * kVec];
+#pragma unroll
+    for (int x = 0; x < kCountChunk * kVec; ++x)
+      if (x < nb * kVec) v[x] = src[x * kCountThreads + tid];
+#pragma unroll
+    for (int x = 0; x < kCountChunk * kVec; ++x)
+      if (x < nb * kVec) dst[x * kCountThreads + tid] = v[x];
+    __syncthreads();
+    for (int bb = 0; bb < nb; ++bb) {
+      const int b = c0 + bb;
+      if (b == a) continue;
+      // keys of an earlier block count when equal: compare against q + 1
+      // (valid keys are at most 0x7F800000, so no wrap; a pad key wraps to 0
+      // and counts nothing, which is never stored)
+      const uint32_t inc = b < a ? 1u : 0u;
+      const uint32_t base = (uint32_t)(bb * kRankTile * 4);  // byte offset of block bb in tab
+      const char* lds = reinterpret_cast<const char*>(tab);
+      const uint32_t top = *reinterpret_cast<const uint32_t*>(lds + base + 4 * (kRankTile - 1));
+      uint32_t kq[kCountItems], off[kCountItems];
+#pragma unroll
+      for (int j = 0; j < kCountItems; ++j) {
+        kq[j] = q[j] + inc;
+        off[j] = base;
+      }
+#pragma unroll
+      for (int step = kRankTile / 2; step > 0; step >>= 1)
+#pragma unroll
+        for (int j = 0; j < kCountItems; ++j) {
+          const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + off[j] + 4 * (step - 1));
+          off[j] += e < kq[j] ? 4u * step : 0u;
+        }
+      // the search alone stops at kRankTile - 1
+#pragma unroll
+      for (int j = 0; j < kCountItems; ++j)
+        c[j] += top < kq[j] ? kRankTile : (int)((off[j] & (kRankTile * 4 - 1)) >> 2);  // base: a multiple of 8 KB
+    }
+  }
+  int32_t* out = part + ((int64_t)w * kRankParts + 1 + g) * N + start;
+  const uint32_t* sidx = sorted_idx + (int64_t)w * Ns + start;
+#pragma unroll
+  for (int j = 0; j < kCountItems; ++j) {
+    const int r = j * kCountThreads + tid;
+    if (r < n) out[sidx[r]] = c[j];
+  }
+}
+
 // Bits of select digit p of a 64-bit key: 11 bits from the top for passes
 // 0-4, the low 9 bits for pass 5.
 __device__ inline int sel_shift(int p) { return p < kSelPasses - 1 ? 64 - kSelBits * (p + 1) : 0; }
@@ -321,7 +515,20 @@ __global__ __launch_bounds__(kThreads) void fuse_kernel(RankIn ranks, const floa
 #pragma unroll
     for (int w = 0; w < kMaxWindow; ++w) {
       if (w < n_win) {
-        r[w] = N > 1 ? (double)ranks.w[w][i] / denom : 0.0;
+        int32_t rk;
+        if (ranks.part[w]) {
+          // every slice load in flight together: slices past n_part read slice 0 and add nothing
+          int32_t c[kRankParts];
+#pragma unroll
+          for (int q = 0; q < kRankParts; ++q) c[q] = ranks.part[w][(int64_t)(q < ranks.n_part ? q : 0) * N + i];
+          rk = 0;
+#pragma unroll
+          for (int q = 0; q < kRankParts; ++q) rk += q < ranks.n_part ? c[q] : 0;
+          ranks.dst[w][i] = rk;
+        } else {
+          rk = ranks.w[w][i];
+        }
+        r[w] = N > 1 ? (double)rk / denom : 0.0;
         acc = acc + r[w];
       }
     }
@@ -654,11 +861,15 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
     return o;
   };
   const size_t wn = (size_t)w_max * (size_t)n_max;
-  z.keys_a = take(wn * 4);
+  z.keys = take(wn * 4);
   z.keys_b = take(wn * 4);
   z.vals_a = take(wn * 4);
   z.vals_b = take(wn * 4);
   z.blk_cnt = take((size_t)w_max * ((n_max + kRankTile - 1) / kRankTile) * 256 * 4);
+  const size_t wb = (size_t)w_max * (size_t)((n_max + kRankTile - 1) / kRankTile * kRankTile);  // whole blocks
+  z.sorted = take(wb * 4);
+  z.sorted_idx = take(wb * 4);
+  z.part = take(wn * kRankParts * 4);
   z.scur = take((size_t)n_max * 4);
   z.shat = take((size_t)n_max * 8);
   z.sel_hist = take((size_t)kSelPasses * kSelBins * 4);
@@ -675,10 +886,28 @@ ClcesSizes clces_sizes(int64_t n_max, int32_t p_max, int32_t w_max, int32_t ts_m
   return z;
 }
 
-hipError_t launch_rank_segments(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b,
-                                uint32_t* blk_cnt, const RankOut& out, int N, int segments, const int32_t* flag,
-                                hipStream_t s) {
+hipError_t launch_rank_sort_count(const uint32_t* keys, uint32_t* sorted, uint32_t* sorted_idx, int32_t* part, int N,
+                                int segments, const int32_t* flag, int* n_part, hipStream_t s) {
   const int nblk = (N + kRankTile - 1) / kRankTile;
+  const int64_t Ns = (int64_t)nblk * kRankTile;
+  const int groups = nblk > 1 ? std::min(nblk, (int)kRankGroups) : 0;
+  rank_sort_kernel<<<dim3((unsigned)nblk, (unsigned)segments), dim3(kRankThreads), 0, s>>>(keys, sorted, sorted_idx,
+                                                                                          part, N, Ns, flag);
+  if (groups > 0) {
+    const int chunk = std::min((nblk + groups - 1) / groups, kCountChunk);  // the largest group, or a chunk of it
+    rank_count_kernel<<<dim3((unsigned)nblk, (unsigned)groups, (unsigned)segments), dim3(kCountThreads),
+                        (size_t)chunk * kRankTile * sizeof(uint32_t), s>>>(sorted, sorted_idx, part, N, Ns, nblk,
+                                                                           groups, chunk, flag);
+  }
+  *n_part = 1 + groups;
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_radix(uint32_t* keys_a, uint32_t* keys_b, uint32_t* vals_a, uint32_t* vals_b, uint32_t* blk_cnt,
+                             int32_t* const* dst, int N, int segments, const int32_t* flag, hipStream_t s) {
+  const int nblk = (N + kRankTile - 1) / kRankTile;
+  RankOut out{};
+  for (int w = 0; w < segments; ++w) out.seg[w] = dst[w];
   uint32_t* kin = keys_a;
   uint32_t* kout = keys_b;
   uint32_t* vin = nullptr;
@@ -698,10 +927,8 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
   const ClcesSizes& z = a.sizes;
   char* ws = a.ws;
   auto* entries = reinterpret_cast<DevEntry*>(ws + z.entries);
-  auto* keys_a = reinterpret_cast<uint32_t*>(ws + z.keys_a);
-  auto* keys_b = reinterpret_cast<uint32_t*>(ws + z.keys_b);
-  auto* vals_a = reinterpret_cast<uint32_t*>(ws + z.vals_a);
-  auto* vals_b = reinterpret_cast<uint32_t*>(ws + z.vals_b);
+  auto* keys = reinterpret_cast<uint32_t*>(ws + z.keys);
+  auto* part = reinterpret_cast<int32_t*>(ws + z.part);
   auto* scur = reinterpret_cast<float*>(ws + z.scur);
   auto* shat = reinterpret_cast<unsigned long long*>(ws + z.shat);
   auto* sel_hist = reinterpret_cast<uint32_t*>(ws + z.sel_hist);
@@ -739,26 +966,43 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
   g.cols = a.score_cols;
   g.col_cur = a.first_layer + W - 1;
   g.N = N;
-  g.keys = keys_a;
+  g.keys = keys;
   g.scur = scur;
   g.flag = flag;
-  RankOut ro{};
+  // Window slot w ranked in this step is segment nseg of the gathered keys.
+  // Block sort + counts: its count slices sum to its rank in fuse, which
+  // stores it at rank_dst[w]; radix passes: the rank goes to rank_dst[w].
+  const int64_t nblk_rank = (N + kRankTile - 1) / kRankTile;
+  const bool radix = a.rank_radix || (int64_t)a.n_rank * nblk_rank * nblk_rank > kSortCountMax;
+  RankIn ri{};
+  int32_t* dst[kMaxWindow] = {};
   int nseg = 0;
-  for (int w = 0; w < W; ++w)
+  for (int w = 0; w < W; ++w) {
     if (a.rank_new[w]) {
       g.seg_col[nseg] = a.first_layer + w;
-      ro.seg[nseg] = a.rank_dst[w];
+      dst[nseg] = a.rank_dst[w];
+      if (!radix) {
+        ri.part[w] = part + (int64_t)nseg * kRankParts * N;
+        ri.dst[w] = a.rank_dst[w];
+      } else {
+        ri.w[w] = a.rank_dst[w];
+      }
       ++nseg;
+    } else {
+      ri.w[w] = a.rank_dst[w];
     }
+  }
   g.n_seg = nseg;
   gather_kernel<<<dim3((unsigned)P, (unsigned)((a.geom.ts + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(g);
   if (nseg > 0) {
-    e = launch_rank_segments(keys_a, keys_b, vals_a, vals_b, reinterpret_cast<uint32_t*>(ws + z.blk_cnt), ro, N, nseg,
-                             flag, s);
+    e = radix ? launch_rank_radix(keys, reinterpret_cast<uint32_t*>(ws + z.keys_b),
+                                  reinterpret_cast<uint32_t*>(ws + z.vals_a), reinterpret_cast<uint32_t*>(ws + z.vals_b),
+                                  reinterpret_cast<uint32_t*>(ws + z.blk_cnt), dst, N, nseg, flag, s)
+              : launch_rank_sort_count(keys, reinterpret_cast<uint32_t*>(ws + z.sorted),
+                                       reinterpret_cast<uint32_t*>(ws + z.sorted_idx), part, N, nseg, flag,
+                                       &ri.n_part, s);
     if (e != hipSuccess) return e;
   }
-  RankIn ri{};
-  for (int w = 0; w < W; ++w) ri.w[w] = a.rank_dst[w];
   fuse_kernel<<<dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
       ri, scur, shat, a.s_hat_out, N, W, a.lambda, std::sqrt(12.0), sel_hist, sel_state, a.keep, flag);
   const int nblk = (N + kSelTile - 1) / kSelTile;

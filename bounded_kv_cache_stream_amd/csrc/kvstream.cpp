@@ -1049,7 +1049,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
     return fail(KV_ERR_ARG, "window %d out of 1..max_window (%d)", params->window, pool->cfg.max_window);
   if (!std::isfinite(params->lambda) || params->lambda < 0) return fail(KV_ERR_ARG, "lambda must be finite and >= 0");
   if (params->keep_count < 0) return fail(KV_ERR_ARG, "keep_count must be >= 0");
-  if (params->flags & ~(KV_CLCES_DEFER | KV_CLCES_REUSE_RANKS))
+  if (params->flags & ~(KV_CLCES_DEFER | KV_CLCES_REUSE_RANKS | KV_CLCES_RANK_RADIX))
     return fail(KV_ERR_ARG, "unknown CLCES flags 0x%x", params->flags);
   auto& L = pool->layers[(size_t)layer];
   if (!L.same_tokens()) return fail(KV_ERR_STATE, "layer %d: heads hold different tokens (diversity-pruned)", layer);
@@ -1094,6 +1094,7 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   a.first_layer = layer - n_win + 1;
   a.n_window = n_win;
   a.lambda = params->lambda;
+  a.rank_radix = (params->flags & KV_CLCES_RANK_RADIX) != 0;
   a.keep = params->keep_count;
   a.keep_ids_out = keep_ids_out_dev;
   a.s_hat_out = params->s_hat_out;

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("KVSTREAM_LIB") or os.path.join(_HERE, "libkvstream.so
 KV_OK, KV_ERR_ARG, KV_ERR_SHAPE, KV_ERR_NO_PAGES, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_NAN = 0, -1, -2, -3, -4, -5, -6
 KV_CLCES_DEFER = 1
 KV_CLCES_REUSE_RANKS = 2
+KV_CLCES_RANK_RADIX = 4
 KV_BF16, KV_FP32 = 0, 1
 KV_TRANSIENT = 1
 
@@ -188,8 +189,10 @@ def kv_append_attend(pool, layer, frame_idx, k_ptr, v_ptr, n_tokens, flags, q_pt
 
 
 def score_and_compact(pool, layer, table_ptr, score_rows, window, lam, keep_count, keep_ids_ptr=None,
-                      ranks_ptr=None, stream=None, defer=False, reuse_ranks=False, s_hat_ptr=None) -> int:
-    flags = (KV_CLCES_DEFER if defer else 0) | (KV_CLCES_REUSE_RANKS if reuse_ranks else 0)
+                      ranks_ptr=None, stream=None, defer=False, reuse_ranks=False, s_hat_ptr=None,
+                      rank_radix=False) -> int:
+    flags = (KV_CLCES_DEFER if defer else 0) | (KV_CLCES_REUSE_RANKS if reuse_ranks else 0) \
+        | (KV_CLCES_RANK_RADIX if rank_radix else 0)
     prm = kv_clces_params(window, flags, lam, keep_count, s_hat_ptr)
     n = ctypes.c_int64()
     _check(lib().score_and_compact(pool, layer, table_ptr, score_rows, ctypes.byref(prm), keep_ids_ptr, ranks_ptr,
@@ -409,7 +412,7 @@ class KVCache:
         return out, n
 
     def score_and_compact(self, layer, score_table, window, lam, keep_count, keep_ids=None, ranks=None,
-                          defer=False, reuse_ranks=False, s_hat=None) -> int:
+                          defer=False, reuse_ranks=False, s_hat=None, rank_radix=False) -> int:
         torch = self.torch
         if score_table.dtype != torch.float32 or not score_table.is_contiguous() or score_table.dim() != 2 \
                 or score_table.shape[1] != self.cfg.num_layers:
@@ -436,7 +439,7 @@ class KVCache:
                                  None if keep_ids is None else ctypes.c_void_p(keep_ids.data_ptr()),
                                  None if ranks is None else ctypes.c_void_p(ranks.data_ptr()), self._stream(),
                                  defer, reuse_ranks,
-                                 None if s_hat is None else ctypes.c_void_p(s_hat.data_ptr()))
+                                 None if s_hat is None else ctypes.c_void_p(s_hat.data_ptr()), rank_radix)
 
     def sync(self, layer=-1) -> None:
         """Complete deferred score_and_compact steps (layer -1: every layer); raises their error, if any."""

@@ -78,13 +78,18 @@ typedef struct {
 } kv_pool_config;
 
 /* score_and_compact flags: return once the step is enqueued; reuse the ranks
- * of window layers from earlier steps over the same candidates (see there). */
+ * of window layers from earlier steps over the same candidates (see there);
+ * rank by the multi-pass radix sort whatever the size (the library otherwise
+ * picks the faster of its two rank methods by size; both give the same
+ * ranks). */
 #define KV_CLCES_DEFER 1u
 #define KV_CLCES_REUSE_RANKS 2u
+#define KV_CLCES_RANK_RADIX 4u
 
 /* Parameters of one CLCES step ([SCV] 2.1.1-2.1.3): window W = 5 layers,
  * lambda = 0.5 on the pages; keep_count = tokens kept (the budget); flags =
- * a combination of KV_CLCES_DEFER and KV_CLCES_REUSE_RANKS; s_hat_out:
+ * a combination of KV_CLCES_DEFER, KV_CLCES_REUSE_RANKS and
+ * KV_CLCES_RANK_RADIX; s_hat_out:
  * optional device float64 [N], the fused score of every candidate in
  * candidate order (NULL: not written). */
 typedef struct {

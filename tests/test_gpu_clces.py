@@ -92,12 +92,14 @@ def test_clces_small_edge_cases():
     assert list(zip(ids, fr, lens)) == b.page_table()
 
 
+@pytest.mark.parametrize("radix", [False, True], ids=["sort_count", "radix"])
 @pytest.mark.parametrize("pattern", ["equal", "two_values"])
-def test_clces_ties_beyond_the_select_list(pattern):
+def test_clces_ties_beyond_the_select_list(pattern, radix):
     # more keys tie at the threshold than the select's final workgroup lists (4096), so its remaining
     # passes scan every key.  equal: every raw score 1.0, every s_hat equal, the first K in candidate order
     # stay (no row moves).  two_values: odd slots 2.0, even slots 1.0: every odd slot stays and the first
-    # even slots in candidate order fill the rest, so kept odd rows move into the dropped even slots
+    # even slots in candidate order fill the rest, so kept odd rows move into the dropped even slots.
+    # The ranks tie across all 5 rank blocks of 2048 keys, by either rank method
     torch = torch_cuda()
     T, H, F = 1004, 2, 10
     cache = kv.KVCache(_cfg(1, T, F + 1, H=H), device="cuda")
@@ -112,11 +114,13 @@ def test_clces_ties_beyond_the_select_list(pattern):
         K = N // 2 + 1500
     table = torch.from_numpy(scores).cuda()
     keep = torch.empty(K, dtype=torch.int32, device="cuda")
-    assert cache.score_and_compact(0, table, 5, 0.5, K, keep_ids=keep) == K
+    ranks = torch.empty((1, N), dtype=torch.int32, device="cuda")
+    assert cache.score_and_compact(0, table, 5, 0.5, K, keep_ids=keep, ranks=ranks, rank_radix=radix) == K
     b = budget.BudgetCache(0, T, K, F + 1)
     for t in range(F):
         b.append(t)
     b.score_and_compact(scores)
+    assert np.array_equal(ranks.cpu().numpy(), b.last["ranks"])
     assert keep.cpu().numpy().tolist() == b.last["keep_ids"].tolist()
     ids, lens, fr = cache.page_table(0)
     assert list(zip(ids, fr, lens)) == b.page_table()
@@ -219,13 +223,15 @@ def test_budget_stream_small_ragged_pages(merge):
         _page_bytes_equal(cache, l, pid, len(idv), krows, vrows, idv)
 
 
-@pytest.mark.parametrize("reuse", [False, True])
-def test_clces_24_layers_72288_tokens_keep_half(reuse):
+@pytest.mark.parametrize("mode", ["all", "reuse", "radix"])
+def test_clces_24_layers_72288_tokens_keep_half(mode):
     # every layer's step against the oracle: ranks of every window layer, the fused score s_hat of every
     # candidate (float64, bit for bit), the kept ids, page tables and sampled page bytes.  With reuse, each
     # step ranks only its own layer and takes the other window layers' ranks from the earlier steps (every
-    # layer holds the same 72 whole frames), with the same results
+    # layer holds the same 72 whole frames), with the same results.  all / reuse: the rank method the
+    # library picks by size (block sort + counts here); radix: the radix passes
     torch = torch_cuda()
+    reuse, radix = mode == "reuse", mode == "radix"
     w = synth.WORKLOADS[3]
     T, H, L, F, K = w["tokens"], w["heads"], w["layers"], w["cache_frames"], w["keep"]
     N = F * T
@@ -243,7 +249,7 @@ def test_clces_24_layers_72288_tokens_keep_half(reuse):
         keep = torch.empty(K, dtype=torch.int32, device="cuda")
         s_hat = torch.empty(N, dtype=torch.float64, device="cuda")
         assert cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep, ranks=ranks,
-                                       s_hat=s_hat, reuse_ranks=reuse) == K
+                                       s_hat=s_hat, reuse_ranks=reuse, rank_radix=radix) == K
         b = budget.BudgetCache(l, T, K, F, window=w["clces_window"], lam=w["lam"])
         for t in range(F):
             b.append(t)
@@ -260,7 +266,7 @@ def test_clces_24_layers_72288_tokens_keep_half(reuse):
             for pid, f, idv in b.table:
                 sl = torch.from_numpy(idv - f * T)
                 _page_bytes_equal(cache, l, pid, len(idv), host[l][f][0][sl], host[l][f][1][sl], idv)
-    say(f"CLCES 24 layers (rank reuse {reuse}): ranks, s_hat, {K} kept ids and page lengths bit-exact; "
+    say(f"CLCES 24 layers ({mode}): ranks, s_hat, {K} kept ids and page lengths bit-exact; "
         f"gap between the {K}th and {K + 1}th s_hat: min {min(gaps):.3e}, median {np.median(gaps):.3e}")
 
 

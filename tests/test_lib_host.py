@@ -374,7 +374,7 @@ def test_clces_flags_and_sync_on_a_metadata_pool():
     c = _meta_pool(0, 0, 1, 5)
     for t in range(3):
         c.append(0, t, None, None)
-    prm = kv.kv_clces_params(5, 4, 0.5, 10)
+    prm = kv.kv_clces_params(5, 8, 0.5, 10)
     n = ctypes.c_int64()
     st = kv.lib().score_and_compact(c.handle, 0, None, 0, ctypes.byref(prm), None, None, ctypes.byref(n), None)
     assert st == kv.KV_ERR_ARG and "flags" in kv.kv_last_error()
