@@ -76,6 +76,9 @@ def parse():
                     help="stream/long/budget workloads: one kv_append_attend call per frame and layer (the page "
                          "write shares the "
                          "table-upload launch) instead of append, evict and attend")
+    ap.add_argument("--tiling", choices=["auto", "page", "packed"], default="auto",
+                    help="KV tiles of the bf16 attention (kv_set_attend_tiling): auto (default), 64-token tiles "
+                         "per page, or packed across page ends")
     ap.add_argument("--heads", type=int, default=0,
                     help="stream workload: heads per GPU (default 16; 2 = one GPU's share when 8 GPUs split the heads)")
     ap.add_argument("--sclk", action="store_true",
@@ -139,6 +142,9 @@ class ClockSampler:
                 "source": "rocm-smi current sclk level, read during the timed steps"}
 
 
+TILINGS = {"auto": 0, "page": 1, "packed": 2}  # KV_TILING_AUTO, KV_TILING_PAGE, KV_TILING_PACKED
+
+
 def recorded_counters(heads, splits):
     """The attention kernel's HBM bytes and MFMA utilisation per call from the committed rocprofv3 summary
     (profile_bench.py), if it was taken with this attention source at this shape (16 heads, the library's
@@ -150,7 +156,8 @@ def recorded_counters(heads, splits):
         return None
     if rec.get("source_sha256_16", {}).get("attend.hip") != source_hash(ATTEND_SOURCE) or heads != 16 or splits:
         return None
-    k = rec.get("kernels", {}).get("attend_bf16_kernel")
+    # the kernel is a template (tiles per page or packed): the stream's pages take one instantiation
+    k = next((v for n, v in rec.get("kernels", {}).items() if "attend_bf16_kernel" in n), None)
     if not k or "fetch_bytes" not in k or "write_bytes" not in k:
         return None
     return {"traffic": k["fetch_bytes"] + k["write_bytes"], "mfma_util_pct": k.get("mfma_util_pct"),
@@ -212,6 +219,7 @@ def run_clces(args):
     cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=0,
                          keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=8, max_window=5)
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     for l in range(L):
         for t in range(F):
             _, k, v = synth.iid_frame(3, l, t, (T, H, 64), device=dev, dtype=torch.bfloat16)
@@ -345,6 +353,7 @@ def run_append(args):
     cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=0, sliding_window=4,
                          keyframe_interval=1, pages_per_layer=5, max_queries=T, max_splits=4)
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     frames = [(torch.randn(L, T, H, D, device=dev).bfloat16(), torch.randn(L, T, H, D, device=dev).bfloat16())
               for _ in range(4)]
     stream = torch.cuda.current_stream(dev)
@@ -406,6 +415,7 @@ def run_long(args):
                          keyframe_interval=k, pages_per_layer=S + Wf + 1 + special_pages, max_queries=S * T,
                          max_splits=16, special_tokens=sp)
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     ar = synth.AR1Stream(2, 0, (T, H, D), device=dev)
     ring = [ar.next() for _ in range(64)]
     out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
@@ -472,6 +482,7 @@ def run_budget(args):
                          keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16,
                          max_window=w["clces_window"])
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     table = torch.from_numpy(synth.raw_scores(4, F * T, L)).to(dev)
     rings = []
     for l in range(L):
@@ -529,7 +540,7 @@ def run_budget(args):
     flops = 4.0 * H * D * T * attended
     pages = [cache.info(l)["persisted_frames"] for l in range(L)]
     ids, lens, _ = cache.page_table(L - 1)
-    tiles = sum((n + 63) // 64 for n in lens) + (T + 63) // 64
+    tiles = (sum(lens) + T + 63) // 64  # the attention packs the tokens into 64-token tiles across page ends
     print(json.dumps({
         "metric": "frames/sec of the 24-layer token-budget stack (append, attend, score_and_compact"
                   + (" deferred" if args.defer else "") + (", merge_pages" if args.merge else "")
@@ -573,6 +584,7 @@ def run_diversity(args):
     cfg = kv.make_config(num_layers=L, num_heads=H, page_tokens=T, scale_frames=1, sliding_window=0,
                          keyframe_interval=1, pages_per_layer=F, max_queries=T, max_splits=16)
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     rings_q, rings_k, rings_v = [], [], []
     ars = [synth.AR1Stream(5, l, (T, H, D), device=dev) for l in range(L)]
     for i in range(8):
@@ -637,7 +649,7 @@ def run_diversity(args):
     attn_flops = float(np.mean([4.0 * D * T * (k.sum() + L * H * T) for k in log["kept"]]))
     pages = [cache.info(l)["persisted_frames"] for l in range(L)]
     hl = np.array(cache.head_lengths(L // 2))
-    tiles = ((hl + 63) // 64).sum(axis=0)
+    tiles = (hl.sum(axis=0) + 63) // 64  # per head: tokens packed into 64-token tiles across page ends
     result = {
         "metric": f"frames/sec of the {L}-layer diversity-pruned stack (append, score, budgets, prune, "
                   + ("page merge, " if args.merge else "") + "attend)",
@@ -726,6 +738,7 @@ def main():
                          keyframe_interval=1, pages_per_layer=S + Wf + 1 + (8 if sp else 0), max_queries=S * T,
                          max_splits=64, special_tokens=sp)
     cache = kv.KVCache(cfg, device=dev)
+    cache.set_tiling(TILINGS[args.tiling])
     if args.splits:
         cache.set_splits(args.splits)
     ar = synth.AR1Stream(1, 0, (T, H, D), device=dev)

@@ -36,8 +36,12 @@
 //     raises the running max, rescales O and l and is redone.  On gfx950 VALU
 //     work does not overlap MFMA work on a SIMD, so every VALU instruction
 //     taken out of the tile loop is time saved;
-//   * the page table is walked with scalar loads (constant address space) and
-//     tile addresses are formed in SGPRs;
+//   * KV tiles per page (a page's last tile partial), or packed over each
+//     head's token sequence (its pages' tokens in table order): a tile may
+//     span page ends and only the sequence's last tile is partial, which
+//     evens out per-head tables whose heads spread equal token counts over
+//     their pages differently.  The page table is walked with scalar loads
+//     (constant address space);
 //   * the KV axis is split across workgroups (split-KV); partial (O, m, l) are
 //     merged by attend_combine.  Workgroup ids are remapped so that all query
 //     tiles of one (head, split) land on the same XCD and share its L2.
@@ -95,6 +99,9 @@ __device__ inline int xcd_remap(int bid, int nwg) {
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // two waves per SIMD: 256 VGPRs per lane for the two query blocks' accumulators
+// PACKED: tiles over each head's token sequence (a tile may span page ends),
+// else tiles per page (a page's last tile is partial).
+template <bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
   constexpr int RPP = 32;          // K/V rows staged per pass (8 threads per 128-byte row)
   constexpr int PP = BN / RPP;     // passes per tile
@@ -133,20 +140,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // The page table is read-only for the kernel's lifetime: read it through the
-  // constant address space so that the walk runs on scalar loads and SALU, and
-  // the tile's base address stays in SGPRs (each load is base + 32-bit lane offset).
+  // constant address space so that the walk over it runs on scalar loads and
+  // SALU.
   typedef const __attribute__((address_space(4))) DevEntry* ConstTable;
   const ConstTable tab = (ConstTable)(p.table + (int64_t)h * p.head_stride);
-  const int total_tiles = p.head_stride ? tab[p.n_entries].tile_start : p.total_tiles;
+  // Packed: tile t holds tokens 64t .. 64t+63 of the head's token sequence
+  // (the entries' tokens in table order) whatever pages they are in, so only
+  // the sequence's last tile is partial.  Per page: the tiles of entry e are
+  // tile_start .. tile_start + ceil(len / 64) - 1.
+  const int total_tokens = p.head_stride ? tab[p.n_entries].tok_start : p.total_tokens;
+  const int total_tiles = PACKED ? (total_tokens + BN - 1) / BN
+                                 : (p.head_stride ? tab[p.n_entries].tile_start : p.total_tiles);
   const int t_begin = (int)((int64_t)sp * total_tiles / p.splits);
   const int t_end = (int)((int64_t)(sp + 1) * total_tiles / p.splits);
 
+  // e: the entry of the next tile to load.  Packed: the entry holding token
+  // 64 t, the last entry whose tok_start is at most that token (entries before
+  // it that start at the same token are empty).  Per page: the last entry
+  // whose first tile is at most t.
   int e = 0;
   {
+    const int j = PACKED ? t_begin * BN : t_begin;
     int lo = 0, hi = p.n_entries - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (tab[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
+      if ((PACKED ? tab[mid].tok_start : tab[mid].tile_start) <= j) lo = mid; else hi = mid - 1;
     }
     e = lo;
   }
@@ -165,23 +183,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   bf16x8 kreg[PP], vreg[PP];
   const uint32_t lane_off = (uint32_t)((lrow * D + lchunk * 8) * sizeof(bf16));
+  // Tile rows of this thread: lrow + RPP * pp.  Per page: the tile's rows
+  // are consecutive rows of its page (address in SGPRs plus the lane's
+  // constant offset; a page's last tile reads up to the token stride, a
+  // multiple of 64).  Packed: a full tile inside one page (most tiles) loads
+  // the same way.  Otherwise the entries the tile spans
+  // are walked with scalar loads, one segment of consecutive tile rows per
+  // entry, and each row's byte offset from the pool comes from its segment;
+  // rows past the last token read row 0 of the tile (their V rows are zeroed
+  // and their scores masked).
   auto load_tile = [&](int t) -> int {
-    while (t >= tab[e].tile_start + ((tab[e].len + BN - 1) / BN)) ++e;
-    const int row0 = (t - tab[e].tile_start) * BN;
-    const int nvalid = min(BN, tab[e].len - row0);
-    const char* base = p.pool + (int64_t)tab[e].phys * g.page_bytes + (head_off + (int64_t)row0 * D) * (int64_t)sizeof(bf16);
-    const char* kt = base + g.k_off;
-    const char* vt = base + g.v_off;
+    if constexpr (!PACKED) {
+      while (t >= tab[e].tile_start + ((tab[e].len + BN - 1) / BN)) ++e;
+      const int row0 = (t - tab[e].tile_start) * BN;
+      const int nvalid = min(BN, tab[e].len - row0);
+      const char* base =
+          p.pool + (int64_t)tab[e].phys * g.page_bytes + (head_off + (int64_t)row0 * D) * (int64_t)sizeof(bf16);
+      const char* kt = base + g.k_off;
+      const char* vt = base + g.v_off;
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp) {
+        kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * RPP * D * sizeof(bf16));
+        vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * RPP * D * sizeof(bf16));
+      }
+      return nvalid;
+    }
+    const int j0 = t * BN;
+    while (e + 1 < p.n_entries && tab[e + 1].tok_start <= j0) ++e;
+    const int nvalid = min(BN, total_tokens - j0);
+    if (tab[e].tok_start + tab[e].len - j0 >= BN) {
+      const char* base = p.pool + (int64_t)tab[e].phys * g.page_bytes +
+                         (head_off + (int64_t)(j0 - tab[e].tok_start) * D) * (int64_t)sizeof(bf16);
+      const char* kt = base + g.k_off;
+      const char* vt = base + g.v_off;
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp) {
+        kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * RPP * D * sizeof(bf16));
+        vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * RPP * D * sizeof(bf16));
+      }
+      return nvalid;
+    }
+    int64_t off[PP];
+    int es = e, seg_start = 0, page_row = j0 - tab[e].tok_start;
+    for (int it = 0; it < BN; ++it) {  // each segment holds at least one row
+      const int seg_end = min(nvalid, seg_start + tab[es].len - page_row);
+      // row r of this segment is page row page_row + (r - seg_start)
+      const int64_t base = (int64_t)tab[es].phys * g.page_bytes +
+                           (head_off + (int64_t)(page_row - seg_start) * D) * (int64_t)sizeof(bf16);
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp) {
+        const int r = lrow + RPP * pp;
+        if (es == e || (r >= seg_start && r < seg_end))
+          off[pp] = base + (int64_t)(r < nvalid ? r : seg_start) * (D * sizeof(bf16));
+      }
+      if (seg_end >= nvalid || es + 1 >= p.n_entries) break;
+      seg_start = seg_end;
+      page_row = 0;
+      do {
+        ++es;
+      } while (tab[es].len == 0 && es + 1 < p.n_entries);  // the next entry with tokens
+    }
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * RPP * D * sizeof(bf16));
-      vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * RPP * D * sizeof(bf16));
+      const char* row = p.pool + off[pp] + lchunk * 8 * sizeof(bf16);
+      kreg[pp] = *reinterpret_cast<const bf16x8*>(row + g.k_off);
+      vreg[pp] = *reinterpret_cast<const bf16x8*>(row + g.v_off);
     }
     return nvalid;
   };
   auto stage = [&](int b, int nvalid) {
     if (nvalid < BN) {
-      // keys past the page's length: zero V rows (their probabilities are 0)
+      // keys past the last token: zero V rows (their probabilities are 0)
 #pragma unroll
       for (int pp = 0; pp < PP; ++pp)
         if (lrow + RPP * pp >= nvalid) vreg[pp] = bf16x8{};
@@ -483,7 +555,10 @@ hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hi
   }
   const int qtiles = (p.n_q + BM - 1) / BM;
   const int64_t nwg = (int64_t)qtiles * g.heads * p.splits;
-  attend_bf16_kernel<<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
+  if (p.packed)
+    attend_bf16_kernel<true><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
+  else
+    attend_bf16_kernel<false><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
   err = hipGetLastError();
   if (err == hipSuccess && ev_stop) err = hipEventRecord(ev_stop, s);
   if (err != hipSuccess || p.splits == 1) return err;

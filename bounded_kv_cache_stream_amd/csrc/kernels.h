@@ -102,12 +102,14 @@ struct AttendParams {
   const char* pool;
   const DevEntry* table;
   int32_t n_entries;
-  int32_t total_tiles;
+  int32_t total_tiles;   // per-page tiles of the shared table
+  int32_t total_tokens;  // tokens of the shared table
   // 0: one table for every head.  Otherwise head h's table starts at
   // table + h * head_stride (n_entries entries, zero-length where the head
   // holds nothing of that page) and entry n_entries of it holds the head's
-  // tile count in tile_start.
+  // per-page tile count in tile_start and token count in tok_start.
   int32_t head_stride;
+  int32_t packed;  // 1: tiles packed over each head's token sequence, 0: tiles per page
   int32_t splits;
   int32_t n_q;
   float scale_log2;  // sm_scale * log2(e)

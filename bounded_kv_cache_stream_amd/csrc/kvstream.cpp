@@ -141,6 +141,7 @@ struct kv_pool {
   char* ws = nullptr;
   bool meta_only = false;
   int32_t splits_override = 0;
+  int32_t tiling = KV_TILING_AUTO;
   std::vector<kvs::LayerPolicy> layers;
   std::vector<int64_t> scored_gen;  // per layer: the table generation its diversity keys belong to (-1: none)
   std::vector<kvs::DevEntry> scratch;  // host staging for table uploads
@@ -821,6 +822,14 @@ kv_status kv_evict(kv_pool_t* pool, int32_t layer, int32_t* n_evicted, void* str
   return ok();
 }
 
+kv_status kv_set_attend_tiling(kv_pool_t* pool, int32_t tiling) {
+  if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
+  if (tiling != KV_TILING_AUTO && tiling != KV_TILING_PAGE && tiling != KV_TILING_PACKED)
+    return fail(KV_ERR_ARG, "tiling %d is none of KV_TILING_AUTO, KV_TILING_PAGE, KV_TILING_PACKED", tiling);
+  pool->tiling = tiling;
+  return ok();
+}
+
 kv_status kv_set_attend_splits(kv_pool_t* pool, int32_t splits) {
   if (!pool) return fail(KV_ERR_ARG, "pool is NULL");
   if (splits < 0 || splits > pool->cfg.max_splits) return fail(KV_ERR_ARG, "splits %d out of 0..max_splits", splits);
@@ -879,18 +888,41 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
     if (per_head || e.len > 0) add(e.page, e.len, e.hlen.empty() ? 0 : 1);
   if (L.transient_pending) add(-1, pool->cfg.page_tokens, 0);
   const int32_t n_entries = (int32_t)ent.size();
-  int32_t min_tiles = tiles;
+  // Tiles per page, or packed over each head's tokens across page ends.
+  // Automatic: packed for per-head tables whose per-page tiles leave more than
+  // 3% of the slots empty.  There the heads hold equal token counts spread
+  // over their pages differently, so per-page tiles give the most fragmented
+  // head the most tiles, and its workgroups set the kernel's time; packed
+  // tiles even the heads out.  A shared table gives every head the same tiles,
+  // and packing only trades the pages' partial tiles for tiles that span page
+  // ends (about even at a budget cache's 340-token pages, a loss at full
+  // 1004-token pages).
+  auto packed_tiles = [](int64_t tokens) { return (int32_t)((tokens + kvs::kTile - 1) / kvs::kTile); };
+  int64_t page_tiles_all = tiles, packed_tiles_all = packed_tiles(toks);
+  int32_t min_page_tiles = tiles, min_packed_tiles = packed_tiles(toks);
   if (per_head) {
-    tiles = 0;
-    min_tiles = INT32_MAX;
+    page_tiles_all = packed_tiles_all = 0;
+    min_page_tiles = min_packed_tiles = INT32_MAX;
     for (int32_t h = 0; h < H; ++h) {
-      int32_t t_h = 0;
-      for (const auto& e : L.table) t_h += (kvs::head_len(e, h) + kvs::kTile - 1) / kvs::kTile;
-      if (L.transient_pending) t_h += (pool->cfg.page_tokens + kvs::kTile - 1) / kvs::kTile;
-      tiles = std::max(tiles, t_h);
-      min_tiles = std::min(min_tiles, t_h);
+      int32_t t_h = 0, tok_h = 0;
+      for (const auto& e : L.table) {
+        const int32_t n = kvs::head_len(e, h);
+        t_h += (n + kvs::kTile - 1) / kvs::kTile;
+        tok_h += n;
+      }
+      if (L.transient_pending) {
+        t_h += (pool->cfg.page_tokens + kvs::kTile - 1) / kvs::kTile;
+        tok_h += pool->cfg.page_tokens;
+      }
+      page_tiles_all += t_h;
+      packed_tiles_all += packed_tiles(tok_h);
+      min_page_tiles = std::min(min_page_tiles, t_h);
+      min_packed_tiles = std::min(min_packed_tiles, packed_tiles(tok_h));
     }
   }
+  const bool packed = pool->tiling == KV_TILING_AUTO ? per_head && packed_tiles_all * 103 < page_tiles_all * 100
+                                                      : pool->tiling == KV_TILING_PACKED;
+  const int32_t min_tiles = packed ? min_packed_tiles : min_page_tiles;
   if (n_entries == 0 || min_tiles == 0) return fail(KV_ERR_STATE, "layer %d holds no token to attend to", layer);
 
   const bool bf16 = pool->cfg.dtype == KV_BF16;
@@ -949,6 +981,8 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
   ap.table = dt;
   ap.n_entries = n_entries;
   ap.total_tiles = tiles;
+  ap.total_tokens = toks;
+  ap.packed = packed ? 1 : 0;
   ap.head_stride = per_head ? n_entries + 1 : 0;
   ap.splits = splits;
   ap.n_q = n_q;

@@ -26,7 +26,7 @@ EXPORTED = (
     "kv_pool_required_bytes", "kv_pool_get_layout", "kv_pool_create", "kv_pool_destroy", "kv_reset",
     "kv_append_frame", "kv_append_frame_layers", "kv_evict", "stream_attend", "stream_attend_scratch",
     "kv_append_attend", "score_and_compact",
-    "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_merge_pages", "kv_merge_pages_layers",
+    "kv_get_info", "kv_get_page_table", "kv_set_attend_splits", "kv_set_attend_tiling", "kv_merge_pages", "kv_merge_pages_layers",
     "kv_diversity_score",
     "kv_diversity_score_layers", "kv_layer_budgets", "kv_diversity_prune", "kv_diversity_prune_layers",
     "kv_get_head_lengths", "kv_sync", "kv_attend_timing", "kv_attend_timing_read", "kv_last_error",
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "kv_get_info": [P, I32, ctypes.POINTER(kv_cache_info)],
             "kv_get_page_table": [P, I32, P, P, P, I32, ctypes.POINTER(I32)],
             "kv_set_attend_splits": [P, I32],
+            "kv_set_attend_tiling": [P, I32],
             "kv_merge_pages": [P, I32, ctypes.POINTER(I32), P],
             "kv_merge_pages_layers": [P, I32, I32, ctypes.POINTER(I32), P],
             "kv_diversity_score": [P, I32, P, I64, ctypes.POINTER(ctypes.c_double), P],
@@ -300,6 +301,13 @@ def kv_set_attend_splits(pool, splits: int) -> None:
     _check(lib().kv_set_attend_splits(pool, splits))
 
 
+KV_TILING_AUTO, KV_TILING_PAGE, KV_TILING_PACKED = 0, 1, 2
+
+
+def kv_set_attend_tiling(pool, tiling: int) -> None:
+    _check(lib().kv_set_attend_tiling(pool, tiling))
+
+
 class KVCache:
     """A pool with its device buffers allocated by PyTorch (``device=None``: metadata only)."""
 
@@ -495,6 +503,10 @@ class KVCache:
 
     def set_splits(self, splits):
         kv_set_attend_splits(self.handle, splits)
+
+    def set_tiling(self, tiling):
+        """KV_TILING_AUTO, KV_TILING_PAGE or KV_TILING_PACKED (the bf16 attention's KV tiles)."""
+        kv_set_attend_tiling(self.handle, tiling)
 
     # -- reading pages back (tests) -------------------------------------------
     def page_view(self, layer, page_id):

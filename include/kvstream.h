@@ -420,6 +420,19 @@ kv_status kv_get_page_table(const kv_pool_t* pool, int32_t layer, int32_t* page_
  * number to use, capped by max_splits, the token tiles and the workspace. */
 kv_status kv_set_attend_splits(kv_pool_t* pool, int32_t splits);
 
+/* KV tiles of the bf16 attention: KV_TILING_AUTO (default: packed for a
+ * diversity-pruned layer, whose heads hold their tokens in different pages,
+ * where tiles per page would leave more than 3% of the tile slots empty;
+ * else per page), KV_TILING_PAGE (64-token tiles within each page, a page's
+ * last tile partial) or KV_TILING_PACKED (64-token tiles over each head's
+ * token sequence, across page ends).  The tiling partitions
+ * the same sum: results agree up to fp32 reassociation.  KV_ERR_ARG for
+ * another value. */
+#define KV_TILING_AUTO 0
+#define KV_TILING_PAGE 1
+#define KV_TILING_PACKED 2
+kv_status kv_set_attend_tiling(kv_pool_t* pool, int32_t tiling);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);
 

@@ -190,12 +190,15 @@ def test_budget_stream_small_ragged_pages(merge):
             host[l][t] = (k.cpu(), v.cpu())
             cache.append(l, t, k, v)
             sims[l].append(t)
-            out = cache.attend(l, q, 1.0)
             ids = sims[l].all_ids()
             K = attention.gather_tokens(lambda f: host[l][f][0].float().numpy(), ids, T).astype(np.float64)
             V = attention.gather_tokens(lambda f: host[l][f][1].float().numpy(), ids, T).astype(np.float64)
             ref, _ = attention.attend(to64(q), K, V, 1.0)
-            assert_close(to64(out), ref, bf16=True, what=f"frame {t} layer {l}")
+            # tiles per page and tiles packed across the ragged pages' ends, then the automatic choice
+            for tiling in (kv.KV_TILING_PAGE, kv.KV_TILING_PACKED, kv.KV_TILING_AUTO):
+                cache.set_tiling(tiling)
+                out = cache.attend(l, q, 1.0)
+                assert_close(to64(out), ref, bf16=True, what=f"frame {t} layer {l} tiling {tiling}")
             keep = torch.empty(B, dtype=torch.int32, device="cuda")
             n_win = min(5, l + 1)
             ranks = torch.empty((n_win, len(ids)), dtype=torch.int32, device="cuda")

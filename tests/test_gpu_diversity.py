@@ -101,7 +101,13 @@ class Stream:
                     assert torch.equal(v[h, :n].cpu().view(bits), ev.view(bits)), f"{what}: V page {pid} head {h}"
 
     def check_attention(self, q, tau, what):
-        out = self.cache.attend(self.layer, q, tau)
+        # every KV tiling of the per-head tables (the automatic choice, tiles per page, tiles packed across
+        # page ends) against the same oracle
+        outs = []
+        for tiling in (kv.KV_TILING_AUTO, kv.KV_TILING_PAGE, kv.KV_TILING_PACKED):
+            self.cache.set_tiling(tiling)
+            outs.append((tiling, self.cache.attend(self.layer, q, tau)))
+        self.cache.set_tiling(kv.KV_TILING_AUTO)
         ref = np.empty(tuple(q.shape), dtype=np.float64)
         q64 = to64(q)
         for h in range(self.H):
@@ -109,7 +115,8 @@ class Stream:
             K = attention.gather_tokens(lambda f: self.frames[f][0][:, h:h + 1].double().numpy(), ids, self.T)
             V = attention.gather_tokens(lambda f: self.frames[f][1][:, h:h + 1].double().numpy(), ids, self.T)
             ref[:, h:h + 1], _ = attention.attend(q64[:, h:h + 1], K, V, tau)
-        assert_close(to64(out), ref, bf16=self.dt == self.torch.bfloat16, what=what)
+        for tiling, out in outs:
+            assert_close(to64(out), ref, bf16=self.dt == self.torch.bfloat16, what=f"{what} (tiling {tiling})")
 
 
 @pytest.mark.parametrize("dname", ["bf16", "fp32"])

@@ -385,6 +385,17 @@ def test_clces_flags_and_sync_on_a_metadata_pool():
     assert c.page_table(0)[1] == [16] * 3
 
 
+def test_attend_tiling_values():
+    # the three tilings are accepted, anything else refused
+    c = _meta_pool(0, 0, 1, 5)
+    for tiling in (kv.KV_TILING_AUTO, kv.KV_TILING_PAGE, kv.KV_TILING_PACKED):
+        kv.kv_set_attend_tiling(c.handle, tiling)
+    for bad in (-1, 3):
+        with pytest.raises(kv.KVError) as e:
+            kv.kv_set_attend_tiling(c.handle, bad)
+        assert e.value.status == kv.KV_ERR_ARG
+
+
 def test_attend_timing_arguments_on_a_metadata_pool():
     # timing off (0 calls) needs no device; bad counts and NULL pools are refused
     c = _meta_pool(0, 0, 1, 5)
