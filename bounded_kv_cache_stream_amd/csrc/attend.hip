@@ -180,6 +180,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
   const int64_t head_off = (int64_t)h * g.ts * D;
+  const int64_t head_off_bytes = head_off * (int64_t)sizeof(bf16);
+  // Packed: entry e's first token and end, and the address of its head's
+  // first row, with the same for the next entry that holds tokens (len 0:
+  // none), kept in SGPRs and reloaded only when the walk enters the next
+  // entry (once per page, not per tile)
+  int e_tok = 0, e_end = 0, n_len = 0;
+  const char* e_rows = nullptr;
+  const char* n_rows = nullptr;
+  auto enter = [&]() {
+    e_tok = tab[e].tok_start;
+    e_end = e_tok + tab[e].len;
+    e_rows = p.pool + (int64_t)tab[e].phys * g.page_bytes + head_off_bytes;
+    int e2 = e + 1;
+    while (e2 < p.n_entries && tab[e2].len == 0) ++e2;
+    n_len = e2 < p.n_entries ? tab[e2].len : 0;
+    n_rows = e2 < p.n_entries ? p.pool + (int64_t)tab[e2].phys * g.page_bytes + head_off_bytes : e_rows;
+  };
+  if constexpr (PACKED) enter();
 
   bf16x8 kreg[PP], vreg[PP];
   const uint32_t lane_off = (uint32_t)((lrow * D + lchunk * 8) * sizeof(bf16));
@@ -209,17 +227,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return nvalid;
     }
     const int j0 = t * BN;
-    while (e + 1 < p.n_entries && tab[e + 1].tok_start <= j0) ++e;
+    // the entry holding token j0: entries are consecutive token ranges, and
+    // empty ones end where they start
+    while (j0 >= e_end && e + 1 < p.n_entries) {
+      ++e;
+      enter();
+    }
     const int nvalid = min(BN, total_tokens - j0);
-    if (tab[e].tok_start + tab[e].len - j0 >= BN) {
-      const char* base = p.pool + (int64_t)tab[e].phys * g.page_bytes +
-                         (head_off + (int64_t)(j0 - tab[e].tok_start) * D) * (int64_t)sizeof(bf16);
+    if (e_end - j0 >= BN) {
+      const char* base = e_rows + (int64_t)(j0 - e_tok) * D * (int64_t)sizeof(bf16);
       const char* kt = base + g.k_off;
       const char* vt = base + g.v_off;
 #pragma unroll
       for (int pp = 0; pp < PP; ++pp) {
         kreg[pp] = *reinterpret_cast<const bf16x8*>(kt + lane_off + pp * RPP * D * sizeof(bf16));
         vreg[pp] = *reinterpret_cast<const bf16x8*>(vt + lane_off + pp * RPP * D * sizeof(bf16));
+      }
+      return nvalid;
+    }
+    if (e_end - j0 + n_len >= nvalid) {
+      // two pages: tile rows r < b1 are entry e's, the rest the next
+      // entry's first rows; rows past the last token read row 0
+      const int b1 = e_end - j0;
+      const char* base_a = e_rows + (int64_t)(j0 - e_tok) * D * (int64_t)sizeof(bf16);
+      const char* base_b = n_rows - (int64_t)b1 * D * (int64_t)sizeof(bf16);
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp) {
+        const int r0 = lrow + RPP * pp;
+        const int r = r0 < nvalid ? r0 : 0;
+        const char* row = (r < b1 ? base_a : base_b) + (uint32_t)(r * D * sizeof(bf16) + lchunk * 8 * sizeof(bf16));
+        kreg[pp] = *reinterpret_cast<const bf16x8*>(row + g.k_off);
+        vreg[pp] = *reinterpret_cast<const bf16x8*>(row + g.v_off);
       }
       return nvalid;
     }
