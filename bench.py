@@ -228,6 +228,7 @@ def run_clces(args):
     keep = torch.empty(K, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     times = []
+    returns = []
     moved = 0
     if args.defer:
         # deferred steps back to back on the stream: the 24 calls' stream time over 24 (events), then the
@@ -251,7 +252,10 @@ def run_clces(args):
             t0 = time.perf_counter()
             cache.score_and_compact(l, table, w["clces_window"], w["lam"], K, keep_ids=keep,
                                     reuse_ranks=args.reuse_ranks)
-            times.append(time.perf_counter() - t0)  # the call synchronises once (new page lengths)
+            t1 = time.perf_counter()  # the call returns once the new page lengths are known
+            torch.cuda.synchronize()  # the rows have moved
+            times.append(time.perf_counter() - t0)
+            returns.append(t1 - t0)
             kept = set(keep.cpu().numpy().tolist())
             moved += moved_tokens([[(t * T + j) in kept for j in range(T)] for t in range(F)])
     calib_copy(args.calib_copy_mib, dev)
@@ -269,7 +273,9 @@ def run_clces(args):
         "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": L, "dtype": "fp64 score / bf16 pages",
         "data": "synthetic (seeded chi-square raw scores, iid N(0,1) K/V)",
         "config": {"workload": w["name"], "layers": L, "tokens": N, "keep": K, "window": w["clces_window"]},
-        "p90_us": times[int(0.9 * (L - 1))] * 1e6, "moved_tokens_per_layer": moved / L,
+        "p90_us": times[int(0.9 * (L - 1))] * 1e6,
+        "call_return_us": sorted(returns)[L // 2] * 1e6 if returns else None,
+        "moved_tokens_per_layer": moved / L,
         "compaction_bytes_per_layer": bytes_per_layer,
         "rooflines_recorded": clces_rooflines(N, w["clces_window"], bytes_per_layer), "cpu_baseline": cpu,
     }), flush=True)

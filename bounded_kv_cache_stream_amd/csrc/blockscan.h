@@ -8,22 +8,31 @@
 namespace kvs {
 
 // Exclusive scan of one value per thread over a workgroup of NT threads
-// (lds: NT ints); *total, if given, receives the sum.  Every thread calls it.
+// (NT a multiple of 64; lds: at least NT / 64 ints); *total, if given,
+// receives the sum.  Every thread calls it.  Each wave scans its lanes with
+// shuffles, then the waves' sums go through LDS (two barriers in all).
 template <int NT>
 __device__ int32_t block_excl_scan(int32_t v, int32_t* lds, int32_t* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int32_t t = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += t;
-    __syncthreads();
+  static_assert(NT % 64 == 0, "whole waves");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
   }
-  const int32_t incl = lds[tid];
-  if (total) *total = lds[NT - 1];
+  if (lane == 63) lds[wave] = incl;
   __syncthreads();
-  return incl - v;
+  int32_t before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int32_t s = lds[w];
+    before += w < wave ? s : 0;
+    sum += s;
+  }
+  if (total) *total = sum;
+  __syncthreads();  // lds may be rewritten by the next call
+  return before + incl - v;
 }
 
 // Add one to cnt[d] for every active lane with `valid`, aggregating lanes of

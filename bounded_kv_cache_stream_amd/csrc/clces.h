@@ -68,7 +68,15 @@ struct ClcesArgs {
   int32_t n_rank;      // slots with rank_new set
   bool rank_radix;     // rank by the radix passes whatever the size
   double* s_hat_out;   // optional float64 [N]
+  // optional: one word per page in host-visible memory (device address),
+  // written by the index step as soon as the page's new length is known, so
+  // that a waiting host can go on while the rows still move:
+  // (slot_seq << 32) | new length, or (slot_seq << 32) | kSlotError | flag
+  unsigned long long* host_slots;
+  uint32_t slot_seq;
 };
+
+constexpr uint32_t kSlotError = 0x80000000u;
 
 // Stable ascending rank of every key within each of `segments` segments of N
 // keys (keys: [segments][N]) as count slices whose sum is the rank: the blocks

@@ -32,7 +32,9 @@
 //   index    per page: its kept count and offsets (from all pages' counts),
 //            the kept token ids in slot order, and the moves: with
 //            n kept, kept slots below n stay and the dropped slots below n
-//            take the kept slots at or past n (both ascending);
+//            take the kept slots at or past n (both ascending); a waiting
+//            host may take each page's new length from a word in mapped host
+//            memory that this step writes;
 //   compact  per page: one workgroup per K head, one per V head and one for
 //            the token ids; sources (>= n) and destinations (< n) are
 //            disjoint, so every row moves independently.
@@ -742,7 +744,14 @@ struct CompactArgs {
   int32_t* keep_ids_out;
   const int32_t* flag;
   int32_t* flag_rw;
+  unsigned long long* host_slots;
+  uint32_t slot_seq;
 };
+
+// The page's word in the host slots, if the caller asked for them.
+__device__ inline void publish_slot(const CompactArgs& a, int e, uint32_t v) {
+  if (a.host_slots) a.host_slots[e] = ((unsigned long long)a.slot_seq << 32) | v;
+}
 
 // Per page: which slots are kept (ties at the threshold in index order, from
 // the plan step's tie rank base), the kept token ids in slot order, and the
@@ -751,7 +760,10 @@ struct CompactArgs {
 // n (ascending).  Sources and destinations are disjoint, so the moves can run
 // in any order.
 __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
-  if (*a.flag) return;
+  if (const int32_t f = *a.flag) {
+    if (threadIdx.x == 0) publish_slot(a, blockIdx.x, kSlotError | (uint32_t)f);
+    return;
+  }
   __shared__ int32_t scan[kThreads];
   __shared__ uint16_t kept[kMaxPageTokensScored];
   const int e = blockIdx.x, tid = threadIdx.x;
@@ -775,41 +787,49 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
   const int32_t nl = a.n_gt[e] + (int32_t)(eq_take < 0 ? 0 : (eq_take > a.n_eq[e] ? a.n_eq[e] : eq_take));
   const int32_t keep_base = gt_tot + (int32_t)(k_rem < eq_tot ? (k_rem < 0 ? 0 : k_rem) : eq_tot);
   if (tid == 0) a.new_len[e] = nl;
+  // thread t takes the per consecutive slots from b = t * per; its keys are
+  // read once, into bit masks (bit q: slot b + q; per <= 32)
   const int per = (len + kThreads - 1) / kThreads;
-  const int b = tid * per, end = min(b + per, len);
+  const int b = tid * per, cnt = max(0, min(per, len - b));
   const unsigned long long* sh = a.shat + en.tok_start;
-  int32_t n_eq = 0;
-  for (int j = b; j < end; ++j) n_eq += (sh[j] & st.mask) == st.prefix;
-  const int32_t eq_start = eq_tot + block_excl_scan<kThreads>(n_eq, scan, nullptr);
-  int32_t eq_rank = eq_start;
-  int32_t n_keep = 0, n_hole = 0;
-  for (int j = b; j < end; ++j) {
-    const unsigned long long k = sh[j] & st.mask;
-    bool keep = k > st.prefix;
-    if (k == st.prefix) keep = eq_rank++ < st.k_rem;
-    n_keep += keep;
-    n_hole += !keep && j < nl;
+  uint32_t gtm = 0, eqm = 0;
+  for (int q = 0; q < cnt; ++q) {
+    const unsigned long long k = sh[b + q] & st.mask;
+    gtm |= (uint32_t)(k > st.prefix) << q;
+    eqm |= (uint32_t)(k == st.prefix) << q;
   }
+  const int32_t n_eq = __popc(eqm);
+  const int32_t eq_start = eq_tot + block_excl_scan<kThreads>(n_eq, scan, nullptr);
+  // keys equal to the threshold are kept in index order while fewer than
+  // k_rem precede them: this thread keeps its first n_take
+  const long long take = k_rem - eq_start;
+  const int n_take = take <= 0 ? 0 : (take >= n_eq ? n_eq : (int)take);
+  uint32_t keepm = gtm, rest = eqm;
+  for (int i = 0; i < n_take; ++i) {
+    const uint32_t low = rest & (0u - rest);
+    keepm |= low;
+    rest ^= low;
+  }
+  const uint32_t validm = cnt >= 32 ? 0xffffffffu : (1u << cnt) - 1u;
+  const int below = max(0, min(cnt, nl - b));  // slots of this thread below nl
+  const uint32_t holem = ~keepm & validm & (below >= 32 ? 0xffffffffu : (1u << below) - 1u);
   int32_t kept_total = 0, holes = 0;
-  int32_t pos = block_excl_scan<kThreads>(n_keep, scan, &kept_total);
-  int32_t hpos = block_excl_scan<kThreads>(n_hole, scan, &holes);
+  int32_t pos = block_excl_scan<kThreads>(__popc(keepm), scan, &kept_total);
+  int32_t hpos = block_excl_scan<kThreads>(__popc(holem), scan, &holes);
   if (kept_total != nl) {  // cannot happen when the plan and this pass agree; never move on a mismatch
     if (tid == 0) {
       atomicOr(a.flag_rw, kClcesErrCount);
       a.n_moves[e] = 0;
+      publish_slot(a, e, kSlotError | (uint32_t)kClcesErrCount);
     }
     return;
   }
   uint16_t* dst = a.move_dst + (int64_t)e * a.g.ts;
-  eq_rank = eq_start;
-  for (int j = b; j < end; ++j) {
-    const unsigned long long k = sh[j] & st.mask;
-    bool keep = k > st.prefix;
-    if (k == st.prefix) keep = eq_rank++ < st.k_rem;
-    if (keep)
-      kept[pos++] = (uint16_t)j;
-    else if (j < nl)
-      dst[hpos++] = (uint16_t)j;
+  for (int q = 0; q < cnt; ++q) {
+    if ((keepm >> q) & 1u)
+      kept[pos++] = (uint16_t)(b + q);
+    else if ((holem >> q) & 1u)
+      dst[hpos++] = (uint16_t)(b + q);
   }
   __syncthreads();
   // fillers: the kept slots at or past nl are the last `holes` entries of the kept list
@@ -819,7 +839,10 @@ __global__ __launch_bounds__(kThreads) void index_kernel(CompactArgs a) {
     const int32_t* ids = reinterpret_cast<const int32_t*>(a.pool + (int64_t)en.phys * a.g.page_bytes + a.g.id_off);
     for (int i = tid; i < nl; i += kThreads) a.keep_ids_out[keep_base + i] = ids[kept[i]];
   }
-  if (tid == 0) a.n_moves[e] = holes;
+  if (tid == 0) {
+    a.n_moves[e] = holes;
+    publish_slot(a, e, (uint32_t)nl);
+  }
 }
 
 
@@ -1021,7 +1044,7 @@ hipError_t enqueue_clces(const ClcesArgs& a, hipStream_t s) {
                  reinterpret_cast<uint16_t*>(ws + z.move_dst),
                  reinterpret_cast<int32_t*>(ws + z.n_moves),
                  shat, sel_state + kSelPasses, counts, counts + P, flag + 1, P, a.pool, a.geom, a.keep_ids_out, flag,
-                 flag};
+                 flag, a.host_slots, a.slot_seq};
   index_kernel<<<dim3((unsigned)P), dim3(kThreads), 0, s>>>(ca);
   dim3 cg((unsigned)P, (unsigned)(2 * a.geom.heads + 1));
   const bool many = (int64_t)(N - a.keep) * 10 > (int64_t)N;  // more than 10% of the tokens drop

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cstdarg>
 #include <cmath>
@@ -166,6 +167,12 @@ struct kv_pool {
   };
   std::vector<Pending> pending;
   int32_t* pinned = nullptr;
+  // synchronous score_and_compact: one word per page in mapped, coherent
+  // pinned memory (allocated at the first such step), written by the index
+  // step with the call's sequence number and the page's new length
+  uint64_t* slots = nullptr;
+  unsigned long long* slots_dev = nullptr;
+  uint32_t slot_seq = 0;
   // CLCES rank history: per slot of the rank-cache region, which score-table
   // column it ranks and over which candidate sequence (score table, its rows,
   // the candidate frames of a layer never compacted, merged or pruned)
@@ -211,6 +218,47 @@ hipError_t clces_pinned(kv_pool_t* p) {
   return hipHostMalloc(reinterpret_cast<void**>(&p->pinned),
                        sizeof(int32_t) * (size_t)p->cfg.num_layers * ((size_t)p->cfg.pages_per_layer + 1),
                        hipHostMallocDefault);
+}
+
+// The page words of synchronous score_and_compact steps.
+hipError_t clces_slots(kv_pool_t* p) {
+  const size_t bytes = sizeof(uint64_t) * (size_t)p->cfg.pages_per_layer;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&p->slots), bytes, hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess) {
+    p->slots = nullptr;
+    return e;
+  }
+  std::memset(p->slots, 0, bytes);
+  e = hipHostGetDevicePointer(reinterpret_cast<void**>(&p->slots_dev), p->slots, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(p->slots);
+    p->slots = nullptr;
+  }
+  return e;
+}
+
+// Waits until the index step of the current synchronous step has written the
+// words of all n pages (the kernels that move the rows may still run; later
+// work on the stream is ordered after them).  Polls the words for kPollUs,
+// then waits for the stream; *complete tells whether every word arrived.
+hipError_t wait_slots(kv_pool_t* p, hipStream_t st, int32_t n, bool* complete) {
+  const volatile uint64_t* w = p->slots;
+  const uint64_t seq = p->slot_seq;
+  int32_t i = 0;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    while (i < n && (w[i] >> 32) == seq) ++i;
+    if (i == n) break;
+    if (std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count() > kPollUs) {
+      const hipError_t e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return e;
+      while (i < n && (w[i] >> 32) == seq) ++i;
+      break;
+    }
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  *complete = i == n;
+  return hipSuccess;
 }
 
 // Completes the layer's deferred score_and_compact, if one is pending: waits
@@ -661,6 +709,7 @@ kv_status kv_pool_destroy(kv_pool_t* pool) {
   for (auto& ps : pool->pending)
     if (ps.done) (void)hipEventDestroy(ps.done);
   if (pool->pinned) (void)hipHostFree(pool->pinned);
+  if (pool->slots) (void)hipHostFree(pool->slots);
   if (pool->div_staged) (void)hipEventDestroy(pool->div_staged);
   if (pool->wait_ev) (void)hipEventDestroy(pool->wait_ev);
   if (pool->div_pinned) (void)hipHostFree(pool->div_pinned);
@@ -1218,19 +1267,26 @@ kv_status score_and_compact(kv_pool_t* pool, int32_t layer, const float* score_t
   std::vector<int32_t> new_lens((size_t)a.n_entries);
   int32_t err_flag = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = pool->pinned ? hipSuccess : clces_pinned(pool);
+  // the index step writes each page's new length (or the error flag) into
+  // the pool's page words as soon as it is known; the host waits for those
+  // words only, while the rows move
+  hipError_t e = pool->slots ? hipSuccess : clces_slots(pool);
+  if (++pool->slot_seq == 0) pool->slot_seq = 1;
+  a.host_slots = pool->slots_dev;
+  a.slot_seq = pool->slot_seq;
   if (e == hipSuccess) e = kvs::enqueue_clces(a, st);
   if (e == hipSuccess) e = copy_ranks(st);
-  // one read-back into the layer's pinned slot: the error flag and, after
-  // it, the new page lengths
-  const int32_t* rb = pool->pinned + (size_t)layer * ((size_t)pool->cfg.pages_per_layer + 1);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(const_cast<int32_t*>(rb), kvs::clces_result(a), sizeof(int32_t) * ((size_t)a.n_entries + 1),
-                       hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = wait_stream(pool, st);
+  bool complete = false;
+  if (e == hipSuccess) e = wait_slots(pool, st, a.n_entries, &complete);
   if (e != hipSuccess) return hip_fail(e, "CLCES step");
-  err_flag = rb[0];
-  std::copy(rb + 1, rb + 1 + a.n_entries, new_lens.begin());
+  if (!complete) return fail(KV_ERR_HIP, "layer %d: the CLCES step did not report every page's length", layer);
+  for (int32_t i = 0; i < a.n_entries; ++i) {
+    const uint32_t v = (uint32_t)(pool->slots[i] & 0xffffffffu);
+    if (v & kvs::kSlotError)
+      err_flag |= (int32_t)(v & ~kvs::kSlotError);
+    else
+      new_lens[(size_t)i] = (int32_t)v;
+  }
   if (err_flag & kvs::kClcesErrNan) return fail(KV_ERR_NAN, "layer %d: a raw score is NaN or negative", layer);
   if (err_flag & kvs::kClcesErrRow) return fail(KV_ERR_ARG, "layer %d: a token id is >= score_rows", layer);
   if (err_flag) return fail(KV_ERR_HIP, "layer %d: CLCES consistency check failed (flag %d)", layer, err_flag);

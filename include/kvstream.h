@@ -289,8 +289,11 @@ kv_status kv_append_attend(kv_pool_t* pool, int32_t layer, int64_t frame_idx, co
  * pool with special_tokens > 0 (compaction would move the special tokens out
  * of a frame's first slots).
  * KV_ERR_NAN if a score read is NaN or negative (state unchanged), KV_ERR_ARG
- * for a token id >= score_rows or a bad parameter.  Synchronises the stream
- * once to read the new page lengths.
+ * for a token id >= score_rows or a bad parameter.  Waits for the new page
+ * lengths only: the step writes each page's length into pinned host memory
+ * mapped into the device (allocated by the pool on first use) as soon as it
+ * is known, and the call returns while the rows may still be moving; work
+ * issued later on the same stream (or one ordered after it) sees them moved.
  * With flags = KV_CLCES_DEFER the call returns once the step and the
  * read-back of its page lengths (into pinned host memory the pool allocates
  * on first use) are enqueued, *n_kept = keep_count, and the layer's host table
