@@ -69,9 +69,11 @@ def parse():
     ap.add_argument("--defer", action="store_true",
                     help="budget / clces workloads: score_and_compact returns once enqueued (KV_CLCES_DEFER); the next call "
                          "on the layer applies the new page lengths")
-    ap.add_argument("--reuse-ranks", action="store_true",
+    ap.add_argument("--reuse-ranks", action=argparse.BooleanOptionalAction, default=True,
                     help="clces workload: each step ranks only its own layer and reuses the earlier steps' ranks of "
-                         "the other window layers (KV_CLCES_REUSE_RANKS; every layer holds the same whole frames)")
+                         "the other window layers, the per-frame rank history of StreamCacheVGGT 2.1.4 "
+                         "(KV_CLCES_REUSE_RANKS; every layer holds the same whole frames). Default on; "
+                         "--no-reuse-ranks ranks every window layer in every step")
     ap.add_argument("--fused", action="store_true",
                     help="stream/long/budget workloads: one kv_append_attend call per frame and layer (the page "
                          "write shares the "
@@ -268,40 +270,48 @@ def run_clces(args):
     print(json.dumps({
         "metric": "score_and_compact us per layer (CLCES W=5, lambda=0.5, keep 50%)"
                   + (", deferred: stream time of 24 back-to-back calls / 24" if args.defer else "")
-                  + (", ranks of earlier layers reused" if args.reuse_ranks else ""),
+                  + (", ranks of earlier layers reused" if args.reuse_ranks else ", every window layer ranked"),
         "value": med * 1e6,
         "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": L, "dtype": "fp64 score / bf16 pages",
         "data": "synthetic (seeded chi-square raw scores, iid N(0,1) K/V)",
-        "config": {"workload": w["name"], "layers": L, "tokens": N, "keep": K, "window": w["clces_window"]},
+        "config": {"workload": w["name"], "layers": L, "tokens": N, "keep": K, "window": w["clces_window"],
+                   "reuse_ranks": args.reuse_ranks},
         "p90_us": times[int(0.9 * (L - 1))] * 1e6,
         "call_return_us": sorted(returns)[L // 2] * 1e6 if returns else None,
         "moved_tokens_per_layer": moved / L,
         "compaction_bytes_per_layer": bytes_per_layer,
-        "rooflines_recorded": clces_rooflines(N, w["clces_window"], bytes_per_layer), "cpu_baseline": cpu,
+        "rooflines_recorded": clces_rooflines(N, w["clces_window"], L, bytes_per_layer, args.reuse_ranks),
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
 CLCES_SOURCE = os.path.join(ROOT, "bounded_kv_cache_stream_amd", "csrc", "clces.hip")
-CLCES_KERNELS = os.path.join(ROOT, "profiles", "kernels_clces.json")  # written by profile_bench.py
+# written by profile_bench.py: ranks reused (the default), and every window layer ranked in every step
+CLCES_KERNELS = {True: os.path.join(ROOT, "profiles", "kernels_clces.json"),
+                 False: os.path.join(ROOT, "profiles", "kernels_clces_rerank.json")}
 
 
-def clces_rooflines(N, W, compaction_bytes):
+def clces_rooflines(N, W, L, compaction_bytes, reuse):
     """HBM position of the scoring kernels and of the compaction, from the committed rocprofv3 record of this
     workload (per call: every kernel's mean time x its launches per call), if clces.hip still hashes as
-    recorded; else None.  Algorithmic bytes of the scoring per call (all window layers ranked): gather 12 B
-    per key and layer + 4 B per token (raw score, id, order key; the current score), fuse 12 B per token, two
-    select passes and mark and index 8 B per token each (48 B per token in all), and per key and layer the
-    rank method the record shows: block sort + counts (sort: key read, sorted key, index and block rank
+    recorded; else None.  Algorithmic bytes of the scoring per call: gather 12 B per key and ranked layer
+    + 4 B per token (raw score, id, order key; the current score), fuse 12 B per token, two
+    select passes and mark and index 8 B per token each (48 B per token in all), and per key and ranked layer
+    the rank method the record shows: block sort + counts (sort: key read, sorted key, index and block rank
     written, 16 B; counts: sorted key and index read once, G = min(8, blocks) count slices written, 8 + 4 G B;
-    fuse: 1 + G slices read and the rank written, 4 G + 8 B), N x ((44 + 8 G) W + 48) bytes; or four radix
-    passes of 20 B (counts read, key and value read and written) and the rank read by fuse, 4 B,
-    N x (96 W + 48) bytes."""
+    fuse: 1 + G slices read and the rank written, 4 G + 8 B), 44 + 8 G B; or four radix passes of 20 B (counts
+    read, key and value read and written) and the rank read by fuse, 96 B.  A window layer whose ranks are
+    reused costs fuse one 4 B rank read per key.  Layer l has min(W, l + 1) window layers; with reuse it ranks
+    one of them (its own), else all of them; the bytes are the mean over the L calls.  The record must have
+    been taken in the same mode (its command names --reuse-ranks exactly when reuse is on)."""
     try:
-        with open(CLCES_KERNELS) as f:
+        with open(CLCES_KERNELS[bool(reuse)]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256_16", {}).get("clces.hip") != source_hash(CLCES_SOURCE):
+        return None
+    if any("--reuse-ranks" in c.split() for c in rec.get("commands", [])) != bool(reuse):
         return None
     ks = rec.get("kernels", {})
     calls = next((e["used"] for k, e in ks.items() if k.startswith("prep_kernel")), None)
@@ -317,12 +327,11 @@ def clces_rooflines(N, W, compaction_bytes):
                                              "select_pass_kernel", "select_finish_kernel", "mark_kernel",
                                              "index_kernel")):
             score_us += per_call
-    if any(k.startswith("rank_count_kernel") for k in ks):
-        G = min(8, (N + 2047) // 2048)
-        score_bytes = N * ((44 + 8 * G) * W + 48)
-    else:
-        score_bytes = N * (96 * W + 48)
-    out = {"source": os.path.relpath(CLCES_KERNELS, ROOT)}
+    per_rank = 44 + 8 * min(8, (N + 2047) // 2048) if any(k.startswith("rank_count_kernel") for k in ks) else 96
+    n_win = [min(W, l + 1) for l in range(L)]
+    n_rank = [1 if reuse else n for n in n_win]
+    score_bytes = N * (sum(per_rank * r + 4 * (n - r) for n, r in zip(n_win, n_rank)) / L + 48)
+    out = {"source": os.path.relpath(CLCES_KERNELS[bool(reuse)], ROOT)}
     for name, by, us in (("scoring", score_bytes, score_us), ("compaction", compaction_bytes, compact_us)):
         gbs = by / (us * 1e-6) / 1e9 if us else None
         out[name] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -54,8 +54,11 @@ WORKLOADS = {
     "stream": {"args": ["--no-cpu-baseline"], "trace_steps": 30, "pmc_steps": 10, "pmc": True, "mfma": True},
     "append": {"args": ["--workload", "append", "--no-cpu-baseline"], "trace_steps": 30, "pmc_steps": 10,
                "pmc": True, "mfma": False},
-    "clces": {"args": ["--workload", "clces", "--no-cpu-baseline"], "trace_steps": None, "pmc_steps": None,
+    "clces": {"args": ["--workload", "clces", "--no-cpu-baseline", "--reuse-ranks"], "trace_steps": None, "pmc_steps": None,
               "pmc": False, "mfma": False},
+    # the same calls with every window layer ranked in every step
+    "clces_rerank": {"args": ["--workload", "clces", "--no-cpu-baseline", "--no-reuse-ranks"], "trace_steps": None,
+                     "pmc_steps": None, "pmc": False, "mfma": False},
     # the stacks: every dispatch from the start of the last trace_steps frames (found from a kernel that runs
     # `per_step` times a frame) counts
     "diversity": {"args": ["--workload", "diversity", "--no-cpu-baseline"], "trace_steps": 10, "pmc_steps": None,
