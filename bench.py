@@ -877,8 +877,8 @@ def main():
                                "the call's stream)",
                      "kernel_avg_us": kernel_avg_s * 1e6,
                      "call": "kv_append_attend (page write with the table upload, attend_bf16_kernel, split-KV "
-                             "combine)" if args.fused else "stream_attend (table upload, attend_bf16_kernel, "
-                                                           "split-KV combine)",
+                             "combine)" if args.fused else "stream_attend (attend_bf16_kernel with the page table in its "
+                                                           "arguments, split-KV combine)",
                      "achieved_call": achieved_call, "frac_call": achieved_call / PEAK_BF16_TFLOPS,
                      "avg_call_us": attend_avg_s * 1e6, "flop_per_call": flops,
                      "median_call_us": attend_sorted[len(attend_sorted) // 2] * 1e3,

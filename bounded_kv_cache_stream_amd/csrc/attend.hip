@@ -102,7 +102,8 @@ __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 // PACKED: tiles over each head's token sequence (a tile may span page ends),
 // else tiles per page (a page's last tile is partial).
 template <bool PACKED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(PageGeom g, AttendParams p, int qtiles,
+                                                                                              const TableChunk inl) {
   constexpr int RPP = 32;          // K/V rows staged per pass (8 threads per 128-byte row)
   constexpr int PP = BN / RPP;     // passes per tile
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * LDS_LD];
@@ -141,9 +142,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // The page table is read-only for the kernel's lifetime: read it through the
   // constant address space so that the walk over it runs on scalar loads and
-  // SALU.
+  // SALU.  A short shared table comes in the kernel's own arguments (the
+  // kernarg segment is constant memory too).
   typedef const __attribute__((address_space(4))) DevEntry* ConstTable;
-  const ConstTable tab = (ConstTable)(p.table + (int64_t)h * p.head_stride);
+  const ConstTable tab = p.inline_table ? (ConstTable)&inl.e[0] : (ConstTable)(p.table + (int64_t)h * p.head_stride);
   // Packed: tile t holds tokens 64t .. 64t+63 of the head's token sequence
   // (the entries' tokens in table order) whatever pages they are in, so only
   // the sequence's last tile is partial.  Per page: the tiles of entry e are
@@ -582,7 +584,7 @@ hipError_t attend_scratch_address(char** out) {
 }
 
 hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s, hipEvent_t ev_start,
-                         hipEvent_t ev_stop) {
+                         hipEvent_t ev_stop, const TableChunk* inl) {
   hipError_t err = ev_start ? hipEventRecord(ev_start, s) : hipSuccess;
   if (err != hipSuccess) return err;
   if (!bf16) {
@@ -593,10 +595,13 @@ hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hi
   }
   const int qtiles = (p.n_q + BM - 1) / BM;
   const int64_t nwg = (int64_t)qtiles * g.heads * p.splits;
+  static const TableChunk kNoTable{};
+  if (p.inline_table && (!inl || inl->count != p.n_entries || p.head_stride != 0)) return hipErrorInvalidValue;
+  const TableChunk& tc = p.inline_table ? *inl : kNoTable;
   if (p.packed)
-    attend_bf16_kernel<true><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
+    attend_bf16_kernel<true><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles, tc);
   else
-    attend_bf16_kernel<false><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles);
+    attend_bf16_kernel<false><<<dim3((unsigned)nwg), dim3(256), 0, s>>>(g, p, qtiles, tc);
   err = hipGetLastError();
   if (err == hipSuccess && ev_stop) err = hipEventRecord(ev_stop, s);
   if (err != hipSuccess || p.splits == 1) return err;

@@ -110,6 +110,7 @@ struct AttendParams {
   // per-page tile count in tile_start and token count in tok_start.
   int32_t head_stride;
   int32_t packed;  // 1: tiles packed over each head's token sequence, 0: tiles per page
+  int32_t inline_table;  // 1: the shared table rides in the launch's TableChunk argument, not in table
   int32_t splits;
   int32_t n_q;
   float scale_log2;  // sm_scale * log2(e)
@@ -117,8 +118,12 @@ struct AttendParams {
 
 // ev_start / ev_stop (optional): recorded on s right before and right after
 // the attention kernel (before the split-KV combine).
+// inl (bf16 only, with p.inline_table set): a shared table of at most
+// kUploadChunk entries passed by value in the kernel's arguments, which saves
+// the table-upload launch.
 hipError_t launch_attend(const PageGeom& g, const AttendParams& p, bool bf16, hipStream_t s,
-                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                         const TableChunk* inl = nullptr);
 
 // Device scratch of the allocation-free attention entry point: a file-scope
 // array in attend.hip, one copy per GPU, holding the split-KV partials.

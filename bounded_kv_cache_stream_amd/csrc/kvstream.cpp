@@ -1009,14 +1009,22 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
     part_ml = reinterpret_cast<float*>(base + o_bytes);
   }
   kvs::DevEntry* dt = dev_table(pool, layer);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   // per-head tables are built on the device from the shared one, uploaded after them
   kvs::DevEntry* up = per_head ? dt + (int64_t)H * (pool->lay.layer_pages + 1) : dt;
-  if (write)
+  // a short shared table rides in the attention launch's arguments: no upload launch
+  const bool inline_table = bf16 && !per_head && !write && n_entries <= kvs::kUploadChunk;
+  kvs::TableChunk chunk;
+  if (inline_table) {
+    chunk.first = 0;
+    chunk.count = n_entries;
+    std::copy(ent.begin(), ent.begin() + n_entries, chunk.e);
+  } else if (write) {
     e = kvs::launch_append_table(pool->lay.geom, write->page, write->k, write->v, pool->cfg.page_tokens,
                                  write->first_id, up, ent.data(), n_entries, st);
-  else
+  } else {
     e = kvs::launch_table_upload(up, ent.data(), n_entries, st);
+  }
   if (e == hipSuccess && per_head) e = kvs::launch_head_tables(dt, up, n_entries, hlens_dev(pool), H, st);
   if (e != hipSuccess) return hip_fail(e, write ? "page write and table upload launch" : "table upload launch");
 
@@ -1032,6 +1040,7 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
   ap.total_tiles = tiles;
   ap.total_tokens = toks;
   ap.packed = packed ? 1 : 0;
+  ap.inline_table = inline_table ? 1 : 0;
   ap.head_stride = per_head ? n_entries + 1 : 0;
   ap.splits = splits;
   ap.n_q = n_q;
@@ -1042,7 +1051,7 @@ kv_status attend_launch(kv_pool_t* pool, int32_t layer, const kvs::LayerPolicy& 
     ev1 = pool->timing[pool->timing_used].second;
     ++pool->timing_used;
   }
-  e = kvs::launch_attend(pool->lay.geom, ap, bf16, st, ev0, ev1);
+  e = kvs::launch_attend(pool->lay.geom, ap, bf16, st, ev0, ev1, inline_table ? &chunk : nullptr);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return KV_OK;
 }
