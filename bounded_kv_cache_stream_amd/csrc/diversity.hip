@@ -106,9 +106,6 @@ struct DivK {
 __device__ inline const DevEntry& tab(const DivK& a, int slot, int h, int p) {
   return a.tabs[((int64_t)slot * a.H + h) * (a.p_max + 1) + p];
 }
-__device__ inline int64_t head_count(const DivK& a, int slot, int h) {
-  return tab(a, slot, h, a.layers[slot].P).tok_start;
-}
 // High plane of head h's keys; the low plane follows at + L.N.
 __device__ inline uint32_t* head_keys(const DivK& a, const DivLayer& L, int h) {
   return a.keys + L.keys_off + (int64_t)h * 2 * L.N;
