@@ -246,7 +246,9 @@ kv_status kv_attend_timing_read(kv_pool_t* pool, double* total_ms, int32_t* n_ca
  * results and page contents as those three calls in that order ([FPS]
  * "Page-Aligned Tensor Layout"; [GCT] "Frame-by-Frame Causal Processing").
  * The page write and the upload of the attention's page table are one
- * launch, so a frame costs one launch fewer than the three calls.  n_q may
+ * launch.  (stream_attend alone passes a shared table of up to 192 entries
+ * in the attention kernel's arguments and uploads only longer or per-head
+ * tables, so the fused call saves a launch only for those.)  n_q may
  * exceed n_tokens (the scale phase: the queries of every scale frame with
  * the last one's append).  n_evicted may be NULL.  On any error nothing
  * changes.  Asynchronous on stream. */

@@ -135,6 +135,14 @@ def test_one_token_pages_window_stream():
     _window_stream(1, 2, 1, 3, 2, 14, None, wid=74)
 
 
+def test_shared_table_past_the_inline_limit():
+    # a shared bf16 table rides in the attention kernel's arguments up to 192 entries and is uploaded beyond:
+    # 4-token frames under a 200-frame window grow the table from 1 to 201 entries, crossing 192 at frame 192;
+    # every row of every frame against the oracle
+    _window_stream(4, 2, 1, 200, 1, 205, None, wid=79)
+    say("shared table of up to 201 entries: window stream matches the oracle on both sides of 192")
+
+
 def test_one_token_pages_budget_stream():
     # one-token pages under a 5-token budget: each step empties a page (its id is released) and the cache
     # stays at 5 pages
