@@ -20,13 +20,15 @@ workloads, every call of the CLCES workload), so a stream pass reads the full
 fields of its roofline (only while the kernel sources still hash as
 recorded).
 
-The CLCES workload gets the trace pass only: its FETCH_SIZE pass went silent
-for minutes where every other pass ends in seconds, with no cause found, so no
-counter pass is run on it.  The diversity and token-budget stacks also get the
-trace pass only (the last 10 frames: per kernel the last 10 dispatches, which
-for the per-layer kernels is the last layers of the last frame).
+The CLCES workload gets the trace pass only, with the rank history (clces)
+and with every window layer ranked in every step (clces_rerank): its
+FETCH_SIZE pass went silent for minutes where every other pass ends in
+seconds, with no cause found, so no counter pass is run on it.  The diversity
+and token-budget stacks also get the trace pass only, over every dispatch of
+their last 10 frames (found from a kernel that runs a fixed number of times
+per frame).
 
-    python profile_bench.py [--workloads stream,append,clces,diversity,budget] [--out gpurun_out/prof]
+    python profile_bench.py [--workloads stream,append,clces,clces_rerank,diversity,budget] [--out gpurun_out/prof]
     python profile_bench.py --parse-only ...    # rebuild the summaries from existing output
 """
 
